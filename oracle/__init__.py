@@ -1,0 +1,23 @@
+"""CPU oracle for Compressed Sparse Attention (CSA) and its HCA variant.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the GPU library imports, links or runs
+this package; only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with the HIP
+kernels.  See ``csa_oracle.py`` for the definitions and their sources.
+"""
+from .csa_oracle import (  # noqa: F401
+    NEG_INF,
+    attend,
+    csa_reference,
+    e2m1_to_e4m3,
+    e2m1_value,
+    e4m3_value,
+    fp4_dequantize,
+    from_bf16_bits,
+    hca_attend,
+    index_scores,
+    pool,
+    round_to_bf16,
+    topk_select,
+    visible_count,
+)

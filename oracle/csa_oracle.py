@@ -1,0 +1,216 @@
+"""Plain fp64 CPU definition of CSA and HCA.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the CPU-baseline leg of the benchmark
+use this module.  It is deliberately slow and literal: each function is the
+definition written out with NumPy in float64, with a library matmul / sort
+as the only building blocks, no blocking and no reordering.
+
+Source: the technical review "DeepSeek V4 技术解读" (takeshell.com):
+  * §2.1 CSA: the KV entries of every m consecutive tokens are merged into one
+    entry by a weighted aggregation (sequence length becomes n/m); a Lightning
+    Indexer forms indexer queries for each query token, scores them against
+    the compressed entries and keeps the top-k compressed blocks; core
+    attention runs only over those k entries.  V4-Pro parameters: m = 4,
+    64 indexer heads of dimension 128, top-k = 1024.
+  * §2.2 HCA: m' = 128 tokens per entry, then full attention over all
+    compressed entries with no sparse selection.
+  * §5 (FP4 quantisation-aware training): the indexer's QK path runs in FP4
+    E2M1, dequantised to FP8 E4M3 without loss.
+
+Where the pages are silent this module takes these readings (each is used
+below and listed with its reason in the design notes):
+  R1 pooling weights: one logit per raw token; a block's weights are the
+     softmax of its m logits; the same weights pool every channel
+     (core K, core V and the indexer key).
+  R2 one shared KV head (K and V separate) for all query heads, and one
+     shared indexer key per compressed entry.
+  R3 index score s(t, j) = sum_h w[t, h] * max(0, q_I[t, h] . k_I[j]),
+     unscaled.
+  R4 causality: entry j is visible to query position t iff m (j + 1) <= t + 1,
+     so V(t) = min(N, floor((t + 1) / m)); no raw tokens are attended.
+  R5 top-k: rank by (score descending, index ascending), -0.0 equal to +0.0;
+     keep min(k, V(t)) entries; return them in ascending index order padded
+     with -1.  One set per query token, shared by all heads.
+  R6 attention: softmax scale 1/sqrt(D) unless given; an empty set gives
+     output 0 and log-sum-exp -inf.
+  R7 FP4: E2M1 codes (sign, 2 exponent bits with bias 1, 1 mantissa bit),
+     element 2i in the low nibble, one fp32 scale per 32 consecutive
+     elements; the value is code value times scale.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Optional
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+# ------------------------------------------------------------------ number formats
+def from_bf16_bits(bits) -> np.ndarray:
+    """bf16 bit patterns (any integer array) -> float64 values (exact)."""
+    u = np.asarray(bits).astype(np.uint32) & 0xFFFF
+    return (u << 16).view(np.float32).astype(np.float64)
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """Round float64 values to the nearest bf16 value, ties to even (fp64 result).
+
+    bf16 has 8 significant bits and fp32's exponent range; below 2**-126 the
+    spacing is fixed at 2**-133.  Overflow goes to +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros_like(x)
+    fin = np.isfinite(x) & (x != 0)
+    _, e = np.frexp(x[fin])                      # x = f * 2**e, 0.5 <= |f| < 1
+    ulp = np.ldexp(1.0, np.maximum(e - 1, -126) - 7)
+    r = np.rint(x[fin] / ulp) * ulp              # rint: half to even
+    max_bf16 = (2.0 - 2.0 ** -7) * 2.0 ** 127
+    r = np.where(np.abs(r) > max_bf16, np.copysign(np.inf, r), r)
+    out[fin] = r
+    out[~np.isfinite(x)] = x[~np.isfinite(x)]
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    """Value of a 4-bit E2M1 code: 1 sign bit, 2 exponent bits (bias 1), 1 mantissa bit."""
+    sign = -1.0 if (code >> 3) & 1 else 1.0
+    e = (code >> 1) & 3
+    mbit = code & 1
+    mag = 0.5 * mbit if e == 0 else 2.0 ** (e - 1) * (1.0 + 0.5 * mbit)
+    return sign * mag
+
+
+def e4m3_value(byte: int) -> float:
+    """Value of an 8-bit E4M3 byte (OCP FP8: bias 7, S.1111.111 is NaN, no infinities)."""
+    sign = -1.0 if (byte >> 7) & 1 else 1.0
+    e = (byte >> 3) & 15
+    mant = byte & 7
+    if e == 15 and mant == 7:
+        return math.nan
+    if e == 0:
+        mag = (mant / 8.0) * 2.0 ** -6
+    else:
+        mag = (1.0 + mant / 8.0) * 2.0 ** (e - 7)
+    return sign * mag
+
+
+def e2m1_to_e4m3(code: int) -> int:
+    """The E4M3 byte that holds exactly the value of an E2M1 code (same sign).
+
+    Found by searching all 256 E4M3 bytes, so it is the definition itself;
+    §5 of the review says this dequantisation loses nothing.
+    """
+    v = e2m1_value(code)
+    want_sign = (code >> 3) & 1
+    for b in range(256):
+        if (b >> 7) == want_sign and e4m3_value(b) == v:
+            return b
+    raise ValueError(f"E2M1 code {code} has no exact E4M3 encoding")
+
+
+def fp4_dequantize(codes, scales, block: int = 32) -> np.ndarray:
+    """Packed E2M1 codes [..., D/2] and fp32 scales [..., D/block] -> float64 [..., D]."""
+    c = np.asarray(codes, dtype=np.uint8)
+    lo = c & 0xF
+    hi = c >> 4
+    nib = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.uint8)
+    nib[..., 0::2] = lo
+    nib[..., 1::2] = hi
+    table = np.array([e2m1_value(i) for i in range(16)], dtype=np.float64)
+    vals = table[nib]
+    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+    D = vals.shape[-1]
+    return vals * np.repeat(s, block, axis=-1)[..., :D]
+
+
+# ------------------------------------------------------------------ CSA / HCA steps
+def visible_count(t: int, m: int, n_entries: int) -> int:
+    """R4: number of compressed entries query position t may see."""
+    return max(0, min(int(n_entries), (int(t) + 1) // int(m)))
+
+
+def pool(x, z, m: int) -> np.ndarray:
+    """§2.1 / §2.2 compression: entry j = sum_i w_i x[m j + i] with w = softmax(z block) (R1).
+
+    x [n, C] (float64 or convertible), z [n] -> [n // m, C] float64.  Only
+    complete blocks are produced.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    z = np.asarray(z, dtype=np.float64)
+    n_blocks = x.shape[0] // m
+    out = np.zeros((n_blocks, x.shape[1]), dtype=np.float64)
+    for j in range(n_blocks):
+        zb = z[m * j: m * j + m]
+        e = np.exp(zb - zb.max())
+        w = e / e.sum()
+        out[j] = w @ x[m * j: m * j + m]
+    return out
+
+
+def index_scores(q_idx, w_idx, k_idx, visible: int) -> np.ndarray:
+    """§2.1 Lightning Indexer score of one query token against every entry (R3).
+
+    q_idx [H_I, D_I], w_idx [H_I], k_idx [N, D_I] -> s [N] float64 with
+    s[j] = sum_h w[h] max(0, q_idx[h] . k_idx[j]) for j < visible, -inf after.
+    """
+    q = np.asarray(q_idx, dtype=np.float64)
+    w = np.asarray(w_idx, dtype=np.float64)
+    K = np.asarray(k_idx, dtype=np.float64)
+    s = np.full(K.shape[0], NEG_INF)
+    if visible > 0:
+        dots = q @ K[:visible].T                   # [H_I, visible]
+        s[:visible] = w @ np.maximum(dots, 0.0)
+    return s
+
+
+def topk_select(scores, visible: int, k: int) -> np.ndarray:
+    """§2.1 top-k of the visible entries (R5): int64 [k], ascending, -1 padded."""
+    s = np.asarray(scores, dtype=np.float64)[:visible] + 0.0   # -0.0 -> +0.0
+    order = np.lexsort((np.arange(visible), -s))               # key (-s, j)
+    take = np.sort(order[: min(k, visible)])
+    out = np.full(k, -1, dtype=np.int64)
+    out[: take.size] = take
+    return out
+
+
+def attend(q, k_cache, v_cache, selected: Iterable[int], scale: Optional[float] = None):
+    """§2.1 core attention over the selected entries only (R2, R6).
+
+    q [H, D], k_cache / v_cache [N, D], ``selected`` entry indices (entries
+    outside [0, N) are ignored).  Returns (o [H, D], lse [H]) in float64.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(k_cache, dtype=np.float64)
+    Vc = np.asarray(v_cache, dtype=np.float64)
+    N = K.shape[0]
+    sel = np.array([int(j) for j in selected if 0 <= int(j) < N], dtype=np.int64)
+    H, D = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if sel.size == 0:
+        return np.zeros((H, D)), np.full(H, NEG_INF)
+    logits = scale * (q @ K[sel].T)                # [H, |S|]
+    mx = logits.max(axis=1, keepdims=True)
+    p = np.exp(logits - mx)
+    l = p.sum(axis=1, keepdims=True)
+    o = (p @ Vc[sel]) / l
+    lse = (mx + np.log(l))[:, 0]
+    return o, lse
+
+
+def hca_attend(q, k_cache, v_cache, visible: int, scale: Optional[float] = None):
+    """§2.2 HCA: attention over every visible compressed entry, no selection."""
+    return attend(q, k_cache, v_cache, range(visible), scale)
+
+
+# ------------------------------------------------------------------ whole path
+def csa_reference(*, q, q_idx, w_idx, k_cache, v_cache, k_idx, q_pos: int, m: int,
+                  k: int, n_entries: int, scale: Optional[float] = None) -> Dict[str, np.ndarray]:
+    """One query token through the §2.1 pipeline on already-compressed caches."""
+    V = visible_count(q_pos, m, n_entries)
+    s = index_scores(q_idx, w_idx, k_idx, V)
+    idx = topk_select(s, V, k)
+    o, lse = attend(q, k_cache, v_cache, idx, scale)
+    return {"visible": V, "scores": s, "idx": idx, "o": o, "lse": lse}

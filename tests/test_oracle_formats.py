@@ -1,0 +1,99 @@
+"""Pins for the oracle's number formats (FP4 E2M1, E4M3, bf16) and the FP4 input encoder."""
+import math
+
+import numpy as np
+import torch
+
+import oracle
+from csa_synth import bf16_bits_from_f32, f32_from_bf16_bits, fp4_quantize
+
+
+def test_e2m1_table_matches_golden(golden):
+    rows = golden("e2m1_codes.txt")
+    assert len(rows) == 16
+    for row in rows:
+        code, value, byte = row.split()
+        code, value, byte = int(code), float(value), int(byte, 16)
+        v = oracle.e2m1_value(code)
+        assert v == value and math.copysign(1.0, v) == math.copysign(1.0, value)
+        assert oracle.e2m1_to_e4m3(code) == byte
+        # the E4M3 byte decodes to exactly the E2M1 value: the dequantisation is lossless
+        assert oracle.e4m3_value(byte) == value
+
+
+def test_e4m3_decoder_known_values():
+    # fixed points of the OCP E4M3 definition: 1.0, max normal 448, min normal 2^-6,
+    # min subnormal 2^-9, NaN encoding S.1111.111
+    assert oracle.e4m3_value(0x38) == 1.0
+    assert oracle.e4m3_value(0x7E) == 448.0
+    assert oracle.e4m3_value(0x08) == 2.0 ** -6
+    assert oracle.e4m3_value(0x01) == 2.0 ** -9
+    assert oracle.e4m3_value(0xB8) == -1.0
+    assert math.isnan(oracle.e4m3_value(0x7F))
+    # monotone over the positive bytes
+    vals = [oracle.e4m3_value(b) for b in range(0x7F)]
+    assert all(a < b for a, b in zip(vals, vals[1:]))
+
+
+def test_fp4_dequantize_unpacks_low_nibble_first():
+    # byte 0x72: low nibble 2 (1.0) is element 0, high nibble 7 (6.0) element 1
+    codes = np.zeros((1, 16), dtype=np.uint8)
+    codes[0, 0] = 0x72
+    codes[0, 1] = 0x9B            # low 11 (-1.5), high 9 (-0.5)
+    scales = np.array([[2.0]], dtype=np.float32)
+    v = oracle.fp4_dequantize(codes, scales)
+    assert v.shape == (1, 32)
+    assert list(v[0, :4]) == [2.0, 12.0, -3.0, -1.0]
+    assert np.all(v[0, 4:] == 0)
+
+
+def test_fp4_encoder_rounding(golden):
+    for row in golden("fp4_rounding.txt"):
+        x, want = (float(t) for t in row.split())
+        blk = torch.zeros(1, 32)
+        blk[0, 0] = x
+        blk[0, 1] = 6.0 if abs(x) <= 6 else abs(x)     # amax 6 -> scale 1 (if |x| <= 6)
+        if abs(x) > 6:
+            continue
+        codes, scale = fp4_quantize(blk)
+        assert float(scale[0, 0]) == 1.0
+        got = oracle.fp4_dequantize(codes.numpy(), scale.numpy())[0, 0]
+        assert got == want, (x, got, want)
+
+
+def test_fp4_encoder_error_bound():
+    # every value is within half a grid step (relative to the scale) of its code
+    g = torch.Generator().manual_seed(5)
+    x = torch.randn(64, 128, generator=g)
+    codes, scale = fp4_quantize(x)
+    deq = oracle.fp4_dequantize(codes.numpy(), scale.numpy())
+    xs = x.numpy().astype(np.float64)
+    s = np.repeat(scale.numpy().astype(np.float64), 32, axis=-1)
+    err = np.abs(deq - xs) / s
+    # the widest E2M1 gap is 2 (between 4 and 6), so the error is at most 1 step unit
+    assert err.max() <= 1.0 + 1e-6
+    # block amax maps to exactly +-6
+    blocks = np.abs(deq).reshape(64, 4, 32).max(axis=-1)
+    assert np.array_equal(blocks, scale.numpy().astype(np.float64) * 6.0)
+
+
+def test_round_to_bf16_matches_bit_rounding():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),      # subnormals
+        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 3.0e38], np.float32),
+    ])
+    want = f32_from_bf16_bits(bf16_bits_from_f32(x)).astype(np.float64)
+    got = oracle.round_to_bf16(x.astype(np.float64))
+    assert np.array_equal(got, want)
+    # ties to even, by hand: 1 + 2^-8 lies halfway between 1 and 1 + 2^-7 -> 1
+    assert oracle.round_to_bf16(np.array([1.0 + 2 ** -8]))[0] == 1.0
+    assert oracle.round_to_bf16(np.array([1.0 + 3 * 2 ** -8]))[0] == 1.0 + 2 ** -6
+
+
+def test_bf16_bits_roundtrip():
+    x = np.array([1.0, -2.5, 0.0078125, 3.140625], dtype=np.float32)   # all exact in bf16
+    bits = bf16_bits_from_f32(x)
+    assert list(bits) == [0x3F80, 0xC020, 0x3C00, 0x4049]
+    assert np.array_equal(oracle.from_bf16_bits(bits), x.astype(np.float64))

@@ -11,7 +11,8 @@ Recipe (every tensor is independent, so any subset can be regenerated):
 * Distributions: pooling logits N(0, 1); Q, K, V, indexer q / k
   N(0, 1)/sqrt(dim); indexer head weights N(0, w_std) in fp32.
 
-Tensor ids: 1 raw tokens (K | V | K_I channels), 2 pooling logits,
+Tensor ids: 1 raw tokens (K | V | K_I channels; drawn sequence by sequence
+from one generator), 2 pooling logits,
 3 cached K_c, 4 cached V_c, 5 cached K_I, 6 q, 7 q_I, 8 w_I.
 """
 from __future__ import annotations
@@ -120,13 +121,20 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
     out: Dict[str, torch.Tensor] = {}
     B, N, D = w.B, w.N, w.D
     if w.n_raw and need("raw"):
-        # Per-channel-group std: K and V by D, K_I by D_I.
-        raw = _normal(w, "raw", (B, w.n_raw, w.C), 1.0, device)
-        raw[..., : 2 * D].mul_(std_for_dim(D))
-        if w.kind == "csa":
-            raw[..., 2 * D:].mul_(std_for_dim(w.D_I))
-        out["raw"] = _store(raw, w.dtype)
-        del raw
+        # Drawn one sequence at a time from one generator (no full-size fp32
+        # temporary); per-channel-group std: K and V by D, K_I by D_I.
+        g = _gen(w, "raw", device)
+        tdt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        raw = torch.empty((B, w.n_raw, w.C), dtype=tdt, device=device)
+        for b in range(B):
+            xb = torch.empty((w.n_raw, w.C), dtype=torch.float32, device=device)
+            xb.normal_(0.0, 1.0, generator=g)
+            xb[:, : 2 * D].mul_(std_for_dim(D))
+            if w.kind == "csa":
+                xb[:, 2 * D:].mul_(std_for_dim(w.D_I))
+            raw[b] = _store(xb, w.dtype)
+            del xb
+        out["raw"] = raw
     if w.n_raw and need("logits"):
         out["logits"] = _normal(w, "logits", (B, w.n_raw), 1.0, device)
     if need("k_cache"):

@@ -1,0 +1,205 @@
+/*
+ * csa.h - Compressed Sparse Attention (CSA) and Heavily Compressed Attention
+ * (HCA) on AMD Instinct MI355X (gfx950).  Plain C ABI.
+ *
+ * The method is the one described in the technical review
+ * "DeepSeek V4 技术解读" (takeshell.com):
+ *   §2.1 CSA  - merge the KV entries of every m tokens into one compressed
+ *               entry by weighted aggregation; a Lightning Indexer scores each
+ *               query token's indexer queries against the compressed entries
+ *               and keeps the top-k; core attention runs over those k only.
+ *               V4-Pro: m = 4, 64 indexer heads x 128 dims, top-k = 1024.
+ *   §2.2 HCA  - m' = 128 tokens per entry, dense attention over all entries.
+ *   §5        - the indexer QK path may run in FP4 E2M1, dequantised to
+ *               FP8 E4M3 without loss.
+ *   §6.2      - kernels are batch invariant: a token's result is bitwise the
+ *               same wherever it sits in a batch; no floating-point atomics.
+ *
+ * Readings of points the pages leave open (all implemented exactly so):
+ *   - pooling weights: softmax of one fp32 logit per raw token within its
+ *     block; the same weights pool every channel of the row (K, V, K_I).
+ *   - one shared KV head (K and V separate arrays) for all query heads; one
+ *     shared indexer key per compressed entry.
+ *   - index score s(t,j) = sum_h w[t,h] * max(0, q_I[t,h] . k_I[j]), unscaled,
+ *     fp32 accumulation.
+ *   - causality: entry j is visible to a query at position t iff
+ *     m * (j + 1) <= t + 1, i.e. V(t) = min(n_entries[b], floor((t+1)/m)).
+ *   - top-k: order (score descending, index ascending), -0.0 == +0.0, keep
+ *     min(k, V(t)); indices returned ascending, padded with -1.  One set per
+ *     query token, shared by all heads.
+ *   - attention: softmax(scale * q . k) over the set; an empty set gives
+ *     output 0 and lse -inf.  lse is the natural-log log-sum-exp.
+ *   - FP4: E2M1 codes, element 2i in the low nibble of byte i, one fp32
+ *     scale per 32 consecutive elements of a vector.
+ *
+ * Conventions for every call
+ *   - All data pointers are DEVICE memory owned by the caller.  The library
+ *     allocates and frees nothing and keeps no state between calls besides
+ *     loaded kernel code; calls are thread-safe.
+ *   - Calls only enqueue work on `stream` and return; results are valid once
+ *     the stream has reached that point.  No call synchronises.
+ *   - Tensors are row-major with the last dimension contiguous.  Strides are
+ *     given in ELEMENTS of the tensor's storage type (bytes for FP4 codes).
+ *     Pointers and row strides must be 16-byte aligned.
+ *   - Validation happens on the host before anything is enqueued; a failed
+ *     check returns a status, enqueues nothing and leaves outputs untouched.
+ *     A failed launch returns CSA_ERR_HIP.  csa_last_error() gives a message
+ *     for the calling thread's last failure.  Nothing aborts or throws.
+ *   - Outputs must not alias inputs.  Overlapping calls on one stream are
+ *     ordered by the stream; workspaces must not be shared by calls that may
+ *     run concurrently.
+ */
+#ifndef CSA_H_
+#define CSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CSA_ABI_VERSION 1
+
+typedef enum {
+  CSA_OK = 0,
+  CSA_ERR_INVALID_ARGUMENT = 1,   /* NULL pointer, bad size, misalignment   */
+  CSA_ERR_UNSUPPORTED = 2,        /* valid but not implemented (shape/dtype) */
+  CSA_ERR_WORKSPACE_TOO_SMALL = 3,
+  CSA_ERR_HIP = 4                 /* a HIP launch failed                     */
+} csa_status_t;
+
+typedef enum {
+  CSA_F32 = 0,        /* float32                                           */
+  CSA_BF16 = 1,       /* bfloat16 (uint16 bit patterns)                    */
+  CSA_FP4_E2M1 = 2    /* packed E2M1 codes + one fp32 scale per 32 values  */
+} csa_dtype_t;
+
+int csa_abi_version(void);
+const char* csa_status_string(csa_status_t status);
+/* Message of the calling thread's most recent non-OK status ("" if none). */
+const char* csa_last_error(void);
+
+/*
+ * csa_compress - token-dimension compression (§2.1 "KV cache compression",
+ * §2.2 with m' = 128).
+ *
+ *   out[b, j, c] = sum_{i<m} w_i x[b, m*j + i, c],
+ *   w = softmax(logits[b, m*j .. m*j+m-1])       for j < n / m, every c < C.
+ *
+ * x       [B, n, C] dtype, strides (x_sb, x_st) elements, channel stride 1.
+ * logits  [B, n] fp32, batch stride z_sb, token stride 1.
+ * out     [B, n/m, C] dtype, strides (o_sb, o_sj).
+ * dtype   CSA_F32 or CSA_BF16 (x and out).  Math in fp32; bf16 output is
+ *         rounded to nearest even.
+ * Only complete blocks are produced; a tail of n % m tokens is ignored.
+ * Requires B, n, C, m >= 1, m <= 4096, C * sizeof(dtype) a multiple of 16.
+ */
+csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st,
+                          const float* logits, int64_t z_sb,
+                          void* out, int64_t o_sb, int64_t o_sj,
+                          csa_dtype_t dtype, int B, int n, int C, int m,
+                          hipStream_t stream);
+
+/*
+ * csa_index_score - Lightning Indexer scores (§2.1), every entry of the cache.
+ *
+ *   scores[b, t, j] = sum_h w_idx[b,t,h] * max(0, q_idx[b,t,h,:] . k_idx[b,j,:])
+ *                     for j < V(b,t), and -inf for V(b,t) <= j < N_max.
+ *
+ * q_idx     [B, Tq, H_I, D_I] contiguous (idx_dtype); for CSA_FP4_E2M1 the
+ *           codes [B, Tq, H_I, D_I/2] bytes plus q_scale [B, Tq, H_I, D_I/32].
+ * w_idx     [B, Tq, H_I] fp32 contiguous.
+ * k_idx     [B, N_max, D_I] with strides (k_sb, k_sn) (FP4: bytes of codes);
+ *           k_scale [B, N_max, D_I/32] with strides (ks_sb, ks_sn) for FP4,
+ *           else NULL.
+ * q_pos     [B, Tq] int32 device: position of each query token.
+ * n_entries [B] int32 device: valid cache rows per sequence (<= N_max).
+ * scores    [B, Tq, N_max] fp32 contiguous.
+ * Supported: F32 / BF16 with H_I <= 64 and D_I in {32, 64, 128};
+ *            FP4 with H_I = 64, D_I = 128.  Tuned: BF16 and FP4 64 x 128.
+ */
+csa_status_t csa_index_score(const void* q_idx, const float* q_scale, const float* w_idx,
+                             const void* k_idx, const float* k_scale,
+                             int64_t k_sb, int64_t k_sn, int64_t ks_sb, int64_t ks_sn,
+                             csa_dtype_t idx_dtype,
+                             const int32_t* q_pos, const int32_t* n_entries,
+                             int B, int Tq, int N_max, int H_I, int D_I, int m,
+                             float* scores, hipStream_t stream);
+
+/*
+ * csa_topk - top-k selection of compressed entries per query token (§2.1).
+ *
+ * scores    [B, Tq, *] fp32 with row stride s_rs (>= N_max); only the first
+ *           V(b,t) entries of a row are considered; they must be finite.
+ * topk_idx  [B, Tq, k] int32: the min(k, V) entries with the largest scores,
+ *           ties to the lower index, in ascending index order, then -1.
+ * topk_score [B, Tq, k] fp32 or NULL: the score of each returned entry
+ *           (-inf for padding).
+ * ws        workspace of at least csa_topk_workspace(...) bytes (may be NULL
+ *           when that size is 0).
+ * Supported: 1 <= k <= 2048, ceil(N_max / 32768) * k <= 32768.
+ */
+csa_status_t csa_topk(const float* scores, int64_t s_rs,
+                      const int32_t* q_pos, const int32_t* n_entries,
+                      int B, int Tq, int N_max, int m, int k,
+                      int32_t* topk_idx, float* topk_score,
+                      void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t csa_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes);
+
+/*
+ * csa_index_topk - csa_index_score followed by csa_topk, with the score
+ * matrix kept in the workspace.  Arguments as in those two calls.
+ */
+csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float* w_idx,
+                            const void* k_idx, const float* k_scale,
+                            int64_t k_sb, int64_t k_sn, int64_t ks_sb, int64_t ks_sn,
+                            csa_dtype_t idx_dtype,
+                            const int32_t* q_pos, const int32_t* n_entries,
+                            int B, int Tq, int N_max, int H_I, int D_I, int m, int k,
+                            int32_t* topk_idx, float* topk_score,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes);
+
+/*
+ * csa_attend - core attention over the selected entries only (§2.1).
+ *
+ *   o[b,t,h,:] = sum_{j in S} softmax_j(scale * q[b,t,h,:] . K[b,j,:]) V[b,j,:]
+ *   S = { topk_idx[b,t,i] : 0 <= topk_idx[b,t,i] < n_entries[b] }.
+ *   lse[b,t,h] = log sum_{j in S} exp(scale * q . K[b,j]).  Empty S: o = 0,
+ *   lse = -inf.  Repeated indices count repeatedly.
+ *
+ * q         [B, Tq, H, D] contiguous (dtype).
+ * k_c, v_c  [B, N_max, D] sharing strides (kv_sb, kv_sn).
+ * topk_idx  [B, Tq, k] int32.
+ * out       [B, Tq, H, D] (dtype); lse [B, Tq, H] fp32 or NULL.
+ * Supported: F32 / BF16 with H <= 64, D in {32, 64, 128}; tuned BF16 64 x 128.
+ */
+csa_status_t csa_attend(const void* q, const void* k_c, const void* v_c,
+                        int64_t kv_sb, int64_t kv_sn,
+                        const int32_t* topk_idx, const int32_t* n_entries,
+                        csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max, int k,
+                        float scale, void* out, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t csa_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int k,
+                                  size_t* bytes);
+
+/*
+ * hca_attend - HCA (§2.2): attention over every visible compressed entry,
+ * S = { j : j < V(b,t) } with V as above for pooling factor m.  Other
+ * arguments and outputs as in csa_attend.
+ */
+csa_status_t hca_attend(const void* q, const void* k_c, const void* v_c,
+                        int64_t kv_sb, int64_t kv_sn,
+                        const int32_t* q_pos, const int32_t* n_entries,
+                        csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max, int m,
+                        float scale, void* out, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t hca_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
+                                  size_t* bytes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CSA_H_ */

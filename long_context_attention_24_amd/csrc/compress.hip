@@ -1,0 +1,145 @@
+// Token-dimension compression: every m consecutive raw tokens become one
+// compressed entry by softmax-weighted aggregation ("DeepSeek V4 技术解读",
+// §2.1 KV cache compression; §2.2 uses m' = 128).
+//
+// HBM-streaming design: one workgroup per compressed entry (b, j).  Thread
+// (p, ch) owns one 16-byte channel chunk ch and the tokens i = p (mod P) of
+// the block, so each wave reads whole 16-byte lanes of consecutive memory.
+// Per-thread partial sums are combined in LDS in a fixed order: the result
+// does not depend on the batch or the grid (batch invariant, no atomics).
+#include "device_common.h"
+#include "internal.h"
+
+namespace csa {
+namespace {
+
+constexpr int kCompressThreads = 256;
+constexpr int kMaxPool = 4096;
+
+template <typename T>
+struct Chunk;   // 16-byte chunk <-> fp32 lanes
+template <>
+struct Chunk<float> {
+  static constexpr int N = 4;
+  __device__ static void unpack(uint4 v, float* f) {
+    f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+template <>
+struct Chunk<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void unpack(uint4 v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static uint4 pack(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+  }
+};
+
+template <typename T>
+__global__ __launch_bounds__(kCompressThreads) void compress_kernel(
+    const T* __restrict__ x, int64_t x_sb, int64_t x_st, const float* __restrict__ z,
+    int64_t z_sb, T* __restrict__ out, int64_t o_sb, int64_t o_sj, int m, int CH, int P) {
+  constexpr int E = Chunk<T>::N;
+  __shared__ float e_s[kMaxPool];
+  __shared__ float red[kCompressThreads / 64];
+  __shared__ float part[kCompressThreads * E];
+
+  const int j = blockIdx.x, b = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
+  const float* zb = z + b * z_sb + static_cast<int64_t>(j) * m;
+
+  // softmax weights of the block's logits (unnormalised; divided at the end)
+  float mx = kNegInf;
+  for (int i = tid; i < m; i += blockDim.x) mx = fmaxf(mx, zb[i]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = red[0];
+  for (int w = 1; w < nwaves; ++w) mx = fmaxf(mx, red[w]);
+  __syncthreads();
+  float sum = 0.f;
+  for (int i = tid; i < m; i += blockDim.x) {
+    const float e = expf(zb[i] - mx);
+    e_s[i] = e;
+    sum += e;
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) red[wave] = sum;
+  __syncthreads();
+  float total = 0.f;
+  for (int w = 0; w < nwaves; ++w) total += red[w];
+
+  // weighted sum of the block's rows, one 16-byte channel chunk per thread
+  const int ch = tid % CH, p = tid / CH;
+  if (p < P) {
+    float acc[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) acc[c] = 0.f;
+    const T* xb = x + b * x_sb + static_cast<int64_t>(j) * m * x_st + ch * E;
+#pragma unroll 4
+    for (int i = p; i < m; i += P) {
+      float f[E];
+      Chunk<T>::unpack(ld16(xb + static_cast<int64_t>(i) * x_st), f);
+      const float e = e_s[i];
+#pragma unroll
+      for (int c = 0; c < E; ++c) acc[c] = fmaf(e, f[c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < E; ++c) part[(p * CH + ch) * E + c] = acc[c];
+  }
+  __syncthreads();
+  if (tid < CH) {
+    float r[E];
+#pragma unroll
+    for (int c = 0; c < E; ++c) r[c] = part[tid * E + c];
+    for (int q = 1; q < P; ++q) {
+#pragma unroll
+      for (int c = 0; c < E; ++c) r[c] += part[(q * CH + tid) * E + c];
+    }
+#pragma unroll
+    for (int c = 0; c < E; ++c) r[c] = r[c] / total;
+    st16(out + b * o_sb + static_cast<int64_t>(j) * o_sj + tid * E, Chunk<T>::pack(r));
+  }
+}
+
+template <typename T>
+hipError_t launch_typed(const void* x, int64_t x_sb, int64_t x_st, const float* z, int64_t z_sb,
+                        void* out, int64_t o_sb, int64_t o_sj, int B, int n, int C, int m,
+                        hipStream_t s) {
+  constexpr int E = Chunk<T>::N;
+  const int CH = C / E;
+  int P = kCompressThreads / CH;
+  if (P > m) P = m;
+  int threads = ((P * CH + 63) / 64) * 64;
+  const int nblk = n / m;
+  if (nblk == 0) return hipSuccess;
+  hipLaunchKernelGGL(compress_kernel<T>, dim3(nblk, B), dim3(threads), 0, s,
+                     static_cast<const T*>(x), x_sb, x_st, z, z_sb, static_cast<T*>(out), o_sb,
+                     o_sj, m, CH, P);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const float* z, int64_t z_sb,
+                           void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dt, int B, int n,
+                           int C, int m, hipStream_t s) {
+  if (dt == CSA_F32)
+    return launch_typed<float>(x, x_sb, x_st, z, z_sb, out, o_sb, o_sj, B, n, C, m, s);
+  return launch_typed<uint16_t>(x, x_sb, x_st, z, z_sb, out, o_sb, o_sj, B, n, C, m, s);
+}
+
+}  // namespace csa

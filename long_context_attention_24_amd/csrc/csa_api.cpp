@@ -1,0 +1,288 @@
+// C ABI of the CSA / HCA library: argument validation, workspace layout and
+// dispatch to the kernels.  Every check runs on the host before anything is
+// enqueued; a failed check leaves the outputs untouched.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "csa.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+csa_status_t fail(csa_status_t st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+csa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return CSA_OK;
+  return fail(CSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t esize(csa_dtype_t dt) { return dt == CSA_F32 ? 4 : 2; }
+
+bool valid_dtype(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP4_E2M1; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// padded row length of the score matrix kept in a workspace (16-byte rows)
+int64_t score_row_stride(int N_max) { return (static_cast<int64_t>(N_max) + 3) / 4 * 4; }
+
+#define CSA_REQUIRE(cond, st, ...) \
+  do {                             \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+csa_status_t check_score_args(const void* q_idx, const float* q_scale, const float* w_idx,
+                              const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
+                              int64_t ks_sb, int64_t ks_sn, csa_dtype_t dt, const int32_t* q_pos,
+                              const int32_t* n_entries, int B, int Tq, int N_max, int H_I, int D_I,
+                              int m) {
+  CSA_REQUIRE(q_idx && w_idx && k_idx && q_pos && n_entries, CSA_ERR_INVALID_ARGUMENT,
+              "index score: NULL input pointer");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && N_max >= 1 && H_I >= 1 && D_I >= 1 && m >= 1,
+              CSA_ERR_INVALID_ARGUMENT, "index score: sizes must be >= 1");
+  CSA_REQUIRE(valid_dtype(dt), CSA_ERR_INVALID_ARGUMENT, "index score: unknown dtype %d", (int)dt);
+  CSA_REQUIRE(csa::score_supported(dt, H_I, D_I), CSA_ERR_UNSUPPORTED,
+              "index score: dtype %d with H_I=%d D_I=%d not supported", (int)dt, H_I, D_I);
+  CSA_REQUIRE(aligned16(q_idx) && aligned16(k_idx) && aligned16(w_idx), CSA_ERR_INVALID_ARGUMENT,
+              "index score: pointers must be 16-byte aligned");
+  if (dt == CSA_FP4_E2M1) {
+    CSA_REQUIRE(q_scale && k_scale, CSA_ERR_INVALID_ARGUMENT, "index score: FP4 needs scales");
+    CSA_REQUIRE(aligned16(q_scale) && aligned16(k_scale), CSA_ERR_INVALID_ARGUMENT,
+                "index score: scale pointers must be 16-byte aligned");
+    CSA_REQUIRE(k_sn >= D_I / 2 && k_sn % 16 == 0 && k_sb % 16 == 0 &&
+                    k_sb >= static_cast<int64_t>(N_max) * k_sn,
+                CSA_ERR_INVALID_ARGUMENT, "index score: bad FP4 code strides");
+    CSA_REQUIRE(ks_sn >= D_I / 32 && ks_sn % 4 == 0 && ks_sb % 4 == 0 &&
+                    ks_sb >= static_cast<int64_t>(N_max) * ks_sn,
+                CSA_ERR_INVALID_ARGUMENT, "index score: bad FP4 scale strides");
+  } else {
+    const int64_t vec = 16 / static_cast<int64_t>(esize(dt));
+    CSA_REQUIRE(k_sn >= D_I && k_sn % vec == 0 && k_sb % vec == 0 &&
+                    (B == 1 || k_sb >= static_cast<int64_t>(N_max) * k_sn),
+                CSA_ERR_INVALID_ARGUMENT, "index score: bad key strides (k_sb=%lld k_sn=%lld)",
+                (long long)k_sb, (long long)k_sn);
+  }
+  return CSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int csa_abi_version(void) { return CSA_ABI_VERSION; }
+
+const char* csa_status_string(csa_status_t st) {
+  switch (st) {
+    case CSA_OK: return "CSA_OK";
+    case CSA_ERR_INVALID_ARGUMENT: return "CSA_ERR_INVALID_ARGUMENT";
+    case CSA_ERR_UNSUPPORTED: return "CSA_ERR_UNSUPPORTED";
+    case CSA_ERR_WORKSPACE_TOO_SMALL: return "CSA_ERR_WORKSPACE_TOO_SMALL";
+    case CSA_ERR_HIP: return "CSA_ERR_HIP";
+  }
+  return "CSA_ERR_UNKNOWN";
+}
+
+const char* csa_last_error(void) { return g_err; }
+
+csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st, const float* logits,
+                          int64_t z_sb, void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dtype,
+                          int B, int n, int C, int m, hipStream_t stream) {
+  g_err[0] = 0;
+  CSA_REQUIRE(x && logits && out, CSA_ERR_INVALID_ARGUMENT, "compress: NULL pointer");
+  CSA_REQUIRE(B >= 1 && n >= 1 && C >= 1 && m >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "compress: sizes must be >= 1");
+  CSA_REQUIRE(m <= 4096, CSA_ERR_UNSUPPORTED, "compress: m=%d > 4096", m);
+  CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+              "compress: dtype must be F32 or BF16");
+  const int64_t es = static_cast<int64_t>(esize(dtype));
+  CSA_REQUIRE((C * es) % 16 == 0, CSA_ERR_UNSUPPORTED, "compress: C*elem_size must be a multiple of 16");
+  CSA_REQUIRE(C * es / 16 <= 256, CSA_ERR_UNSUPPORTED, "compress: C too large (%d)", C);
+  CSA_REQUIRE(aligned16(x) && aligned16(out), CSA_ERR_INVALID_ARGUMENT,
+              "compress: pointers must be 16-byte aligned");
+  CSA_REQUIRE((x_st * es) % 16 == 0 && (x_sb * es) % 16 == 0 && (o_sj * es) % 16 == 0 &&
+                  (o_sb * es) % 16 == 0,
+              CSA_ERR_INVALID_ARGUMENT, "compress: strides must be multiples of 16 bytes");
+  CSA_REQUIRE(x_st >= C && o_sj >= C && z_sb >= n, CSA_ERR_INVALID_ARGUMENT,
+              "compress: strides smaller than the rows");
+  return hip_status(csa::launch_compress(x, x_sb, x_st, logits, z_sb, out, o_sb, o_sj, dtype, B,
+                                         n, C, m, stream),
+                    "compress launch");
+}
+
+csa_status_t csa_index_score(const void* q_idx, const float* q_scale, const float* w_idx,
+                             const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
+                             int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
+                             const int32_t* q_pos, const int32_t* n_entries, int B, int Tq,
+                             int N_max, int H_I, int D_I, int m, float* scores,
+                             hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
+                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(scores, CSA_ERR_INVALID_ARGUMENT, "index score: NULL scores");
+  csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, N_max};
+  return hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
+}
+
+csa_status_t csa_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes) {
+  g_err[0] = 0;
+  CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "topk workspace: NULL result");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && N_max >= 1 && k >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "topk workspace: sizes must be >= 1");
+  CSA_REQUIRE(csa::topk_supported(N_max, k), CSA_ERR_UNSUPPORTED,
+              "topk: N_max=%d with k=%d not supported", N_max, k);
+  *bytes = csa::topk_workspace_bytes(B * Tq, N_max, k);
+  return CSA_OK;
+}
+
+csa_status_t csa_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
+                      const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
+                      int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                      hipStream_t stream) {
+  g_err[0] = 0;
+  CSA_REQUIRE(scores && q_pos && n_entries && topk_idx, CSA_ERR_INVALID_ARGUMENT,
+              "topk: NULL pointer");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && N_max >= 1 && m >= 1 && k >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "topk: sizes must be >= 1");
+  CSA_REQUIRE(s_rs >= N_max && s_rs % 4 == 0 && aligned16(scores), CSA_ERR_INVALID_ARGUMENT,
+              "topk: score rows must be 16-byte aligned and hold N_max values");
+  CSA_REQUIRE(csa::topk_supported(N_max, k), CSA_ERR_UNSUPPORTED,
+              "topk: N_max=%d with k=%d not supported", N_max, k);
+  const size_t need = csa::topk_workspace_bytes(B * Tq, N_max, k);
+  CSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), CSA_ERR_WORKSPACE_TOO_SMALL,
+              "topk: workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(csa::launch_topk(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, topk_idx,
+                                     topk_score, ws, stream),
+                    "topk launch");
+}
+
+csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes) {
+  g_err[0] = 0;
+  size_t t = 0;
+  csa_status_t st = csa_topk_workspace(B, Tq, N_max, k, &t);
+  if (st != CSA_OK) return st;
+  *bytes = round_up(static_cast<size_t>(B) * Tq * score_row_stride(N_max) * sizeof(float)) +
+           round_up(t);
+  return CSA_OK;
+}
+
+csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float* w_idx,
+                            const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
+                            int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
+                            const int32_t* q_pos, const int32_t* n_entries, int B, int Tq,
+                            int N_max, int H_I, int D_I, int m, int k, int32_t* topk_idx,
+                            float* topk_score, void* ws, size_t ws_bytes, hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
+                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(topk_idx && k >= 1, CSA_ERR_INVALID_ARGUMENT, "index topk: bad output / k");
+  size_t need = 0;
+  st = csa_index_topk_workspace(B, Tq, N_max, k, &need);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
+              "index topk: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
+  const int64_t srs = score_row_stride(N_max);
+  float* scores = static_cast<float*>(ws);
+  void* tws = static_cast<char*>(ws) +
+              round_up(static_cast<size_t>(B) * Tq * srs * sizeof(float));
+  csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs};
+  st = hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
+  if (st != CSA_OK) return st;
+  return hip_status(csa::launch_topk(scores, srs, q_pos, n_entries, B, Tq, N_max, m, k, topk_idx,
+                                     topk_score, tws, stream),
+                    "topk launch");
+}
+
+static csa_status_t check_attend(const void* q, const void* k_c, const void* v_c, int64_t kv_sb,
+                                 int64_t kv_sn, const int32_t* n_entries, csa_dtype_t dtype, int B,
+                                 int Tq, int H, int D, int N_max, void* out) {
+  CSA_REQUIRE(q && k_c && v_c && n_entries && out, CSA_ERR_INVALID_ARGUMENT,
+              "attend: NULL pointer");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1 && D >= 1 && N_max >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "attend: sizes must be >= 1");
+  CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+              "attend: dtype must be F32 or BF16");
+  CSA_REQUIRE(csa::attend_supported(dtype, H, D), CSA_ERR_UNSUPPORTED,
+              "attend: H=%d D=%d not supported", H, D);
+  CSA_REQUIRE(aligned16(q) && aligned16(k_c) && aligned16(v_c) && aligned16(out),
+              CSA_ERR_INVALID_ARGUMENT, "attend: pointers must be 16-byte aligned");
+  const int64_t vec = 16 / static_cast<int64_t>(esize(dtype));
+  CSA_REQUIRE(kv_sn >= D && kv_sn % vec == 0 && kv_sb % vec == 0 &&
+                  (B == 1 || kv_sb >= static_cast<int64_t>(N_max) * kv_sn),
+              CSA_ERR_INVALID_ARGUMENT, "attend: bad cache strides");
+  return CSA_OK;
+}
+
+csa_status_t csa_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int k,
+                                  size_t* bytes) {
+  g_err[0] = 0;
+  CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "attend workspace: NULL result");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1 && D >= 1 && k >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "attend workspace: sizes must be >= 1");
+  *bytes = csa::attend_workspace_bytes(dtype, false, B, Tq, H, D, k);
+  return CSA_OK;
+}
+
+csa_status_t csa_attend(const void* q, const void* k_c, const void* v_c, int64_t kv_sb,
+                        int64_t kv_sn, const int32_t* topk_idx, const int32_t* n_entries,
+                        csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max, int k,
+                        float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_attend(q, k_c, v_c, kv_sb, kv_sn, n_entries, dtype, B, Tq, H, D, N_max,
+                                 out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(topk_idx && k >= 1, CSA_ERR_INVALID_ARGUMENT, "attend: bad topk_idx / k");
+  const size_t need = csa::attend_workspace_bytes(dtype, false, B, Tq, H, D, k);
+  CSA_REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))),
+              CSA_ERR_WORKSPACE_TOO_SMALL, "attend: workspace %zu < %zu bytes", ws_bytes, need);
+  csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, topk_idx, nullptr, n_entries, B, Tq, H, D,
+                    N_max, k, 1, scale, out, lse, ws};
+  return hip_status(csa::launch_attend(a, dtype, false, stream), "attend launch");
+}
+
+csa_status_t hca_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
+                                  size_t* bytes) {
+  g_err[0] = 0;
+  CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "hca workspace: NULL result");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1 && D >= 1 && N_max >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "hca workspace: sizes must be >= 1");
+  *bytes = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D, N_max);
+  return CSA_OK;
+}
+
+csa_status_t hca_attend(const void* q, const void* k_c, const void* v_c, int64_t kv_sb,
+                        int64_t kv_sn, const int32_t* q_pos, const int32_t* n_entries,
+                        csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max, int m,
+                        float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_attend(q, k_c, v_c, kv_sb, kv_sn, n_entries, dtype, B, Tq, H, D, N_max,
+                                 out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(q_pos && m >= 1, CSA_ERR_INVALID_ARGUMENT, "hca: bad q_pos / m");
+  const size_t need = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D, N_max);
+  CSA_REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))),
+              CSA_ERR_WORKSPACE_TOO_SMALL, "hca: workspace %zu < %zu bytes", ws_bytes, need);
+  csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, nullptr, q_pos, n_entries, B, Tq, H, D,
+                    N_max, 0, m, scale, out, lse, ws};
+  return hip_status(csa::launch_attend(a, dtype, true, stream), "hca launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,288 @@
+// Lightning Indexer scores ("DeepSeek V4 技术解读", §2.1: per query token,
+// 64 indexer heads of dim 128 score the compressed entries; §5: the indexer
+// QK path may run in FP4 E2M1 dequantised to FP8 E4M3).
+//
+//   s(t, j) = sum_h w[t, h] * max(0, q_I[t, h] . k_I[j])   for j < V(t)
+//
+// Decode is HBM-bound: every key row (256 B in bf16) is read once and costs
+// 64 x 128 MACs, 64 FLOP/B, above the fp32 VALU ridge, so the dot products
+// run on MFMA with the 64 heads of one query as the M dimension and keys as
+// N.  In the 32x32 accumulator layout a lane holds one key and 16 heads, so
+// ReLU, head weight and the head sum stay in registers, followed by a single
+// exchange between lanes l and l^32.  K rows are loaded straight into the B
+// operand (lane l%32 = key row, 16 contiguous bytes per lane per k-step),
+// one tile ahead of the MFMAs.
+//
+// The MFMA k-slot order does not matter for a dot product as long as A and
+// B use the same one, so slot (lane/32, e) of k-step s holds dimension
+// 16*s + 8*(lane/32) + e for both operands.
+#include "device_common.h"
+#include "internal.h"
+
+namespace csa {
+namespace {
+
+// ---------------------------------------------------------------- generic (VALU)
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p);
+template <>
+__device__ __forceinline__ float ld_elem<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) { return bf16_to_f32(*p); }
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void score_generic_kernel(
+    const T* __restrict__ q, const float* __restrict__ w, const T* __restrict__ k, int64_t k_sb,
+    int64_t k_sn, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
+    int N_max, int m, int H, float* __restrict__ scores, int64_t s_rs) {
+  __shared__ float qs[64 * D];
+  __shared__ float ws[64];
+  const int row = blockIdx.y, b = row / Tq, tid = threadIdx.x;
+  const T* qrow = q + static_cast<int64_t>(row) * H * D;
+  for (int i = tid; i < H * D; i += blockDim.x) qs[i] = ld_elem<T>(qrow + i);
+  for (int i = tid; i < H; i += blockDim.x) ws[i] = w[static_cast<int64_t>(row) * H + i];
+  __syncthreads();
+  const int j = blockIdx.x * blockDim.x + tid;
+  if (j >= N_max) return;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  float* srow = scores + row * s_rs;
+  if (j >= V) {
+    srow[j] = kNegInf;
+    return;
+  }
+  const T* kr = k + b * k_sb + static_cast<int64_t>(j) * k_sn;
+  float kv[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) kv[d] = ld_elem<T>(kr + d);
+  float s = 0.f;
+  for (int h = 0; h < H; ++h) {
+    float dot = 0.f;
+#pragma unroll
+    for (int d = 0; d < D; ++d) dot = fmaf(qs[h * D + d], kv[d], dot);
+    s = fmaf(ws[h], fmaxf(dot, 0.f), s);
+  }
+  srow[j] = s;
+}
+
+// ---------------------------------------------------------------- bf16, 64 heads x 128
+constexpr int kWavesPerWg = 4;
+constexpr int kKeysPerWave = 256;
+constexpr int kKeysPerWg = kWavesPerWg * kKeysPerWave;
+
+__global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
+    int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
+    int64_t s_rs) {
+  const int row = blockIdx.y, b = row / Tq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int jl = lane & 31, g = lane >> 5;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const int key0 = (blockIdx.x * kWavesPerWg + wave) * kKeysPerWave;
+  if (key0 >= N_max) return;
+  const int key_end = min(key0 + kKeysPerWave, N_max);
+  const int vis_end = min(key_end, V);
+  float* srow = scores + row * s_rs;
+  for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
+  if (key0 >= vis_end) return;
+
+  // A operand: q_I rows (heads) of this query; two 32-head tiles x 8 k-steps
+  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
+  bf16x8_t a0[8], a1[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    a0[s] = ld_bf16x8(qrow + jl * 128 + 16 * s + 8 * g);
+    a1[s] = ld_bf16x8(qrow + (32 + jl) * 128 + 16 * s + 8 * g);
+  }
+  // head weights in accumulator-row order: row = 8*(r/4) + 4*g + r%4
+  const float* wrow = w + static_cast<int64_t>(row) * 64;
+  float w0[16], w1[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int h = 8 * (r >> 2) + 4 * g + (r & 3);
+    w0[r] = wrow[h];
+    w1[r] = wrow[32 + h];
+  }
+  const uint16_t* kb = k + b * k_sb + 8 * g;
+  bf16x8_t cur[8], nxt[8];
+  {
+    const int j = min(key0 + jl, vis_end - 1);
+    const uint16_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) cur[s] = ld_bf16x8(kr + 16 * s);
+  }
+  for (int j0 = key0; j0 < vis_end; j0 += 32) {
+    if (j0 + 32 < vis_end) {
+      const int j = min(j0 + 32 + jl, vis_end - 1);
+      const uint16_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) nxt[s] = ld_bf16x8(kr + 16 * s);
+    }
+    f32x16_t c0 = {}, c1 = {};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], cur[s], c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], cur[s], c1, 0, 0, 0);
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum = fmaf(w0[r], fmaxf(c0[r], 0.f), sum);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], fmaxf(c1[r], 0.f), sum);
+    const float other = __shfl_xor(sum, 32, 64);
+    const float tot = sum + other;     // commutative: both halves get the same bits
+    const int j = j0 + jl;
+    if (g == 0 && j < vis_end) srow[j] = tot;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) cur[s] = nxt[s];
+  }
+}
+
+// ---------------------------------------------------------------- FP4, 64 heads x 128
+// E2M1 magnitude (3 bits) -> E4M3 byte: 0, .5, 1, 1.5, 2, 3, 4, 6 are
+// 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C; the sign bit moves from bit 3 of
+// the nibble to bit 7 of the byte.  Exact: E4M3 has more exponent range and
+// mantissa bits than E2M1.
+constexpr uint32_t kE4m3Lo = 0x3C383000u;   // bytes for magnitudes 0..3
+constexpr uint32_t kE4m3Hi = 0x4C484440u;   // bytes for magnitudes 4..7
+
+// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
+// -> eight E4M3 bytes.  Order: even elements in the low word, odd elements in
+// the high word.  A and B use the same order, so dot products are unchanged.
+__device__ __forceinline__ uint64_t fp4x8_to_fp8x8(uint32_t c) {
+  const uint32_t ev = c & 0x0F0F0F0Fu, od = (c >> 4) & 0x0F0F0F0Fu;
+  const uint32_t e8 = __builtin_amdgcn_perm(kE4m3Hi, kE4m3Lo, ev & 0x07070707u) |
+                      ((ev & 0x08080808u) << 4);
+  const uint32_t o8 = __builtin_amdgcn_perm(kE4m3Hi, kE4m3Lo, od & 0x07070707u) |
+                      ((od & 0x08080808u) << 4);
+  return (static_cast<uint64_t>(o8) << 32) | e8;
+}
+
+// 16x16x32 fp8 MFMA: K = 32 is exactly one scale block, so each MFMA gives
+// the exact per-block partial dot product; block scales are applied in fp32.
+// A operand lane l: head row l%16, dims 8*(l/16) .. +7 of the block.
+__global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k, const float* __restrict__ k_scale, int64_t k_sb, int64_t k_sn,
+    int64_t ks_sb, int64_t ks_sn, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
+    int64_t s_rs) {
+  const int row = blockIdx.y, b = row / Tq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const int key0 = (blockIdx.x * kWavesPerWg + wave) * kKeysPerWave;
+  if (key0 >= N_max) return;
+  const int key_end = min(key0 + kKeysPerWave, N_max);
+  const int vis_end = min(key_end, V);
+  float* srow = scores + row * s_rs;
+  for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
+  if (key0 >= vis_end) return;
+
+  // q: [64 heads][64 bytes] codes, [64][4] scales
+  const uint8_t* qrow = q + static_cast<int64_t>(row) * 64 * 64;
+  const float* qsrow = q_scale + static_cast<int64_t>(row) * 64 * 4;
+  uint64_t a[4][4];   // [head tile][block]
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const uint32_t c =
+          *reinterpret_cast<const uint32_t*>(qrow + (16 * mt + nl) * 64 + 16 * blk + 4 * g);
+      a[mt][blk] = fp4x8_to_fp8x8(c);
+    }
+  // accumulator rows: head = 16*mt + 4*g + r
+  float sq[4][4][4];   // [mt][r][blk]
+  float wv[4][4];
+  const float* wrow = w + static_cast<int64_t>(row) * 64;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 16 * mt + 4 * g + r;
+      wv[mt][r] = wrow[h];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) sq[mt][r][blk] = qsrow[h * 4 + blk];
+    }
+
+  const uint8_t* kb = k + b * k_sb + 4 * g;
+  const float* ksb = k_scale + b * ks_sb;
+  for (int j0 = key0; j0 < vis_end; j0 += 16) {
+    const int j = min(j0 + nl, vis_end - 1);
+    const uint8_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+    uint32_t kc[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) kc[blk] = *reinterpret_cast<const uint32_t*>(kr + 16 * blk);
+    const float4 sk = *reinterpret_cast<const float4*>(ksb + static_cast<int64_t>(j) * ks_sn);
+    const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
+    uint64_t bop[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) bop[blk] = fp4x8_to_fp8x8(kc[blk]);
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4_t p[4];
+#pragma unroll
+      for (int blk = 0; blk < 4; ++blk) {
+        const f32x4_t z = {};
+        p[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+            static_cast<long>(a[mt][blk]), static_cast<long>(bop[blk]), z, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float t = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) t = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], t);
+        sum = fmaf(wv[mt][r], fmaxf(t, 0.f), sum);
+      }
+    }
+    // heads are spread over the four 16-lane groups of the key's column
+    sum = sum + __shfl_xor(sum, 16, 64);
+    sum = sum + __shfl_xor(sum, 32, 64);
+    const int jj = j0 + nl;
+    if (g == 0 && jj < vis_end) srow[jj] = sum;
+  }
+}
+
+template <typename T, int D>
+void launch_generic(const ScoreArgs& a, hipStream_t s) {
+  const dim3 grid((a.N_max + 255) / 256, a.B * a.Tq);
+  hipLaunchKernelGGL((score_generic_kernel<T, D>), grid, dim3(256), 0, s,
+                     static_cast<const T*>(a.q), a.w, static_cast<const T*>(a.k), a.k_sb, a.k_sn,
+                     a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.H, a.scores, a.s_rs);
+}
+
+}  // namespace
+
+bool score_supported(csa_dtype_t dt, int H, int D) {
+  if (dt == CSA_FP4_E2M1) return H == 64 && D == 128;
+  if (dt != CSA_F32 && dt != CSA_BF16) return false;
+  return H >= 1 && H <= 64 && (D == 32 || D == 64 || D == 128);
+}
+
+hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
+  if (dt == CSA_FP4_E2M1) {
+    const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
+    hipLaunchKernelGGL(score_fp4_h64d128_kernel, grid, dim3(256), 0, s,
+                       static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
+                       static_cast<const uint8_t*>(a.k), a.k_scale, a.k_sb, a.k_sn, a.ks_sb,
+                       a.ks_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs);
+  } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
+    const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
+    hipLaunchKernelGGL(score_bf16_h64d128_kernel, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
+                       a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
+                       a.s_rs);
+  } else if (dt == CSA_BF16) {
+    if (a.D == 32) launch_generic<uint16_t, 32>(a, s);
+    else if (a.D == 64) launch_generic<uint16_t, 64>(a, s);
+    else launch_generic<uint16_t, 128>(a, s);
+  } else {
+    if (a.D == 32) launch_generic<float, 32>(a, s);
+    else if (a.D == 64) launch_generic<float, 64>(a, s);
+    else launch_generic<float, 128>(a, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace csa

@@ -1,0 +1,62 @@
+// Host-side launchers implemented in the .hip files; called by csa_api.cpp
+// after argument validation.  Each returns the HIP error of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "csa.h"
+
+namespace csa {
+
+// ---- compress.hip
+hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const float* z, int64_t z_sb,
+                           void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dt, int B, int n,
+                           int C, int m, hipStream_t s);
+
+// ---- index_score.hip
+struct ScoreArgs {
+  const void* q;            // [B*Tq, H_I, D_I] (FP4: codes)
+  const float* q_scale;     // FP4 only
+  const float* w;           // [B*Tq, H_I]
+  const void* k;            // cache base
+  const float* k_scale;     // FP4 only
+  int64_t k_sb, k_sn, ks_sb, ks_sn;
+  const int32_t* q_pos;
+  const int32_t* n_entries;
+  int B, Tq, N_max, H, D, m;
+  float* scores;            // [B*Tq, s_rs]
+  int64_t s_rs;             // row stride of scores (elements)
+};
+hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s);
+bool score_supported(csa_dtype_t dt, int H, int D);
+
+// ---- topk.hip
+// Workspace bytes needed for rows of N_max scores and a given k.
+size_t topk_workspace_bytes(int rows, int N_max, int k);
+bool topk_supported(int N_max, int k);
+hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
+                       const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
+                       int32_t* idx, float* out_scores, void* ws, hipStream_t s);
+
+// ---- attend.hip
+struct AttendArgs {
+  const void* q;            // [B*Tq, H, D]
+  const void* kc;           // cache bases
+  const void* vc;
+  int64_t kv_sb, kv_sn;
+  const int32_t* idx;       // CSA: [B*Tq, k]; HCA: NULL
+  const int32_t* q_pos;     // HCA: [B*Tq]
+  const int32_t* n_entries; // [B]
+  int B, Tq, H, D, N_max, topk, m;
+  float scale;
+  void* out;
+  float* lse;
+  void* ws;
+};
+size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax);
+bool attend_supported(csa_dtype_t dt, int H, int D);
+hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s);
+
+}  // namespace csa

@@ -1,0 +1,257 @@
+"""GPU parity on small inputs: the tiny fp32 workload stage by stage, the
+generic (VALU) kernels, ragged shapes and the method's degenerate cases.
+
+Every case is checked against the oracle on the exact input bits the GPU
+consumed (stage-wise: each stage's oracle uses the GPU's previous output)."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_24_amd as csa
+import oracle
+from csa_synth import WORKLOADS, make_inputs
+from parity import check_attention, check_compress, check_lse, check_topk, np64, score_bound
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _gen(seed):
+    return torch.Generator(device=DEV).manual_seed(seed)
+
+
+def _randn(shape, std, dtype, seed):
+    x = torch.empty(shape, device=DEV, dtype=torch.float32).normal_(0, 1, generator=_gen(seed))
+    return (x * std).to(dtype)
+
+
+def test_tiny_csa_stagewise():
+    w = WORKLOADS["tiny_csa"]
+    _say("tiny_csa: compress")
+    inp = make_inputs(w, device=DEV)
+    raw, z = inp["raw"], inp["logits"]
+    cache = csa.compress(raw, z, w.m)                    # [1, 64, 160] = K | V | K_I
+    torch.cuda.synchronize()
+    frac = check_compress(np64(cache)[0], np64(raw)[0], np64(z)[0], w.m, "f32")
+    kc, vc, ki = cache[..., :64], cache[..., 64:128], cache[..., 128:]
+    q, qi, wi = inp["q"], inp["q_idx"], inp["w_idx"]
+    q_pos, n_ent = inp["q_pos"], inp["n_entries"]
+
+    _say("tiny_csa: index scores / top-k")
+    scores = csa.index_score(qi, wi, ki, q_pos, n_ent, w.m)
+    idx, sel_scores = csa.index_topk(qi, wi, ki, q_pos, n_ent, w.m, w.k, with_scores=True)
+    idx2 = csa.topk(scores, q_pos, n_ent, w.m, w.k)
+    torch.cuda.synchronize()
+    S = np64(scores)[0]
+    I = np64(idx)[0]
+    ki64, qi64, wi64 = np64(ki)[0], np64(qi)[0], np64(wi)[0]
+    assert np.array_equal(I, np64(idx2)[0])
+    n_amb = 0
+    for t in range(w.Tq):
+        V = oracle.visible_count(t, w.m, w.N)
+        s_ref = oracle.index_scores(qi64[t], wi64[t], ki64, V)
+        assert np.all(np.isneginf(S[t, V:]))
+        bound = score_bound(qi64[t], wi64[t], ki64[:V], w.D_I, w.H_I)
+        assert np.all(np.abs(S[t, :V] - s_ref[:V]) <= bound + 1e-30)
+        # selection of the GPU's own fp32 scores is exact
+        assert np.array_equal(I[t], oracle.topk_select(S[t], V, w.k))
+        n_amb += check_topk(I[t], s_ref, V, w.k)
+        sel = I[t][I[t] >= 0]
+        assert np.array_equal(np64(sel_scores)[0, t, : sel.size], S[t, sel])
+    _say(f"tiny_csa: ambiguous top-k entries {n_amb}")
+
+    _say("tiny_csa: attention")
+    o, lse = csa.attend(q, kc, vc, idx, n_ent, with_lse=True)
+    oh, lseh = csa.hca_attend(q, kc, vc, q_pos, n_ent, w.m, with_lse=True)
+    torch.cuda.synchronize()
+    kc64, vc64, q64 = np64(kc)[0], np64(vc)[0], np64(q)[0]
+    o_ref = np.zeros_like(q64)
+    l_ref = np.zeros(q64.shape[:2])
+    oh_ref = np.zeros_like(q64)
+    lh_ref = np.zeros(q64.shape[:2])
+    for t in range(w.Tq):
+        o_ref[t], l_ref[t] = oracle.attend(q64[t], kc64, vc64, I[t])
+        oh_ref[t], lh_ref[t] = oracle.hca_attend(q64[t], kc64, vc64, oracle.visible_count(t, w.m, w.N))
+    check_attention(np64(o)[0], o_ref, "f32", "csa")
+    check_lse(np64(lse)[0], l_ref, 1e-5)
+    check_attention(np64(oh)[0], oh_ref, "f32", "hca")
+    check_lse(np64(lseh)[0], lh_ref, 1e-5)
+    # positions 0..2 see nothing: zero output, -inf lse, all -1 indices
+    assert np.all(I[:3] == -1) and np.all(np64(o)[0, :3] == 0)
+    # at t >= 63 every query sees at least k entries
+    assert np.all(I[63:] >= 0)
+    _say(f"tiny_csa: ok (compress off-by-rounding fraction {frac:.2e})")
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("H,D,HI,DI", [(8, 64, 16, 64), (3, 32, 5, 128), (64, 128, 7, 32)])
+def test_generic_shapes_ragged(dtype, H, D, HI, DI):
+    """Ragged caches: per-sequence valid rows, mixed query positions, odd sizes."""
+    B, Tq, N_max, m, k = 3, 5, 517, 4, 37
+    tag = "f32" if dtype == torch.float32 else "bf16"
+    _say(f"generic {tag} H={H} D={D} HI={HI} DI={DI}")
+    seed = 100 + H + D + HI
+    q = _randn((B, Tq, H, D), 1 / math.sqrt(D), dtype, seed)
+    kc = _randn((B, N_max, D), 1 / math.sqrt(D), dtype, seed + 1)
+    vc = _randn((B, N_max, D), 1 / math.sqrt(D), dtype, seed + 2)
+    qi = _randn((B, Tq, HI, DI), 1 / math.sqrt(DI), dtype, seed + 3)
+    ki = _randn((B, N_max, DI), 1 / math.sqrt(DI), dtype, seed + 4)
+    wi = _randn((B, Tq, HI), 0.5, torch.float32, seed + 5)
+    q_pos = torch.tensor([[0, 3, 150, 700, 5000], [10, 11, 12, 400, 2067],
+                          [2067, 4, 999, 1, 77]], dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor([517, 300, 0], dtype=torch.int32, device=DEV)
+    scale = 0.3
+    idx, sel = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k, with_scores=True)
+    o, lse = csa.attend(q, kc, vc, idx, n_ent, scale=scale, with_lse=True)
+    oh, lseh = csa.hca_attend(q, kc, vc, q_pos, n_ent, m, scale=scale, with_lse=True)
+    torch.cuda.synchronize()
+    I = np64(idx)
+    Q, K, Vv, QI, KI, W = (np64(t) for t in (q, kc, vc, qi, ki, wi))
+    qp, ne = q_pos.cpu().numpy(), n_ent.cpu().numpy()
+    O, L, OH, LH = np64(o), np64(lse), np64(oh), np64(lseh)
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible_count(int(qp[b, t]), m, int(ne[b]))
+            s_ref = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+            check_topk(I[b, t], s_ref, V, k)
+            o_ref, l_ref = oracle.attend(Q[b, t], K[b], Vv[b], I[b, t], scale)
+            check_attention(O[b, t], o_ref, tag, f"csa b={b} t={t}")
+            check_lse(L[b, t], l_ref, 1e-5 if tag == "f32" else 2.5e-3)
+            oh_ref, lh_ref = oracle.hca_attend(Q[b, t], K[b], Vv[b], V, scale)
+            check_attention(OH[b, t], oh_ref, tag, f"hca b={b} t={t}")
+            check_lse(LH[b, t], lh_ref, 1e-5 if tag == "f32" else 2.5e-3)
+    # sequence 2 has no valid rows: nothing selected, zero output
+    assert np.all(I[2] == -1) and np.all(O[2] == 0) and np.all(np.isneginf(L[2]))
+
+
+def test_tuned_kernels_ragged():
+    """bf16 64 x 128 (the MFMA kernels) on ragged sizes: partial tiles, V < k,
+    partially valid caches, an empty sequence."""
+    B, Tq, N_max, m, k = 4, 2, 1000 + 3 * 8, 4, 300
+    _say("tuned ragged bf16 64x128")
+    q = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 7)
+    kc = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 8)
+    vc = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 9)
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 10)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 11)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 12)
+    q_pos = torch.tensor([[5000, 2], [803, 1200], [4095, 100000], [9, 3]], dtype=torch.int32,
+                         device=DEV)
+    n_ent = torch.tensor([N_max, 777, 1001, 0], dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qi, wi, ki, q_pos, n_ent, m)
+    idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k)
+    o, lse = csa.attend(q, kc, vc, idx, n_ent, with_lse=True)
+    oh, lseh = csa.hca_attend(q, kc, vc, q_pos, n_ent, m, with_lse=True)
+    torch.cuda.synchronize()
+    S, I = np64(scores), np64(idx)
+    Q, K, Vv, QI, KI, W = (np64(t) for t in (q, kc, vc, qi, ki, wi))
+    qp, ne = q_pos.cpu().numpy(), n_ent.cpu().numpy()
+    O, L, OH, LH = np64(o), np64(lse), np64(oh), np64(lseh)
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible_count(int(qp[b, t]), m, int(ne[b]))
+            s_ref = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+            assert np.all(np.isneginf(S[b, t, V:]))
+            if V:
+                bound = score_bound(QI[b, t], W[b, t], KI[b, :V], 128, 64)
+                assert np.all(np.abs(S[b, t, :V] - s_ref[:V]) <= bound)
+            check_topk(I[b, t], s_ref, V, k)
+            o_ref, l_ref = oracle.attend(Q[b, t], K[b], Vv[b], I[b, t])
+            check_attention(O[b, t], o_ref, "bf16", f"csa b={b} t={t}")
+            check_lse(L[b, t], l_ref, 2.5e-3)
+            oh_ref, lh_ref = oracle.hca_attend(Q[b, t], K[b], Vv[b], V)
+            check_attention(OH[b, t], oh_ref, "bf16", f"hca b={b} t={t}")
+            check_lse(LH[b, t], lh_ref, 2.5e-3)
+
+
+def test_attention_sharp_and_single_entry():
+    """Sharp softmax (logit std ~3) where the absolute gates bite, repeated and
+    invalid indices, and a single selected entry (output = that value row)."""
+    B, Tq, N_max, k = 2, 3, 4096, 1024
+    _say("sharp attention bf16 64x128")
+    q = _randn((B, Tq, 64, 128), 3.0, torch.bfloat16, 21)
+    kc = _randn((B, N_max, 128), 1.0, torch.bfloat16, 22)
+    vc = _randn((B, N_max, 128), 1.0, torch.bfloat16, 23)
+    g = _gen(24)
+    idx = torch.randint(-50, N_max + 50, (B, Tq, k), generator=g, device=DEV, dtype=torch.int32)
+    idx[1, 2] = -1
+    idx[1, 2, 17] = 3000                                   # single valid entry
+    idx[0, 1, :512] = idx[0, 1, 512:]                      # repeated entries
+    n_ent = torch.tensor([N_max, 3500], dtype=torch.int32, device=DEV)
+    o, lse = csa.attend(q, kc, vc, idx, n_ent, with_lse=True)
+    torch.cuda.synchronize()
+    Q, K, Vv, I = np64(q), np64(kc), np64(vc), np64(idx)
+    O, L = np64(o), np64(lse)
+    ne = n_ent.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            sel = [j for j in I[b, t] if 0 <= j < ne[b]]
+            o_ref, l_ref = oracle.attend(Q[b, t], K[b], Vv[b], sel)
+            check_attention(O[b, t], o_ref, "bf16", f"sharp b={b} t={t}")
+            check_lse(L[b, t], l_ref, 2e-2)
+    assert np.array_equal(O[1, 2], np.tile(Vv[1, 3000], (64, 1)))
+
+
+def test_compress_edge_cases():
+    _say("compress edge cases")
+    g = _gen(31)
+    # m = 1 is an exact copy; a ragged tail of n % m tokens is ignored
+    x = torch.randn((2, 37, 64), generator=g, device=DEV).to(torch.bfloat16)
+    z = torch.randn((2, 37), generator=g, device=DEV)
+    out = csa.compress(x, z, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x)
+    out = csa.compress(x, z, 4)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 9, 64)
+    for b in range(2):
+        check_compress(np64(out)[b], np64(x)[b][:36], np64(z)[b][:36], 4, "bf16")
+    # large pooling factor, strided output rows, fp32
+    x = torch.randn((1, 8192, 32), generator=g, device=DEV)
+    z = torch.randn((1, 8192), generator=g, device=DEV) * 4
+    dst = torch.zeros((1, 2, 48), device=DEV)
+    csa.compress(x, z, 4096, out=dst[..., :32])
+    torch.cuda.synchronize()
+    check_compress(np64(dst)[0, :, :32], np64(x)[0], np64(z)[0], 4096, "f32")
+    assert np.all(np64(dst)[0, :, 32:] == 0)
+
+
+def test_batch_invariance_and_determinism():
+    """A sequence's results are bitwise identical alone, in a batch, and with
+    different batch-mates; repeated runs are bitwise identical."""
+    _say("batch invariance")
+    N, k = 8192 + 96, 1024
+    def draw(B, seed):
+        return dict(
+            q=_randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.bfloat16, seed),
+            kc=_randn((B, N, 128), 1 / math.sqrt(128), torch.bfloat16, seed + 1),
+            vc=_randn((B, N, 128), 1 / math.sqrt(128), torch.bfloat16, seed + 2),
+            qi=_randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.bfloat16, seed + 3),
+            ki=_randn((B, N, 128), 1 / math.sqrt(128), torch.bfloat16, seed + 4),
+            wi=_randn((B, 1, 64), 1 / 8, torch.float32, seed + 5))
+    def run(d, m=4):
+        B = d["q"].shape[0]
+        pos = torch.full((B, 1), 4 * N, dtype=torch.int32, device=DEV)
+        ne = torch.full((B,), N, dtype=torch.int32, device=DEV)
+        idx = csa.index_topk(d["qi"], d["wi"], d["ki"], pos, ne, m, k)
+        o = csa.attend(d["q"], d["kc"], d["vc"], idx, ne)
+        oh = csa.hca_attend(d["q"], d["kc"], d["vc"], pos, ne, m)
+        torch.cuda.synchronize()
+        return idx, o, oh
+    a = draw(4, 40)
+    b = draw(4, 50)
+    mix = {key: torch.cat([a[key][:1], b[key][1:]]) for key in a}
+    alone = {key: a[key][:1].contiguous() for key in a}
+    r1, r2, r3, r4 = run(a), run(a), run(mix), run(alone)
+    for x, y in zip(r1, r2):
+        assert torch.equal(x, y)
+    for x, y, z in zip(r1, r3, r4):
+        assert torch.equal(x[:1], y[:1]) and torch.equal(x[:1], z)

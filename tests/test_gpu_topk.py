@@ -1,0 +1,86 @@
+"""GPU top-k selection on given fp32 score matrices.  Selection involves no
+floating-point arithmetic, so the result must equal the oracle's exactly:
+same indices, same order, same padding, for every row."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import long_context_attention_24_amd as csa
+import oracle
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run(scores: np.ndarray, visible: np.ndarray, k: int):
+    """scores [R, N] float32, visible [R] -> GPU idx [R, k], selected scores."""
+    R, N = scores.shape
+    print(f"topk R={R} N={N} k={k}", flush=True)
+    sys.stdout.flush()
+    s = torch.from_numpy(scores.astype(np.float32)).to(DEV).reshape(1, R, N)
+    q_pos = torch.from_numpy(visible.astype(np.int32) - 1).to(DEV).reshape(1, R)
+    n_ent = torch.tensor([N], dtype=torch.int32, device=DEV)
+    idx, val = csa.topk(s, q_pos, n_ent, 1, k, with_scores=True)     # m = 1: V = q_pos + 1
+    torch.cuda.synchronize()
+    return idx.cpu().numpy()[0], val.cpu().numpy()[0]
+
+
+def _check(scores, visible, k):
+    idx, val = _run(scores, visible, k)
+    for r in range(scores.shape[0]):
+        V = int(min(visible[r], scores.shape[1]))
+        ref = oracle.topk_select(scores[r].astype(np.float64), V, k)
+        assert np.array_equal(idx[r], ref), f"row {r}: first diff at {np.nonzero(idx[r] != ref)[0][:5]}"
+        n = int((ref >= 0).sum())
+        assert np.array_equal(val[r, :n], scores[r, ref[:n]])
+        assert np.all(np.isneginf(val[r, n:]))
+
+
+@pytest.mark.parametrize("N,k", [(1, 1), (7, 3), (64, 16), (1000, 37), (4096, 1024),
+                                 (32768, 1024), (40000, 1024), (66560, 1024), (262144, 1024),
+                                 (100000, 2048)])
+def test_topk_random(N, k):
+    rng = np.random.default_rng(N + k)
+    R = 6
+    s = rng.standard_normal((R, N)).astype(np.float32) * 0.05
+    vis = np.array([N, max(1, N // 2), min(N, k), max(1, k - 1), 1, N])
+    _check(s, vis, k)
+
+
+@pytest.mark.parametrize("N", [300, 32768, 70000])
+def test_topk_ties_and_signed_zeros(N):
+    rng = np.random.default_rng(N)
+    k = min(1024, N // 3)
+    ties = rng.integers(-3, 4, size=(2, N)).astype(np.float32)         # 7 distinct values
+    zeros = np.where(rng.random((2, N)) < 0.5, -0.0, 0.0).astype(np.float32)
+    zeros[1, ::7] = 1.0
+    const = np.full((1, N), 0.125, np.float32)
+    s = np.concatenate([ties, zeros, const])
+    vis = np.full(5, N)
+    _check(s, vis, k)
+
+
+def test_topk_hard_distributions():
+    N, k = 32768, 1024
+    rng = np.random.default_rng(3)
+    rows = []
+    # one far outlier compresses everything else into the lowest bins
+    r = rng.standard_normal(N).astype(np.float32)
+    r[123] = 1e30
+    rows.append(r)
+    # values spread over many binades: many refinement passes
+    r = (2.0 ** -rng.integers(0, 120, N)).astype(np.float32) * rng.choice([-1, 1], N)
+    rows.append(r.astype(np.float32))
+    # neighbouring floats around the boundary
+    base = np.float32(0.3)
+    r = np.nextafter(base, np.float32(1), dtype=np.float32) * np.ones(N, np.float32)
+    r[: N // 2] = base
+    rows.append(r)
+    # subnormals and huge magnitudes
+    r = rng.standard_normal(N).astype(np.float32) * np.float32(1e-40)
+    r[::5] = np.float32(3e38) * np.sign(rng.standard_normal(N // 5 + 1)[: len(r[::5])])
+    rows.append(r.astype(np.float32))
+    s = np.stack(rows)
+    _check(s, np.full(len(rows), N), k)

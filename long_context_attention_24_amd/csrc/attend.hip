@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
 }
 
 // ---------------------------------------------------------------- bf16 64 x 128, split
-constexpr int kCsaSplit = 128;     // entries of the top-k list per workgroup
+constexpr int kCsaSplit = 64;      // entries of the top-k list per workgroup (one tile per wave)
 constexpr int kHcaSplit = 512;     // visible entries per workgroup
 constexpr int kPartStride = 132;   // floats per (split, head): O[128], m, l, pad
 constexpr int kVtRow = 36;         // bf16 per V^T row in LDS (32 entries + pad)
@@ -291,46 +291,71 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
   }
 }
 
-// One workgroup per query row: 256 threads = 64 heads x 4 quarters of D.
+// Merge of the split partials.  Grid (rows, 4 head groups); thread (h, c)
+// owns 8 output dims of one head.  All splits' maxima are read first (one
+// round of independent loads), then all partial rows.
+constexpr int kCombineUnroll = 8;
+
 __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ part,
                                                              int nsplit, uint16_t* __restrict__ out,
                                                              float* __restrict__ lse) {
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int h = tid >> 2, qd = tid & 3;
-  const float* base = part + static_cast<int64_t>(row) * nsplit * 64 * kPartStride;
+  const int h = blockIdx.y * 16 + (tid >> 4), dc = (tid & 15) * 8;
+  const int64_t sstride = 64 * kPartStride;
+  const float* base = part + (static_cast<int64_t>(row) * nsplit * 64 + h) * kPartStride;
   float M = kNegInf;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, base[(s * 64 + h) * kPartStride + 128]);
-  float L = 0.f;
-  float acc[32];
+  int s = 0;
+  for (; s + kCombineUnroll <= nsplit; s += kCombineUnroll) {
+    float mm[kCombineUnroll];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
+    for (int u = 0; u < kCombineUnroll; ++u) mm[u] = base[(s + u) * sstride + 128];
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) M = fmaxf(M, mm[u]);
+  }
+  for (; s < nsplit; ++s) M = fmaxf(M, base[s * sstride + 128]);
+  float L = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (M != kNegInf) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float* ps = base + (s * 64 + h) * kPartStride;
+    s = 0;
+    for (; s + kCombineUnroll <= nsplit; s += kCombineUnroll) {
+      float4 lo[kCombineUnroll], hi[kCombineUnroll];
+      float ml[kCombineUnroll], ll[kCombineUnroll];
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const float* ps = base + (s + u) * sstride;
+        lo[u] = *reinterpret_cast<const float4*>(ps + dc);
+        hi[u] = *reinterpret_cast<const float4*>(ps + dc + 4);
+        ml[u] = ps[128];
+        ll[u] = ps[129];
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const float w = exp2_fast(ml[u] - M);
+        L = fmaf(w, ll[u], L);
+        acc[0] = fmaf(w, lo[u].x, acc[0]); acc[1] = fmaf(w, lo[u].y, acc[1]);
+        acc[2] = fmaf(w, lo[u].z, acc[2]); acc[3] = fmaf(w, lo[u].w, acc[3]);
+        acc[4] = fmaf(w, hi[u].x, acc[4]); acc[5] = fmaf(w, hi[u].y, acc[5]);
+        acc[6] = fmaf(w, hi[u].z, acc[6]); acc[7] = fmaf(w, hi[u].w, acc[7]);
+      }
+    }
+    for (; s < nsplit; ++s) {
+      const float* ps = base + s * sstride;
       const float w = exp2_fast(ps[128] - M);
       L = fmaf(w, ps[129], L);
 #pragma unroll
-      for (int i = 0; i < 32; i += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(ps + 32 * qd + i);
-        acc[i] = fmaf(w, v.x, acc[i]);
-        acc[i + 1] = fmaf(w, v.y, acc[i + 1]);
-        acc[i + 2] = fmaf(w, v.z, acc[i + 2]);
-        acc[i + 3] = fmaf(w, v.w, acc[i + 3]);
-      }
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, ps[dc + i], acc[i]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* oh = out + (static_cast<int64_t>(row) * 64 + h) * 128 + 32 * qd;
-#pragma unroll
-  for (int i = 0; i < 32; i += 8) {
-    uint4 v;
-    v.x = pack_bf16x2(acc[i] * inv, acc[i + 1] * inv);
-    v.y = pack_bf16x2(acc[i + 2] * inv, acc[i + 3] * inv);
-    v.z = pack_bf16x2(acc[i + 4] * inv, acc[i + 5] * inv);
-    v.w = pack_bf16x2(acc[i + 6] * inv, acc[i + 7] * inv);
-    st16(oh + i, v);
-  }
-  if (lse != nullptr && qd == 0)
+  uint4 v;
+  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
+  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
+  st16(out + (static_cast<int64_t>(row) * 64 + h) * 128 + dc, v);
+  if (lse != nullptr && dc == 0)
     lse[static_cast<int64_t>(row) * 64 + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
@@ -399,7 +424,7 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
                        a.n_entries, a.Tq, a.N_max, a.m, scale_log2, sl, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.B * a.Tq), dim3(256), 0, s, part, nsplit,
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.B * a.Tq, 4), dim3(256), 0, s, part, nsplit,
                      static_cast<uint16_t*>(a.out), a.lse);
   return hipGetLastError();
 }

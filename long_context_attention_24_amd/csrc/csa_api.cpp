@@ -78,6 +78,26 @@ csa_status_t check_score_args(const void* q_idx, const float* q_scale, const flo
   return CSA_OK;
 }
 
+// Chunk bounds written by the tuned score kernels: one per 256-key chunk of a
+// row, each the c-th largest score of its chunk (see topk.hip).
+int bound_chunks(int N_max) {
+  return (N_max + csa::score_chunk_keys() - 1) / csa::score_chunk_keys();
+}
+// The k the score kernel's chunk bounds serve, or 0 when no bounds are used
+// (untuned score shape, or rows too long for the bounded selection).
+int bound_k(csa_dtype_t dt, int H_I, int D_I, int N_max, int k) {
+  return csa::score_tuned(dt, H_I, D_I) && csa::topk_bounded_workspace_bytes(1, N_max) > 0 ? k : 0;
+}
+
+// scores | chunk bounds | selection workspace
+size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws) {
+  const size_t rows = static_cast<size_t>(B) * Tq;
+  const size_t bws = csa::topk_bounded_workspace_bytes(static_cast<int>(rows), N_max);
+  return round_up(rows * score_row_stride(N_max) * sizeof(float)) +
+         round_up(rows * bound_chunks(N_max) * sizeof(float)) +
+         round_up(topk_ws > bws ? topk_ws : bws);
+}
+
 }  // namespace
 
 extern "C" {
@@ -134,7 +154,8 @@ csa_status_t csa_index_score(const void* q_idx, const float* q_scale, const floa
   if (st != CSA_OK) return st;
   CSA_REQUIRE(scores, CSA_ERR_INVALID_ARGUMENT, "index score: NULL scores");
   csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
-                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, N_max};
+                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, N_max,
+                   nullptr, 0, 0};
   return hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
 }
 
@@ -165,8 +186,8 @@ csa_status_t csa_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
   const size_t need = csa::topk_workspace_bytes(B * Tq, N_max, k);
   CSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), CSA_ERR_WORKSPACE_TOO_SMALL,
               "topk: workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(csa::launch_topk(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, topk_idx,
-                                     topk_score, ws, stream),
+  return hip_status(csa::launch_topk(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, nullptr,
+                                     0, topk_idx, topk_score, ws, stream),
                     "topk launch");
 }
 
@@ -175,10 +196,10 @@ csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* b
   size_t t = 0;
   csa_status_t st = csa_topk_workspace(B, Tq, N_max, k, &t);
   if (st != CSA_OK) return st;
-  *bytes = round_up(static_cast<size_t>(B) * Tq * score_row_stride(N_max) * sizeof(float)) +
-           round_up(t);
+  *bytes = index_topk_ws_bytes(B, Tq, N_max, t);
   return CSA_OK;
 }
+
 
 csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float* w_idx,
                             const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
@@ -197,15 +218,21 @@ csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float
   CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
               "index topk: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
   const int64_t srs = score_row_stride(N_max);
-  float* scores = static_cast<float*>(ws);
-  void* tws = static_cast<char*>(ws) +
-              round_up(static_cast<size_t>(B) * Tq * srs * sizeof(float));
+  const size_t rows = static_cast<size_t>(B) * Tq;
+  char* base = static_cast<char*>(ws);
+  float* scores = reinterpret_cast<float*>(base);
+  base += round_up(rows * srs * sizeof(float));
+  const int n_chunks = bound_chunks(N_max);
+  const int bk = bound_k(idx_dtype, H_I, D_I, N_max, k);
+  float* bounds = bk > 0 ? reinterpret_cast<float*>(base) : nullptr;
+  base += round_up(rows * n_chunks * sizeof(float));
   csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
-                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs};
+                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs,
+                   bounds, n_chunks, bk};
   st = hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
   if (st != CSA_OK) return st;
-  return hip_status(csa::launch_topk(scores, srs, q_pos, n_entries, B, Tq, N_max, m, k, topk_idx,
-                                     topk_score, tws, stream),
+  return hip_status(csa::launch_topk(scores, srs, q_pos, n_entries, B, Tq, N_max, m, k, bounds,
+                                     n_chunks, topk_idx, topk_score, base, stream),
                     "topk launch");
 }
 

@@ -39,53 +39,42 @@ __device__ __forceinline__ int visible_count(int q_pos, int m, int n_entries, in
   return v < 0 ? 0 : static_cast<int>(v);
 }
 
+// Selection bound shared by the score and top-k kernels: every chunk of
+// kBoundChunk keys reports its c-th largest score, c being the smallest value
+// with floor(V / kBoundChunk) * c >= k for a row with V visible entries.  The
+// minimum of the reports is then at most the row's k-th largest score.
+// Returns 0 (no bound) when that c would exceed kMaxBoundC.
+constexpr int kBoundChunk = 256;
+constexpr int kMaxBoundC = 16;
+__device__ __forceinline__ int bound_c_row(int V, int k) {
+  const int full = V / kBoundChunk;
+  if (full == 0 || k <= 0) return 0;
+  const int c = (k + full - 1) / full;
+  return c <= kMaxBoundC ? c : 0;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// ---- wave64 reductions (fixed butterfly order: deterministic) -------------
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_min(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
+// ---- wave64 reductions and scans -------------------------------------------
+// The device library's DPP implementations (row shifts and broadcasts, no LDS
+// round trips).  Each uses a fixed combination order, so results are
+// deterministic.  All 64 lanes must be active.
+extern "C" __device__ float __ockl_wfred_max_f32(float);
+extern "C" __device__ float __ockl_wfred_min_f32(float);
+extern "C" __device__ float __ockl_wfred_add_f32(float);
+extern "C" __device__ uint32_t __ockl_wfred_add_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfscan_add_u32(uint32_t, bool);
+
+__device__ __forceinline__ float wave_max(float v) { return __ockl_wfred_max_f32(v); }
+__device__ __forceinline__ float wave_min(float v) { return __ockl_wfred_min_f32(v); }
+__device__ __forceinline__ float wave_sum(float v) { return __ockl_wfred_add_f32(v); }
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return __ockl_wfred_add_u32(v); }
 __device__ __forceinline__ int wave_sum_int(int v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return static_cast<int>(__ockl_wfred_add_u32(static_cast<uint32_t>(v)));
 }
 // inclusive prefix sum over the 64 lanes
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-
 __device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return __ockl_wfscan_add_u32(v, true);
 }
 
 // 16-byte vector load / store helpers

@@ -11,7 +11,7 @@
 // ReLU, head weight and the head sum stay in registers, followed by a single
 // exchange between lanes l and l^32.  K rows are loaded straight into the B
 // operand (lane l%32 = key row, 16 contiguous bytes per lane per k-step),
-// one tile ahead of the MFMAs.
+// two tiles ahead of the MFMAs.
 //
 // The MFMA k-slot order does not matter for a dot product as long as A and
 // B use the same one, so slot (lane/32, e) of k-step s holds dimension
@@ -64,27 +64,91 @@ __global__ __launch_bounds__(256) void score_generic_kernel(
   srow[j] = s;
 }
 
+// ---------------------------------------------------------------- selection bound
+// Each wave also reports the c-th largest of the scores it produced (its
+// chunk of kBoundChunk keys), with c = bound_c_row(V, k) for the row.  Every
+// chunk that reports a finite value holds c entries at or above it, and the
+// floor(V / kBoundChunk) full chunks all do, so the minimum report is at most
+// the row's k-th largest score.  The top-k kernels use that bound to drop
+// most entries before selecting.  A chunk with fewer than c valid entries
+// reports +inf; rows with no bound (c = 0) write nothing.
+constexpr float kPosInf = __builtin_inff();
+
+template <int NV>
+__device__ float wave_cth_largest(const float (&vals)[NV], bool active, int c) {
+  const int lane = threadIdx.x & 63;
+  float v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = active ? vals[i] : kNegInf;
+  float cur = kPosInf;
+  for (int r = 0; r < c; ++r) {
+    float lm = v[0];
+#pragma unroll
+    for (int i = 1; i < NV; ++i) lm = fmaxf(lm, v[i]);
+    const float wm = wave_max(lm);
+    if (wm == kNegInf) {
+      cur = kPosInf;
+      break;
+    }
+    const unsigned long long msk = __ballot(lm == wm);
+    if (lane == __ffsll(msk) - 1) {     // remove one occurrence of the maximum
+      bool done = false;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        if (!done && v[i] == wm) {
+          v[i] = kNegInf;
+          done = true;
+        }
+      }
+    }
+    cur = wm;
+  }
+  return cur;
+}
+
 // ---------------------------------------------------------------- bf16, 64 heads x 128
 constexpr int kWavesPerWg = 4;
-constexpr int kKeysPerWave = 256;
+constexpr int kTilesPerWave = 8;                  // tiles of 32 keys
+constexpr int kKeysPerWave = 32 * kTilesPerWave;  // one selection chunk
 constexpr int kKeysPerWg = kWavesPerWg * kKeysPerWave;
+static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 
+// Straight-line code over the wave's 8 tiles with a 3-deep ring of B-operand
+// registers: the loads of tile t+2 are issued before the MFMAs of tile t and
+// no register is copied, so the compiler's wait counts leave two tiles (16 KB
+// per wave) in flight behind the math.  Rows past the visible range are
+// clamped to the last visible row (in bounds, L2 hits) and masked on output.
 __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
-    int64_t s_rs) {
+    int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 31, g = lane >> 5;
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-  const int key0 = (blockIdx.x * kWavesPerWg + wave) * kKeysPerWave;
+  const int chunk = blockIdx.x * kWavesPerWg + wave;
+  const int key0 = chunk * kKeysPerWave;
   if (key0 >= N_max) return;
   const int key_end = min(key0 + kKeysPerWave, N_max);
   const int vis_end = min(key_end, V);
   float* srow = scores + row * s_rs;
   for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
-  if (key0 >= vis_end) return;
+  if (key0 >= vis_end) {
+    if (chunk_thr != nullptr && lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = kPosInf;
+    return;
+  }
+
+  const uint16_t* kb = k + b * k_sb + 8 * g;
+  bf16x8_t kt[3][8];
+  auto load_tile = [&](int t, bf16x8_t (&dst)[8]) {
+    const int j = min(key0 + 32 * t + jl, vis_end - 1);
+    const uint16_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) dst[s] = ld_bf16x8(kr + 16 * s);
+  };
+  load_tile(0, kt[0]);
+  load_tile(1, kt[1]);
 
   // A operand: q_I rows (heads) of this query; two 32-head tiles x 8 k-steps
   const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
@@ -103,21 +167,16 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     w0[r] = wrow[h];
     w1[r] = wrow[32 + h];
   }
-  const uint16_t* kb = k + b * k_sb + 8 * g;
-  bf16x8_t cur[8], nxt[8];
-  {
-    const int j = min(key0 + jl, vis_end - 1);
-    const uint16_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+
+  float sc[kTilesPerWave];
+  // sched_barrier(0) keeps the scheduler from sinking the prefetch loads
+  // below the MFMAs of the current tile (it would, to shorten live ranges).
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) cur[s] = ld_bf16x8(kr + 16 * s);
-  }
-  for (int j0 = key0; j0 < vis_end; j0 += 32) {
-    if (j0 + 32 < vis_end) {
-      const int j = min(j0 + 32 + jl, vis_end - 1);
-      const uint16_t* kr = kb + static_cast<int64_t>(j) * k_sn;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) nxt[s] = ld_bf16x8(kr + 16 * s);
-    }
+  for (int t = 0; t < kTilesPerWave; ++t) {
+    if (t + 2 < kTilesPerWave) load_tile(t + 2, kt[(t + 2) % 3]);
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8_t (&cur)[8] = kt[t % 3];
     f32x16_t c0 = {}, c1 = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -131,10 +190,16 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], fmaxf(c1[r], 0.f), sum);
     const float other = __shfl_xor(sum, 32, 64);
     const float tot = sum + other;     // commutative: both halves get the same bits
-    const int j = j0 + jl;
-    if (g == 0 && j < vis_end) srow[j] = tot;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) cur[s] = nxt[s];
+    const int j = key0 + 32 * t + jl;
+    const bool ok = j < vis_end;
+    if (g == 0 && ok) srow[j] = tot;
+    sc[t] = ok ? tot : kNegInf;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int thr_c = bound_c_row(V, bound_k);
+  if (chunk_thr != nullptr && thr_c > 0) {
+    const float cth = wave_cth_largest<kTilesPerWave>(sc, g == 0, thr_c);
+    if (lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = cth;
   }
 }
 
@@ -160,24 +225,45 @@ __device__ __forceinline__ uint64_t fp4x8_to_fp8x8(uint32_t c) {
 
 // 16x16x32 fp8 MFMA: K = 32 is exactly one scale block, so each MFMA gives
 // the exact per-block partial dot product; block scales are applied in fp32.
-// A operand lane l: head row l%16, dims 8*(l/16) .. +7 of the block.
+// A operand lane l: head row l%16, dims 8*(l/16) .. +7 of the block.  A wave
+// covers 256 keys as 16 tiles of 16 keys, unrolled, loads two tiles ahead.
+constexpr int kFp4Tiles = kKeysPerWave / 16;
+
 __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale, int64_t k_sb, int64_t k_sn,
     int64_t ks_sb, int64_t ks_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
-    int64_t s_rs) {
+    int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-  const int key0 = (blockIdx.x * kWavesPerWg + wave) * kKeysPerWave;
+  const int chunk = blockIdx.x * kWavesPerWg + wave;
+  const int key0 = chunk * kKeysPerWave;
   if (key0 >= N_max) return;
   const int key_end = min(key0 + kKeysPerWave, N_max);
   const int vis_end = min(key_end, V);
   float* srow = scores + row * s_rs;
   for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
-  if (key0 >= vis_end) return;
+  if (key0 >= vis_end) {
+    if (chunk_thr != nullptr && lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = kPosInf;
+    return;
+  }
+
+  const uint8_t* kb = k + b * k_sb + 4 * g;
+  const float* ksb = k_scale + b * ks_sb;
+  uint32_t kc[3][4];
+  float4 ks[3];
+  auto load_tile = [&](int t, uint32_t (&c)[4], float4& sc4) {
+    const int j = min(key0 + 16 * t + nl, vis_end - 1);
+    const uint8_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) c[blk] = *reinterpret_cast<const uint32_t*>(kr + 16 * blk);
+    sc4 = *reinterpret_cast<const float4*>(ksb + static_cast<int64_t>(j) * ks_sn);
+  };
+  load_tile(0, kc[0], ks[0]);
+  load_tile(1, kc[1], ks[1]);
 
   // q: [64 heads][64 bytes] codes, [64][4] scales
   const uint8_t* qrow = q + static_cast<int64_t>(row) * 64 * 64;
@@ -205,19 +291,17 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
       for (int blk = 0; blk < 4; ++blk) sq[mt][r][blk] = qsrow[h * 4 + blk];
     }
 
-  const uint8_t* kb = k + b * k_sb + 4 * g;
-  const float* ksb = k_scale + b * ks_sb;
-  for (int j0 = key0; j0 < vis_end; j0 += 16) {
-    const int j = min(j0 + nl, vis_end - 1);
-    const uint8_t* kr = kb + static_cast<int64_t>(j) * k_sn;
-    uint32_t kc[4];
+  float scv[kFp4Tiles];
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) kc[blk] = *reinterpret_cast<const uint32_t*>(kr + 16 * blk);
-    const float4 sk = *reinterpret_cast<const float4*>(ksb + static_cast<int64_t>(j) * ks_sn);
+  for (int t = 0; t < kFp4Tiles; ++t) {
+    if (t + 2 < kFp4Tiles) load_tile(t + 2, kc[(t + 2) % 3], ks[(t + 2) % 3]);
+    __builtin_amdgcn_sched_barrier(0);
+    const float4 sk = ks[t % 3];
     const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
     uint64_t bop[4];
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) bop[blk] = fp4x8_to_fp8x8(kc[blk]);
+    for (int blk = 0; blk < 4; ++blk) bop[blk] = fp4x8_to_fp8x8(kc[t % 3][blk]);
     float sum = 0.f;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
@@ -230,17 +314,25 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float t = 0.f;
+        float tv = 0.f;
 #pragma unroll
-        for (int blk = 0; blk < 4; ++blk) t = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], t);
-        sum = fmaf(wv[mt][r], fmaxf(t, 0.f), sum);
+        for (int blk = 0; blk < 4; ++blk) tv = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], tv);
+        sum = fmaf(wv[mt][r], fmaxf(tv, 0.f), sum);
       }
     }
     // heads are spread over the four 16-lane groups of the key's column
     sum = sum + __shfl_xor(sum, 16, 64);
     sum = sum + __shfl_xor(sum, 32, 64);
-    const int jj = j0 + nl;
-    if (g == 0 && jj < vis_end) srow[jj] = sum;
+    const int jj = key0 + 16 * t + nl;
+    const bool ok = jj < vis_end;
+    if (g == 0 && ok) srow[jj] = sum;
+    scv[t] = ok ? sum : kNegInf;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int thr_c = bound_c_row(V, bound_k);
+  if (chunk_thr != nullptr && thr_c > 0) {
+    const float cth = wave_cth_largest<kFp4Tiles>(scv, g == 0, thr_c);
+    if (lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = cth;
   }
 }
 
@@ -254,6 +346,12 @@ void launch_generic(const ScoreArgs& a, hipStream_t s) {
 
 }  // namespace
 
+bool score_tuned(csa_dtype_t dt, int H, int D) {
+  return (dt == CSA_FP4_E2M1 || dt == CSA_BF16) && H == 64 && D == 128;
+}
+
+int score_chunk_keys() { return kKeysPerWave; }
+
 bool score_supported(csa_dtype_t dt, int H, int D) {
   if (dt == CSA_FP4_E2M1) return H == 64 && D == 128;
   if (dt != CSA_F32 && dt != CSA_BF16) return false;
@@ -266,13 +364,14 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
     hipLaunchKernelGGL(score_fp4_h64d128_kernel, grid, dim3(256), 0, s,
                        static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                        static_cast<const uint8_t*>(a.k), a.k_scale, a.k_sb, a.k_sn, a.ks_sb,
-                       a.ks_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs);
+                       a.ks_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs,
+                       a.chunk_thr, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
     const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
     hipLaunchKernelGGL(score_bf16_h64d128_kernel, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
                        a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
-                       a.s_rs);
+                       a.s_rs, a.chunk_thr, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16) {
     if (a.D == 32) launch_generic<uint16_t, 32>(a, s);
     else if (a.D == 64) launch_generic<uint16_t, 64>(a, s);

@@ -28,17 +28,26 @@ struct ScoreArgs {
   int B, Tq, N_max, H, D, m;
   float* scores;            // [B*Tq, s_rs]
   int64_t s_rs;             // row stride of scores (elements)
+  float* chunk_thr;         // [B*Tq, n_chunks] selection bounds (tuned kernels), or NULL
+  int n_chunks, bound_k;    // bound_k: the k the bounds serve (0: none)
 };
 hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s);
 bool score_supported(csa_dtype_t dt, int H, int D);
+bool score_tuned(csa_dtype_t dt, int H, int D);   // writes chunk bounds
+int score_chunk_keys();                            // keys per bound chunk
 
 // ---- topk.hip
-// Workspace bytes needed for rows of N_max scores and a given k.
+// Selection from rows of N_max scores.  chunk_thr (nullable): per-row bounds
+// written by the tuned score kernels (one report per 256-key chunk, n_chunks
+// per row, for the same k).  The workspace is topk_bounded_workspace_bytes
+// with bounds, topk_workspace_bytes without.
 size_t topk_workspace_bytes(int rows, int N_max, int k);
+size_t topk_bounded_workspace_bytes(int rows, int N_max);   // 0: bounds not usable
 bool topk_supported(int N_max, int k);
 hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
-                       int32_t* idx, float* out_scores, void* ws, hipStream_t s);
+                       const float* chunk_thr, int n_chunks, int32_t* idx,
+                       float* out_scores, void* ws, hipStream_t s);
 
 // ---- attend.hip
 struct AttendArgs {

@@ -19,7 +19,10 @@ def _run(scores: np.ndarray, visible: np.ndarray, k: int):
     R, N = scores.shape
     print(f"topk R={R} N={N} k={k}", flush=True)
     sys.stdout.flush()
-    s = torch.from_numpy(scores.astype(np.float32)).to(DEV).reshape(1, R, N)
+    Np = (N + 3) // 4 * 4                       # rows must be 16-byte aligned
+    padded = np.full((R, Np), -np.inf, np.float32)
+    padded[:, :N] = scores
+    s = torch.from_numpy(padded).to(DEV).reshape(1, R, Np)[..., :N]
     q_pos = torch.from_numpy(visible.astype(np.int32) - 1).to(DEV).reshape(1, R)
     n_ent = torch.tensor([N], dtype=torch.int32, device=DEV)
     idx, val = csa.topk(s, q_pos, n_ent, 1, k, with_scores=True)     # m = 1: V = q_pos + 1

@@ -86,16 +86,14 @@ int bound_chunks(int N_max) {
 // The k the score kernel's chunk bounds serve, or 0 when no bounds are used
 // (untuned score shape, or rows too long for the bounded selection).
 int bound_k(csa_dtype_t dt, int H_I, int D_I, int N_max, int k) {
-  return csa::score_tuned(dt, H_I, D_I) && csa::topk_bounded_workspace_bytes(1, N_max) > 0 ? k : 0;
+  return csa::score_tuned(dt, H_I, D_I) && csa::topk_bounded_ok(N_max) ? k : 0;
 }
 
 // scores | chunk bounds | selection workspace
 size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws) {
   const size_t rows = static_cast<size_t>(B) * Tq;
-  const size_t bws = csa::topk_bounded_workspace_bytes(static_cast<int>(rows), N_max);
   return round_up(rows * score_row_stride(N_max) * sizeof(float)) +
-         round_up(rows * bound_chunks(N_max) * sizeof(float)) +
-         round_up(topk_ws > bws ? topk_ws : bws);
+         round_up(rows * bound_chunks(N_max) * sizeof(float)) + round_up(topk_ws);
 }
 
 }  // namespace

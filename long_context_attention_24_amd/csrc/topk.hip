@@ -18,19 +18,18 @@
 // Only integer LDS atomics (counts) are used, so results are deterministic.
 //
 // Drivers.
-//   * Bounded (topk_filter_kernel + topk_select_kernel), used with the chunk
-//     bounds the tuned score kernels leave: per 256-key chunk of a row its
-//     c-th largest score, whose minimum over the row is at most the row's
-//     k-th largest (see bound_c_row).  Entries below it can never be selected.
-//     The filter spreads the row over many workgroups (4096 entries each) and
-//     compacts the survivors of each slice in index order; the select kernel
-//     gathers a row's survivors into LDS and selects from them.
+//   * Bounded (topk_bounded_kernel), used with the chunk bounds the tuned
+//     score kernels leave: per 256-key chunk of a row its c-th largest
+//     score, whose minimum over the row is at most the row's k-th largest
+//     (see bound_c_row).  Entries below it can never be selected, so one
+//     workgroup per row keeps the few survivors in LDS and selects there.
 //   * Unbounded (topk_seg_kernel): one workgroup per row segment of up to
 //     32768 scores.  Rows longer than one segment take two passes: each
 //     segment keeps its own top-k (a superset of its share of the row's
 //     top-k) and one workgroup selects from the concatenation, which is in
 //     index order.
 #include <float.h>
+#include <limits.h>
 
 #include "device_common.h"
 #include "internal.h"
@@ -57,7 +56,9 @@ struct Scratch {
   float f0[2][kMaxWaves];
   float f1[2][kMaxWaves];
   uint32_t u[2][kMaxWaves];
+  uint32_t tab[1024];                 // per-thread prefix of the index bitmap
   int bstar, bstar_above, bstar_cnt;
+  uint32_t list_n;                    // survivors appended so far
 };
 __shared__ Scratch g_sm;
 
@@ -110,6 +111,7 @@ __device__ __forceinline__ void zero_hist() {
 // A run gives thread t the values at positions t*len() .. t*len()+len()-1
 // (-inf for invalid ones, including positions past the end).
 struct LdsRun {                   // LDS, linear, n values
+  static constexpr int kUnroll = 1;
   const lds_float* v;
   int n, r;
   __device__ __forceinline__ int len() const { return r; }
@@ -143,19 +145,23 @@ __device__ __forceinline__ int bin_of(float x, double dlo, double inv) {
   return f >= static_cast<double>(kBins - 1) ? kBins - 1 : static_cast<int>(f);
 }
 
-// Selects the top-k of the valid values (> -inf) of the block's run and calls
-// emit(position, value, slot) for each, slots 0.. in ascending position
-// order.  Returns the number selected, min(k, #valid).  On entry the
-// histogram is zero and a barrier separates its zeroing (and any LDS writes
-// of the run) from this call.
+// Threshold search over the valid values (> -inf) of the block's run: on
+// return the top-k are every value > T plus the first take_eq values == T in
+// position order (take_eq = 1 << 30: all of them).  On entry the histogram
+// is zero and a barrier separates its zeroing (and any LDS writes of the run)
+// from this call; on return it is zero again.  Run::kUnroll > 1 marks a run
+// held in registers, whose loops must be unrolled completely.
 template <int NW, typename Run>
-__device__ __forceinline__ int block_select(const Run run, int k, int& p, const Emitter emit) {
+__device__ __forceinline__ void threshold_search(const Run& run, int k, int& p, float& T,
+                                                 int& take_eq) {
   constexpr int THREADS = NW * 64;
   constexpr int BPT = kBins / THREADS;           // histogram bins per thread
+  constexpr int UF = Run::kUnroll;
   const int tid = threadIdx.x;
   const int R = run.len();
   uint32_t n_valid = 0;
   float mn = FLT_MAX, mx = -FLT_MAX;
+#pragma unroll UF
   for (int i = 0; i < R; ++i) {
     const float x = run.get(i);
     if (x > kNegInf) {
@@ -165,72 +171,84 @@ __device__ __forceinline__ int block_select(const Run run, int k, int& p, const 
     }
   }
   block_minmax_count<NW>(mn, mx, n_valid, p);
-
-  float T = kNegInf;          // selection: all v > T, plus the first take_eq with v == T
-  int take_eq = 0;
-  if (n_valid > static_cast<uint32_t>(k)) {
-    float lo = mn, hi = mx;
-    int need = k;
-    for (int iter = 0;; ++iter) {
-      if (lo == hi || iter >= 64) {     // all candidates equal (64 is never reached)
-        T = lo;
-        take_eq = need;
-        break;
-      }
-      const double dlo = static_cast<double>(lo);
-      const double inv = static_cast<double>(kBins) / (static_cast<double>(hi) - dlo);
-      for (int i = 0; i < R; ++i) {
-        const float x = run.get(i);
-        if (x >= lo && x <= hi) atomicAdd(&g_sm.hist[bin_of(x, dlo, inv)], 1);
-      }
-      __syncthreads();
-      // locate the bin b* holding the need-th largest candidate
-      uint32_t h[BPT];
-      uint32_t hs = 0;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) {
-        h[j] = g_sm.hist[BPT * tid + j];
-        hs += h[j];
-      }
-      uint32_t tot;
-      const uint32_t pre = block_excl_scan<NW>(hs, tot, p);
-      uint32_t above = tot - pre - hs;                 // candidates in bins above this thread's
-      const uint32_t un = static_cast<uint32_t>(need);
-#pragma unroll
-      for (int j = BPT - 1; j >= 0; --j) {
-        if (above < un && un <= above + h[j]) {
-          g_sm.bstar = BPT * tid + j;
-          g_sm.bstar_above = static_cast<int>(above);
-          g_sm.bstar_cnt = static_cast<int>(h[j]);
-        }
-        above += h[j];
-      }
-      __syncthreads();
-      const int bstar = g_sm.bstar;
-      need -= g_sm.bstar_above;
-      const int cnt = g_sm.bstar_cnt;
-#pragma unroll
-      for (int j = 0; j < BPT; ++j) g_sm.hist[BPT * tid + j] = 0;   // ready for the next pass
-      float bmn = FLT_MAX, bmx = -FLT_MAX;
-      uint32_t unused = 0;
-      for (int i = 0; i < R; ++i) {
-        const float x = run.get(i);
-        if (x >= lo && x <= hi && bin_of(x, dlo, inv) == bstar) {
-          bmn = fminf(bmn, x);
-          bmx = fmaxf(bmx, x);
-        }
-      }
-      block_minmax_count<NW>(bmn, bmx, unused, p);
-      if (cnt == need) {                // the whole bin is selected
-        T = bmn;
-        take_eq = 1 << 30;
-        break;
-      }
-      lo = bmn;
-      hi = bmx;
+  T = kNegInf;
+  take_eq = 0;
+  if (n_valid <= static_cast<uint32_t>(k)) return;
+  float lo = mn, hi = mx;
+  int need = k;
+  for (int iter = 0;; ++iter) {
+    if (lo == hi || iter >= 64) {     // all candidates equal (64 is never reached)
+      T = lo;
+      take_eq = need;
+      return;
     }
+    const double dlo = static_cast<double>(lo);
+    const double inv = static_cast<double>(kBins) / (static_cast<double>(hi) - dlo);
+#pragma unroll UF
+    for (int i = 0; i < R; ++i) {
+      const float x = run.get(i);
+      if (x >= lo && x <= hi) atomicAdd(&g_sm.hist[bin_of(x, dlo, inv)], 1);
+    }
+    __syncthreads();
+    // locate the bin b* holding the need-th largest candidate
+    uint32_t h[BPT];
+    uint32_t hs = 0;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      h[j] = g_sm.hist[BPT * tid + j];
+      hs += h[j];
+    }
+    uint32_t tot;
+    const uint32_t pre = block_excl_scan<NW>(hs, tot, p);
+    uint32_t above = tot - pre - hs;                 // candidates in bins above this thread's
+    const uint32_t un = static_cast<uint32_t>(need);
+#pragma unroll
+    for (int j = BPT - 1; j >= 0; --j) {
+      if (above < un && un <= above + h[j]) {
+        g_sm.bstar = BPT * tid + j;
+        g_sm.bstar_above = static_cast<int>(above);
+        g_sm.bstar_cnt = static_cast<int>(h[j]);
+      }
+      above += h[j];
+    }
+    __syncthreads();
+    const int bstar = g_sm.bstar;
+    need -= g_sm.bstar_above;
+    const int cnt = g_sm.bstar_cnt;
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) g_sm.hist[BPT * tid + j] = 0;   // ready for the next pass
+    float bmn = FLT_MAX, bmx = -FLT_MAX;
+    uint32_t unused = 0;
+#pragma unroll UF
+    for (int i = 0; i < R; ++i) {
+      const float x = run.get(i);
+      if (x >= lo && x <= hi && bin_of(x, dlo, inv) == bstar) {
+        bmn = fminf(bmn, x);
+        bmx = fmaxf(bmx, x);
+      }
+    }
+    block_minmax_count<NW>(bmn, bmx, unused, p);
+    if (cnt == need) {                // the whole bin is selected
+      T = bmn;
+      take_eq = 1 << 30;
+      return;
+    }
+    lo = bmn;
+    hi = bmx;
   }
+}
 
+// Selects the top-k of the block's run, whose positions are contiguous per
+// thread (thread t holds positions t*len() ..), and calls emit(position,
+// value, slot) for each, slots 0.. in ascending position order.  Returns the
+// number selected, min(k, #valid).  Entry conditions as threshold_search.
+template <int NW, typename Run>
+__device__ __forceinline__ int block_select(const Run run, int k, int& p, const Emitter emit) {
+  const int tid = threadIdx.x;
+  const int R = run.len();
+  float T;
+  int take_eq;
+  threshold_search<NW>(run, k, p, T, take_eq);
   // ordered compaction
   uint32_t gt = 0, eq = 0;
   for (int i = 0; i < R; ++i) {
@@ -290,6 +308,7 @@ __device__ __forceinline__ float row_bound(const float* __restrict__ thr, int n_
 // LDS run of R values per thread in the transposed layout v[i*THREADS + t].
 template <int THREADS>
 struct SplitRun {
+  static constexpr int kUnroll = 1;
   const lds_float* v;
   int r;
   __device__ __forceinline__ int len() const { return r; }
@@ -298,6 +317,7 @@ struct SplitRun {
 
 // Global-memory run, linear, n values (-0.0 read as +0.0).
 struct GlobalRun {
+  static constexpr int kUnroll = 1;
   const float* __restrict__ v;
   int n, r;
   __device__ __forceinline__ int len() const { return r; }
@@ -417,152 +437,352 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 }
 
 // ============================================================ bounded path
-constexpr int kFiltSeg = 4096;                    // entries per filter workgroup (16 per thread)
-constexpr int kMaxSlices = kSegThreads;           // slices per row: N_max <= 1M
-constexpr int kSelCap = 16384;                    // survivors a select workgroup holds in LDS
+// topk_bounded_kernel: one 1024-thread workgroup per row.
+//   1. The row bound comes from the chunk reports (one block reduction).
+//   2. The row is streamed in chunks of 32768 scores (eight coalesced 16-byte
+//      loads per thread, the next chunk's loads in flight while the current
+//      one is filtered); entries at or above the bound are appended to an LDS
+//      list, one LDS atomic per wave reserving the wave's range.  The list is
+//      unordered.
+//   3. Radix selection on order-preserving 32-bit keys, offset by the
+//      smallest survivor key: each pass histograms the next (up to) 11 bits
+//      of the keys still in play (2048 LDS bins, two per thread), one block
+//      scan locates the bin of the k-th largest, and the pass ends the search
+//      when that bin is wholly taken or holds a single key.
+//   4. The taken entries set their bit in an LDS bitmap over entry indices; a
+//      block scan of its popcounts gives every taken entry its output slot,
+//      which puts the result in ascending index order.  Among entries equal
+//      to the threshold value only the lowest indices are taken.
+// A row whose survivors overflow the list selects from the score row
+// directly (block_select, slow but exact).
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kRadixBits = 11;
+static_assert((1 << kRadixBits) == kBins && kBins == 2 * kSelThreads, "two bins per thread");
+constexpr int kMaxBoundedN = 262144;              // index bitmap: 8192 words of LDS
+constexpr int kBitmapWords = kMaxBoundedN / 32;
+constexpr int kStageVec = 8;                      // 16-byte loads per thread per chunk
+constexpr int kStageChunk = kSelThreads * 4 * kStageVec;
+constexpr int kListCap = 12 * kSelThreads;        // survivors held in LDS
 
-// One workgroup per (slice of 4096 entries, row).  The slice's scores (four
-// coalesced 16-byte loads per thread) and the row's chunk bounds are all in
-// flight together; the entries at or above the row bound (all valid entries
-// when the row has no bound) are written, in index order, to the front of the
-// slice's region of the survivor buffers, and their number to slice_cnt.
-__global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(
-    const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
-    const float* __restrict__ chunk_thr, int n_chunks, int nslice,
-    float* __restrict__ slice_val, int32_t* __restrict__ slice_idx,
-    int32_t* __restrict__ slice_cnt) {
-  constexpr int NW = kSegThreads / 64;
-  const int seg = blockIdx.x, row = blockIdx.y, b = row / Tq;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-  const int seg0 = seg * kFiltSeg;
-  const int L = max(0, min(V - seg0, kFiltSeg));
-  const float* srow = scores + row * s_rs + seg0;
-  float v[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = kSegThreads * 4 * i + 4 * tid;
-    if (q + 3 < L) {
-      const float4 x = *reinterpret_cast<const float4*>(srow + q);
-      v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < L) ? srow[q + e] : kNegInf;
-    }
-  }
-  int p = 0;
-  const float bound = row_bound<NW>(chunk_thr + static_cast<int64_t>(row) * n_chunks, n_chunks,
-                                    bound_c_row(V, k), k, p);
-  // positions: 1024 i + 4 tid + e, so (i, wave, lane, e) order is index order
-  uint32_t c[4], incl[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    c[i] = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) c[i] += (v[i][e] > kNegInf && v[i][e] >= bound) ? 1u : 0u;
-    incl[i] = wave_incl_scan_u32(c[i]);
-    if (lane == 63) g_sm.u[p][NW * i + wave] = incl[i];
-  }
-  __syncthreads();
-  const uint32_t x = lane < 4 * NW ? g_sm.u[p][lane] : 0u;
-  const uint32_t y = wave_incl_scan_u32(x);
-  const int64_t slice = (static_cast<int64_t>(row) * nslice + seg) * kFiltSeg;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t o = __builtin_amdgcn_readlane(y, NW * i + wave) -
-                 __builtin_amdgcn_readlane(x, NW * i + wave) + incl[i] - c[i];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (v[i][e] > kNegInf && v[i][e] >= bound) {
-        slice_val[slice + o] = v[i][e] + 0.0f;   // -0.0 -> +0.0
-        slice_idx[slice + o] = seg0 + kSegThreads * 4 * i + 4 * tid + e;
-        ++o;
-      }
-    }
-  }
-  if (tid == 0) {
-    slice_cnt[static_cast<int64_t>(row) * nslice + seg] =
-        static_cast<int32_t>(__builtin_amdgcn_readlane(y, 4 * NW - 1));
-  }
+typedef __attribute__((address_space(3))) uint32_t lds_uint;
+
+// order-preserving key of a float that is not NaN and not -0.0
+__device__ __forceinline__ uint32_t ord_key(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-// One workgroup per row: slice counts -> block scan -> every survivor loaded
-// (consecutive survivors to consecutive threads, slice found by binary search
-// over the LDS prefix) and stored at its rank in LDS -> block_select.  Rows
-// with more survivors than LDS holds select from the score row directly.
-__global__ __launch_bounds__(kSegThreads) void topk_select_kernel(
-    const float* __restrict__ slice_val, const int32_t* __restrict__ slice_idx,
-    const int32_t* __restrict__ slice_cnt, int nslice, const float* __restrict__ scores,
-    int64_t s_rs, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries,
-    int Tq, int N_max, int m, int k, int32_t* __restrict__ out_idx, float* __restrict__ out_val) {
-  constexpr int NW = kSegThreads / 64;
-  constexpr int U = 8;                            // survivor loads in flight per thread
-  __shared__ float cv[kSelCap];
-  __shared__ int cp[kSelCap];
-  __shared__ int offs[kMaxSlices];
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const uint32_t my_cnt =
-      tid < nslice ? static_cast<uint32_t>(slice_cnt[static_cast<int64_t>(row) * nslice + tid]) : 0u;
-  zero_hist<kSegThreads>();
-  int p = 0;
-  uint32_t n_u;
-  const uint32_t pre = block_excl_scan<NW>(my_cnt, n_u, p);
-  if (tid < nslice) offs[tid] = static_cast<int>(pre);
-  __syncthreads();
-  const int n = static_cast<int>(n_u);
-  Emitter em;
-  em.oi = out_idx + static_cast<int64_t>(row) * k;
-  em.ov = out_val ? out_val + static_cast<int64_t>(row) * k : nullptr;
-  em.base = 0;
-  em.use_lmap = false;
-  em.lmap = nullptr;
-  em.gmap = nullptr;
-  int n_sel;
-  if (n <= kSelCap) {
-    const float* sv = slice_val + static_cast<int64_t>(row) * nslice * kFiltSeg;
-    const int32_t* si = slice_idx + static_cast<int64_t>(row) * nslice * kFiltSeg;
-    for (int q0 = 0; q0 < n; q0 += U * kSegThreads) {
-      float xv[U];
-      int xi[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = q0 + u * kSegThreads + tid;
-        int lo = 0, hi = nslice;                  // largest s with offs[s] <= q
-        while (hi - lo > 1) {
-          const int mid = (lo + hi) >> 1;
-          if (offs[mid] <= q) lo = mid;
-          else hi = mid;
+// Survivors of one row: element (i, thread t) is survivor i * 1024 + t.
+template <int NV>
+struct RegSrc {                         // held in registers
+  static constexpr int kUnroll = NV;
+  float v[NV];
+  int e[NV];
+  __device__ __forceinline__ int len() const { return NV; }
+  __device__ __forceinline__ float val(int i) const { return v[i]; }
+  __device__ __forceinline__ int idx(int i) const { return e[i]; }
+};
+__device__ __forceinline__ void set_bit(lds_uint* bm, int e) {
+  __hip_atomic_fetch_or(&bm[e >> 5], 1u << (e & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Bitmap ranks: after the bits are set and a barrier, bitmap_prefix gives each
+// thread the number of set bits before its words (WPT words per thread) in
+// g_sm.tab; after one more barrier bitmap_rank(e) is the number of set bits
+// below bit e.
+__device__ __forceinline__ uint32_t bitmap_prefix(const lds_uint* bm, int W, int WPT, int& p) {
+  uint32_t ps = 0;
+  for (int j = 0; j < WPT; ++j) {
+    const int w = threadIdx.x * WPT + j;
+    if (w < W) ps += __popc(bm[w]);
+  }
+  uint32_t tot;
+  g_sm.tab[threadIdx.x] = block_excl_scan<kSelWaves>(ps, tot, p);
+  return tot;
+}
+__device__ __forceinline__ int bitmap_rank(const lds_uint* bm, int WPT, int e) {
+  const int w = e >> 5, t = w / WPT;
+  uint32_t r = g_sm.tab[t];
+  for (int x = t * WPT; x < w; ++x) r += __popc(bm[x]);
+  return static_cast<int>(r + __popc(bm[w] & ((1u << (e & 31)) - 1u)));
+}
+
+template <typename Src>
+__device__ __forceinline__ void radix_select(const Src& src, int n, uint32_t kmin, uint32_t kmax,
+                                             int k, int W, int WPT, lds_uint* bm, int& p,
+                                             int32_t* __restrict__ oi, float* __restrict__ ov) {
+  constexpr int NW = kSelWaves;
+  constexpr int UF = Src::kUnroll;
+  const int tid = threadIdx.x;
+  const int R = src.len();
+  // selection: key u = ord_key(x) - kmin; taken if u > Tu, or u == Tu and
+  // index <= Emax
+  int64_t Tu = -1;
+  int take_eq = 0;
+  if (n > k) {
+    const uint32_t range = kmax - kmin;
+    int hs = range == 0 ? 0 : 32 - __clz(range);  // keys still in play: (u >> hs) == prefix
+    uint64_t prefix = 0;
+    int need = k;
+    if (hs == 0) {
+      Tu = 0;
+      take_eq = k;
+    }
+    while (hs > 0) {
+      const int shift = max(hs - kRadixBits, 0);
+      const uint32_t dmask = (1u << (hs - shift)) - 1u;
+#pragma unroll UF
+      for (int i = 0; i < R; ++i) {
+        const float x = src.val(i);
+        if (x > kNegInf) {
+          const uint64_t u = ord_key(x) - kmin;
+          if ((u >> hs) == prefix) atomicAdd(&g_sm.hist[(u >> shift) & dmask], 1);
         }
-        const int64_t at = static_cast<int64_t>(lo) * kFiltSeg + (q - offs[lo]);
-        xv[u] = q < n ? sv[at] : 0.f;
-        xi[u] = q < n ? si[at] : 0;
       }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int q = q0 + u * kSegThreads + tid;
-        if (q < n) {
-          cv[q] = xv[u];
-          cp[q] = xi[u];
-        }
+      __syncthreads();
+      const uint32_t h0 = g_sm.hist[2 * tid], h1 = g_sm.hist[2 * tid + 1];
+      uint32_t tot;
+      const uint32_t pre = block_excl_scan<NW>(h0 + h1, tot, p);
+      uint32_t above = tot - pre - h0 - h1;
+      const uint32_t un = static_cast<uint32_t>(need);
+      if (above < un && un <= above + h1) {
+        g_sm.bstar = 2 * tid + 1;
+        g_sm.bstar_above = static_cast<int>(above);
+        g_sm.bstar_cnt = static_cast<int>(h1);
+      }
+      above += h1;
+      if (above < un && un <= above + h0) {
+        g_sm.bstar = 2 * tid;
+        g_sm.bstar_above = static_cast<int>(above);
+        g_sm.bstar_cnt = static_cast<int>(h0);
+      }
+      g_sm.hist[2 * tid] = 0;
+      g_sm.hist[2 * tid + 1] = 0;
+      __syncthreads();
+      need -= g_sm.bstar_above;
+      const int cnt = g_sm.bstar_cnt;
+      prefix = (prefix << (hs - shift)) | static_cast<uint64_t>(g_sm.bstar);
+      hs = shift;
+      if (cnt == need) {                          // the whole bin is taken
+        Tu = static_cast<int64_t>(prefix << hs) - 1;
+        take_eq = 0;
+        break;
+      }
+      if (hs == 0) {                              // the bin is the single key Tu
+        Tu = static_cast<int64_t>(prefix);
+        take_eq = need;
+      }
+    }
+  }
+  int emax = INT_MAX;
+  if (take_eq > 0) {
+    // more entries equal the threshold than are taken: keep the take_eq
+    // lowest indices, found from the ranks of the equal entries' bits
+#pragma unroll UF
+    for (int i = 0; i < R; ++i) {
+      const float x = src.val(i);
+      if (x > kNegInf && static_cast<int64_t>(ord_key(x) - kmin) == Tu) {
+        const int e = src.idx(i);
+        set_bit(bm, e);
       }
     }
     __syncthreads();
-    em.use_lmap = true;
-    em.lmap = (const lds_int*)cp;
-    // an odd run length keeps the strided run reads free of bank conflicts
-    const int r = ((n + kSegThreads - 1) / kSegThreads) | 1;
-    n_sel = block_select<NW>(LdsRun{(const lds_float*)cv, n, r}, k, p, em);
-  } else {
-    const int b = row / Tq;
-    const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-    n_sel = block_select<NW>(GlobalRun{scores + row * s_rs, V, (V + kSegThreads - 1) / kSegThreads},
-                             k, p, em);
+    bitmap_prefix(bm, W, WPT, p);
+    __syncthreads();
+#pragma unroll UF
+    for (int i = 0; i < R; ++i) {
+      const float x = src.val(i);
+      if (x > kNegInf && static_cast<int64_t>(ord_key(x) - kmin) == Tu) {
+        const int e = src.idx(i);
+        if (bitmap_rank(bm, WPT, e) == take_eq - 1) g_sm.bstar = e;
+      }
+    }
+    __syncthreads();
+    emax = g_sm.bstar;
+    for (int j = 0; j < WPT; ++j) {
+      const int w = tid * WPT + j;
+      if (w < W) bm[w] = 0;
+    }
+    __syncthreads();
   }
-  pad_output<kSegThreads>(em, n_sel, k);
+  // bitmap of the taken indices -> output slots
+#pragma unroll UF
+  for (int i = 0; i < R; ++i) {
+    const float x = src.val(i);
+    if (x > kNegInf) {
+      const int64_t u = static_cast<int64_t>(ord_key(x) - kmin);
+      const int e = src.idx(i);
+      if (u > Tu || (u == Tu && e <= emax)) set_bit(bm, e);
+    }
+  }
+  __syncthreads();
+  const int n_sel = static_cast<int>(bitmap_prefix(bm, W, WPT, p));
+  __syncthreads();
+#pragma unroll UF
+  for (int i = 0; i < R; ++i) {
+    const float x = src.val(i);
+    if (x > kNegInf) {
+      const int64_t u = static_cast<int64_t>(ord_key(x) - kmin);
+      const int e = src.idx(i);
+      if (u > Tu || (u == Tu && e <= emax)) {
+        const int slot = bitmap_rank(bm, WPT, e);
+        if (slot < k) {                           // always true; keeps writes in bounds
+          oi[slot] = e;
+          if (ov != nullptr) ov[slot] = x;
+        }
+      }
+    }
+  }
+  for (int sl = n_sel + tid; sl < k; sl += kSelThreads) {
+    oi[sl] = -1;
+    if (ov != nullptr) ov[sl] = kNegInf;
+  }
 }
 
-int bounded_slices(int N_max) { return (N_max + kFiltSeg - 1) / kFiltSeg; }
+template <int NV>
+__device__ __forceinline__ void select_list(const lds_float* lv, const lds_int* li, int n,
+                                            uint32_t kmin, uint32_t kmax, int k, int W, int WPT,
+                                            lds_uint* bm, int& p, int32_t* __restrict__ oi,
+                                            float* __restrict__ ov) {
+  RegSrc<NV> src;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int q = i * kSelThreads + threadIdx.x;
+    src.v[i] = q < n ? lv[q] : kNegInf;
+    src.e[i] = q < n ? li[q] : 0;
+  }
+  radix_select(src, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
+}
+
+__device__ __forceinline__ void load_stage(const float* __restrict__ srow, int c0, int V,
+                                           float4 (&x)[kStageVec]) {
+#pragma unroll
+  for (int i = 0; i < kStageVec; ++i) {
+    const int q = c0 + 4 * (i * kSelThreads + static_cast<int>(threadIdx.x));
+    if (q + 3 < V) {
+      x[i] = *reinterpret_cast<const float4*>(srow + q);
+    } else {
+      x[i].x = q < V ? srow[q] : kNegInf;
+      x[i].y = q + 1 < V ? srow[q + 1] : kNegInf;
+      x[i].z = q + 2 < V ? srow[q + 2] : kNegInf;
+      x[i].w = q + 3 < V ? srow[q + 3] : kNegInf;
+    }
+  }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
+    const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
+    const float* __restrict__ chunk_thr, int n_chunks, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_val) {
+  constexpr int NW = kSelWaves;
+  __shared__ uint32_t bm_s[kBitmapWords];
+  __shared__ float lv_s[kListCap];
+  __shared__ int li_s[kListCap];
+  lds_uint* bm = (lds_uint*)bm_s;
+  lds_float* lv = (lds_float*)lv_s;
+  lds_int* li = (lds_int*)li_s;
+  const int row = blockIdx.x, b = row / Tq;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const float* srow = scores + row * s_rs;
+  float4 x[kStageVec];
+  load_stage(srow, 0, V, x);
+  const int W = (N_max + 31) >> 5;
+  const int WPT = (W + kSelThreads - 1) / kSelThreads;
+  g_sm.hist[2 * tid] = 0;
+  g_sm.hist[2 * tid + 1] = 0;
+  for (int j = 0; j < WPT; ++j) {
+    const int w = tid * WPT + j;
+    if (w < W) bm[w] = 0;
+  }
+  if (tid == 0) g_sm.list_n = 0;
+  // 1. row bound
+  const int c = bound_c_row(V, k);
+  float bmn = FLT_MAX, unused_f = -FLT_MAX;
+  uint32_t bcnt = 0;
+  if (c > 0) {
+    const float* thr = chunk_thr + static_cast<int64_t>(row) * n_chunks;
+    for (int i = tid; i < n_chunks; i += kSelThreads) {
+      const float t = thr[i];
+      if (t != kPosInf) {
+        bmn = fminf(bmn, t);
+        ++bcnt;
+      }
+    }
+  }
+  int p = 0;
+  block_minmax_count<NW>(bmn, unused_f, bcnt, p);   // barrier: LDS state zeroed
+  const float bound = (c > 0 && static_cast<long long>(bcnt) * c >= k) ? bmn : kNegInf;
+  // 2. stream the row, appending survivors
+  float smin = FLT_MAX, smax = -FLT_MAX;
+  for (int c0 = 0; c0 < V; c0 += kStageChunk) {
+    float4 y[kStageVec];
+    const bool more = c0 + kStageChunk < V;
+    if (more) load_stage(srow, c0 + kStageChunk, V, y);
+    uint32_t cl = 0;
+#pragma unroll
+    for (int i = 0; i < kStageVec; ++i) {
+      const float e4[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) cl += (e4[e] > kNegInf && e4[e] >= bound) ? 1u : 0u;
+    }
+    const uint32_t incl = wave_incl_scan_u32(cl);
+    const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
+    if (tot > 0) {                                  // uniform in the wave
+      uint32_t base = 0;
+      if (lane == 0) base = atomicAdd(&g_sm.list_n, tot);
+      base = __builtin_amdgcn_readfirstlane(base);
+      uint32_t o = base + incl - cl;
+#pragma unroll
+      for (int i = 0; i < kStageVec; ++i) {
+        const float e4[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = e4[e];
+          if (v > kNegInf && v >= bound) {
+            smin = fminf(smin, v);
+            smax = fmaxf(smax, v);
+            if (o < static_cast<uint32_t>(kListCap)) {
+              lv[o] = v + 0.0f;                     // -0.0 -> +0.0
+              li[o] = c0 + 4 * (i * kSelThreads + tid) + e;
+            }
+            ++o;
+          }
+        }
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < kStageVec; ++i) x[i] = y[i];
+    }
+  }
+  uint32_t unused_u = 0;
+  block_minmax_count<NW>(smin, smax, unused_u, p);  // barrier: the list is complete
+  const int n = static_cast<int>(g_sm.list_n);
+  int32_t* oi = out_idx + static_cast<int64_t>(row) * k;
+  float* ov = out_val ? out_val + static_cast<int64_t>(row) * k : nullptr;
+  const uint32_t kmin = ord_key(smin + 0.0f), kmax = ord_key(smax + 0.0f);
+  if (n <= 4 * kSelThreads) {
+    select_list<4>(lv, li, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
+  } else if (n <= 8 * kSelThreads) {
+    select_list<8>(lv, li, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
+  } else if (n <= kListCap) {
+    select_list<12>(lv, li, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
+  } else {
+    Emitter em;
+    em.oi = oi;
+    em.ov = ov;
+    em.base = 0;
+    em.use_lmap = false;
+    em.lmap = nullptr;
+    em.gmap = nullptr;
+    const int n_sel =
+        block_select<NW>(GlobalRun{srow, V, (V + kSelThreads - 1) / kSelThreads}, k, p, em);
+    pad_output<kSelThreads>(em, n_sel, k);
+  }
+}
 
 int num_segments(int N_max) { return (N_max + kSegCap - 1) / kSegCap; }
 
@@ -580,13 +800,7 @@ size_t topk_workspace_bytes(int rows, int N_max, int k) {
   return static_cast<size_t>(rows) * nseg * k * (sizeof(float) + sizeof(int32_t));
 }
 
-bool topk_bounded_ok(int N_max) { return bounded_slices(N_max) <= kMaxSlices; }
-
-size_t topk_bounded_workspace_bytes(int rows, int N_max) {
-  if (!topk_bounded_ok(N_max)) return 0;
-  const size_t ns = static_cast<size_t>(rows) * bounded_slices(N_max);
-  return ns * kFiltSeg * (sizeof(float) + sizeof(int32_t)) + ns * sizeof(int32_t);
-}
+bool topk_bounded_ok(int N_max) { return N_max <= kMaxBoundedN; }
 
 hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
@@ -594,17 +808,8 @@ hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        void* ws, hipStream_t s) {
   const int rows = B * Tq;
   if (chunk_thr != nullptr && topk_bounded_ok(N_max)) {
-    const int ns = bounded_slices(N_max);
-    const size_t slots = static_cast<size_t>(rows) * ns * kFiltSeg;
-    float* sv = static_cast<float*>(ws);
-    int32_t* si = reinterpret_cast<int32_t*>(sv + slots);
-    int32_t* sc = si + slots;
-    hipLaunchKernelGGL(topk_filter_kernel, dim3(ns, rows), dim3(kSegThreads), 0, s, scores, s_rs,
-                       q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, ns, sv, si, sc);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_select_kernel, dim3(rows), dim3(kSegThreads), 0, s, sv, si, sc, ns,
-                       scores, s_rs, q_pos, n_entries, Tq, N_max, m, k, idx, out_scores);
+    hipLaunchKernelGGL(topk_bounded_kernel, dim3(rows), dim3(kSelThreads), 0, s, scores, s_rs,
+                       q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, idx, out_scores);
     return hipGetLastError();
   }
   const int nseg = num_segments(N_max);

@@ -11,9 +11,14 @@ rotate through independent input copies (4 x 403 MB) and every step streams
 from HBM.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (only 1),
---graph (time the step captured in a HIP graph), --no-cpu-baseline,
---copy-calibration (run only a plain device copy of known size, for scaling
-rocprofv3 FETCH_SIZE / WRITE_SIZE counters).
+--graph (also time the step captured in a HIP graph), --no-cpu-baseline,
+--score-only (launch only the indexer score kernel, for hardware-counter
+runs), --copy-calibration (run only a plain device copy of known size, for
+scaling the FETCH_SIZE / WRITE_SIZE counters).
+
+roofline.traffic is read from the counter summary committed under profiles/;
+it is null when the score kernel's source no longer matches the one the
+counters were taken on.
 """
 from __future__ import annotations
 
@@ -32,6 +37,9 @@ METRIC = "CSA decode tokens/sec + achieved HBM GB/s at 128K context, 1 MI355X"
 WORKLOAD = "csa_decode_128k"
 HBM_PEAK_GBS = 8000.0
 N_COPIES = 4
+SCORE_KERNEL = "score_bf16_h64d128_kernel"
+SCORE_SOURCE = os.path.join(ROOT, "long_context_attention_24_amd", "csrc", "index_score.hip")
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_bf16_h64d128_csa_decode_128k_traffic.txt")
 
 
 def parse():
@@ -43,6 +51,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true")
+    p.add_argument("--score-only", action="store_true")
     return p.parse_args()
 
 
@@ -75,17 +84,20 @@ def _calibrate_sleep() -> float:
 
 
 def copy_calibration():
-    n = 1 << 30
-    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    """A plain elementwise copy (x * 1.0) of 2**28 fp32 values: 1 GiB read and
+    1 GiB written per launch, for scaling hardware byte counters."""
+    n = 1 << 28
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(5):
-        dst.copy_(src)
+        torch.mul(src, 1.0, out=dst)
     torch.cuda.synchronize()
-    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}))
+    print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5}))
 
 
 def cpu_baseline(w, inputs, seconds):
-    """The oracle as it stands, on this host, on a bounded sample of sequences."""
+    """The oracle as it stands, on this host: passes over the batch's
+    sequences (one decode token each) until about `seconds` have elapsed."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_info
@@ -94,8 +106,8 @@ def cpu_baseline(w, inputs, seconds):
         if t.dtype == torch.bfloat16 else t.cpu().double().numpy()
     host = {k: f64(v) for k, v in inputs.items() if v.dtype != torch.int32}
     done, t0 = 0, time.perf_counter()
-    while done < w.B:
-        b = done
+    while True:
+        b = done % w.B
         oracle.csa_reference(q=host["q"][b, 0], q_idx=host["q_idx"][b, 0], w_idx=host["w_idx"][b, 0],
                              k_cache=host["k_cache"][b], v_cache=host["v_cache"][b],
                              k_idx=host["ki_cache"][b], q_pos=w.q_pos0, m=w.m, k=w.k, n_entries=w.N)
@@ -105,8 +117,27 @@ def cpu_baseline(w, inputs, seconds):
     el = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} of {w.B} sequences of {WORKLOAD} (one decode token each), "
-                      f"fp64 NumPy oracle, {el:.1f} s"}
+            "sample": f"{done} decode tokens ({done / w.B:.1f} passes over the {w.B} sequences of "
+                      f"{WORKLOAD}), fp64 NumPy oracle, {el:.1f} s"}
+
+
+def recorded_traffic():
+    """HBM bytes per score-kernel launch from the committed counter summary,
+    or None if it is missing or was taken on a different kernel source."""
+    import hashlib
+    try:
+        lines = open(TRAFFIC_SUMMARY).read().splitlines()
+    except OSError:
+        return None
+    kv = {}
+    for ln in lines:
+        if ":" in ln and not ln.startswith(" "):
+            key, val = ln.split(":", 1)
+            kv[key.strip()] = val.strip()
+    src = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
+    if kv.get("source_sha256") != src or "hbm_bytes_per_launch" not in kv:
+        return None
+    return int(kv["hbm_bytes_per_launch"])
 
 
 def main():
@@ -144,9 +175,10 @@ def main():
         csa.index_score(c["q_idx"], c["w_idx"], c["ki_cache"], c["q_pos"], c["n_entries"], w.m,
                         out=scores)
 
-    def topk_only(i):
+    def index_topk_only(i):
         c = copies[i % N_COPIES]
-        csa.topk(scores, c["q_pos"], c["n_entries"], w.m, w.k)
+        csa.index_topk(c["q_idx"], c["w_idx"], c["ki_cache"], c["q_pos"], c["n_entries"], w.m, w.k,
+                       workspace=ws_topk, out=idx[i % N_COPIES])
 
     def attend_only(i):
         c = copies[i % N_COPIES]
@@ -201,9 +233,13 @@ def main():
             graphs.append(g)
         graph_ms = timed(lambda i: graphs[i % N_COPIES].replay(), args.steps, args.warmup)
 
+    if args.score_only:
+        ms = timed(score_only, args.steps, args.warmup, per_launch=True)
+        print(json.dumps({"score_only_ms": round(ms, 5), "launches": args.steps + args.warmup}))
+        return
     ms = timed(step, args.steps, args.warmup)
     score_ms = timed(score_only, args.steps, args.warmup, per_launch=True)
-    topk_ms = timed(topk_only, args.steps, args.warmup, per_launch=True)
+    index_topk_ms = timed(index_topk_only, args.steps, args.warmup, per_launch=True)
     attend_ms = timed(attend_only, args.steps, args.warmup, per_launch=True)
     best_ms = min(ms, graph_ms) if graph_ms else ms
 
@@ -232,12 +268,14 @@ def main():
         "step_algorithmic_bytes": step_bytes,
         "ms_per_step_eager": round(ms, 5),
         "ms_per_step_graph": round(graph_ms, 5) if graph_ms else None,
-        "kernel_ms": {"index_score": round(score_ms, 5), "topk": round(topk_ms, 5),
-                      "attend_split_and_combine": round(attend_ms, 5)},
-        "roofline": {"kernel": "score_bf16_h64d128_kernel", "bound": "hbm",
+        "call_ms": {"index_score": round(score_ms, 5),
+                    "index_topk (score + selection)": round(index_topk_ms, 5),
+                    "attend (split + combine)": round(attend_ms, 5)},
+        "roofline": {"kernel": SCORE_KERNEL, "bound": "hbm",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                     "algorithmic_bytes_per_launch": score_bytes},
+                     "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "algorithmic_bytes_per_launch": score_bytes,
+                     "avg_launch_ms": round(score_ms, 5)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, copies[0], args.cpu_seconds)

@@ -114,26 +114,158 @@ __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
 }
 
 // ---------------------------------------------------------------- bf16 64 x 128, split
-constexpr int kCsaSplit = 64;      // entries of the top-k list per workgroup (one tile per wave)
+constexpr int kCsaSplit = 128;     // entries of the top-k list per workgroup
 constexpr int kHcaSplit = 512;     // visible entries per workgroup
-constexpr int kPartStride = 132;   // floats per (split, head): O[128], m, l, pad
-constexpr int kVtRow = 36;         // bf16 per V^T row in LDS (32 entries + pad)
+constexpr int kPartRows = 130;     // per (query, split): O^T[128][64], then m[64], l[64]
+constexpr int kVPitch = 160;       // bf16 per V row in LDS (256 B + 64 B pad)
+constexpr int kKPitch = 136;       // bf16 per K row in LDS (256 B + 16 B pad)
+constexpr float kRescaleLog2 = 8.f; // probabilities stay below 2^8 between rescales
 
-struct AttnSmem {
-  uint16_t vt[2][2][128 * kVtRow];   // [buffer][key group][d][entry]
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
+
+struct __attribute__((aligned(16))) AttnSmem {
+  uint16_t v[2][2][32 * kVPitch];    // [buffer][key group][entry][d], row-major V tiles
+  uint16_t k[2][2][32 * kKPitch];    // [buffer][key group][entry][d], row-major K tiles
+};
+__shared__ AttnSmem g_attn;
+
+// Per-round loads of one thread: four 16-byte chunks of its key group's K
+// tile and four of its V tile (chunk c = t128 + 128 i: tile row c / 16,
+// 16-byte column c % 16), so every load instruction reads whole rows.
+struct RoundRegs {
+  uint4 kv[4];
+  uint4 vv[4];
+  uint32_t vmask;                    // bit j: tile row j holds a valid entry
 };
 
+// ej: this lane's entry for tile row jl (lanes 0..31 and 32..63 agree), -1 if
+// none; a chunk's row takes its entry from lane (row) by a shuffle.
+__device__ __forceinline__ void load_round(const uint16_t* __restrict__ Kb,
+                                           const uint16_t* __restrict__ Vb, int64_t kv_sn, int ej,
+                                           int t128, RoundRegs& rr) {
+  rr.vmask = static_cast<uint32_t>(__ballot(ej >= 0));
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int pair = t128 + 128 * it;
+    const int vr = pair >> 4, ch = pair & 15;
+    const int ev = __shfl(ej, vr, 64);
+    const int64_t off = static_cast<int64_t>(ev) * kv_sn + 8 * ch;
+    rr.kv[it] = ev >= 0 ? ld16(Kb + off) : make_uint4(0, 0, 0, 0);
+    rr.vv[it] = ev >= 0 ? ld16(Vb + off) : make_uint4(0, 0, 0, 0);
+  }
+}
+
+// One key group of the workgroup processes one 32-entry tile per round:
+//   K and V rows -> LDS (row-major, 16-byte writes), barrier,
+//   S^T = K q^T (8 MFMA 32x32x16, K rows read back in the A-operand layout),
+//   online softmax per lane (each lane owns one head column),
+//   O^T += V^T P^T with V^T read from LDS by transposing loads
+//   (ds_read_b64_tr_b16) and P^T straight from the S accumulator.
+__device__ __forceinline__ void process_round(const RoundRegs& rr, bool active, int buf, int kg,
+                                              int t128, int jl, int g, const bf16x8_t (&bq)[8],
+                                              float scale_log2, float& m_run, float& l_run,
+                                              f32x16_t (&o)[4]) {
+  lds_u16* vt = (lds_u16*)&g_attn.v[buf][kg][0];
+  lds_u16* kt = (lds_u16*)&g_attn.k[buf][kg][0];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int pair = t128 + 128 * it;
+    const int vr = pair >> 4, ch = pair & 15;
+    const uint4 x = rr.kv[it];
+    *(lds_u32x4*)(kt + vr * kKPitch + 8 * ch) = u32x4{x.x, x.y, x.z, x.w};
+    const uint4 y = rr.vv[it];
+    *(lds_u32x4*)(vt + vr * kVPitch + 8 * ch) = u32x4{y.x, y.y, y.z, y.w};
+  }
+  __syncthreads();
+  if (!active) return;
+  f32x16_t sacc = {};
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const u32x4 w = *(const lds_u32x4*)(kt + jl * kKPitch + 16 * s + 8 * g);
+    bf16x8_t a;
+    __builtin_memcpy(&a, &w, 16);
+    sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq[s], sacc, 0, 0, 0);
+  }
+  float x[16];
+  float tmax = kNegInf;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int j = 8 * (i >> 2) + 4 * g + (i & 3);
+    x[i] = ((rr.vmask >> j) & 1u) ? sacc[i] * scale_log2 : kNegInf;
+    tmax = fmaxf(tmax, x[i]);
+  }
+  tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+  // Lazy rescaling: the reference maximum m_run only moves when the tile's
+  // maximum exceeds it by more than kRescaleLog2, so probabilities stay
+  // below 2^kRescaleLog2 and O is rescaled only when some lane moved.
+  float alpha = 1.f;
+  if (tmax > m_run + kRescaleLog2) {
+    alpha = exp2_fast(m_run - tmax);            // 0 when m_run is -inf
+    m_run = tmax;
+  }
+  uint32_t pb[8];
+  float psum = 0.f;
+  if (m_run != kNegInf) {
+#pragma unroll
+    for (int i = 0; i < 16; i += 2) {
+      pb[i >> 1] = pack_bf16x2(exp2_fast(x[i] - m_run), exp2_fast(x[i + 1] - m_run));
+      psum += __uint_as_float(pb[i >> 1] << 16) + __uint_as_float(pb[i >> 1] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) pb[i] = 0;
+  }
+  l_run = l_run * alpha + psum;
+  if (__ballot(alpha != 1.f) != 0) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
+  }
+  // A operand lane l: row d = 32 dt + l % 32, k-slots e -> entries
+  // 16 s2 + 8 (e / 4) + 4 g + e % 4 (the order of the S accumulator rows).
+  // Transposing load, per 16-lane group: source lane 4r + a addresses entry
+  // row jb + r at column dbase + 4a; output lane i gets column dbase + i.
+  const int lg = jl >> 4, li = jl & 15;
+  const int r4 = li >> 2, a4 = li & 3;
+#pragma unroll
+  for (int s2 = 0; s2 < 2; ++s2) {
+    bf16x8_t bp;
+    __builtin_memcpy(&bp, &pb[4 * s2], 16);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int dbase = 32 * dt + 16 * lg;
+      const int jb = 16 * s2 + 4 * g;
+      const lds_u16* p0 = vt + (jb + r4) * kVPitch + dbase + 4 * a4;
+      const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+      const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p0 + 8 * kVPitch));
+      bf16x8_t a;
+      __builtin_memcpy(&a, &lo, 8);
+      __builtin_memcpy(reinterpret_cast<char*>(&a) + 8, &hi, 8);
+      o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[dt], 0, 0, 0);
+    }
+  }
+}
+
+// One workgroup per (split, query row); 4 waves = 2 key groups x 2 head
+// halves.  Key group kg takes tiles 2r + kg in round r.  The K/V operands of
+// round r + 1 are in flight while round r computes; CSA entry indices are
+// loaded one round further ahead.  Two workgroups fit on a compute unit.  Output: the split's unnormalised O^T, running maximum m and
+// sum l (base-2 logits) in d-major rows, written with coalesced stores.
 template <bool HCA>
-__global__ __launch_bounds__(256) void attend_split_kernel(
+__global__ __launch_bounds__(256, 2) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn, const int32_t* __restrict__ idx,
     int kk, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
     int N_max, int m, float scale_log2, int split_len, int nsplit, float* __restrict__ part) {
-  __shared__ AttnSmem sm;
   const int split = blockIdx.x, row = blockIdx.y, b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = wave & 1, kg = wave >> 1;
   const int jl = lane & 31, g = lane >> 5;
+  const int t128 = hh * 64 + lane;
   const int h = 32 * hh + jl;        // this lane's head (S^T / O^T column)
   const int n_ent = min(n_entries[b], N_max);
   const int n = HCA ? visible_count(q_pos[row], m, n_entries[b], N_max) : kk;
@@ -141,6 +273,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
   const int s_end = min(n, s0 + split_len);
   const int ntiles = s_end > s0 ? (s_end - s0 + 31) / 32 : 0;
   const int nrounds = (ntiles + 1) / 2;
+  const int32_t* irow = HCA ? nullptr : idx + static_cast<int64_t>(row) * kk;
 
   // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
   const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
@@ -153,112 +286,48 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
   f32x16_t o[4] = {};
   float m_run = kNegInf, l_run = 0.f;
 
-  for (int r = 0; r < nrounds; ++r) {
-    const int t = 2 * r + kg;
-    const bool active = t < ntiles;
-    const int p0 = s0 + 32 * t;
-    // entry of tile row jl (the A-operand row this lane loads)
-    int ej = -1;
-    if (active && p0 + jl < s_end) {
-      ej = HCA ? p0 + jl : idx[static_cast<int64_t>(row) * kk + p0 + jl];
-      if (ej < 0 || ej >= n_ent) ej = -1;
-    }
-    const uint32_t vmask = static_cast<uint32_t>(__ballot(ej >= 0));   // bits 0..31: rows
-    // A operand: K rows (zero for invalid rows)
-    bf16x8_t ak[8];
-    if (ej >= 0) {
-      const uint16_t* kr = Kb + static_cast<int64_t>(ej) * kv_sn + 8 * g;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) ak[s] = ld_bf16x8(kr + 16 * s);
-    } else {
-#pragma unroll
-      for (int s = 0; s < 8; ++s) ak[s] = bf16x8_t{};
-    }
-    // V rows -> V^T in LDS: the key group's 128 threads cover 32 rows x 16 chunks
-    uint16_t* vt = sm.vt[r & 1][kg];
-    {
-      const int t128 = hh * 64 + lane;
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int pair = t128 + 128 * it;      // 0..511
-        const int vr = pair >> 4, ch = pair & 15;
-        int ev = -1;
-        if (active && p0 + vr < s_end) {
-          ev = HCA ? p0 + vr : idx[static_cast<int64_t>(row) * kk + p0 + vr];
-          if (ev < 0 || ev >= n_ent) ev = -1;
-        }
-        uint4 x = make_uint4(0, 0, 0, 0);
-        if (ev >= 0) x = ld16(Vb + static_cast<int64_t>(ev) * kv_sn + 8 * ch);
-        const uint32_t w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vt[(8 * ch + 2 * e) * kVtRow + vr] = static_cast<uint16_t>(w4[e] & 0xffffu);
-          vt[(8 * ch + 2 * e + 1) * kVtRow + vr] = static_cast<uint16_t>(w4[e] >> 16);
-        }
-      }
-    }
-    __syncthreads();
-    if (!active) continue;
+// entry of tile row jl in round rr (-1: none)
+#define CSA_ENTRY(rr, out)                                                       \
+  do {                                                                           \
+    const int t_ = 2 * (rr) + kg, p_ = s0 + 32 * t_ + jl;                        \
+    int e_ = -1;                                                                 \
+    if (t_ < ntiles && p_ < s_end) {                                             \
+      e_ = HCA ? p_ : irow[p_];                                                  \
+      if (e_ < 0 || e_ >= n_ent) e_ = -1;                                        \
+    }                                                                            \
+    (out) = e_;                                                                  \
+  } while (0)
 
-    // S^T = K q^T : lane holds column h, rows j = 8*(i/4) + 4*g + i%4
-    f32x16_t sacc = {};
-#pragma unroll
-    for (int s = 0; s < 8; ++s) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ak[s], bq[s], sacc, 0, 0, 0);
-    float x[16];
-    float tmax = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int j = 8 * (i >> 2) + 4 * g + (i & 3);
-      x[i] = ((vmask >> j) & 1u) ? sacc[i] * scale_log2 : kNegInf;
-      tmax = fmaxf(tmax, x[i]);
-    }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-    const float m_new = fmaxf(m_run, tmax);
-    float alpha = 1.f;
-    uint32_t pb[8];
-    float psum = 0.f;
-    if (m_new != kNegInf) {
-      alpha = exp2_fast(m_run - m_new);
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        const uint16_t lo = f32_to_bf16(exp2_fast(x[i] - m_new));
-        const uint16_t hi = f32_to_bf16(exp2_fast(x[i + 1] - m_new));
-        psum += bf16_to_f32(lo) + bf16_to_f32(hi);
-        pb[i >> 1] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pb[i] = 0;
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] *= alpha;
-    // O^T += V^T P^T over the tile's two 16-entry k-steps
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      bf16x8_t bp;
-      __builtin_memcpy(&bp, &pb[4 * s2], 16);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const uint16_t* vrow = vt + (32 * dt + jl) * kVtRow + 16 * s2 + 4 * g;
-        uint2 lo = *reinterpret_cast<const uint2*>(vrow);
-        uint2 hi = *reinterpret_cast<const uint2*>(vrow + 8);
-        const uint32_t av[4] = {lo.x, lo.y, hi.x, hi.y};
-        bf16x8_t a;
-        __builtin_memcpy(&a, av, 16);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, o[dt], 0, 0, 0);
-      }
+  // two register sets: while round r computes, the loads of round r + 1 are
+  // in flight (rounds unrolled by two, so no set is copied)
+  RoundRegs ra, rb;
+  int ejn;
+  {
+    int e0;
+    CSA_ENTRY(0, e0);
+    CSA_ENTRY(1, ejn);
+    load_round(Kb, Vb, kv_sn, e0, t128, ra);
+  }
+  for (int r = 0; r < nrounds; r += 2) {
+    if (r + 1 < nrounds) load_round(Kb, Vb, kv_sn, ejn, t128, rb);
+    CSA_ENTRY(r + 2, ejn);
+    process_round(ra, 2 * r + kg < ntiles, 0, kg, t128, jl, g, bq, scale_log2, m_run, l_run, o);
+    if (r + 1 < nrounds) {
+      if (r + 2 < nrounds) load_round(Kb, Vb, kv_sn, ejn, t128, ra);
+      CSA_ENTRY(r + 3, ejn);
+      process_round(rb, 2 * (r + 1) + kg < ntiles, 1, kg, t128, jl, g, bq, scale_log2, m_run,
+                    l_run, o);
     }
   }
+#undef CSA_ENTRY
 
-  // merge the two key groups of each head half through LDS (reuses V^T space)
+  // merge the two key groups of each head half through LDS (reuses the V tiles)
   l_run = l_run + __shfl_xor(l_run, 32, 64);
   __syncthreads();
-  float* xo = reinterpret_cast<float*>(&sm.vt[0][0][0]);   // [hh][lane][64 + 2]
+  lds_f32* xo = (lds_f32*)&g_attn.v[0][0][0];      // [hh][lane][64 + 2]
   constexpr int kX = 66;
   if (kg == 1) {
-    float* dst = xo + (hh * 64 + lane) * kX;
+    lds_f32* dst = xo + (hh * 64 + lane) * kX;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -268,7 +337,7 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
   }
   __syncthreads();
   if (kg == 0) {
-    const float* src = xo + (hh * 64 + lane) * kX;
+    const lds_f32* src = xo + (hh * 64 + lane) * kX;
     const float m1 = src[64], l1 = src[65];
     const float M = fmaxf(m_run, m1);
     float a0 = 0.f, a1 = 0.f;
@@ -276,76 +345,65 @@ __global__ __launch_bounds__(256) void attend_split_kernel(
       a0 = exp2_fast(m_run - M);
       a1 = exp2_fast(m1 - M);
     }
-    float* pr = part + ((static_cast<int64_t>(row) * nsplit + split) * 64 + h) * kPartStride;
+    float* pr = part + (static_cast<int64_t>(row) * nsplit + split) * kPartRows * 64;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
-        pr[d] = a0 * o[dt][i] + a1 * src[16 * dt + i];
+        pr[d * 64 + h] = a0 * o[dt][i] + a1 * src[16 * dt + i];
       }
     if (g == 0) {
-      pr[128] = M;
-      pr[129] = a0 * l_run + a1 * l1;
+      pr[128 * 64 + h] = M;
+      pr[129 * 64 + h] = a0 * l_run + a1 * l1;
     }
   }
 }
 
-// Merge of the split partials.  Grid (rows, 4 head groups); thread (h, c)
-// owns 8 output dims of one head.  All splits' maxima are read first (one
-// round of independent loads), then all partial rows.
-constexpr int kCombineUnroll = 8;
-
+// Merge of the split partials.  Grid (rows, 4 dim quarters); thread (h, c)
+// owns output dims 32 y + 8 c .. +7 of head h: every read is a coalesced
+// 64-float row of a partial.
 __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ part,
                                                              int nsplit, uint16_t* __restrict__ out,
                                                              float* __restrict__ lse) {
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int h = blockIdx.y * 16 + (tid >> 4), dc = (tid & 15) * 8;
-  const int64_t sstride = 64 * kPartStride;
-  const float* base = part + (static_cast<int64_t>(row) * nsplit * 64 + h) * kPartStride;
+  const int h = tid & 63, d0 = 32 * blockIdx.y + 8 * (tid >> 6);
+  const int64_t sstride = static_cast<int64_t>(kPartRows) * 64;
+  const float* base = part + static_cast<int64_t>(row) * nsplit * sstride + h;
+  // pass 1: the maxima (independent loads); pass 2: splits in groups of four
+  // with every load of a group issued before its arithmetic
+  constexpr int U = 4;
   float M = kNegInf;
-  int s = 0;
-  for (; s + kCombineUnroll <= nsplit; s += kCombineUnroll) {
-    float mm[kCombineUnroll];
+  for (int s = 0; s < nsplit; s += U) {
+    float mm[U];
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) mm[u] = base[(s + u) * sstride + 128];
+    for (int u = 0; u < U; ++u) mm[u] = s + u < nsplit ? base[(s + u) * sstride + 128 * 64] : kNegInf;
 #pragma unroll
-    for (int u = 0; u < kCombineUnroll; ++u) M = fmaxf(M, mm[u]);
+    for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
   }
-  for (; s < nsplit; ++s) M = fmaxf(M, base[s * sstride + 128]);
   float L = 0.f;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   if (M != kNegInf) {
-    s = 0;
-    for (; s + kCombineUnroll <= nsplit; s += kCombineUnroll) {
-      float4 lo[kCombineUnroll], hi[kCombineUnroll];
-      float ml[kCombineUnroll], ll[kCombineUnroll];
+    for (int s = 0; s < nsplit; s += U) {
+      float v[U][8], ms[U], ls[U];
 #pragma unroll
-      for (int u = 0; u < kCombineUnroll; ++u) {
-        const float* ps = base + (s + u) * sstride;
-        lo[u] = *reinterpret_cast<const float4*>(ps + dc);
-        hi[u] = *reinterpret_cast<const float4*>(ps + dc + 4);
-        ml[u] = ps[128];
-        ll[u] = ps[129];
+      for (int u = 0; u < U; ++u) {
+        const bool ok = s + u < nsplit;
+        const float* ps = base + static_cast<int64_t>(ok ? s + u : s) * sstride;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[u][i] = ps[(d0 + i) * 64];
+        ms[u] = ok ? ps[128 * 64] : kNegInf;
+        ls[u] = ps[129 * 64];
       }
 #pragma unroll
-      for (int u = 0; u < kCombineUnroll; ++u) {
-        const float w = exp2_fast(ml[u] - M);
-        L = fmaf(w, ll[u], L);
-        acc[0] = fmaf(w, lo[u].x, acc[0]); acc[1] = fmaf(w, lo[u].y, acc[1]);
-        acc[2] = fmaf(w, lo[u].z, acc[2]); acc[3] = fmaf(w, lo[u].w, acc[3]);
-        acc[4] = fmaf(w, hi[u].x, acc[4]); acc[5] = fmaf(w, hi[u].y, acc[5]);
-        acc[6] = fmaf(w, hi[u].z, acc[6]); acc[7] = fmaf(w, hi[u].w, acc[7]);
-      }
-    }
-    for (; s < nsplit; ++s) {
-      const float* ps = base + s * sstride;
-      const float w = exp2_fast(ps[128] - M);
-      L = fmaf(w, ps[129], L);
+      for (int u = 0; u < U; ++u) {
+        const float w = ms[u] == kNegInf ? 0.f : exp2_fast(ms[u] - M);
+        L = fmaf(w, ls[u], L);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, ps[dc + i], acc[i]);
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -354,8 +412,8 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
   v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
   v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
   v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  st16(out + (static_cast<int64_t>(row) * 64 + h) * 128 + dc, v);
-  if (lse != nullptr && dc == 0)
+  st16(out + (static_cast<int64_t>(row) * 64 + h) * 128 + d0, v);
+  if (lse != nullptr && blockIdx.y == 0 && tid < 64)
     lse[static_cast<int64_t>(row) * 64 + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
 
@@ -391,7 +449,7 @@ size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, in
   if (!tuned(dt, H, D)) return 0;
   const int sl = split_len(hca);
   const int nsplit = (k_or_nmax + sl - 1) / sl;
-  return static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * 64 * kPartStride * sizeof(float);
+  return static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * kPartRows * 64 * sizeof(float);
 }
 
 hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s) {

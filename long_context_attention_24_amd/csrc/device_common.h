@@ -19,15 +19,17 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
 }
 
 // float -> bf16 bits, round to nearest even (inputs are finite; NaN stays NaN).
+// fp32 -> bf16, round to nearest even (gfx950 converts in hardware:
+// v_cvt_pk_bf16_f32)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Entries visible to a query at position q_pos for pooling factor m:
@@ -82,6 +84,11 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 __device__ __forceinline__ bf16x8_t ld_bf16x8(const uint16_t* p) {
   return *reinterpret_cast<const bf16x8_t*>(p);
+}
+// 16-byte load marked non-temporal: streamed data that is read once
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
 }
 
 }  // namespace csa

@@ -113,16 +113,23 @@ constexpr int kKeysPerWave = 32 * kTilesPerWave;  // one selection chunk
 constexpr int kKeysPerWg = kWavesPerWg * kKeysPerWave;
 static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 
-// Straight-line code over the wave's 8 tiles with a 3-deep ring of B-operand
+// Straight-line code over the wave's 8 tiles of 32 keys with a 3-deep ring of
 // registers: the loads of tile t+2 are issued before the MFMAs of tile t and
-// no register is copied, so the compiler's wait counts leave two tiles (16 KB
-// per wave) in flight behind the math.  Rows past the visible range are
-// clamped to the last visible row (in bounds, L2 hits) and masked on output.
+// no register is copied, so two tiles (16 KB per wave) stay in flight behind
+// the math.  Loads are coalesced and non-temporal (instruction i of a tile
+// reads key rows 4i .. 4i+3 whole, 16 lanes per row); each tile then passes
+// through a wave-private LDS buffer to reach the MFMA B-operand layout (lane
+// (j, g) holds dims 16s + 8g .. +7 of key j).  Rows past the visible range are
+// clamped to the last visible row (in bounds, cache hits) and masked on
+// output.
+constexpr int kKeyPitch = 136;                    // bf16 per key row in LDS (256 B + 16 B)
+
 __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
     int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
+  __shared__ __attribute__((aligned(16))) uint16_t key_lds[kWavesPerWg][32 * kKeyPitch];
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 31, g = lane >> 5;
@@ -139,16 +146,21 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     return;
   }
 
-  const uint16_t* kb = k + b * k_sb + 8 * g;
-  bf16x8_t kt[3][8];
-  auto load_tile = [&](int t, bf16x8_t (&dst)[8]) {
-    const int j = min(key0 + 32 * t + jl, vis_end - 1);
-    const uint16_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+  const uint16_t* kb = k + b * k_sb + 8 * (lane & 15);
+  const int lrow = lane >> 4;                     // row within each 4-row load
+  u32x4_t kt[3][8];
+  auto load_tile = [&](int t, u32x4_t (&dst)[8]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) dst[s] = ld_bf16x8(kr + 16 * s);
+    for (int i = 0; i < 8; ++i) {
+      const int j = min(key0 + 32 * t + 4 * i + lrow, vis_end - 1);
+      dst[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
+    }
   };
   load_tile(0, kt[0]);
   load_tile(1, kt[1]);
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  lds_u16* kl = (lds_u16*)&key_lds[wave][0];
 
   // A operand: q_I rows (heads) of this query; two 32-head tiles x 8 k-steps
   const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
@@ -176,7 +188,16 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
   for (int t = 0; t < kTilesPerWave; ++t) {
     if (t + 2 < kTilesPerWave) load_tile(t + 2, kt[(t + 2) % 3]);
     __builtin_amdgcn_sched_barrier(0);
-    const bf16x8_t (&cur)[8] = kt[t % 3];
+    // tile t: registers -> LDS (rows 4i + lrow) -> B operand (row jl)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *(lds_u32x4*)(kl + (4 * i + lrow) * kKeyPitch + 8 * (lane & 15)) = kt[t % 3][i];
+    bf16x8_t cur[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4_t x = *(const lds_u32x4*)(kl + jl * kKeyPitch + 16 * s + 8 * g);
+      __builtin_memcpy(&cur[s], &x, 16);
+    }
     f32x16_t c0 = {}, c1 = {};
 #pragma unroll
     for (int s = 0; s < 8; ++s) {

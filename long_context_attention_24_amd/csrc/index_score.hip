@@ -224,6 +224,152 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
   }
 }
 
+// ---------------------------------------------------------------- bf16 prefill (many queries)
+// With many query tokens per sequence the score is a GEMM with the (query,
+// head) pairs as rows, keys as columns and the 128 dims as the reduction,
+// followed by the per-query epilogue sum_h w[h] ReLU(.).  One workgroup of
+// 8 waves takes 8 queries of one sequence (one per wave: two 32-row A tiles
+// of q_I held in registers) against 2048 keys.  Key tiles of 32 rows are read
+// once per workgroup with coalesced loads (one 16-byte load per thread per
+// tile), kept four tiles ahead in registers, staged through a triple-buffered
+// LDS tile shared by the waves (one barrier per tile) and multiplied by all 8
+// queries: 16 MFMA 32x32x16 per wave per 8 KB tile.  Two waves per SIMD let
+// one wave's epilogue overlap the other's MFMAs.  The selection bounds are
+// produced per 256-key chunk exactly as in the decode kernel.
+constexpr int kPfQueries = 8;
+constexpr int kPfThreads = 64 * kPfQueries;
+constexpr int kPfKeys = 2048;
+constexpr int kPfStages = 4;
+
+__global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
+    int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
+    int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  __shared__ __attribute__((aligned(16))) uint16_t tile_lds[3][32 * kKeyPitch];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int jl = lane & 31, g = lane >> 5;
+  const int groups = (Tq + kPfQueries - 1) / kPfQueries;
+  const int kblk = blockIdx.x, qgrp = blockIdx.y;
+  const int b = qgrp / groups;
+  const int t0 = (qgrp % groups) * kPfQueries;
+  const int j0 = kblk * kPfKeys;
+  const int j1 = min(j0 + kPfKeys, N_max);
+  const int n_ent = n_entries[b];
+  // visible counts of the workgroup's queries (invalid query: 0)
+  int vmax = 0, vq = 0;
+#pragma unroll
+  for (int u = 0; u < kPfQueries; ++u) {
+    const int t = t0 + u;
+    const int v = t < Tq ? visible_count(q_pos[b * Tq + t], m, n_ent, N_max) : 0;
+    vmax = max(vmax, v);
+    if (u == wave) vq = v;
+  }
+  const int rowq = t0 + wave < Tq ? b * Tq + t0 + wave : -1;
+  const int je = min(j1, vmax);                   // keys past je are masked for all queries
+  const int ntiles = je > j0 ? (je - j0 + 31) / 32 : 0;
+
+  // -inf for every key this workgroup covers but does not compute
+  if (rowq >= 0) {
+    float* srow = scores + rowq * s_rs;
+    for (int j = j0 + 32 * ntiles + lane; j < j1; j += 64) srow[j] = kNegInf;
+  }
+  const uint16_t* kb = k + b * k_sb + 8 * (tid & 15);
+  const int jcap = max(vmax, 1) - 1;              // clamp rows to visible ones (in bounds)
+  const int lrow = tid >> 4;                      // tile row this thread loads
+  u32x4_t ring[kPfStages];
+#pragma unroll
+  for (int u = 0; u < kPfStages; ++u)
+    if (u < ntiles) ring[u] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * u + lrow, jcap)) * k_sn);
+
+  // A operand: q_I rows of the wave's query (zero for an invalid one)
+  bf16x8_t a[2][8];
+  float wv[2][16];
+  {
+    const uint16_t* qrow = q + static_cast<int64_t>(max(rowq, 0)) * 64 * 128;
+    const float* wrow = w + static_cast<int64_t>(max(rowq, 0)) * 64;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int s2 = 0; s2 < 8; ++s2)
+        a[hf][s2] = rowq >= 0 ? ld_bf16x8(qrow + (32 * hf + jl) * 128 + 16 * s2 + 8 * g) : bf16x8_t{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) wv[hf][r] = wrow[32 * hf + 8 * (r >> 2) + 4 * g + (r & 3)];
+    }
+  }
+  const int cq = chunk_thr != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0;
+  float sc[kTilesPerWave];
+  lds_u16* const st_ptr0 = (lds_u16*)&tile_lds[0][0] + lrow * kKeyPitch + 8 * (tid & 15);
+  const lds_u16* const ld_ptr0 = (const lds_u16*)&tile_lds[0][0] + jl * kKeyPitch + 8 * g;
+  constexpr int kBufElems = 32 * kKeyPitch;
+  // MFMAs of one key tile from LDS buffer `buf` into acc
+  auto mfma_tile = [&](int buf, f32x16_t (&acc)[2]) {
+    const lds_u16* src = ld_ptr0 + buf * kBufElems;
+    acc[0] = f32x16_t{};
+    acc[1] = f32x16_t{};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const u32x4_t x = *(const lds_u32x4*)(src + 16 * s2);
+      bf16x8_t bb;
+      __builtin_memcpy(&bb, &x, 16);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s2], bb, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s2], bb, acc[1], 0, 0, 0);
+    }
+  };
+  auto load_tile = [&](int t) -> u32x4_t {
+    return *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * t + lrow, jcap)) * k_sn);
+  };
+  f32x16_t acc[2][2];
+
+  // Software pipeline, one barrier per tile.  Iteration tt: stage tile tt+2
+  // into LDS buffer (tt+2)%3, load tile tt+6 into the freed register slot,
+  // issue the MFMAs of tile tt+1, then the epilogue of tile tt (whose MFMAs
+  // were issued one iteration earlier) while they run.
+  if (ntiles > 0) *(lds_u32x4*)st_ptr0 = ring[0];
+  if (ntiles > 1) *(lds_u32x4*)(st_ptr0 + kBufElems) = ring[1];
+  if (4 < ntiles) ring[0] = load_tile(4);
+  if (5 < ntiles) ring[1] = load_tile(5);
+  __syncthreads();
+  if (ntiles > 0) mfma_tile(0, acc[0]);
+  for (int t = 0; t < ntiles; t += kTilesPerWave) {   // one 256-key chunk per pass
+#pragma unroll
+    for (int u = 0; u < kTilesPerWave; ++u) {
+      const int tt = t + u;
+      if (tt < ntiles) {
+        __syncthreads();
+        if (tt + 2 < ntiles) *(lds_u32x4*)(st_ptr0 + ((tt + 2) % 3) * kBufElems) = ring[(u + 2) % kPfStages];
+        if (tt + 6 < ntiles) ring[(u + 2) % kPfStages] = load_tile(tt + 6);
+        if (tt + 1 < ntiles) mfma_tile((tt + 1) % 3, acc[(u + 1) & 1]);
+        const f32x16_t (&c)[2] = acc[u & 1];
+        float sum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum = fmaf(wv[0][r], fmaxf(c[0][r], 0.f), sum);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sum = fmaf(wv[1][r], fmaxf(c[1][r], 0.f), sum);
+        const float tot = sum + __shfl_xor(sum, 32, 64);
+        const int j = j0 + 32 * tt + jl;
+        const bool ok = j < vq;
+        if (g == 0 && rowq >= 0 && j < j1) scores[rowq * s_rs + j] = ok ? tot : kNegInf;
+        sc[u] = ok ? tot : kNegInf;
+        // after each 256-key chunk (or the last computed tile): its bound
+        if (cq > 0 && (u == kTilesPerWave - 1 || tt == ntiles - 1)) {
+#pragma unroll
+          for (int v = u + 1; v < kTilesPerWave; ++v) sc[v] = kNegInf;
+          const float cth = wave_cth_largest<kTilesPerWave>(sc, g == 0, cq);
+          if (lane == 0) chunk_thr[static_cast<int64_t>(rowq) * n_chunks + (j0 + 32 * tt) / kBoundChunk] = cth;
+        }
+      }
+    }
+  }
+  // chunks with no computed key: no bound
+  if (cq > 0 && lane == 0) {
+    for (int ch = (j0 + 32 * ntiles + kBoundChunk - 1) / kBoundChunk; ch * kBoundChunk < j1; ++ch)
+      chunk_thr[static_cast<int64_t>(rowq) * n_chunks + ch] = kPosInf;
+  }
+}
+
 // ---------------------------------------------------------------- FP4, 64 heads x 128
 // E2M1 magnitude (3 bits) -> E4M3 byte: 0, .5, 1, 1.5, 2, 3, 4, 6 are
 // 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C; the sign bit moves from bit 3 of
@@ -387,6 +533,13 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
                        static_cast<const uint8_t*>(a.k), a.k_scale, a.k_sb, a.k_sn, a.ks_sb,
                        a.ks_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs,
                        a.chunk_thr, a.n_chunks, a.bound_k);
+  } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128 && a.Tq >= kPfQueries) {
+    const int groups = (a.Tq + kPfQueries - 1) / kPfQueries;
+    const dim3 grid((a.N_max + kPfKeys - 1) / kPfKeys, a.B * groups);
+    hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel, grid, dim3(kPfThreads), 0, s,
+                       static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
+                       a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
+                       a.s_rs, a.chunk_thr, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
     const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
     hipLaunchKernelGGL(score_bf16_h64d128_kernel, grid, dim3(256), 0, s,

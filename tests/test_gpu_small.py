@@ -172,6 +172,40 @@ def test_tuned_kernels_ragged():
             check_lse(LH[b, t], lh_ref, 2.5e-3)
 
 
+def test_tuned_prefill_scores_ragged():
+    """bf16 64 x 128 with many queries per sequence (the prefill score
+    kernel: 8 queries per workgroup, 2048 keys per workgroup): a query count
+    that is not a multiple of 8, several key blocks with a ragged tail,
+    visible counts from 0 to all, a partially valid cache.  Scores, the
+    chunk bounds (through the selection) and the selection are checked."""
+    B, Tq, N_max, m, k = 2, 13, 2 * 2048 + 300, 4, 300
+    _say("tuned prefill bf16 64x128 ragged")
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 31)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 32)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 33)
+    pos = [[4 * N_max + 7, 2, 3, 4 * 1024 - 1, 4 * 2048 - 1, 4 * 2048 + 3, 4 * 2100 + 1, 4 * 4000,
+            4 * 4095 + 3, 4 * 4096 - 1, 4 * 4100, 4 * 300 + 2, 4 * 37],
+           [4 * 1000, 4 * 2500, 4 * 4300, 1, 4 * 257, 4 * 256 - 1, 4 * 512, 4 * 3000, 4 * 3500,
+            4 * 4000, 4 * 4200, 4 * 4390, 4 * 100]]
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor([N_max, 3333], dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qi, wi, ki, q_pos, n_ent, m)
+    idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k)
+    torch.cuda.synchronize()
+    S, I = np64(scores), np64(idx)
+    QI, KI, W = np64(qi), np64(ki), np64(wi)
+    ne = n_ent.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible_count(pos[b][t], m, int(ne[b]))
+            s_ref = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+            assert np.all(np.isneginf(S[b, t, V:])), (b, t, V)
+            if V:
+                bound = score_bound(QI[b, t], W[b, t], KI[b, :V], 128, 64)
+                assert np.all(np.abs(S[b, t, :V] - s_ref[:V]) <= bound), (b, t, V)
+            check_topk(I[b, t], s_ref, V, k)
+
+
 def test_attention_sharp_and_single_entry():
     """Sharp softmax (logit std ~3) where the absolute gates bite, repeated and
     invalid indices, and a single selected entry (output = that value row)."""

@@ -92,8 +92,10 @@ int bound_k(csa_dtype_t dt, int H_I, int D_I, int N_max, int k) {
 // scores | chunk bounds | selection workspace
 size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws) {
   const size_t rows = static_cast<size_t>(B) * Tq;
+  const size_t bws = csa::topk_bounded_workspace_bytes(static_cast<int>(rows), N_max);
   return round_up(rows * score_row_stride(N_max) * sizeof(float)) +
-         round_up(rows * bound_chunks(N_max) * sizeof(float)) + round_up(topk_ws);
+         round_up(rows * bound_chunks(N_max) * sizeof(float)) +
+         round_up(topk_ws > bws ? topk_ws : bws);
 }
 
 }  // namespace

@@ -70,6 +70,8 @@ extern "C" __device__ uint32_t __ockl_wfscan_add_u32(uint32_t, bool);
 __device__ __forceinline__ float wave_max(float v) { return __ockl_wfred_max_f32(v); }
 __device__ __forceinline__ float wave_min(float v) { return __ockl_wfred_min_f32(v); }
 __device__ __forceinline__ float wave_sum(float v) { return __ockl_wfred_add_f32(v); }
+extern "C" __device__ int32_t __ockl_wfred_max_i32(int32_t);
+__device__ __forceinline__ int wave_max_int(int v) { return __ockl_wfred_max_i32(v); }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return __ockl_wfred_add_u32(v); }
 __device__ __forceinline__ int wave_sum_int(int v) {
   return static_cast<int>(__ockl_wfred_add_u32(static_cast<uint32_t>(v)));

@@ -39,11 +39,13 @@ int score_chunk_keys();                            // keys per bound chunk
 // ---- topk.hip
 // Selection from rows of N_max scores.  chunk_thr (nullable): per-row bounds
 // written by the tuned score kernels (one report per 256-key chunk, n_chunks
-// per row, for the same k); they are used when topk_bounded_ok(N_max), and
-// that path needs no workspace.  Otherwise the workspace is
+// per row, for the same k); they are used when topk_bounded_ok(N_max), with
+// a workspace of topk_bounded_workspace_bytes (zero for rows short enough to
+// be streamed by one workgroup).  Otherwise the workspace is
 // topk_workspace_bytes.
 size_t topk_workspace_bytes(int rows, int N_max, int k);
 bool topk_bounded_ok(int N_max);
+size_t topk_bounded_workspace_bytes(int rows, int N_max);
 bool topk_supported(int N_max, int k);
 hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,

@@ -671,10 +671,95 @@ __device__ __forceinline__ void load_stage(const float* __restrict__ srow, int c
   }
 }
 
+// Few long rows (more than kStreamMaxN entries, at most kRegionMaxRows rows:
+// too little parallelism for one workgroup per row) are filtered first by
+// topk_filter_kernel: one 256-thread workgroup per 4096 entries, each wave
+// owning 1024 of them (a region) and working alone (no barrier, no atomic):
+// it derives the row bound from the chunk reports, compacts its entries at or
+// above the bound to the front of its region of the survivor buffers and
+// stores their number.  The bounded kernel then gathers the regions instead
+// of streaming the row.
+constexpr int kStreamMaxN = 65536;
+constexpr int kRegionMaxRows = 64;
+constexpr int kFiltSeg = 4096;
+constexpr int kRegion = 1024;
+
+__global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(
+    const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
+    const float* __restrict__ chunk_thr, int n_chunks, int nreg, float* __restrict__ reg_val,
+    int32_t* __restrict__ reg_idx, int32_t* __restrict__ reg_cnt) {
+  const int seg = blockIdx.x, row = blockIdx.y, b = row / Tq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const int e0 = seg * kFiltSeg + wave * kRegion;
+  const int L = max(0, min(V - e0, kRegion));
+  const int r = seg * (kFiltSeg / kRegion) + wave;
+  if (r >= nreg) return;
+  const float* src = scores + row * s_rs + e0;
+  float v[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = 256 * i + 4 * lane;
+    if (q + 3 < L) {
+      const float4 x = *reinterpret_cast<const float4*>(src + q);
+      v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < L) ? src[q + e] : kNegInf;
+    }
+  }
+  const int c = bound_c_row(V, k);
+  float bound = kNegInf;
+  if (c > 0) {
+    const float* thr = chunk_thr + static_cast<int64_t>(row) * n_chunks;
+    float mn = FLT_MAX;
+    uint32_t cnt = 0;
+    for (int i = lane; i < n_chunks; i += 64) {
+      const float t = thr[i];
+      if (t != kPosInf) {
+        mn = fminf(mn, t);
+        ++cnt;
+      }
+    }
+    mn = wave_min(mn);
+    cnt = wave_sum_u32(cnt);
+    if (static_cast<long long>(cnt) * c >= k) bound = mn;
+  }
+  uint32_t cl = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cl += (v[i][e] > kNegInf && v[i][e] >= bound) ? 1u : 0u;
+  const uint32_t incl = wave_incl_scan_u32(cl);
+  const int64_t base = (static_cast<int64_t>(row) * nreg + r) * kRegion;
+  uint32_t o = incl - cl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (v[i][e] > kNegInf && v[i][e] >= bound) {
+        reg_val[base + o] = v[i][e] + 0.0f;       // -0.0 -> +0.0
+        reg_idx[base + o] = e0 + 256 * i + 4 * lane + e;
+        ++o;
+      }
+    }
+  }
+  if (lane == 63) reg_cnt[static_cast<int64_t>(row) * nreg + r] = static_cast<int32_t>(incl);
+}
+
+int filter_regions(int N_max) { return (N_max + kFiltSeg - 1) / kFiltSeg * (kFiltSeg / kRegion); }
+
+// REGIONS: the survivors come from topk_filter_kernel's regions (wave w
+// takes regions w, w + 16, ...; the counts and the first 128 survivors of
+// eight regions are loaded together); otherwise the row is streamed.
+template <bool REGIONS>
 __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
     const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
-    const float* __restrict__ chunk_thr, int n_chunks, int32_t* __restrict__ out_idx,
+    const float* __restrict__ chunk_thr, int n_chunks, int nreg,
+    const float* __restrict__ reg_val, const int32_t* __restrict__ reg_idx,
+    const int32_t* __restrict__ reg_cnt, int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   constexpr int NW = kSelWaves;
   __shared__ uint32_t bm_s[kBitmapWords];
@@ -688,7 +773,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const float* srow = scores + row * s_rs;
   float4 x[kStageVec];
-  load_stage(srow, 0, V, x);
+  if (!REGIONS) load_stage(srow, 0, V, x);
   const int W = (N_max + 31) >> 5;
   const int WPT = (W + kSelThreads - 1) / kSelThreads;
   g_sm.hist[2 * tid] = 0;
@@ -698,6 +783,67 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
     if (w < W) bm[w] = 0;
   }
   if (tid == 0) g_sm.list_n = 0;
+  float smin = FLT_MAX, smax = -FLT_MAX;
+  int p = 0;
+  if (REGIONS) {
+    __syncthreads();                                // LDS state zeroed
+    const int wave = tid >> 6;
+    const int32_t* cnt_row = reg_cnt + static_cast<int64_t>(row) * nreg;
+    constexpr int kBatch = 8;
+    for (int r0 = wave; r0 < nreg; r0 += kSelWaves * kBatch) {
+      int cnt[kBatch];
+      float v0[kBatch], v1[kBatch];
+      int i0[kBatch], i1[kBatch];
+#pragma unroll
+      for (int rr = 0; rr < kBatch; ++rr) {
+        const int r = r0 + kSelWaves * rr;
+        if (r < nreg) {
+          const int64_t base = (static_cast<int64_t>(row) * nreg + r) * kRegion;
+          cnt[rr] = cnt_row[r];
+          v0[rr] = reg_val[base + lane];
+          v1[rr] = reg_val[base + 64 + lane];
+          i0[rr] = reg_idx[base + lane];
+          i1[rr] = reg_idx[base + 64 + lane];
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < kBatch; ++rr) {
+        const int r = r0 + kSelWaves * rr;
+        if (r < nreg && cnt[rr] > 0) {
+          const int c = cnt[rr];
+          uint32_t base = 0;
+          if (lane == 0) base = atomicAdd(&g_sm.list_n, static_cast<uint32_t>(c));
+          base = __builtin_amdgcn_readfirstlane(base);
+          if (lane < c) {
+            smin = fminf(smin, v0[rr]);
+            smax = fmaxf(smax, v0[rr]);
+            if (base + lane < kListCap) {
+              lv[base + lane] = v0[rr];
+              li[base + lane] = i0[rr];
+            }
+          }
+          if (64 + lane < c) {
+            smin = fminf(smin, v1[rr]);
+            smax = fmaxf(smax, v1[rr]);
+            if (base + 64 + lane < kListCap) {
+              lv[base + 64 + lane] = v1[rr];
+              li[base + 64 + lane] = i1[rr];
+            }
+          }
+          const int64_t rb = (static_cast<int64_t>(row) * nreg + r) * kRegion;
+          for (int j = 128 + lane; j < c; j += 64) {   // rare: more than 128 survivors
+            const float x1 = reg_val[rb + j];
+            smin = fminf(smin, x1);
+            smax = fmaxf(smax, x1);
+            if (base + j < kListCap) {
+              lv[base + j] = x1;
+              li[base + j] = reg_idx[rb + j];
+            }
+          }
+        }
+      }
+    }
+  } else {
   // 1. row bound
   const int c = bound_c_row(V, k);
   float bmn = FLT_MAX, unused_f = -FLT_MAX;
@@ -712,11 +858,9 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
       }
     }
   }
-  int p = 0;
   block_minmax_count<NW>(bmn, unused_f, bcnt, p);   // barrier: LDS state zeroed
   const float bound = (c > 0 && static_cast<long long>(bcnt) * c >= k) ? bmn : kNegInf;
   // 2. stream the row, appending survivors
-  float smin = FLT_MAX, smax = -FLT_MAX;
   for (int c0 = 0; c0 < V; c0 += kStageChunk) {
     float4 y[kStageVec];
     const bool more = c0 + kStageChunk < V;
@@ -757,6 +901,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
 #pragma unroll
       for (int i = 0; i < kStageVec; ++i) x[i] = y[i];
     }
+  }
   }
   uint32_t unused_u = 0;
   block_minmax_count<NW>(smin, smax, unused_u, p);  // barrier: the list is complete
@@ -802,14 +947,39 @@ size_t topk_workspace_bytes(int rows, int N_max, int k) {
 
 bool topk_bounded_ok(int N_max) { return N_max <= kMaxBoundedN; }
 
+bool use_regions(int rows, int N_max) { return N_max > kStreamMaxN && rows <= kRegionMaxRows; }
+
+size_t topk_bounded_workspace_bytes(int rows, int N_max) {
+  if (!topk_bounded_ok(N_max) || !use_regions(rows, N_max)) return 0;
+  const size_t regs = static_cast<size_t>(rows) * filter_regions(N_max);
+  return regs * kRegion * (sizeof(float) + sizeof(int32_t)) + regs * sizeof(int32_t);
+}
+
 hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
                        const float* chunk_thr, int n_chunks, int32_t* idx, float* out_scores,
                        void* ws, hipStream_t s) {
   const int rows = B * Tq;
   if (chunk_thr != nullptr && topk_bounded_ok(N_max)) {
-    hipLaunchKernelGGL(topk_bounded_kernel, dim3(rows), dim3(kSelThreads), 0, s, scores, s_rs,
-                       q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, idx, out_scores);
+    if (!use_regions(rows, N_max)) {
+      hipLaunchKernelGGL(topk_bounded_kernel<false>, dim3(rows), dim3(kSelThreads), 0, s, scores,
+                         s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, 0, nullptr,
+                         nullptr, nullptr, idx, out_scores);
+      return hipGetLastError();
+    }
+    const int nreg = filter_regions(N_max);
+    const size_t slots = static_cast<size_t>(rows) * nreg * kRegion;
+    float* rv = static_cast<float*>(ws);
+    int32_t* ri = reinterpret_cast<int32_t*>(rv + slots);
+    int32_t* rc = ri + slots;
+    hipLaunchKernelGGL(topk_filter_kernel, dim3((N_max + kFiltSeg - 1) / kFiltSeg, rows),
+                       dim3(kSegThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
+                       chunk_thr, n_chunks, nreg, rv, ri, rc);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_bounded_kernel<true>, dim3(rows), dim3(kSelThreads), 0, s, scores,
+                       s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, nreg, rv, ri,
+                       rc, idx, out_scores);
     return hipGetLastError();
   }
   const int nseg = num_segments(N_max);

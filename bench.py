@@ -12,6 +12,8 @@ from HBM.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (only 1),
 --graph (also time the step captured in a HIP graph), --no-cpu-baseline,
+--workload NAME (another workload's own line instead of the headline one:
+hca_decode_1m, csa_decode_1m_fp4 or csa_prefill_chunk; see other_workload),
 --score-only (launch only the indexer score kernel, for hardware-counter
 runs), --copy-calibration (run only a plain device copy of known size, for
 scaling the FETCH_SIZE / WRITE_SIZE counters).
@@ -52,6 +54,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true")
     p.add_argument("--score-only", action="store_true")
+    p.add_argument("--workload", default=WORKLOAD)
     return p.parse_args()
 
 
@@ -140,6 +143,171 @@ def recorded_traffic():
     return int(kv["hbm_bytes_per_launch"])
 
 
+def _timer():
+    """(hold_gpu(ms), timed(fn, steps, warmup) -> ms per call) as in main()."""
+    cycles_per_ms = _calibrate_sleep()
+
+    def timed(fn, steps, warmup):
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(cycles_per_ms * (20.0 + 0.05 * steps)))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+    return timed
+
+
+def other_workload(args):
+    """One JSON line for a workload other than the headline one.
+
+    hca_decode_1m: compress the 1M-token raw stream 128:1 (timed once per
+      sequence batch, reported), then HCA decode steps (32 tokens) over the
+      compressed caches; roofline: the attention's K/V stream against HBM.
+    csa_decode_1m_fp4: FP4 indexer scores + top-k + sparse attention for 4
+      decode tokens at 1M context; roofline: the FP4 score kernel's bytes.
+    csa_prefill_chunk: compress the 4096 new tokens, score / select / attend
+      all 4096 queries; roofline: the prefill score kernel's FLOPs against the
+      bf16 MFMA peak.
+    """
+    import long_context_attention_24_amd as csa
+    from csa_synth import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = "cuda"
+    timed = _timer()
+    base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if w.name == "hca_decode_1m":
+        inp = make_inputs(w, device=dev, parts=["raw", "logits", "q", "q_pos", "n_entries"])
+        caches = []
+        comp_ms = None
+        for c in range(N_COPIES):
+            kv = torch.empty((w.B, w.N, 2 * w.D), dtype=torch.bfloat16, device=dev)
+            if c == 0:
+                comp_ms = timed(lambda i: csa.compress(inp["raw"], inp["logits"], w.m, out=kv), 3, 1)
+            else:
+                csa.compress(inp["raw"], inp["logits"], w.m, out=kv)
+            caches.append(kv)
+        del inp["raw"]
+        ws = torch.empty(csa.hca_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.N),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(inp["q"])
+
+        def step(i):
+            kv = caches[i % N_COPIES]
+            csa.hca_attend(inp["q"], kv[..., :w.D], kv[..., w.D:], inp["q_pos"], inp["n_entries"],
+                           w.m, workspace=ws, out=out)
+        ms = timed(step, args.steps, args.warmup)
+        kv_bytes = w.B * w.N * w.D * 2 * 2
+        step_bytes = kv_bytes + 2 * w.B * w.H * w.D * 2
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        raw_bytes = w.B * w.n_raw * (2 * w.D * 2 + 4) + w.B * w.N * 2 * w.D * 2
+        res = dict(metric="HCA decode tokens/sec at 1M context (m'=128), 1 MI355X",
+                   value=round(w.B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                   config={"workload": w.name, "batch": w.B, "context_tokens": w.q_pos0,
+                           "compressed_entries": w.N, "m": w.m, "heads": f"{w.H}x{w.D}"},
+                   roofline={"kernel": "attend_split_kernel<HCA> + combine", "bound": "hbm",
+                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                   compress_ms=round(comp_ms, 4),
+                   compress_gbs=round(raw_bytes / (comp_ms * 1e-3) / 1e9, 1))
+    elif w.name == "csa_decode_1m_fp4":
+        # one quantised draw; the other copies hold its entries rolled along
+        # the entry axis (distinct memory for the cache rotation)
+        first = make_inputs(w, device=dev)
+        copies = [first]
+        for c in range(1, N_COPIES):
+            cp = dict(first)
+            for name in ("ki_codes", "ki_scale", "k_cache", "v_cache"):
+                cp[name] = torch.roll(first[name], shifts=997 * c, dims=1)
+            copies.append(cp)
+        ws_topk = torch.empty(csa.index_topk_workspace_bytes(w.B, 1, w.N, w.k), dtype=torch.uint8,
+                              device=dev)
+        ws_attn = torch.empty(csa.attend_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.k),
+                              dtype=torch.uint8, device=dev)
+        idx = torch.empty((w.B, 1, w.k), dtype=torch.int32, device=dev)
+        out = torch.empty_like(copies[0]["q"])
+        scores = torch.empty((w.B, 1, w.N), dtype=torch.float32, device=dev)
+
+        def step(i):
+            c = copies[i % N_COPIES]
+            csa.index_topk(c["q_codes"], c["w_idx"], c["ki_codes"], c["q_pos"], c["n_entries"], w.m,
+                           w.k, q_scale=c["q_scale"], k_scale=c["ki_scale"], workspace=ws_topk,
+                           out=idx)
+            csa.attend(c["q"], c["k_cache"], c["v_cache"], idx, c["n_entries"], workspace=ws_attn,
+                       out=out)
+
+        def score_only(i):
+            c = copies[i % N_COPIES]
+            csa.index_score(c["q_codes"], c["w_idx"], c["ki_codes"], c["q_pos"], c["n_entries"], w.m,
+                            q_scale=c["q_scale"], k_scale=c["ki_scale"], out=scores)
+        ms = timed(step, args.steps, args.warmup)
+        sms = timed(score_only, args.steps, args.warmup)
+        score_bytes = w.B * w.N * (64 + 16 + 4) + w.B * w.H_I * (64 + 16 + 4)
+        gbs = score_bytes / (sms * 1e-3) / 1e9
+        res = dict(metric="CSA decode tokens/sec at 1M context, FP4 indexer, 1 MI355X",
+                   value=round(w.B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                   config={"workload": w.name, "batch": w.B, "context_tokens": w.q_pos0,
+                           "compressed_entries": w.N, "m": w.m, "indexer": "64x128 FP4 E2M1",
+                           "top_k": w.k},
+                   roofline={"kernel": "score_fp4_h64d128_kernel", "bound": "hbm",
+                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                             "algorithmic_bytes_per_launch": score_bytes,
+                             "avg_launch_ms": round(sms, 5)})
+    elif w.name == "csa_prefill_chunk":
+        inp = make_inputs(w, device=dev)
+        cache = torch.empty((1, w.N, 384), dtype=torch.bfloat16, device=dev)
+        cache[..., :128] = inp["k_cache"]
+        cache[..., 128:256] = inp["v_cache"]
+        cache[..., 256:] = inp["ki_cache"]
+        kc, vc, ki = cache[..., :128], cache[..., 128:256], cache[..., 256:]
+        ws_topk = torch.empty(csa.index_topk_workspace_bytes(1, w.Tq, w.N, w.k), dtype=torch.uint8,
+                              device=dev)
+        ws_attn = torch.empty(csa.attend_workspace_bytes(torch.bfloat16, 1, w.Tq, w.H, w.D, w.k),
+                              dtype=torch.uint8, device=dev)
+        idx = torch.empty((1, w.Tq, w.k), dtype=torch.int32, device=dev)
+        out = torch.empty_like(inp["q"])
+        scores = torch.empty((1, w.Tq, w.N), dtype=torch.float32, device=dev)
+
+        def step(i):
+            csa.compress(inp["raw"], inp["logits"], w.m, out=cache[:, w.n_cache:])
+            csa.index_topk(inp["q_idx"], inp["w_idx"], ki, inp["q_pos"], inp["n_entries"], w.m, w.k,
+                           workspace=ws_topk, out=idx)
+            csa.attend(inp["q"], kc, vc, idx, inp["n_entries"], workspace=ws_attn, out=out)
+
+        def score_only(i):
+            csa.index_score(inp["q_idx"], inp["w_idx"], ki, inp["q_pos"], inp["n_entries"], w.m,
+                            out=scores)
+        steps, warm = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
+        ms = timed(step, steps, warm)
+        sms = timed(score_only, steps, warm)
+        # visible (query, entry) pairs x 64 heads x 128 dims x 2
+        vis = sum(w.n_cache + (i + 1) // w.m for i in range(w.Tq))
+        flop = vis * w.H_I * w.D_I * 2
+        tfs = flop / (sms * 1e-3) / 1e12
+        res = dict(metric="CSA prefill tokens/sec (4096-token chunk at 256K context), 1 MI355X",
+                   value=round(w.Tq / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                   config={"workload": w.name, "batch": 1, "chunk_tokens": w.Tq,
+                           "context_tokens": w.q_pos0, "compressed_entries": w.N, "m": w.m,
+                           "top_k": w.k},
+                   roofline={"kernel": "score_prefill_bf16_h64d128_kernel", "bound": "mfma",
+                             "achieved": round(tfs, 1), "peak": 2500.0, "unit": "TFLOP/s",
+                             "frac": round(tfs / 2500.0, 4), "traffic": None,
+                             "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(sms, 4)})
+        base["steps"], base["warmup"] = steps, warm
+    else:
+        print(f"unknown workload {w.name}", file=sys.stderr)
+        sys.exit(2)
+    base.update(res)
+    print(json.dumps(base))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -148,6 +316,10 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+
+    if args.workload != WORKLOAD:
+        other_workload(args)
         return
 
     import long_context_attention_24_amd as csa

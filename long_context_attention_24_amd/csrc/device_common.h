@@ -55,6 +55,13 @@ __device__ __forceinline__ int bound_c_row(int V, int k) {
   return c <= kMaxBoundC ? c : 0;
 }
 
+// max(x, 0) as one integer max on the bit pattern: negative values (sign bit
+// set, so negative as integers) and -0.0 become +0.0, the rest pass through.
+// A float max would first canonicalise x, costing a second instruction.
+__device__ __forceinline__ float relu_f32(float x) {
+  return __int_as_float(max(__float_as_int(x), 0));
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- wave64 reductions and scans -------------------------------------------

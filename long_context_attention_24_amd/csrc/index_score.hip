@@ -206,9 +206,9 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     }
     float sum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sum = fmaf(w0[r], fmaxf(c0[r], 0.f), sum);
+    for (int r = 0; r < 16; ++r) sum = fmaf(w0[r], relu_f32(c0[r]), sum);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], fmaxf(c1[r], 0.f), sum);
+    for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], relu_f32(c1[r]), sum);
     const float other = __shfl_xor(sum, 32, 64);
     const float tot = sum + other;     // commutative: both halves get the same bits
     const int j = key0 + 32 * t + jl;
@@ -345,9 +345,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
         const f32x16_t (&c)[2] = acc[u & 1];
         float sum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum = fmaf(wv[0][r], fmaxf(c[0][r], 0.f), sum);
+        for (int r = 0; r < 16; ++r) sum = fmaf(wv[0][r], relu_f32(c[0][r]), sum);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum = fmaf(wv[1][r], fmaxf(c[1][r], 0.f), sum);
+        for (int r = 0; r < 16; ++r) sum = fmaf(wv[1][r], relu_f32(c[1][r]), sum);
         const float tot = sum + __shfl_xor(sum, 32, 64);
         const int j = j0 + 32 * tt + jl;
         const bool ok = j < vq;
@@ -484,7 +484,7 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
         float tv = 0.f;
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) tv = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], tv);
-        sum = fmaf(wv[mt][r], fmaxf(tv, 0.f), sum);
+        sum = fmaf(wv[mt][r], relu_f32(tv), sum);
       }
     }
     // heads are spread over the four 16-lane groups of the key's column

@@ -267,9 +267,12 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
     vmax = max(vmax, v);
     if (u == wave) vq = v;
   }
-  const int rowq = t0 + wave < Tq ? b * Tq + t0 + wave : -1;
+  // wave-uniform values, made visibly uniform so their branches stay scalar
+  vmax = __builtin_amdgcn_readfirstlane(vmax);
+  vq = __builtin_amdgcn_readfirstlane(vq);
+  const int rowq = __builtin_amdgcn_readfirstlane(t0 + wave < Tq ? b * Tq + t0 + wave : -1);
   const int je = min(j1, vmax);                   // keys past je are masked for all queries
-  const int ntiles = je > j0 ? (je - j0 + 31) / 32 : 0;
+  const int ntiles = __builtin_amdgcn_readfirstlane(je > j0 ? (je - j0 + 31) / 32 : 0);
 
   // -inf for every key this workgroup covers but does not compute
   if (rowq >= 0) {
@@ -299,7 +302,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
       for (int r = 0; r < 16; ++r) wv[hf][r] = wrow[32 * hf + 8 * (r >> 2) + 4 * g + (r & 3)];
     }
   }
-  const int cq = chunk_thr != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0;
+  const int cq = __builtin_amdgcn_readfirstlane(chunk_thr != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0);
   float sc[kTilesPerWave];
   lds_u16* const st_ptr0 = (lds_u16*)&tile_lds[0][0] + lrow * kKeyPitch + 8 * (tid & 15);
   const lds_u16* const ld_ptr0 = (const lds_u16*)&tile_lds[0][0] + jl * kKeyPitch + 8 * g;

@@ -370,41 +370,41 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
   const int h = tid & 63, d0 = 32 * blockIdx.y + 8 * (tid >> 6);
   const int64_t sstride = static_cast<int64_t>(kPartRows) * 64;
   const float* base = part + static_cast<int64_t>(row) * nsplit * sstride + h;
-  // pass 1: the maxima (independent loads); pass 2: splits in groups of four
-  // with every load of a group issued before its arithmetic
-  constexpr int U = 4;
-  float M = kNegInf;
-  for (int s = 0; s < nsplit; s += U) {
-    float mm[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) mm[u] = s + u < nsplit ? base[(s + u) * sstride + 128 * 64] : kNegInf;
-#pragma unroll
-    for (int u = 0; u < U; ++u) M = fmaxf(M, mm[u]);
-  }
-  float L = 0.f;
+  // One pass over the splits in groups of eight: every load of a group
+  // (maxima, sums, partial rows) is issued before its arithmetic, and the
+  // running maximum rescales what is already summed.
+  constexpr int U = 8;
+  float M = kNegInf, L = 0.f;
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-  if (M != kNegInf) {
-    for (int s = 0; s < nsplit; s += U) {
-      float v[U][8], ms[U], ls[U];
+  for (int s = 0; s < nsplit; s += U) {
+    float v[U][8], ms[U], ls[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const bool ok = s + u < nsplit;
-        const float* ps = base + static_cast<int64_t>(ok ? s + u : s) * sstride;
+    for (int u = 0; u < U; ++u) {
+      const bool ok = s + u < nsplit;
+      const float* ps = base + static_cast<int64_t>(ok ? s + u : s) * sstride;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[u][i] = ps[(d0 + i) * 64];
-        ms[u] = ok ? ps[128 * 64] : kNegInf;
-        ls[u] = ps[129 * 64];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const float w = ms[u] == kNegInf ? 0.f : exp2_fast(ms[u] - M);
-        L = fmaf(w, ls[u], L);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[u][i], acc[i]);
-      }
+      for (int i = 0; i < 8; ++i) v[u][i] = ps[(d0 + i) * 64];
+      ms[u] = ok ? ps[128 * 64] : kNegInf;
+      ls[u] = ps[129 * 64];
     }
+    float mg = M;
+#pragma unroll
+    for (int u = 0; u < U; ++u) mg = fmaxf(mg, ms[u]);
+    if (mg == kNegInf) continue;
+    const float a = M == kNegInf ? 0.f : exp2_fast(M - mg);
+    L *= a;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= a;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float wu = ms[u] == kNegInf ? 0.f : exp2_fast(ms[u] - mg);
+      L = fmaf(wu, ls[u], L);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
+    }
+    M = mg;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint4 v;

@@ -78,8 +78,8 @@ csa_status_t check_score_args(const void* q_idx, const float* q_scale, const flo
   return CSA_OK;
 }
 
-// Chunk bounds written by the tuned score kernels: one per 256-key chunk of a
-// row, each the c-th largest score of its chunk (see topk.hip).
+// Chunk reports written by the tuned score kernels: one per 256-key chunk of a
+// row, the c-th largest and the largest score of the chunk (see topk.hip).
 int bound_chunks(int N_max) {
   return (N_max + csa::score_chunk_keys() - 1) / csa::score_chunk_keys();
 }
@@ -94,7 +94,7 @@ size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws) {
   const size_t rows = static_cast<size_t>(B) * Tq;
   const size_t bws = csa::topk_bounded_workspace_bytes(static_cast<int>(rows), N_max);
   return round_up(rows * score_row_stride(N_max) * sizeof(float)) +
-         round_up(rows * bound_chunks(N_max) * sizeof(float)) +
+         round_up(rows * bound_chunks(N_max) * sizeof(float2)) +
          round_up(topk_ws > bws ? topk_ws : bws);
 }
 
@@ -224,8 +224,8 @@ csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float
   base += round_up(rows * srs * sizeof(float));
   const int n_chunks = bound_chunks(N_max);
   const int bk = bound_k(idx_dtype, H_I, D_I, N_max, k);
-  float* bounds = bk > 0 ? reinterpret_cast<float*>(base) : nullptr;
-  base += round_up(rows * n_chunks * sizeof(float));
+  float2* bounds = bk > 0 ? reinterpret_cast<float2*>(base) : nullptr;
+  base += round_up(rows * n_chunks * sizeof(float2));
   csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
                    q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs,
                    bounds, n_chunks, bk};

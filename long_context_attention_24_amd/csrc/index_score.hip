@@ -65,27 +65,30 @@ __global__ __launch_bounds__(256) void score_generic_kernel(
 }
 
 // ---------------------------------------------------------------- selection bound
-// Each wave also reports the c-th largest of the scores it produced (its
-// chunk of kBoundChunk keys), with c = bound_c_row(V, k) for the row.  Every
-// chunk that reports a finite value holds c entries at or above it, and the
-// floor(V / kBoundChunk) full chunks all do, so the minimum report is at most
-// the row's k-th largest score.  The top-k kernels use that bound to drop
-// most entries before selecting.  A chunk with fewer than c valid entries
-// reports +inf; rows with no bound (c = 0) write nothing.
+// Each wave also reports, for the scores it produced (its chunk of
+// kBoundChunk keys), the c-th largest with c = bound_c_row(V, k) for the row,
+// and the largest.  Every chunk that reports a finite c-th largest holds c
+// entries at or above it, and the floor(V / kBoundChunk) full chunks all do,
+// so the minimum report is at most the row's k-th largest score.  The top-k
+// kernels use that bound to drop most entries before selecting, and the
+// largest report as the top of the survivors' range.  A chunk with fewer
+// than c valid entries reports +inf as its c-th largest (-inf as its largest
+// when it has none); rows with no bound (c = 0) write nothing.
 constexpr float kPosInf = __builtin_inff();
 
 template <int NV>
-__device__ float wave_cth_largest(const float (&vals)[NV], bool active, int c) {
+__device__ float2 wave_chunk_report(const float (&vals)[NV], bool active, int c) {
   const int lane = threadIdx.x & 63;
   float v[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = active ? vals[i] : kNegInf;
-  float cur = kPosInf;
+  float cur = kPosInf, top = kNegInf;
   for (int r = 0; r < c; ++r) {
     float lm = v[0];
 #pragma unroll
     for (int i = 1; i < NV; ++i) lm = fmaxf(lm, v[i]);
     const float wm = wave_max(lm);
+    if (r == 0) top = wm;
     if (wm == kNegInf) {
       cur = kPosInf;
       break;
@@ -103,7 +106,7 @@ __device__ float wave_cth_largest(const float (&vals)[NV], bool active, int c) {
     }
     cur = wm;
   }
-  return cur;
+  return make_float2(cur, top);
 }
 
 // ---------------------------------------------------------------- bf16, 64 heads x 128
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
-    int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
+    int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
   __shared__ __attribute__((aligned(16))) uint16_t key_lds[kWavesPerWg][32 * kKeyPitch];
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
   float* srow = scores + row * s_rs;
   for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
   if (key0 >= vis_end) {
-    if (chunk_thr != nullptr && lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = kPosInf;
+    if (chunk_rep != nullptr && lane == 0)
+      chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
     return;
   }
 
@@ -218,9 +222,9 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   const int thr_c = bound_c_row(V, bound_k);
-  if (chunk_thr != nullptr && thr_c > 0) {
-    const float cth = wave_cth_largest<kTilesPerWave>(sc, g == 0, thr_c);
-    if (lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = cth;
+  if (chunk_rep != nullptr && thr_c > 0) {
+    const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, thr_c);
+    if (lane == 0) chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = rep;
   }
 }
 
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
-    int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
+    int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   __shared__ __attribute__((aligned(16))) uint16_t tile_lds[3][32 * kKeyPitch];
@@ -302,7 +306,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
       for (int r = 0; r < 16; ++r) wv[hf][r] = wrow[32 * hf + 8 * (r >> 2) + 4 * g + (r & 3)];
     }
   }
-  const int cq = __builtin_amdgcn_readfirstlane(chunk_thr != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0);
+  const int cq = __builtin_amdgcn_readfirstlane(chunk_rep != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0);
   float sc[kTilesPerWave];
   lds_u16* const st_ptr0 = (lds_u16*)&tile_lds[0][0] + lrow * kKeyPitch + 8 * (tid & 15);
   const lds_u16* const ld_ptr0 = (const lds_u16*)&tile_lds[0][0] + jl * kKeyPitch + 8 * g;
@@ -360,8 +364,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
         if (cq > 0 && (u == kTilesPerWave - 1 || tt == ntiles - 1)) {
 #pragma unroll
           for (int v = u + 1; v < kTilesPerWave; ++v) sc[v] = kNegInf;
-          const float cth = wave_cth_largest<kTilesPerWave>(sc, g == 0, cq);
-          if (lane == 0) chunk_thr[static_cast<int64_t>(rowq) * n_chunks + (j0 + 32 * tt) / kBoundChunk] = cth;
+          const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, cq);
+          if (lane == 0) chunk_rep[static_cast<int64_t>(rowq) * n_chunks + (j0 + 32 * tt) / kBoundChunk] = rep;
         }
       }
     }
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   // chunks with no computed key: no bound
   if (cq > 0 && lane == 0) {
     for (int ch = (j0 + 32 * ntiles + kBoundChunk - 1) / kBoundChunk; ch * kBoundChunk < j1; ++ch)
-      chunk_thr[static_cast<int64_t>(rowq) * n_chunks + ch] = kPosInf;
+      chunk_rep[static_cast<int64_t>(rowq) * n_chunks + ch] = make_float2(kPosInf, kNegInf);
   }
 }
 
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     const uint8_t* __restrict__ k, const float* __restrict__ k_scale, int64_t k_sb, int64_t k_sn,
     int64_t ks_sb, int64_t ks_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
-    int64_t s_rs, float* __restrict__ chunk_thr, int n_chunks, int bound_k) {
+    int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -417,7 +421,8 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
   float* srow = scores + row * s_rs;
   for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
   if (key0 >= vis_end) {
-    if (chunk_thr != nullptr && lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = kPosInf;
+    if (chunk_rep != nullptr && lane == 0)
+      chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
     return;
   }
 
@@ -500,9 +505,9 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     __builtin_amdgcn_sched_barrier(0);
   }
   const int thr_c = bound_c_row(V, bound_k);
-  if (chunk_thr != nullptr && thr_c > 0) {
-    const float cth = wave_cth_largest<kFp4Tiles>(scv, g == 0, thr_c);
-    if (lane == 0) chunk_thr[static_cast<int64_t>(row) * n_chunks + chunk] = cth;
+  if (chunk_rep != nullptr && thr_c > 0) {
+    const float2 rep = wave_chunk_report<kFp4Tiles>(scv, g == 0, thr_c);
+    if (lane == 0) chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = rep;
   }
 }
 
@@ -535,20 +540,20 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
                        static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
                        static_cast<const uint8_t*>(a.k), a.k_scale, a.k_sb, a.k_sn, a.ks_sb,
                        a.ks_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs,
-                       a.chunk_thr, a.n_chunks, a.bound_k);
+                       a.chunk_rep, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128 && a.Tq >= kPfQueries) {
     const int groups = (a.Tq + kPfQueries - 1) / kPfQueries;
     const dim3 grid((a.N_max + kPfKeys - 1) / kPfKeys, a.B * groups);
     hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel, grid, dim3(kPfThreads), 0, s,
                        static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
                        a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
-                       a.s_rs, a.chunk_thr, a.n_chunks, a.bound_k);
+                       a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
     const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
     hipLaunchKernelGGL(score_bf16_h64d128_kernel, grid, dim3(256), 0, s,
                        static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
                        a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
-                       a.s_rs, a.chunk_thr, a.n_chunks, a.bound_k);
+                       a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16) {
     if (a.D == 32) launch_generic<uint16_t, 32>(a, s);
     else if (a.D == 64) launch_generic<uint16_t, 64>(a, s);

@@ -28,7 +28,7 @@ struct ScoreArgs {
   int B, Tq, N_max, H, D, m;
   float* scores;            // [B*Tq, s_rs]
   int64_t s_rs;             // row stride of scores (elements)
-  float* chunk_thr;         // [B*Tq, n_chunks] selection bounds (tuned kernels), or NULL
+  float2* chunk_rep;        // [B*Tq, n_chunks] (c-th largest, largest) per chunk, or NULL
   int n_chunks, bound_k;    // bound_k: the k the bounds serve (0: none)
 };
 hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s);
@@ -37,8 +37,8 @@ bool score_tuned(csa_dtype_t dt, int H, int D);   // writes chunk bounds
 int score_chunk_keys();                            // keys per bound chunk
 
 // ---- topk.hip
-// Selection from rows of N_max scores.  chunk_thr (nullable): per-row bounds
-// written by the tuned score kernels (one report per 256-key chunk, n_chunks
+// Selection from rows of N_max scores.  chunk_rep (nullable): per-row chunk
+// reports written by the tuned score kernels (one per 256-key chunk, n_chunks
 // per row, for the same k); they are used when topk_bounded_ok(N_max), with
 // a workspace of topk_bounded_workspace_bytes (zero for rows short enough to
 // be streamed by one workgroup).  Otherwise the workspace is
@@ -49,7 +49,7 @@ size_t topk_bounded_workspace_bytes(int rows, int N_max);
 bool topk_supported(int N_max, int k);
 hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
-                       const float* chunk_thr, int n_chunks, int32_t* idx,
+                       const float2* chunk_rep, int n_chunks, int32_t* idx,
                        float* out_scores, void* ws, hipStream_t s);
 
 // ---- attend.hip

@@ -18,11 +18,14 @@
 // Only integer LDS atomics (counts) are used, so results are deterministic.
 //
 // Drivers.
-//   * Bounded (topk_bounded_kernel), used with the chunk bounds the tuned
-//     score kernels leave: per 256-key chunk of a row its c-th largest
-//     score, whose minimum over the row is at most the row's k-th largest
-//     (see bound_c_row).  Entries below it can never be selected, so one
-//     workgroup per row keeps the few survivors in LDS and selects there.
+//   * Bounded (topk_bounded_kernel), used with the chunk reports the tuned
+//     score kernels leave: per 256-key chunk of a row its c-th largest and
+//     its largest score.  The minimum c-th largest over the row is at most
+//     the row's k-th largest (see bound_c_row), so entries below it can never
+//     be selected: one workgroup per row keeps the few survivors in LDS, in
+//     index order, and selects there (select_sorted_list: the same histogram
+//     search over [bound, largest report], finished by pairwise ranks inside
+//     a small bin).
 //   * Unbounded (topk_seg_kernel): one workgroup per row segment of up to
 //     32768 scores.  Rows longer than one segment take two passes: each
 //     segment keeps its own top-k (a superset of its share of the row's
@@ -56,9 +59,11 @@ struct Scratch {
   float f0[2][kMaxWaves];
   float f1[2][kMaxWaves];
   uint32_t u[2][kMaxWaves];
-  uint32_t tab[1024];                 // per-thread prefix of the index bitmap
+  uint32_t tab[1024];                 // region offsets, then threshold candidates
   int bstar, bstar_above, bstar_cnt;
-  uint32_t list_n;                    // survivors appended so far
+  uint32_t cand_n;                    // threshold candidates gathered so far
+  float tval;
+  int teq;
 };
 __shared__ Scratch g_sm;
 
@@ -286,25 +291,6 @@ __device__ __forceinline__ void pad_output(const Emitter& em, int n, int k) {
   }
 }
 
-// ================================================================ bounds
-// Per-row bound from the chunk values; -inf if unusable.
-template <int NW>
-__device__ __forceinline__ float row_bound(const float* __restrict__ thr, int n_chunks, int c, int k,
-                                           int& p) {
-  float mn = FLT_MAX, unused = -FLT_MAX;
-  uint32_t cnt = 0;
-  const int nc = c > 0 ? n_chunks : 0;           // no bound: the reports are not written
-  for (int i = threadIdx.x; i < nc; i += NW * 64) {
-    const float x = thr[i];
-    if (x != kPosInf) {
-      mn = fminf(mn, x);
-      ++cnt;
-    }
-  }
-  block_minmax_count<NW>(mn, unused, cnt, p);
-  return static_cast<long long>(cnt) * c >= k ? mn : kNegInf;
-}
-
 // LDS run of R values per thread in the transposed layout v[i*THREADS + t].
 template <int THREADS>
 struct SplitRun {
@@ -457,94 +443,75 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 // directly (block_select, slow but exact).
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-constexpr int kRadixBits = 11;
-static_assert((1 << kRadixBits) == kBins && kBins == 2 * kSelThreads, "two bins per thread");
-constexpr int kMaxBoundedN = 262144;              // index bitmap: 8192 words of LDS
-constexpr int kBitmapWords = kMaxBoundedN / 32;
-constexpr int kStageVec = 8;                      // 16-byte loads per thread per chunk
-constexpr int kStageChunk = kSelThreads * 4 * kStageVec;
-constexpr int kListCap = 12 * kSelThreads;        // survivors held in LDS
+static_assert(kBins == 2 * kSelThreads, "two bins per thread");
+constexpr int kMaxBoundedN = 262144;
+constexpr int kListCap = 16 * kSelThreads;        // survivors held in LDS (< 65536: packed scans)
+constexpr int kBrute = 256;                       // bin size finished by pairwise ranks
+constexpr int kStreamSlots = 16;                  // 4-byte loads per lane per round
+constexpr int kWaveSeg = 64 * kStreamSlots;       // entries per wave per round
+constexpr int kRoundLen = kSelWaves * kWaveSeg;   // entries per round
 
-typedef __attribute__((address_space(3))) uint32_t lds_uint;
+// survivor list: (score bits, entry index) pairs in ascending index order
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2_t lds_u32x2;
 
-// order-preserving key of a float that is not NaN and not -0.0
-__device__ __forceinline__ uint32_t ord_key(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
+__device__ __forceinline__ float lval(const lds_u32x2* lp, int j) { return __uint_as_float(lp[j].x); }
 
-// Survivors of one row: element (i, thread t) is survivor i * 1024 + t.
-template <int NV>
-struct RegSrc {                         // held in registers
-  static constexpr int kUnroll = NV;
-  float v[NV];
-  int e[NV];
-  __device__ __forceinline__ int len() const { return NV; }
-  __device__ __forceinline__ float val(int i) const { return v[i]; }
-  __device__ __forceinline__ int idx(int i) const { return e[i]; }
-};
-__device__ __forceinline__ void set_bit(lds_uint* bm, int e) {
-  __hip_atomic_fetch_or(&bm[e >> 5], 1u << (e & 31), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-}
-
-// Bitmap ranks: after the bits are set and a barrier, bitmap_prefix gives each
-// thread the number of set bits before its words (WPT words per thread) in
-// g_sm.tab; after one more barrier bitmap_rank(e) is the number of set bits
-// below bit e.
-__device__ __forceinline__ uint32_t bitmap_prefix(const lds_uint* bm, int W, int WPT, int& p) {
-  uint32_t ps = 0;
-  for (int j = 0; j < WPT; ++j) {
-    const int w = threadIdx.x * WPT + j;
-    if (w < W) ps += __popc(bm[w]);
-  }
-  uint32_t tot;
-  g_sm.tab[threadIdx.x] = block_excl_scan<kSelWaves>(ps, tot, p);
-  return tot;
-}
-__device__ __forceinline__ int bitmap_rank(const lds_uint* bm, int WPT, int e) {
-  const int w = e >> 5, t = w / WPT;
-  uint32_t r = g_sm.tab[t];
-  for (int x = t * WPT; x < w; ++x) r += __popc(bm[x]);
-  return static_cast<int>(r + __popc(bm[w] & ((1u << (e & 31)) - 1u)));
-}
-
-template <typename Src>
-__device__ __forceinline__ void radix_select(const Src& src, int n, uint32_t kmin, uint32_t kmax,
-                                             int k, int W, int WPT, lds_uint* bm, int& p,
-                                             int32_t* __restrict__ oi, float* __restrict__ ov) {
+// Top-k of the survivor list lp[0..n) (values > -inf, -0.0 and +0.0 equal,
+// all within [lo, hi] when have_range, else the range is computed here).
+// Writes min(k, n) entry indices in ascending order to oi (their scores to
+// ov), pads with -1 / -inf.
+//   Threshold: one 2048-bin histogram over [lo, hi] (the bin is a monotone
+//   function of the score) locates the bin of the k-th largest; a bin of at
+//   most kBrute entries is finished by pairwise ranks (each candidate counts
+//   the larger and the equal ones), a larger one narrows [lo, hi] to the bin
+//   and repeats.
+//   Output: the list is in index order, so one block scan of (count > T,
+//   count == T) over contiguous per-thread runs gives every output slot;
+//   entries equal to T are taken lowest index first.
+// Entry: the histogram is zero, g_sm.cand_n is zero and a barrier separates
+// the list writes from this call.
+__device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, float lo, float hi,
+                                                   bool have_range, int k, int& p,
+                                                   int32_t* __restrict__ oi,
+                                                   float* __restrict__ ov) {
   constexpr int NW = kSelWaves;
-  constexpr int UF = Src::kUnroll;
   const int tid = threadIdx.x;
-  const int R = src.len();
-  // selection: key u = ord_key(x) - kmin; taken if u > Tu, or u == Tu and
-  // index <= Emax
-  int64_t Tu = -1;
-  int take_eq = 0;
+  float T = kNegInf;
+  int take_eq = 1 << 30;                          // n <= k: everything is taken
   if (n > k) {
-    const uint32_t range = kmax - kmin;
-    int hs = range == 0 ? 0 : 32 - __clz(range);  // keys still in play: (u >> hs) == prefix
-    uint64_t prefix = 0;
-    int need = k;
-    if (hs == 0) {
-      Tu = 0;
-      take_eq = k;
+    if (!have_range) {
+      float mn = FLT_MAX, mx = -FLT_MAX;
+      uint32_t unused = 0;
+      for (int j = tid; j < n; j += kSelThreads) {
+        const float x = lval(lp, j);
+        mn = fminf(mn, x);
+        mx = fmaxf(mx, x);
+      }
+      block_minmax_count<NW>(mn, mx, unused, p);
+      lo = mn;
+      hi = mx;
     }
-    while (hs > 0) {
-      const int shift = max(hs - kRadixBits, 0);
-      const uint32_t dmask = (1u << (hs - shift)) - 1u;
-#pragma unroll UF
-      for (int i = 0; i < R; ++i) {
-        const float x = src.val(i);
-        if (x > kNegInf) {
-          const uint64_t u = ord_key(x) - kmin;
-          if ((u >> hs) == prefix) atomicAdd(&g_sm.hist[(u >> shift) & dmask], 1);
-        }
+    lo += 0.0f;                                   // -0.0 -> +0.0
+    hi += 0.0f;
+    int need = k;
+    for (int iter = 0;; ++iter) {
+      if (lo == hi || iter >= 64) {               // all candidates equal (64 is never reached)
+        T = lo;
+        take_eq = need;
+        break;
+      }
+      const double dlo = static_cast<double>(lo);
+      const double inv = static_cast<double>(kBins) / (static_cast<double>(hi) - dlo);
+      for (int j = tid; j < n; j += kSelThreads) {
+        const float x = lval(lp, j);
+        if (x >= lo && x <= hi) atomicAdd(&g_sm.hist[bin_of(x, dlo, inv)], 1);
       }
       __syncthreads();
       const uint32_t h0 = g_sm.hist[2 * tid], h1 = g_sm.hist[2 * tid + 1];
       uint32_t tot;
       const uint32_t pre = block_excl_scan<NW>(h0 + h1, tot, p);
-      uint32_t above = tot - pre - h0 - h1;
+      uint32_t above = tot - pre - h0 - h1;       // candidates in higher bins
       const uint32_t un = static_cast<uint32_t>(need);
       if (above < un && un <= above + h1) {
         g_sm.bstar = 2 * tid + 1;
@@ -560,115 +527,143 @@ __device__ __forceinline__ void radix_select(const Src& src, int n, uint32_t kmi
       g_sm.hist[2 * tid] = 0;
       g_sm.hist[2 * tid + 1] = 0;
       __syncthreads();
+      const int bstar = g_sm.bstar;
       need -= g_sm.bstar_above;
       const int cnt = g_sm.bstar_cnt;
-      prefix = (prefix << (hs - shift)) | static_cast<uint64_t>(g_sm.bstar);
-      hs = shift;
-      if (cnt == need) {                          // the whole bin is taken
-        Tu = static_cast<int64_t>(prefix << hs) - 1;
-        take_eq = 0;
+      if (cnt <= kBrute) {
+        // the need-th largest of the bin: the candidate with fewer than need
+        // larger ones and at least need larger-or-equal ones
+        for (int j = tid; j < n; j += kSelThreads) {
+          const float x = lval(lp, j);
+          if (x >= lo && x <= hi && bin_of(x, dlo, inv) == bstar) {
+            const uint32_t slot = atomicAdd(&g_sm.cand_n, 1u);
+            g_sm.tab[slot] = __float_as_uint(x);
+          }
+        }
+        __syncthreads();
+        if (tid < cnt) {
+          const float v = __uint_as_float(g_sm.tab[tid]);
+          int g = 0, e = 0;
+          for (int u = 0; u < cnt; ++u) {
+            const float y = __uint_as_float(g_sm.tab[u]);
+            g += y > v ? 1 : 0;
+            e += y == v ? 1 : 0;
+          }
+          if (g < need && need <= g + e) {        // every such candidate writes the same
+            g_sm.tval = v + 0.0f;
+            g_sm.teq = need - g;
+          }
+        }
+        __syncthreads();
+        T = g_sm.tval;
+        take_eq = g_sm.teq;
         break;
       }
-      if (hs == 0) {                              // the bin is the single key Tu
-        Tu = static_cast<int64_t>(prefix);
-        take_eq = need;
-      }
-    }
-  }
-  int emax = INT_MAX;
-  if (take_eq > 0) {
-    // more entries equal the threshold than are taken: keep the take_eq
-    // lowest indices, found from the ranks of the equal entries' bits
-#pragma unroll UF
-    for (int i = 0; i < R; ++i) {
-      const float x = src.val(i);
-      if (x > kNegInf && static_cast<int64_t>(ord_key(x) - kmin) == Tu) {
-        const int e = src.idx(i);
-        set_bit(bm, e);
-      }
-    }
-    __syncthreads();
-    bitmap_prefix(bm, W, WPT, p);
-    __syncthreads();
-#pragma unroll UF
-    for (int i = 0; i < R; ++i) {
-      const float x = src.val(i);
-      if (x > kNegInf && static_cast<int64_t>(ord_key(x) - kmin) == Tu) {
-        const int e = src.idx(i);
-        if (bitmap_rank(bm, WPT, e) == take_eq - 1) g_sm.bstar = e;
-      }
-    }
-    __syncthreads();
-    emax = g_sm.bstar;
-    for (int j = 0; j < WPT; ++j) {
-      const int w = tid * WPT + j;
-      if (w < W) bm[w] = 0;
-    }
-    __syncthreads();
-  }
-  // bitmap of the taken indices -> output slots
-#pragma unroll UF
-  for (int i = 0; i < R; ++i) {
-    const float x = src.val(i);
-    if (x > kNegInf) {
-      const int64_t u = static_cast<int64_t>(ord_key(x) - kmin);
-      const int e = src.idx(i);
-      if (u > Tu || (u == Tu && e <= emax)) set_bit(bm, e);
-    }
-  }
-  __syncthreads();
-  const int n_sel = static_cast<int>(bitmap_prefix(bm, W, WPT, p));
-  __syncthreads();
-#pragma unroll UF
-  for (int i = 0; i < R; ++i) {
-    const float x = src.val(i);
-    if (x > kNegInf) {
-      const int64_t u = static_cast<int64_t>(ord_key(x) - kmin);
-      const int e = src.idx(i);
-      if (u > Tu || (u == Tu && e <= emax)) {
-        const int slot = bitmap_rank(bm, WPT, e);
-        if (slot < k) {                           // always true; keeps writes in bounds
-          oi[slot] = e;
-          if (ov != nullptr) ov[slot] = x;
+      float bmn = FLT_MAX, bmx = -FLT_MAX;
+      uint32_t unused = 0;
+      for (int j = tid; j < n; j += kSelThreads) {
+        const float x = lval(lp, j);
+        if (x >= lo && x <= hi && bin_of(x, dlo, inv) == bstar) {
+          bmn = fminf(bmn, x);
+          bmx = fmaxf(bmx, x);
         }
       }
+      block_minmax_count<NW>(bmn, bmx, unused, p);
+      lo = bmn + 0.0f;
+      hi = bmx + 0.0f;
     }
   }
+  // ordered compaction over contiguous runs of R list positions per thread
+  const int R = (n + kSelThreads - 1) / kSelThreads;
+  const int j0 = tid * R, j1 = min(n, j0 + R);
+  uint32_t gt = 0, eq = 0;
+  for (int j = j0; j < j1; ++j) {
+    const float x = lval(lp, j);
+    gt += x > T ? 1u : 0u;
+    eq += x == T ? 1u : 0u;
+  }
+  uint32_t tot;
+  const uint32_t pre = block_excl_scan<NW>(gt | (eq << 16), tot, p);
+  int eq_before = static_cast<int>(pre >> 16);
+  int slot = static_cast<int>(pre & 0xffffu) + min(eq_before, take_eq);
+  for (int j = j0; j < j1; ++j) {
+    const u32x2_t e = lp[j];
+    const float x = __uint_as_float(e.x);
+    bool take = x > T;
+    if (!take && x == T) {
+      take = eq_before < take_eq;
+      ++eq_before;
+    }
+    if (take) {
+      if (slot < k) {                             // always true; keeps writes in bounds
+        oi[slot] = static_cast<int32_t>(e.y);
+        if (ov != nullptr) ov[slot] = x + 0.0f;
+      }
+      ++slot;
+    }
+  }
+  const int n_sel =
+      min(k, static_cast<int>(tot & 0xffffu) + min(static_cast<int>(tot >> 16), take_eq));
   for (int sl = n_sel + tid; sl < k; sl += kSelThreads) {
     oi[sl] = -1;
     if (ov != nullptr) ov[sl] = kNegInf;
   }
 }
 
-template <int NV>
-__device__ __forceinline__ void select_list(const lds_float* lv, const lds_int* li, int n,
-                                            uint32_t kmin, uint32_t kmax, int k, int W, int WPT,
-                                            lds_uint* bm, int& p, int32_t* __restrict__ oi,
-                                            float* __restrict__ ov) {
-  RegSrc<NV> src;
+// One round of a wave's contiguous segment: lane l holds entries
+// base + 64 s + l, s < kStreamSlots (-inf at or past N_max).
+__device__ __forceinline__ void load_round(const float* __restrict__ srow, int base, int N_max,
+                                           float (&x)[kStreamSlots]) {
+  const int lane = threadIdx.x & 63;
+  if (base + kWaveSeg <= N_max) {
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    const int q = i * kSelThreads + threadIdx.x;
-    src.v[i] = q < n ? lv[q] : kNegInf;
-    src.e[i] = q < n ? li[q] : 0;
-  }
-  radix_select(src, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
-}
-
-__device__ __forceinline__ void load_stage(const float* __restrict__ srow, int c0, int V,
-                                           float4 (&x)[kStageVec]) {
+    for (int s = 0; s < kStreamSlots; ++s) x[s] = srow[base + 64 * s + lane];
+  } else {
 #pragma unroll
-  for (int i = 0; i < kStageVec; ++i) {
-    const int q = c0 + 4 * (i * kSelThreads + static_cast<int>(threadIdx.x));
-    if (q + 3 < V) {
-      x[i] = *reinterpret_cast<const float4*>(srow + q);
-    } else {
-      x[i].x = q < V ? srow[q] : kNegInf;
-      x[i].y = q + 1 < V ? srow[q + 1] : kNegInf;
-      x[i].z = q + 2 < V ? srow[q + 2] : kNegInf;
-      x[i].w = q + 3 < V ? srow[q + 3] : kNegInf;
+    for (int s = 0; s < kStreamSlots; ++s) {
+      const int q = base + 64 * s + lane;
+      x[s] = q < N_max ? srow[q] : kNegInf;
     }
   }
+}
+
+// Row bound and range top from the chunk reports, computed by every wave on
+// its own.  bound: the minimum c-th largest report when the reporting chunks
+// hold at least k entries at or above their reports, else -inf.  top: the
+// largest report (at least every score of the row).  c = 0: no reports were
+// written; both are -inf.  The reports are loaded before c is looked at (they
+// are in bounds either way), four per lane at a time.
+__device__ __forceinline__ float2 wave_row_bound(const float2* __restrict__ rep, int n_chunks,
+                                                 int c, int k) {
+  const int lane = threadIdx.x & 63;
+  float mn = FLT_MAX, mx = -FLT_MAX;
+  uint32_t cnt = 0;
+  for (int i0 = 0; i0 < n_chunks; i0 += 256) {
+    float2 t[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + 64 * u + lane;
+      t[u] = i < n_chunks ? rep[i] : make_float2(kPosInf, kNegInf);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (t[u].x != kPosInf) {
+        mn = fminf(mn, t[u].x);
+        ++cnt;
+      }
+      mx = fmaxf(mx, t[u].y);
+    }
+  }
+  if (c <= 0) return make_float2(kNegInf, kNegInf);
+  mn = wave_min(mn);
+  mx = wave_max(mx);
+  cnt = wave_sum_u32(cnt);
+  return make_float2(static_cast<long long>(cnt) * c >= k ? mn : kNegInf, mx);
+}
+
+__device__ __forceinline__ uint32_t lanes_below(uint64_t msk, uint32_t add) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(msk >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(msk), add));
 }
 
 // Few long rows (more than kStreamMaxN entries, at most kRegionMaxRows rows:
@@ -676,245 +671,205 @@ __device__ __forceinline__ void load_stage(const float* __restrict__ srow, int c
 // topk_filter_kernel: one 256-thread workgroup per 4096 entries, each wave
 // owning 1024 of them (a region) and working alone (no barrier, no atomic):
 // it derives the row bound from the chunk reports, compacts its entries at or
-// above the bound to the front of its region of the survivor buffers and
-// stores their number.  The bounded kernel then gathers the regions instead
-// of streaming the row.
+// above the bound, in index order, to the front of its region of the
+// survivor buffers and stores their number.  The bounded kernel then gathers
+// the regions instead of streaming the row.
 constexpr int kStreamMaxN = 65536;
 constexpr int kRegionMaxRows = 64;
 constexpr int kFiltSeg = 4096;
 constexpr int kRegion = 1024;
+static_assert(kMaxBoundedN / kRegion <= kSelThreads, "one region per thread in the offset scan");
 
 __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(
     const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
-    const float* __restrict__ chunk_thr, int n_chunks, int nreg, float* __restrict__ reg_val,
+    const float2* __restrict__ chunk_rep, int n_chunks, int nreg, float* __restrict__ reg_val,
     int32_t* __restrict__ reg_idx, int32_t* __restrict__ reg_cnt) {
   const int seg = blockIdx.x, row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int e0 = seg * kFiltSeg + wave * kRegion;
-  const int L = max(0, min(V - e0, kRegion));
   const int r = seg * (kFiltSeg / kRegion) + wave;
   if (r >= nreg) return;
+  // loads bounded by N_max, issued before the visible count is known
+  const int Ln = max(0, min(N_max - e0, kRegion));
   const float* src = scores + row * s_rs + e0;
   float v[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = 256 * i + 4 * lane;
-    if (q + 3 < L) {
+    if (q + 3 < Ln) {
       const float4 x = *reinterpret_cast<const float4*>(src + q);
       v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < L) ? src[q + e] : kNegInf;
+      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < Ln) ? src[q + e] : kNegInf;
     }
   }
-  const int c = bound_c_row(V, k);
-  float bound = kNegInf;
-  if (c > 0) {
-    const float* thr = chunk_thr + static_cast<int64_t>(row) * n_chunks;
-    float mn = FLT_MAX;
-    uint32_t cnt = 0;
-    for (int i = lane; i < n_chunks; i += 64) {
-      const float t = thr[i];
-      if (t != kPosInf) {
-        mn = fminf(mn, t);
-        ++cnt;
-      }
-    }
-    mn = wave_min(mn);
-    cnt = wave_sum_u32(cnt);
-    if (static_cast<long long>(cnt) * c >= k) bound = mn;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const int L = max(0, min(V - e0, kRegion));
+  if (L < kRegion) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (256 * i + 4 * lane + e >= L) v[i][e] = kNegInf;
   }
-  uint32_t cl = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) cl += (v[i][e] > kNegInf && v[i][e] >= bound) ? 1u : 0u;
-  const uint32_t incl = wave_incl_scan_u32(cl);
+  const float bound = wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks,
+                                     bound_c_row(V, k), k).x;
+  const float bnd = bound > kNegInf ? bound : -FLT_MAX;   // x >= bnd: a finite survivor
   const int64_t base = (static_cast<int64_t>(row) * nreg + r) * kRegion;
-  uint32_t o = incl - cl;
+  uint32_t o = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
+    uint32_t cl = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) cl += v[i][e] >= bnd ? 1u : 0u;
+    const uint32_t incl = wave_incl_scan_u32(cl);
+    uint32_t q = o + incl - cl;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (v[i][e] > kNegInf && v[i][e] >= bound) {
-        reg_val[base + o] = v[i][e] + 0.0f;       // -0.0 -> +0.0
-        reg_idx[base + o] = e0 + 256 * i + 4 * lane + e;
-        ++o;
+      if (v[i][e] >= bnd) {
+        reg_val[base + q] = v[i][e];
+        reg_idx[base + q] = e0 + 256 * i + 4 * lane + e;
+        ++q;
       }
     }
+    o += __builtin_amdgcn_readlane(incl, 63);
   }
-  if (lane == 63) reg_cnt[static_cast<int64_t>(row) * nreg + r] = static_cast<int32_t>(incl);
+  if (lane == 0) reg_cnt[static_cast<int64_t>(row) * nreg + r] = static_cast<int32_t>(o);
 }
 
 int filter_regions(int N_max) { return (N_max + kFiltSeg - 1) / kFiltSeg * (kFiltSeg / kRegion); }
 
-// REGIONS: the survivors come from topk_filter_kernel's regions (wave w
-// takes regions w, w + 16, ...; the counts and the first 128 survivors of
-// eight regions are loaded together); otherwise the row is streamed.
+// One 1024-thread workgroup per row builds the row's survivor list in LDS in
+// ascending index order and selects from it (select_sorted_list).
+// Streaming (REGIONS false): rounds of kRoundLen entries, wave w owning the
+// round's w-th contiguous segment with lane l taking every 64th entry from l;
+// the score loads are issued before the row's visible count and bound are
+// known (bounded by N_max, masked after), and the next round's loads before
+// the current round is compacted.  Each round: per-wave survivor counts
+// (ballots) -> block scan -> every wave writes its survivors at its offset
+// plus their rank among the wave's survivors, i.e. in index order.
+// REGIONS: the per-region counts of topk_filter_kernel are scanned in region
+// order and wave w copies regions w, w + 16, ... (the counts and first 128
+// survivors of eight regions are loaded together).
+// The bound (when the row has one) and the largest chunk report delimit the
+// survivors' range.  More than kListCap survivors (inputs far from the
+// expected distribution): the row is selected from global memory by
+// block_select instead.
 template <bool REGIONS>
 __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
     const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
-    const float* __restrict__ chunk_thr, int n_chunks, int nreg,
+    const float2* __restrict__ chunk_rep, int n_chunks, int nreg,
     const float* __restrict__ reg_val, const int32_t* __restrict__ reg_idx,
     const int32_t* __restrict__ reg_cnt, int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   constexpr int NW = kSelWaves;
-  __shared__ uint32_t bm_s[kBitmapWords];
-  __shared__ float lv_s[kListCap];
-  __shared__ int li_s[kListCap];
-  lds_uint* bm = (lds_uint*)bm_s;
-  lds_float* lv = (lds_float*)lv_s;
-  lds_int* li = (lds_int*)li_s;
+  __shared__ u32x2_t lp_s[kListCap];
+  lds_u32x2* lp = (lds_u32x2*)lp_s;
   const int row = blockIdx.x, b = row / Tq;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* srow = scores + row * s_rs;
-  float4 x[kStageVec];
-  if (!REGIONS) load_stage(srow, 0, V, x);
-  const int W = (N_max + 31) >> 5;
-  const int WPT = (W + kSelThreads - 1) / kSelThreads;
+  float x[kStreamSlots];
+  if (!REGIONS) load_round(srow, wave * kWaveSeg, N_max, x);
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  float2 rb = make_float2(kNegInf, kNegInf);
+  if (!REGIONS)
+    rb = wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks, bound_c_row(V, k), k);
   g_sm.hist[2 * tid] = 0;
   g_sm.hist[2 * tid + 1] = 0;
-  for (int j = 0; j < WPT; ++j) {
-    const int w = tid * WPT + j;
-    if (w < W) bm[w] = 0;
-  }
-  if (tid == 0) g_sm.list_n = 0;
-  float smin = FLT_MAX, smax = -FLT_MAX;
+  if (tid == 0) g_sm.cand_n = 0;
   int p = 0;
+  int n = 0;                                      // block-uniform
   if (REGIONS) {
-    __syncthreads();                                // LDS state zeroed
-    const int wave = tid >> 6;
     const int32_t* cnt_row = reg_cnt + static_cast<int64_t>(row) * nreg;
-    constexpr int kBatch = 8;
-    for (int r0 = wave; r0 < nreg; r0 += kSelWaves * kBatch) {
-      int cnt[kBatch];
-      float v0[kBatch], v1[kBatch];
-      int i0[kBatch], i1[kBatch];
+    uint32_t total;
+    const uint32_t off = block_excl_scan<NW>(tid < nreg ? static_cast<uint32_t>(cnt_row[tid]) : 0u,
+                                             total, p);
+    if (tid < nreg) g_sm.tab[tid] = off;
+    n = static_cast<int>(total);
+    __syncthreads();                              // offsets visible
+    if (n <= kListCap) {
+      constexpr int kBatch = 8;
+      for (int r0 = wave; r0 < nreg; r0 += kSelWaves * kBatch) {
+        int cnt[kBatch];
+        float v0[kBatch], v1[kBatch];
+        int i0[kBatch], i1[kBatch];
 #pragma unroll
-      for (int rr = 0; rr < kBatch; ++rr) {
-        const int r = r0 + kSelWaves * rr;
-        if (r < nreg) {
-          const int64_t base = (static_cast<int64_t>(row) * nreg + r) * kRegion;
-          cnt[rr] = cnt_row[r];
-          v0[rr] = reg_val[base + lane];
-          v1[rr] = reg_val[base + 64 + lane];
-          i0[rr] = reg_idx[base + lane];
-          i1[rr] = reg_idx[base + 64 + lane];
+        for (int rr = 0; rr < kBatch; ++rr) {
+          const int r = r0 + kSelWaves * rr;
+          if (r < nreg) {
+            const int64_t base = (static_cast<int64_t>(row) * nreg + r) * kRegion;
+            cnt[rr] = cnt_row[r];
+            v0[rr] = reg_val[base + lane];
+            v1[rr] = reg_val[base + 64 + lane];
+            i0[rr] = reg_idx[base + lane];
+            i1[rr] = reg_idx[base + 64 + lane];
+          }
         }
-      }
 #pragma unroll
-      for (int rr = 0; rr < kBatch; ++rr) {
-        const int r = r0 + kSelWaves * rr;
-        if (r < nreg && cnt[rr] > 0) {
-          const int c = cnt[rr];
-          uint32_t base = 0;
-          if (lane == 0) base = atomicAdd(&g_sm.list_n, static_cast<uint32_t>(c));
-          base = __builtin_amdgcn_readfirstlane(base);
-          if (lane < c) {
-            smin = fminf(smin, v0[rr]);
-            smax = fmaxf(smax, v0[rr]);
-            if (base + lane < kListCap) {
-              lv[base + lane] = v0[rr];
-              li[base + lane] = i0[rr];
-            }
-          }
-          if (64 + lane < c) {
-            smin = fminf(smin, v1[rr]);
-            smax = fmaxf(smax, v1[rr]);
-            if (base + 64 + lane < kListCap) {
-              lv[base + 64 + lane] = v1[rr];
-              li[base + 64 + lane] = i1[rr];
-            }
-          }
-          const int64_t rb = (static_cast<int64_t>(row) * nreg + r) * kRegion;
-          for (int j = 128 + lane; j < c; j += 64) {   // rare: more than 128 survivors
-            const float x1 = reg_val[rb + j];
-            smin = fminf(smin, x1);
-            smax = fmaxf(smax, x1);
-            if (base + j < kListCap) {
-              lv[base + j] = x1;
-              li[base + j] = reg_idx[rb + j];
-            }
+        for (int rr = 0; rr < kBatch; ++rr) {
+          const int r = r0 + kSelWaves * rr;
+          if (r < nreg && cnt[rr] > 0) {
+            const int c = cnt[rr];
+            const int o = static_cast<int>(g_sm.tab[r]);
+            if (lane < c) lp[o + lane] = u32x2_t{__float_as_uint(v0[rr]), static_cast<uint32_t>(i0[rr])};
+            if (64 + lane < c)
+              lp[o + 64 + lane] = u32x2_t{__float_as_uint(v1[rr]), static_cast<uint32_t>(i1[rr])};
+            const int64_t rg = (static_cast<int64_t>(row) * nreg + r) * kRegion;
+            for (int j = 128 + lane; j < c; j += 64)   // rare: more than 128 survivors
+              lp[o + j] = u32x2_t{__float_as_uint(reg_val[rg + j]), static_cast<uint32_t>(reg_idx[rg + j])};
           }
         }
       }
     }
+    rb = wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks, bound_c_row(V, k), k);
   } else {
-  // 1. row bound
-  const int c = bound_c_row(V, k);
-  float bmn = FLT_MAX, unused_f = -FLT_MAX;
-  uint32_t bcnt = 0;
-  if (c > 0) {
-    const float* thr = chunk_thr + static_cast<int64_t>(row) * n_chunks;
-    for (int i = tid; i < n_chunks; i += kSelThreads) {
-      const float t = thr[i];
-      if (t != kPosInf) {
-        bmn = fminf(bmn, t);
-        ++bcnt;
+    const float bnd = rb.x > kNegInf ? rb.x : -FLT_MAX;     // x >= bnd: a finite survivor
+    for (int r0 = 0; r0 < V; r0 += kRoundLen) {
+      float y[kStreamSlots];
+      const bool more = r0 + kRoundLen < V;
+      if (more) load_round(srow, r0 + kRoundLen + wave * kWaveSeg, N_max, y);
+      const int sb = r0 + wave * kWaveSeg;
+      if (sb + kWaveSeg > V) {                     // entries at or past V are not visible
+#pragma unroll
+        for (int s = 0; s < kStreamSlots; ++s)
+          if (sb + 64 * s + lane >= V) x[s] = kNegInf;
+      }
+      uint32_t wt = 0;
+#pragma unroll
+      for (int s = 0; s < kStreamSlots; ++s)
+        wt += static_cast<uint32_t>(__builtin_popcountll(__builtin_amdgcn_ballot_w64(x[s] >= bnd)));
+      if (lane == 0) g_sm.u[p][wave] = wt;
+      __syncthreads();
+      const uint32_t xs = lane < NW ? g_sm.u[p][lane] : 0u;
+      const uint32_t ys = wave_incl_scan_u32(xs);
+      uint32_t o = static_cast<uint32_t>(n) + __builtin_amdgcn_readlane(ys, wave) -
+                   __builtin_amdgcn_readlane(xs, wave);
+      n += static_cast<int>(__builtin_amdgcn_readlane(ys, NW - 1));
+      p ^= 1;
+      if (n > kListCap) break;                    // uniform: fall back below
+#pragma unroll
+      for (int s = 0; s < kStreamSlots; ++s) {
+        const bool take = x[s] >= bnd;
+        const uint64_t msk = __builtin_amdgcn_ballot_w64(take);
+        if (take)
+          lp[lanes_below(msk, o)] = u32x2_t{__float_as_uint(x[s]), static_cast<uint32_t>(sb + 64 * s + lane)};
+        o += static_cast<uint32_t>(__builtin_popcountll(msk));
+      }
+      if (more) {
+#pragma unroll
+        for (int s = 0; s < kStreamSlots; ++s) x[s] = y[s];
       }
     }
   }
-  block_minmax_count<NW>(bmn, unused_f, bcnt, p);   // barrier: LDS state zeroed
-  const float bound = (c > 0 && static_cast<long long>(bcnt) * c >= k) ? bmn : kNegInf;
-  // 2. stream the row, appending survivors
-  for (int c0 = 0; c0 < V; c0 += kStageChunk) {
-    float4 y[kStageVec];
-    const bool more = c0 + kStageChunk < V;
-    if (more) load_stage(srow, c0 + kStageChunk, V, y);
-    uint32_t cl = 0;
-#pragma unroll
-    for (int i = 0; i < kStageVec; ++i) {
-      const float e4[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) cl += (e4[e] > kNegInf && e4[e] >= bound) ? 1u : 0u;
-    }
-    const uint32_t incl = wave_incl_scan_u32(cl);
-    const uint32_t tot = __builtin_amdgcn_readlane(incl, 63);
-    if (tot > 0) {                                  // uniform in the wave
-      uint32_t base = 0;
-      if (lane == 0) base = atomicAdd(&g_sm.list_n, tot);
-      base = __builtin_amdgcn_readfirstlane(base);
-      uint32_t o = base + incl - cl;
-#pragma unroll
-      for (int i = 0; i < kStageVec; ++i) {
-        const float e4[4] = {x[i].x, x[i].y, x[i].z, x[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = e4[e];
-          if (v > kNegInf && v >= bound) {
-            smin = fminf(smin, v);
-            smax = fmaxf(smax, v);
-            if (o < static_cast<uint32_t>(kListCap)) {
-              lv[o] = v + 0.0f;                     // -0.0 -> +0.0
-              li[o] = c0 + 4 * (i * kSelThreads + tid) + e;
-            }
-            ++o;
-          }
-        }
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < kStageVec; ++i) x[i] = y[i];
-    }
-  }
-  }
-  uint32_t unused_u = 0;
-  block_minmax_count<NW>(smin, smax, unused_u, p);  // barrier: the list is complete
-  const int n = static_cast<int>(g_sm.list_n);
+  __syncthreads();                                // the list is complete
   int32_t* oi = out_idx + static_cast<int64_t>(row) * k;
   float* ov = out_val ? out_val + static_cast<int64_t>(row) * k : nullptr;
-  const uint32_t kmin = ord_key(smin + 0.0f), kmax = ord_key(smax + 0.0f);
-  if (n <= 4 * kSelThreads) {
-    select_list<4>(lv, li, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
-  } else if (n <= 8 * kSelThreads) {
-    select_list<8>(lv, li, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
-  } else if (n <= kListCap) {
-    select_list<12>(lv, li, n, kmin, kmax, k, W, WPT, bm, p, oi, ov);
+  if (n <= kListCap) {
+    const bool have_range = rb.x > kNegInf;       // survivors lie in [bound, largest report]
+    select_sorted_list(lp, n, rb.x, rb.y, have_range, k, p, oi, ov);
   } else {
     Emitter em;
     em.oi = oi;
@@ -957,13 +912,13 @@ size_t topk_bounded_workspace_bytes(int rows, int N_max) {
 
 hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
-                       const float* chunk_thr, int n_chunks, int32_t* idx, float* out_scores,
+                       const float2* chunk_rep, int n_chunks, int32_t* idx, float* out_scores,
                        void* ws, hipStream_t s) {
   const int rows = B * Tq;
-  if (chunk_thr != nullptr && topk_bounded_ok(N_max)) {
+  if (chunk_rep != nullptr && topk_bounded_ok(N_max)) {
     if (!use_regions(rows, N_max)) {
       hipLaunchKernelGGL(topk_bounded_kernel<false>, dim3(rows), dim3(kSelThreads), 0, s, scores,
-                         s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, 0, nullptr,
+                         s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, 0, nullptr,
                          nullptr, nullptr, idx, out_scores);
       return hipGetLastError();
     }
@@ -974,11 +929,11 @@ hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
     int32_t* rc = ri + slots;
     hipLaunchKernelGGL(topk_filter_kernel, dim3((N_max + kFiltSeg - 1) / kFiltSeg, rows),
                        dim3(kSegThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
-                       chunk_thr, n_chunks, nreg, rv, ri, rc);
+                       chunk_rep, n_chunks, nreg, rv, ri, rc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_bounded_kernel<true>, dim3(rows), dim3(kSelThreads), 0, s, scores,
-                       s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_thr, n_chunks, nreg, rv, ri,
+                       s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, nreg, rv, ri,
                        rc, idx, out_scores);
     return hipGetLastError();
   }

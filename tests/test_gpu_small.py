@@ -206,6 +206,60 @@ def test_tuned_prefill_scores_ragged():
             check_topk(I[b, t], s_ref, V, k)
 
 
+def test_bounded_selection_ties_and_degenerate():
+    """The bounded selection (chunk bounds + survivor list) on inputs far from
+    Gaussian, where ties decide: all scores equal (more survivors than the
+    list holds, and fewer), two distinct key rows (one value fills the
+    threshold bin), integer-valued inputs (exact scores with many ties).
+    The scores are exact or their distinct values far apart, so the set must
+    equal the oracle's exactly (ties to the lower index)."""
+    m = 4
+    bf = torch.bfloat16
+
+    def run(qi, wi, ki, ne, k):
+        B, N = ki.shape[0], ki.shape[1]
+        pos = torch.full((B, 1), 4 * N + 3, dtype=torch.int32, device=DEV)
+        n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+        idx = csa.index_topk(qi, wi, ki, pos, n_ent, m, k)
+        torch.cuda.synchronize()
+        I, QI, KI, W = np64(idx), np64(qi), np64(ki), np64(wi)
+        for b in range(B):
+            V = oracle.visible_count(4 * N + 3, m, ne[b])
+            s = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
+            ref = oracle.topk_select(s, V, k)
+            assert np.array_equal(I[b, 0], ref), (b, V, k, np.nonzero(I[b, 0] != ref)[0][:8])
+
+    _say("bounded selection: all scores equal")
+    N = 32768
+    qi = _randn((2, 1, 64, 128), 1 / math.sqrt(128), bf, 61)
+    ki = _randn((2, N, 128), 1 / math.sqrt(128), bf, 62)
+    run(qi, torch.zeros((2, 1, 64), dtype=torch.float32, device=DEV), ki, [N, 12000], 1024)
+
+    _say("bounded selection: two distinct key rows")
+    N = 16384
+    qi = _randn((2, 1, 64, 128), 1 / math.sqrt(128), bf, 63)
+    wi = _randn((2, 1, 64), 1 / 8, torch.float32, 64).abs()
+    kv = _randn((2, 2, 128), 1 / math.sqrt(128), bf, 65)
+    QI, W, KV = np64(qi), np64(wi), np64(kv)
+    rng = np.random.default_rng(66)
+    ki = torch.empty((2, N, 128), dtype=bf, device=DEV)
+    for b in range(2):
+        s2 = [float(W[b, 0] @ np.maximum(QI[b, 0] @ KV[b, j], 0.0)) for j in (0, 1)]
+        assert abs(s2[0] - s2[1]) > 1e-3 * max(abs(s2[0]), abs(s2[1]))
+        hi_j = int(s2[1] > s2[0])
+        pick = np.where(rng.random(N) < 0.05, hi_j, 1 - hi_j)
+        ki[b] = kv[b][torch.from_numpy(pick).to(DEV)]
+    run(qi, wi, ki, [N, N - 5], 1024)
+    run(qi, wi, ki, [N, N - 5], 512)
+
+    _say("bounded selection: integer-valued inputs")
+    N = 32768
+    qi = torch.round(_randn((2, 1, 64, 128), 1.0, torch.float32, 67)).to(bf)
+    ki = torch.round(_randn((2, N, 128), 1.5, torch.float32, 68)).to(bf)
+    wi = torch.full((2, 1, 64), 1 / 64, dtype=torch.float32, device=DEV)
+    run(qi, wi, ki, [N, 30001], 1024)
+
+
 def test_attention_sharp_and_single_entry():
     """Sharp softmax (logit std ~3) where the absolute gates bite, repeated and
     invalid indices, and a single selected entry (output = that value row)."""

@@ -275,12 +275,6 @@ __global__ __launch_bounds__(256, 2) void attend_split_kernel(
   const int nrounds = (ntiles + 1) / 2;
   const int32_t* irow = HCA ? nullptr : idx + static_cast<int64_t>(row) * kk;
 
-  // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
-  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
-  bf16x8_t bq[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) bq[s] = ld_bf16x8(qrow + h * 128 + 16 * s + 8 * g);
-
   const uint16_t* Kb = K + b * kv_sb;
   const uint16_t* Vb = Vc + b * kv_sb;
   f32x16_t o[4] = {};
@@ -308,6 +302,12 @@ __global__ __launch_bounds__(256, 2) void attend_split_kernel(
     CSA_ENTRY(1, ejn);
     load_round(Kb, Vb, kv_sn, e0, t128, ra);
   }
+  // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
+  // (loaded after the first gathers are issued: those wait on the entries)
+  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
+  bf16x8_t bq[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) bq[s] = ld_bf16x8(qrow + h * 128 + 16 * s + 8 * g);
   for (int r = 0; r < nrounds; r += 2) {
     if (r + 1 < nrounds) load_round(Kb, Vb, kv_sn, ejn, t128, rb);
     CSA_ENTRY(r + 2, ejn);
@@ -321,24 +321,26 @@ __global__ __launch_bounds__(256, 2) void attend_split_kernel(
   }
 #undef CSA_ENTRY
 
-  // merge the two key groups of each head half through LDS (reuses the V tiles)
+  // Merge the two key groups of each head half through LDS (reuses the V
+  // tiles): key group 0 finishes d-tiles 0-1 and key group 1 d-tiles 2-3;
+  // each hands the other the half it does not finish, then both store.
   l_run = l_run + __shfl_xor(l_run, 32, 64);
   __syncthreads();
-  lds_f32* xo = (lds_f32*)&g_attn.v[0][0][0];      // [hh][lane][64 + 2]
-  constexpr int kX = 66;
-  if (kg == 1) {
-    lds_f32* dst = xo + (hh * 64 + lane) * kX;
+  lds_f32* xo = (lds_f32*)&g_attn.v[0][0][0];      // [kg][hh][lane][32 + 2]
+  constexpr int kX = 34;
+  {
+    lds_f32* dst = xo + ((kg * 2 + hh) * 64 + lane) * kX;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[16 * dt + i] = o[dt][i];
-    dst[64] = m_run;
-    dst[65] = l_run;
+      for (int i = 0; i < 16; ++i) dst[16 * dd + i] = kg == 0 ? o[2 + dd][i] : o[dd][i];
+    dst[32] = m_run;
+    dst[33] = l_run;
   }
   __syncthreads();
-  if (kg == 0) {
-    const lds_f32* src = xo + (hh * 64 + lane) * kX;
-    const float m1 = src[64], l1 = src[65];
+  {
+    const lds_f32* src = xo + (((1 - kg) * 2 + hh) * 64 + lane) * kX;
+    const float m1 = src[32], l1 = src[33];
     const float M = fmaxf(m_run, m1);
     float a0 = 0.f, a1 = 0.f;
     if (M != kNegInf) {
@@ -346,28 +348,30 @@ __global__ __launch_bounds__(256, 2) void attend_split_kernel(
       a1 = exp2_fast(m1 - M);
     }
     float* pr = part + (static_cast<int64_t>(row) * nsplit + split) * kPartRows * 64;
+    const int dt0 = 2 * kg;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dd = 0; dd < 2; ++dd)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
-        pr[d * 64 + h] = a0 * o[dt][i] + a1 * src[16 * dt + i];
+        const int d = 32 * (dt0 + dd) + 8 * (i >> 2) + 4 * g + (i & 3);
+        const float mine = kg == 0 ? o[dd][i] : o[2 + dd][i];
+        pr[d * 64 + h] = a0 * mine + a1 * src[16 * dd + i];
       }
-    if (g == 0) {
+    if (kg == 0 && g == 0) {
       pr[128 * 64 + h] = M;
       pr[129 * 64 + h] = a0 * l_run + a1 * l1;
     }
   }
 }
 
-// Merge of the split partials.  Grid (rows, 4 dim quarters); thread (h, c)
-// owns output dims 32 y + 8 c .. +7 of head h: every read is a coalesced
+// Merge of the split partials.  Grid (rows, 8 dim blocks); thread (h, c)
+// owns output dims 16 y + 4 c .. +3 of head h: every read is a coalesced
 // 64-float row of a partial.
 __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ part,
                                                              int nsplit, uint16_t* __restrict__ out,
                                                              float* __restrict__ lse) {
   const int row = blockIdx.x, tid = threadIdx.x;
-  const int h = tid & 63, d0 = 32 * blockIdx.y + 8 * (tid >> 6);
+  const int h = tid & 63, d0 = 16 * blockIdx.y + 4 * (tid >> 6);
   const int64_t sstride = static_cast<int64_t>(kPartRows) * 64;
   const float* base = part + static_cast<int64_t>(row) * nsplit * sstride + h;
   // One pass over the splits in groups of eight: every load of a group
@@ -375,17 +379,17 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
   // running maximum rescales what is already summed.
   constexpr int U = 8;
   float M = kNegInf, L = 0.f;
-  float acc[8];
+  float acc[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int i = 0; i < 4; ++i) acc[i] = 0.f;
   for (int s = 0; s < nsplit; s += U) {
-    float v[U][8], ms[U], ls[U];
+    float v[U][4], ms[U], ls[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool ok = s + u < nsplit;
       const float* ps = base + static_cast<int64_t>(ok ? s + u : s) * sstride;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = ps[(d0 + i) * 64];
+      for (int i = 0; i < 4; ++i) v[u][i] = ps[(d0 + i) * 64];
       ms[u] = ok ? ps[128 * 64] : kNegInf;
       ls[u] = ps[129 * 64];
     }
@@ -396,23 +400,21 @@ __global__ __launch_bounds__(256) void attend_combine_kernel(const float* __rest
     const float a = M == kNegInf ? 0.f : exp2_fast(M - mg);
     L *= a;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= a;
+    for (int i = 0; i < 4; ++i) acc[i] *= a;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const float wu = ms[u] == kNegInf ? 0.f : exp2_fast(ms[u] - mg);
       L = fmaf(wu, ls[u], L);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
+      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
     }
     M = mg;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint4 v;
+  uint2 v;
   v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  v.z = pack_bf16x2(acc[4] * inv, acc[5] * inv);
-  v.w = pack_bf16x2(acc[6] * inv, acc[7] * inv);
-  st16(out + (static_cast<int64_t>(row) * 64 + h) * 128 + d0, v);
+  *reinterpret_cast<uint2*>(out + (static_cast<int64_t>(row) * 64 + h) * 128 + d0) = v;
   if (lse != nullptr && blockIdx.y == 0 && tid < 64)
     lse[static_cast<int64_t>(row) * 64 + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
 }
@@ -482,7 +484,7 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
                        a.n_entries, a.Tq, a.N_max, a.m, scale_log2, sl, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.B * a.Tq, 4), dim3(256), 0, s, part, nsplit,
+  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.B * a.Tq, 8), dim3(256), 0, s, part, nsplit,
                      static_cast<uint16_t*>(a.out), a.lse);
   return hipGetLastError();
 }

@@ -260,6 +260,56 @@ def test_bounded_selection_ties_and_degenerate():
     run(qi, wi, ki, [N, 30001], 1024)
 
 
+def test_step_graph_replay_matches_eager():
+    """The decode step (index_topk + attend, and hca_attend) captured in a HIP
+    graph with caller-owned workspaces: every replay, with eager work and
+    synchronisations between replays, reproduces the eager results bitwise."""
+    B, N, k, m = 4, 8192 + 96, 1024, 4
+    bf = torch.bfloat16
+    _say("graph capture of the decode step")
+    q = _randn((B, 1, 64, 128), 1 / math.sqrt(128), bf, 71)
+    kc = _randn((B, N, 128), 1 / math.sqrt(128), bf, 72)
+    vc = _randn((B, N, 128), 1 / math.sqrt(128), bf, 73)
+    qi = _randn((B, 1, 64, 128), 1 / math.sqrt(128), bf, 74)
+    ki = _randn((B, N, 128), 1 / math.sqrt(128), bf, 75)
+    wi = _randn((B, 1, 64), 1 / 8, torch.float32, 76)
+    pos = torch.tensor([[4 * N], [4 * N - 9], [4000], [4 * 5000 + 1]], dtype=torch.int32, device=DEV)
+    ne = torch.tensor([N, N, N, 6000], dtype=torch.int32, device=DEV)
+    u8 = torch.uint8
+    ws_t = torch.empty(csa.index_topk_workspace_bytes(B, 1, N, k), dtype=u8, device=DEV)
+    ws_a = torch.empty(csa.attend_workspace_bytes(bf, B, 1, 64, 128, k), dtype=u8, device=DEV)
+    ws_h = torch.empty(csa.hca_workspace_bytes(bf, B, 1, 64, 128, N), dtype=u8, device=DEV)
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
+    o, oh = torch.empty_like(q), torch.empty_like(q)
+
+    def step():
+        csa.index_topk(qi, wi, ki, pos, ne, m, k, workspace=ws_t, out=idx)
+        csa.attend(q, kc, vc, idx, ne, workspace=ws_a, out=o)
+        csa.hca_attend(q, kc, vc, pos, ne, m, workspace=ws_h, out=oh)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (idx.clone(), o.clone(), oh.clone())
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        idx.fill_(-7)
+        o.zero_()
+        oh.zero_()
+        ws_t.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref[0]) and torch.equal(o, ref[1]) and torch.equal(oh, ref[2]), rep
+
+
 def test_attention_sharp_and_single_entry():
     """Sharp softmax (logit std ~3) where the absolute gates bite, repeated and
     invalid indices, and a single selected entry (output = that value row)."""

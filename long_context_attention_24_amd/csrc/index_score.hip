@@ -119,7 +119,7 @@ static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 // Straight-line code over the wave's 8 tiles of 32 keys with a 3-deep ring of
 // registers: the loads of tile t+2 are issued before the MFMAs of tile t and
 // no register is copied, so two tiles (16 KB per wave) stay in flight behind
-// the math.  Loads are coalesced and non-temporal (instruction i of a tile
+// the math; the epilogue of tile t-1 runs while the MFMAs of tile t do.  Loads are coalesced and non-temporal (instruction i of a tile
 // reads key rows 4i .. 4i+3 whole, 16 lanes per row); each tile then passes
 // through a wave-private LDS buffer to reach the MFMA B-operand layout (lane
 // (j, g) holds dims 16s + 8g .. +7 of key j).  Rows past the visible range are
@@ -127,17 +127,32 @@ static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 // output.
 constexpr int kKeyPitch = 136;                    // bf16 per key row in LDS (256 B + 16 B)
 
-__global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
+__global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
     int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
   __shared__ __attribute__((aligned(16))) uint16_t key_lds[kWavesPerWg][32 * kKeyPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[64 * kKeyPitch];
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 31, g = lane >> 5;
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int chunk = blockIdx.x * kWavesPerWg + wave;
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  {
+    // q_I rows (heads) of this query into LDS, read back per tile as the A
+    // operand (the registers hold the accumulators of two tiles instead)
+    const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int c = static_cast<int>(threadIdx.x) + 256 * i;     // 16-byte chunk: head c / 16
+      *(lds_u32x4*)((lds_u16*)q_lds + (c >> 4) * kKeyPitch + 8 * (c & 15)) =
+          *reinterpret_cast<const u32x4_t*>(qrow + 8 * c);
+    }
+  }
+  __syncthreads();                                // the only barrier: early exits follow
   const int key0 = chunk * kKeysPerWave;
   if (key0 >= N_max) return;
   const int key_end = min(key0 + kKeysPerWave, N_max);
@@ -162,18 +177,8 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
   };
   load_tile(0, kt[0]);
   load_tile(1, kt[1]);
-  typedef __attribute__((address_space(3))) uint16_t lds_u16;
-  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   lds_u16* kl = (lds_u16*)&key_lds[wave][0];
-
-  // A operand: q_I rows (heads) of this query; two 32-head tiles x 8 k-steps
-  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
-  bf16x8_t a0[8], a1[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    a0[s] = ld_bf16x8(qrow + jl * 128 + 16 * s + 8 * g);
-    a1[s] = ld_bf16x8(qrow + (32 + jl) * 128 + 16 * s + 8 * g);
-  }
+  const lds_u16* ql = (const lds_u16*)q_lds + jl * kKeyPitch + 8 * g;
   // head weights in accumulator-row order: row = 8*(r/4) + 4*g + r%4
   const float* wrow = w + static_cast<int64_t>(row) * 64;
   float w0[16], w1[16];
@@ -185,8 +190,26 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
   }
 
   float sc[kTilesPerWave];
+  // epilogue of tile t from its accumulators: sum_h w[h] ReLU(s_h), then the
+  // two lane halves (32 heads each) add up
+  auto epilogue = [&](int t, const f32x16_t& c0, const f32x16_t& c1) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum = fmaf(w0[r], relu_f32(c0[r]), sum);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], relu_f32(c1[r]), sum);
+    const float other = __shfl_xor(sum, 32, 64);
+    const float tot = sum + other;     // commutative: both halves get the same bits
+    const int j = key0 + 32 * t + jl;
+    const bool ok = j < vis_end;
+    if (g == 0 && ok) srow[j] = tot;
+    sc[t] = ok ? tot : kNegInf;
+  };
+  // Iteration t: loads of tile t+2, tile t through LDS into the MFMAs, and
+  // the epilogue of tile t-1 while those MFMAs run (two accumulator sets).
   // sched_barrier(0) keeps the scheduler from sinking the prefetch loads
   // below the MFMAs of the current tile (it would, to shorten live ranges).
+  f32x16_t acc[2][2];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
@@ -202,25 +225,24 @@ __global__ __launch_bounds__(256) void score_bf16_h64d128_kernel(
       const u32x4_t x = *(const lds_u32x4*)(kl + jl * kKeyPitch + 16 * s + 8 * g);
       __builtin_memcpy(&cur[s], &x, 16);
     }
-    f32x16_t c0 = {}, c1 = {};
+    f32x16_t (&c)[2] = acc[t & 1];
+    c[0] = f32x16_t{};
+    c[1] = f32x16_t{};
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);     // re-read the A operands from LDS
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[s], cur[s], c0, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[s], cur[s], c1, 0, 0, 0);
+      bf16x8_t a0, a1;
+      const u32x4_t x0 = *(const lds_u32x4*)(ql + 16 * s);
+      const u32x4_t x1 = *(const lds_u32x4*)(ql + 32 * kKeyPitch + 16 * s);
+      __builtin_memcpy(&a0, &x0, 16);
+      __builtin_memcpy(&a1, &x1, 16);
+      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cur[s], c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cur[s], c[1], 0, 0, 0);
     }
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum = fmaf(w0[r], relu_f32(c0[r]), sum);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], relu_f32(c1[r]), sum);
-    const float other = __shfl_xor(sum, 32, 64);
-    const float tot = sum + other;     // commutative: both halves get the same bits
-    const int j = key0 + 32 * t + jl;
-    const bool ok = j < vis_end;
-    if (g == 0 && ok) srow[j] = tot;
-    sc[t] = ok ? tot : kNegInf;
+    if (t > 0) epilogue(t - 1, acc[(t - 1) & 1][0], acc[(t - 1) & 1][1]);
     __builtin_amdgcn_sched_barrier(0);
   }
+  epilogue(kTilesPerWave - 1, acc[(kTilesPerWave - 1) & 1][0], acc[(kTilesPerWave - 1) & 1][1]);
   const int thr_c = bound_c_row(V, bound_k);
   if (chunk_rep != nullptr && thr_c > 0) {
     const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, thr_c);

@@ -73,6 +73,15 @@ def algorithmic_bytes(w):
     return step, score_kernel
 
 
+def stage_bytes(w):
+    """Algorithmic bytes of the selection and attention stages of one step
+    (the score workspace is counted where it is read)."""
+    B, N, H, D, k = w.B, w.N, w.H, w.D, w.k
+    select = B * N * 4 + B * k * 4                 # scores read, indices written
+    attend = B * k * D * 2 * 2 + B * H * D * 2 * 2 + B * k * 4   # K/V gathers, q, o, indices
+    return select, attend
+
+
 def _calibrate_sleep() -> float:
     """Spin-kernel cycles per millisecond on this GPU."""
     torch.cuda._sleep(1000)
@@ -308,6 +317,20 @@ def other_workload(args):
     print(json.dumps(base))
 
 
+def _stages(w, score_ms, index_topk_ms, attend_ms, score_bytes):
+    """Per-stage time, algorithmic bytes and HBM fraction (selection = the
+    index_topk call minus the score kernel, so it includes one launch gap)."""
+    sel_b, att_b = stage_bytes(w)
+    out = {}
+    for name, ms, b in (("score", score_ms, score_bytes),
+                        ("selection", index_topk_ms - score_ms, sel_b),
+                        ("attention", attend_ms, att_b)):
+        gbs = b / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        out[name] = {"ms": round(ms, 5), "algorithmic_bytes": b, "gbs": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -443,6 +466,7 @@ def main():
         "call_ms": {"index_score": round(score_ms, 5),
                     "index_topk (score + selection)": round(index_topk_ms, 5),
                     "attend (split + combine)": round(attend_ms, 5)},
+        "stages": _stages(w, score_ms, index_topk_ms, attend_ms, score_bytes),
         "roofline": {"kernel": SCORE_KERNEL, "bound": "hbm",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),

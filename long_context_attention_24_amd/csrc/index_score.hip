@@ -422,8 +422,16 @@ __device__ __forceinline__ uint64_t fp4x8_to_fp8x8(uint32_t c) {
 // 16x16x32 fp8 MFMA: K = 32 is exactly one scale block, so each MFMA gives
 // the exact per-block partial dot product; block scales are applied in fp32.
 // A operand lane l: head row l%16, dims 8*(l/16) .. +7 of the block.  A wave
-// covers 256 keys as 16 tiles of 16 keys, unrolled, loads two tiles ahead.
+// covers 256 keys as 16 tiles of 16 keys.  Keys arrive in units of 64 (4 KB
+// of codes, 1 KB of scales) with coalesced 16-byte loads, two units ahead,
+// and pass through a wave-private LDS buffer whose 80-byte row pitch makes
+// the MFMA-layout reads (lane (key n, group g): bytes 16 b + 4 g of row n)
+// bank-conflict free.
 constexpr int kFp4Tiles = kKeysPerWave / 16;
+constexpr int kF4Unit = 64;                        // keys per load unit
+constexpr int kF4Units = kKeysPerWave / kF4Unit;
+constexpr int kF4Pitch = 80;                       // LDS bytes per key row of codes
+constexpr int kF4WaveLds = kF4Unit * kF4Pitch + kF4Unit * 16;
 
 __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -431,6 +439,7 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     int64_t ks_sb, int64_t ks_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
     int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
+  __shared__ __attribute__((aligned(16))) uint8_t f4_lds[kWavesPerWg][kF4WaveLds];
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -448,19 +457,24 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     return;
   }
 
-  const uint8_t* kb = k + b * k_sb + 4 * g;
+  // unit u: lane L loads codes bytes 16 (L % 4) .. +15 of keys 16 i + L / 4
+  // (i < 4) and the four scales of key L; keys past the visible range are
+  // clamped to the last visible one (in bounds, masked on output)
+  const uint8_t* kb = k + b * k_sb + 16 * (lane & 3);
   const float* ksb = k_scale + b * ks_sb;
-  uint32_t kc[3][4];
-  float4 ks[3];
-  auto load_tile = [&](int t, uint32_t (&c)[4], float4& sc4) {
-    const int j = min(key0 + 16 * t + nl, vis_end - 1);
-    const uint8_t* kr = kb + static_cast<int64_t>(j) * k_sn;
+  u32x4_t kc[3][4];
+  u32x4_t ks[3];
+  auto load_unit = [&](int u, u32x4_t (&c)[4], u32x4_t& sc4) {
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) c[blk] = *reinterpret_cast<const uint32_t*>(kr + 16 * blk);
-    sc4 = *reinterpret_cast<const float4*>(ksb + static_cast<int64_t>(j) * ks_sn);
+    for (int i = 0; i < 4; ++i) {
+      const int j = min(key0 + kF4Unit * u + 16 * i + (lane >> 2), vis_end - 1);
+      c[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
+    }
+    const int js = min(key0 + kF4Unit * u + lane, vis_end - 1);
+    sc4 = ld16_stream(ksb + static_cast<int64_t>(js) * ks_sn);
   };
-  load_tile(0, kc[0], ks[0]);
-  load_tile(1, kc[1], ks[1]);
+  load_unit(0, kc[0], ks[0]);
+  load_unit(1, kc[1], ks[1]);
 
   // q: [64 heads][64 bytes] codes, [64][4] scales
   const uint8_t* qrow = q + static_cast<int64_t>(row) * 64 * 64;
@@ -488,42 +502,61 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
       for (int blk = 0; blk < 4; ++blk) sq[mt][r][blk] = qsrow[h * 4 + blk];
     }
 
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
+  typedef __attribute__((address_space(3))) uint32_t lds_u32;
+  lds_u8* cl = (lds_u8*)&f4_lds[wave][0];
+  lds_u8* sl = cl + kF4Unit * kF4Pitch;
+
   float scv[kFp4Tiles];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < kFp4Tiles; ++t) {
-    if (t + 2 < kFp4Tiles) load_tile(t + 2, kc[(t + 2) % 3], ks[(t + 2) % 3]);
+  for (int u = 0; u < kF4Units; ++u) {
+    if (u + 2 < kF4Units) load_unit(u + 2, kc[(u + 2) % 3], ks[(u + 2) % 3]);
     __builtin_amdgcn_sched_barrier(0);
-    const float4 sk = ks[t % 3];
-    const float skv[4] = {sk.x, sk.y, sk.z, sk.w};
-    uint64_t bop[4];
+    // unit u -> LDS (the previous unit's reads precede these writes in the
+    // wave's LDS queue)
 #pragma unroll
-    for (int blk = 0; blk < 4; ++blk) bop[blk] = fp4x8_to_fp8x8(kc[t % 3][blk]);
-    float sum = 0.f;
+    for (int i = 0; i < 4; ++i)
+      *(lds_u32x4*)(cl + (16 * i + (lane >> 2)) * kF4Pitch + 16 * (lane & 3)) = kc[u % 3][i];
+    *(lds_u32x4*)(sl + 16 * lane) = ks[u % 3];
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      f32x4_t p[4];
+    for (int tt = 0; tt < kF4Unit / 16; ++tt) {
+      const int t = (kF4Unit / 16) * u + tt;
+      const int kr = 16 * tt + nl;                 // key row within the unit
+      const u32x4_t skr = *(const lds_u32x4*)(sl + 16 * kr);
+      const float skv[4] = {__uint_as_float(skr[0]), __uint_as_float(skr[1]),
+                            __uint_as_float(skr[2]), __uint_as_float(skr[3])};
+      uint64_t bop[4];
 #pragma unroll
-      for (int blk = 0; blk < 4; ++blk) {
-        const f32x4_t z = {};
-        p[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-            static_cast<long>(a[mt][blk]), static_cast<long>(bop[blk]), z, 0, 0, 0);
+      for (int blk = 0; blk < 4; ++blk)
+        bop[blk] = fp4x8_to_fp8x8(*(const lds_u32*)(cl + kr * kF4Pitch + 16 * blk + 4 * g));
+      float sum = 0.f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        f32x4_t p[4];
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) {
+          const f32x4_t z = {};
+          p[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
+              static_cast<long>(a[mt][blk]), static_cast<long>(bop[blk]), z, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float tv = 0.f;
+#pragma unroll
+          for (int blk = 0; blk < 4; ++blk) tv = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], tv);
+          sum = fmaf(wv[mt][r], relu_f32(tv), sum);
+        }
       }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float tv = 0.f;
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) tv = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], tv);
-        sum = fmaf(wv[mt][r], relu_f32(tv), sum);
-      }
+      // heads are spread over the four 16-lane groups of the key's column
+      sum = sum + __shfl_xor(sum, 16, 64);
+      sum = sum + __shfl_xor(sum, 32, 64);
+      const int jj = key0 + 16 * t + nl;
+      const bool ok = jj < vis_end;
+      if (g == 0 && ok) srow[jj] = sum;
+      scv[t] = ok ? sum : kNegInf;
     }
-    // heads are spread over the four 16-lane groups of the key's column
-    sum = sum + __shfl_xor(sum, 16, 64);
-    sum = sum + __shfl_xor(sum, 32, 64);
-    const int jj = key0 + 16 * t + nl;
-    const bool ok = jj < vis_end;
-    if (g == 0 && ok) srow[jj] = sum;
-    scv[t] = ok ? sum : kNegInf;
     __builtin_amdgcn_sched_barrier(0);
   }
   const int thr_c = bound_c_row(V, bound_k);

@@ -206,6 +206,38 @@ def test_tuned_prefill_scores_ragged():
             check_topk(I[b, t], s_ref, V, k)
 
 
+def test_fp4_scores_ragged():
+    """FP4 indexer (E2M1 codes, one fp32 scale per 32 elements) on ragged
+    sizes: a partial last load unit and chunk, visible counts inside the first
+    unit, a partially valid cache.  Scores against the oracle fed the same
+    quantised inputs (fp32 accumulation bound), then the selection."""
+    from csa_synth.generate import fp4_quantize
+    B, N_max, m, k = 3, 1000 + 37, 4, 300
+    _say("fp4 ragged scores")
+    qi = _randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.float32, 81)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.float32, 82)
+    wi = _randn((B, 1, 64), 1 / 8, torch.float32, 83)
+    qc, qs = (t.to(DEV) for t in fp4_quantize(qi))
+    kc, ks = (t.to(DEV) for t in fp4_quantize(ki))
+    pos = [4 * N_max + 3, 4 * 50 + 1, 4 * 777]
+    q_pos = torch.tensor([[p] for p in pos], dtype=torch.int32, device=DEV)
+    ne = [N_max, 900, 1001]
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qc, wi, kc, q_pos, n_ent, m, q_scale=qs, k_scale=ks)
+    idx = csa.index_topk(qc, wi, kc, q_pos, n_ent, m, k, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    S, I, W = np64(scores), np64(idx), np64(wi)
+    QI = oracle.fp4_dequantize(qc.cpu().numpy(), qs.cpu().numpy())
+    KI = oracle.fp4_dequantize(kc.cpu().numpy(), ks.cpu().numpy())
+    for b in range(B):
+        V = oracle.visible_count(pos[b], m, ne[b])
+        s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
+        assert np.all(np.isneginf(S[b, 0, V:])), (b, V)
+        bound = score_bound(QI[b, 0], W[b, 0], KI[b, :V], 128, 64)
+        assert np.all(np.abs(S[b, 0, :V] - s_ref[:V]) <= bound), (b, V)
+        check_topk(I[b, 0], s_ref, V, k)
+
+
 def test_bounded_selection_ties_and_degenerate():
     """The bounded selection (chunk bounds + survivor list) on inputs far from
     Gaussian, where ties decide: all scores equal (more survivors than the

@@ -400,38 +400,20 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
 }
 
 // ---------------------------------------------------------------- FP4, 64 heads x 128
-// E2M1 magnitude (3 bits) -> E4M3 byte: 0, .5, 1, 1.5, 2, 3, 4, 6 are
-// 0x00 0x30 0x38 0x3C 0x40 0x44 0x48 0x4C; the sign bit moves from bit 3 of
-// the nibble to bit 7 of the byte.  Exact: E4M3 has more exponent range and
-// mantissa bits than E2M1.
-constexpr uint32_t kE4m3Lo = 0x3C383000u;   // bytes for magnitudes 0..3
-constexpr uint32_t kE4m3Hi = 0x4C484440u;   // bytes for magnitudes 4..7
-
-// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
-// -> eight E4M3 bytes.  Order: even elements in the low word, odd elements in
-// the high word.  A and B use the same order, so dot products are unchanged.
-__device__ __forceinline__ uint64_t fp4x8_to_fp8x8(uint32_t c) {
-  const uint32_t ev = c & 0x0F0F0F0Fu, od = (c >> 4) & 0x0F0F0F0Fu;
-  const uint32_t e8 = __builtin_amdgcn_perm(kE4m3Hi, kE4m3Lo, ev & 0x07070707u) |
-                      ((ev & 0x08080808u) << 4);
-  const uint32_t o8 = __builtin_amdgcn_perm(kE4m3Hi, kE4m3Lo, od & 0x07070707u) |
-                      ((od & 0x08080808u) << 4);
-  return (static_cast<uint64_t>(o8) << 32) | e8;
-}
-
-// 16x16x32 fp8 MFMA: K = 32 is exactly one scale block, so each MFMA gives
-// the exact per-block partial dot product; block scales are applied in fp32.
-// A operand lane l: head row l%16, dims 8*(l/16) .. +7 of the block.  A wave
-// covers 256 keys as 16 tiles of 16 keys.  Keys arrive in units of 64 (4 KB
-// of codes, 1 KB of scales) with coalesced 16-byte loads, two units ahead,
-// and pass through a wave-private LDS buffer whose 80-byte row pitch makes
-// the MFMA-layout reads (lane (key n, group g): bytes 16 b + 4 g of row n)
-// bank-conflict free.
+// gfx950's block-scaled MFMA (16x16x128, f8f6f4 with both operands E2M1)
+// multiplies the E2M1 codes directly: lane l supplies row / column l % 16 and
+// the 32 elements k = 32 (l / 16) .. +31, i.e. scale block l / 16, as 16 bytes
+// in memory order (element 2i in the low nibble of byte i).  Its E8M0 block
+// scales hold only powers of two, so they stay at 1 and the fp32 scales of
+// the pages' recipe are applied in the epilogue: each block's partial dot
+// product comes from an MFMA whose B operand keeps only that block's lanes
+// (the others zero), so every partial is exact (products of E2M1 values are
+// multiples of 1/4 below 36, 32 of them summed in fp32).  A wave covers 256
+// keys as 16 tiles of 16 keys; lane (key n, block g) loads its 16 bytes of
+// codes directly in the operand layout (a tile's 1 KB of codes is one
+// coalesced 16-byte load per lane) and its key's four scales, two tiles ahead.
+typedef int v8i32_t __attribute__((ext_vector_type(8)));
 constexpr int kFp4Tiles = kKeysPerWave / 16;
-constexpr int kF4Unit = 64;                        // keys per load unit
-constexpr int kF4Units = kKeysPerWave / kF4Unit;
-constexpr int kF4Pitch = 80;                       // LDS bytes per key row of codes
-constexpr int kF4WaveLds = kF4Unit * kF4Pitch + kF4Unit * 16;
 
 __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
@@ -439,7 +421,6 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     int64_t ks_sb, int64_t ks_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
     int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
-  __shared__ __attribute__((aligned(16))) uint8_t f4_lds[kWavesPerWg][kF4WaveLds];
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
@@ -457,37 +438,29 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     return;
   }
 
-  // unit u: lane L loads codes bytes 16 (L % 4) .. +15 of keys 16 i + L / 4
-  // (i < 4) and the four scales of key L; keys past the visible range are
-  // clamped to the last visible one (in bounds, masked on output)
-  const uint8_t* kb = k + b * k_sb + 16 * (lane & 3);
+  // keys past the visible range are clamped to the last visible one (in
+  // bounds, masked on output)
+  const uint8_t* kb = k + b * k_sb + 16 * g;
   const float* ksb = k_scale + b * ks_sb;
-  u32x4_t kc[3][4];
-  u32x4_t ks[3];
-  auto load_unit = [&](int u, u32x4_t (&c)[4], u32x4_t& sc4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = min(key0 + kF4Unit * u + 16 * i + (lane >> 2), vis_end - 1);
-      c[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
-    }
-    const int js = min(key0 + kF4Unit * u + lane, vis_end - 1);
-    sc4 = ld16_stream(ksb + static_cast<int64_t>(js) * ks_sn);
+  u32x4_t kc[3], ks[3];
+  auto load_tile = [&](int t, u32x4_t& c, u32x4_t& sc4) {
+    const int j = min(key0 + 16 * t + nl, vis_end - 1);
+    c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
+    sc4 = ld16_stream(ksb + static_cast<int64_t>(j) * ks_sn);
   };
-  load_unit(0, kc[0], ks[0]);
-  load_unit(1, kc[1], ks[1]);
+  load_tile(0, kc[0], ks[0]);
+  load_tile(1, kc[1], ks[1]);
 
-  // q: [64 heads][64 bytes] codes, [64][4] scales
+  // A operand per head tile mt: head 16 mt + n, block g (16 bytes of codes)
   const uint8_t* qrow = q + static_cast<int64_t>(row) * 64 * 64;
   const float* qsrow = q_scale + static_cast<int64_t>(row) * 64 * 4;
-  uint64_t a[4][4];   // [head tile][block]
+  v8i32_t qa[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int blk = 0; blk < 4; ++blk) {
-      const uint32_t c =
-          *reinterpret_cast<const uint32_t*>(qrow + (16 * mt + nl) * 64 + 16 * blk + 4 * g);
-      a[mt][blk] = fp4x8_to_fp8x8(c);
-    }
+  for (int mt = 0; mt < 4; ++mt) {
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(qrow + (16 * mt + nl) * 64 + 16 * g);
+    qa[mt] = v8i32_t{static_cast<int>(c[0]), static_cast<int>(c[1]), static_cast<int>(c[2]),
+                     static_cast<int>(c[3]), 0, 0, 0, 0};
+  }
   // accumulator rows: head = 16*mt + 4*g + r
   float sq[4][4][4];   // [mt][r][blk]
   float wv[4][4];
@@ -502,61 +475,47 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
       for (int blk = 0; blk < 4; ++blk) sq[mt][r][blk] = qsrow[h * 4 + blk];
     }
 
-  typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  typedef __attribute__((address_space(3))) uint32_t lds_u32;
-  lds_u8* cl = (lds_u8*)&f4_lds[wave][0];
-  lds_u8* sl = cl + kF4Unit * kF4Pitch;
-
   float scv[kFp4Tiles];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < kF4Units; ++u) {
-    if (u + 2 < kF4Units) load_unit(u + 2, kc[(u + 2) % 3], ks[(u + 2) % 3]);
+  for (int t = 0; t < kFp4Tiles; ++t) {
+    if (t + 2 < kFp4Tiles) load_tile(t + 2, kc[(t + 2) % 3], ks[(t + 2) % 3]);
     __builtin_amdgcn_sched_barrier(0);
-    // unit u -> LDS (the previous unit's reads precede these writes in the
-    // wave's LDS queue)
+    const u32x4_t c = kc[t % 3];
+    const u32x4_t skr = ks[t % 3];
+    const float skv[4] = {__uint_as_float(skr[0]), __uint_as_float(skr[1]),
+                          __uint_as_float(skr[2]), __uint_as_float(skr[3])};
+    f32x4_t p[4][4];     // [mt][blk]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *(lds_u32x4*)(cl + (16 * i + (lane >> 2)) * kF4Pitch + 16 * (lane & 3)) = kc[u % 3][i];
-    *(lds_u32x4*)(sl + 16 * lane) = ks[u % 3];
-#pragma unroll
-    for (int tt = 0; tt < kF4Unit / 16; ++tt) {
-      const int t = (kF4Unit / 16) * u + tt;
-      const int kr = 16 * tt + nl;                 // key row within the unit
-      const u32x4_t skr = *(const lds_u32x4*)(sl + 16 * kr);
-      const float skv[4] = {__uint_as_float(skr[0]), __uint_as_float(skr[1]),
-                            __uint_as_float(skr[2]), __uint_as_float(skr[3])};
-      uint64_t bop[4];
-#pragma unroll
-      for (int blk = 0; blk < 4; ++blk)
-        bop[blk] = fp4x8_to_fp8x8(*(const lds_u32*)(cl + kr * kF4Pitch + 16 * blk + 4 * g));
-      float sum = 0.f;
+    for (int blk = 0; blk < 4; ++blk) {
+      const bool mine = g == blk;
+      const v8i32_t bm = {mine ? static_cast<int>(c[0]) : 0, mine ? static_cast<int>(c[1]) : 0,
+                          mine ? static_cast<int>(c[2]) : 0, mine ? static_cast<int>(c[3]) : 0,
+                          0, 0, 0, 0};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        f32x4_t p[4];
-#pragma unroll
-        for (int blk = 0; blk < 4; ++blk) {
-          const f32x4_t z = {};
-          p[blk] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-              static_cast<long>(a[mt][blk]), static_cast<long>(bop[blk]), z, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float tv = 0.f;
-#pragma unroll
-          for (int blk = 0; blk < 4; ++blk) tv = fmaf(sq[mt][r][blk] * skv[blk], p[blk][r], tv);
-          sum = fmaf(wv[mt][r], relu_f32(tv), sum);
-        }
+        const f32x4_t z = {};
+        p[mt][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], bm, z, 4, 4, 0, 127,
+                                                                        0, 127);
       }
-      // heads are spread over the four 16-lane groups of the key's column
-      sum = sum + __shfl_xor(sum, 16, 64);
-      sum = sum + __shfl_xor(sum, 32, 64);
-      const int jj = key0 + 16 * t + nl;
-      const bool ok = jj < vis_end;
-      if (g == 0 && ok) srow[jj] = sum;
-      scv[t] = ok ? sum : kNegInf;
     }
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float tv = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) tv = fmaf(sq[mt][r][blk] * skv[blk], p[mt][blk][r], tv);
+        sum = fmaf(wv[mt][r], relu_f32(tv), sum);
+      }
+    // heads are spread over the four 16-lane groups of the key's column
+    sum = sum + __shfl_xor(sum, 16, 64);
+    sum = sum + __shfl_xor(sum, 32, 64);
+    const int jj = key0 + 16 * t + nl;
+    const bool ok = jj < vis_end;
+    if (g == 0 && ok) srow[jj] = sum;
+    scv[t] = ok ? sum : kNegInf;
     __builtin_amdgcn_sched_barrier(0);
   }
   const int thr_c = bound_c_row(V, bound_k);

@@ -26,6 +26,9 @@ COMMON_FLAGS = [
     "-I", INCLUDE, "-I", CSRC,
     # keep the compiler from emitting packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the epilogues read them with plain
+    # VALU operands instead of one v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
 ]
 

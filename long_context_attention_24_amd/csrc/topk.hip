@@ -443,7 +443,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 // directly (block_select, slow but exact).
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
-static_assert(kBins == 2 * kSelThreads, "two bins per thread");
+static_assert(kBins % kSelThreads == 0, "whole bins per thread");
 constexpr int kMaxBoundedN = 262144;
 constexpr int kListCap = 16 * kSelThreads;        // survivors held in LDS (< 65536: packed scans)
 constexpr int kBrute = 256;                       // bin size finished by pairwise ranks
@@ -471,11 +471,13 @@ __device__ __forceinline__ float lval(const lds_u32x2* lp, int j) { return __uin
 //   entries equal to T are taken lowest index first.
 // Entry: the histogram is zero, g_sm.cand_n is zero and a barrier separates
 // the list writes from this call.
+template <int NT>
 __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, float lo, float hi,
                                                    bool have_range, int k, int& p,
                                                    int32_t* __restrict__ oi,
                                                    float* __restrict__ ov) {
-  constexpr int NW = kSelWaves;
+  constexpr int NW = NT / 64;
+  constexpr int BPT = kBins / NT;                 // histogram bins per thread
   const int tid = threadIdx.x;
   float T = kNegInf;
   int take_eq = 1 << 30;                          // n <= k: everything is taken
@@ -483,7 +485,7 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
     if (!have_range) {
       float mn = FLT_MAX, mx = -FLT_MAX;
       uint32_t unused = 0;
-      for (int j = tid; j < n; j += kSelThreads) {
+      for (int j = tid; j < n; j += NT) {
         const float x = lval(lp, j);
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
@@ -503,29 +505,33 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
       }
       const double dlo = static_cast<double>(lo);
       const double inv = static_cast<double>(kBins) / (static_cast<double>(hi) - dlo);
-      for (int j = tid; j < n; j += kSelThreads) {
+      for (int j = tid; j < n; j += NT) {
         const float x = lval(lp, j);
         if (x >= lo && x <= hi) atomicAdd(&g_sm.hist[bin_of(x, dlo, inv)], 1);
       }
       __syncthreads();
-      const uint32_t h0 = g_sm.hist[2 * tid], h1 = g_sm.hist[2 * tid + 1];
+      uint32_t h[BPT];
+      uint32_t hs = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        h[j] = g_sm.hist[BPT * tid + j];
+        hs += h[j];
+      }
       uint32_t tot;
-      const uint32_t pre = block_excl_scan<NW>(h0 + h1, tot, p);
-      uint32_t above = tot - pre - h0 - h1;       // candidates in higher bins
+      const uint32_t pre = block_excl_scan<NW>(hs, tot, p);
+      uint32_t above = tot - pre - hs;            // candidates in higher bins
       const uint32_t un = static_cast<uint32_t>(need);
-      if (above < un && un <= above + h1) {
-        g_sm.bstar = 2 * tid + 1;
-        g_sm.bstar_above = static_cast<int>(above);
-        g_sm.bstar_cnt = static_cast<int>(h1);
+#pragma unroll
+      for (int j = BPT - 1; j >= 0; --j) {
+        if (above < un && un <= above + h[j]) {
+          g_sm.bstar = BPT * tid + j;
+          g_sm.bstar_above = static_cast<int>(above);
+          g_sm.bstar_cnt = static_cast<int>(h[j]);
+        }
+        above += h[j];
       }
-      above += h1;
-      if (above < un && un <= above + h0) {
-        g_sm.bstar = 2 * tid;
-        g_sm.bstar_above = static_cast<int>(above);
-        g_sm.bstar_cnt = static_cast<int>(h0);
-      }
-      g_sm.hist[2 * tid] = 0;
-      g_sm.hist[2 * tid + 1] = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) g_sm.hist[BPT * tid + j] = 0;
       __syncthreads();
       const int bstar = g_sm.bstar;
       need -= g_sm.bstar_above;
@@ -533,7 +539,7 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
       if (cnt <= kBrute) {
         // the need-th largest of the bin: the candidate with fewer than need
         // larger ones and at least need larger-or-equal ones
-        for (int j = tid; j < n; j += kSelThreads) {
+        for (int j = tid; j < n; j += NT) {
           const float x = lval(lp, j);
           if (x >= lo && x <= hi && bin_of(x, dlo, inv) == bstar) {
             const uint32_t slot = atomicAdd(&g_sm.cand_n, 1u);
@@ -561,7 +567,7 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
       }
       float bmn = FLT_MAX, bmx = -FLT_MAX;
       uint32_t unused = 0;
-      for (int j = tid; j < n; j += kSelThreads) {
+      for (int j = tid; j < n; j += NT) {
         const float x = lval(lp, j);
         if (x >= lo && x <= hi && bin_of(x, dlo, inv) == bstar) {
           bmn = fminf(bmn, x);
@@ -574,7 +580,7 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
     }
   }
   // ordered compaction over contiguous runs of R list positions per thread
-  const int R = (n + kSelThreads - 1) / kSelThreads;
+  const int R = (n + NT - 1) / NT;
   const int j0 = tid * R, j1 = min(n, j0 + R);
   uint32_t gt = 0, eq = 0;
   for (int j = j0; j < j1; ++j) {
@@ -604,7 +610,7 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
   }
   const int n_sel =
       min(k, static_cast<int>(tot & 0xffffu) + min(static_cast<int>(tot >> 16), take_eq));
-  for (int sl = n_sel + tid; sl < k; sl += kSelThreads) {
+  for (int sl = n_sel + tid; sl < k; sl += NT) {
     oi[sl] = -1;
     if (ov != nullptr) ov[sl] = kNegInf;
   }
@@ -869,7 +875,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
   float* ov = out_val ? out_val + static_cast<int64_t>(row) * k : nullptr;
   if (n <= kListCap) {
     const bool have_range = rb.x > kNegInf;       // survivors lie in [bound, largest report]
-    select_sorted_list(lp, n, rb.x, rb.y, have_range, k, p, oi, ov);
+    select_sorted_list<kSelThreads>(lp, n, rb.x, rb.y, have_range, k, p, oi, ov);
   } else {
     Emitter em;
     em.oi = oi;

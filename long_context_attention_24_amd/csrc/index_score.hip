@@ -370,13 +370,23 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
         __syncthreads();
         if (tt + 2 < ntiles) *(lds_u32x4*)(st_ptr0 + ((tt + 2) % 3) * kBufElems) = ring[(u + 2) % kPfStages];
         if (tt + 6 < ntiles) ring[(u + 2) % kPfStages] = load_tile(tt + 6);
-        if (tt + 1 < ntiles) mfma_tile((tt + 1) % 3, acc[(u + 1) & 1]);
+        // the MFMAs of tile tt+1 (past the last tile they read a stale
+        // buffer and are discarded: unconditional, so they share one
+        // scheduling region with the epilogue of tile tt) interleaved with
+        // that epilogue's VALU work
+        mfma_tile((tt + 1) % 3, acc[(u + 1) & 1]);
         const f32x16_t (&c)[2] = acc[u & 1];
         float sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) sum = fmaf(wv[0][r], relu_f32(c[0][r]), sum);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sum = fmaf(wv[1][r], relu_f32(c[1][r]), sum);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // B-operand LDS reads
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0); // four VALU
+        }
         const float tot = sum + __shfl_xor(sum, 32, 64);
         const int j = j0 + 32 * tt + jl;
         const bool ok = j < vq;

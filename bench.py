@@ -402,7 +402,11 @@ def main():
                 fn(i)
                 ev[i][1].record()
             torch.cuda.synchronize()
-            return sum(a.elapsed_time(b) for a, b in ev) / steps
+            times = [a.elapsed_time(b) for a, b in ev]
+            if per_launch == "quantiles":
+                times.sort()
+                return [times[int(q * (steps - 1))] for q in (0.1, 0.5, 0.9)]
+            return sum(times) / steps
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
@@ -433,6 +437,7 @@ def main():
         print(json.dumps({"score_only_ms": round(ms, 5), "launches": args.steps + args.warmup}))
         return
     ms = timed(step, args.steps, args.warmup)
+    step_q = timed(step, args.steps, args.warmup, per_launch="quantiles")
     score_ms = timed(score_only, args.steps, args.warmup, per_launch=True)
     index_topk_ms = timed(index_topk_only, args.steps, args.warmup, per_launch=True)
     attend_ms = timed(attend_only, args.steps, args.warmup, per_launch=True)
@@ -462,6 +467,7 @@ def main():
         "step_achieved_gbs": round(step_bytes / (best_ms * 1e-3) / 1e9, 1),
         "step_algorithmic_bytes": step_bytes,
         "ms_per_step_eager": round(ms, 5),
+        "step_ms_p10_p50_p90": [round(x, 5) for x in step_q],
         "ms_per_step_graph": round(graph_ms, 5) if graph_ms else None,
         "call_ms": {"index_score": round(score_ms, 5),
                     "index_topk (score + selection)": round(index_topk_ms, 5),

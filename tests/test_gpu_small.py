@@ -291,6 +291,23 @@ def test_bounded_selection_ties_and_degenerate():
     wi = torch.full((2, 1, 64), 1 / 64, dtype=torch.float32, device=DEV)
     run(qi, wi, ki, [N, 30001], 1024)
 
+    _say("bounded selection: one outlier key, keys spread over many binades")
+    N = 32768
+    qi = _randn((2, 1, 64, 128), 1 / math.sqrt(128), bf, 69)
+    wi = _randn((2, 1, 64), 1 / 8, torch.float32, 70).abs()
+    kf = _randn((2, N, 128), 1 / math.sqrt(128), torch.float32, 71)
+    kf[0, 1234] *= 4096.0                         # one score far above the rest
+    kf[1] *= torch.pow(2.0, -(torch.arange(N, device=DEV) % 48).float())[:, None]
+    ki = kf.to(bf)
+    pos = torch.full((2, 1), 4 * N, dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor([N, N], dtype=torch.int32, device=DEV)
+    idx = csa.index_topk(qi, wi, ki, pos, n_ent, m, 1024)
+    torch.cuda.synchronize()
+    I, QI, KI, W = np64(idx), np64(qi), np64(ki), np64(wi)
+    for b in range(2):
+        s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], N)
+        check_topk(I[b, 0], s_ref, N, 1024)
+
 
 def test_step_graph_replay_matches_eager():
     """The decode step (index_topk + attend, and hca_attend) captured in a HIP

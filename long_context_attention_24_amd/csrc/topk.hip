@@ -114,17 +114,8 @@ __device__ __forceinline__ void zero_hist() {
 
 // ---- value runs ------------------------------------------------------------
 // A run gives thread t the values at positions t*len() .. t*len()+len()-1
-// (-inf for invalid ones, including positions past the end).
-struct LdsRun {                   // LDS, linear, n values
-  static constexpr int kUnroll = 1;
-  const lds_float* v;
-  int n, r;
-  __device__ __forceinline__ int len() const { return r; }
-  __device__ __forceinline__ float get(int i) const {
-    const int q = threadIdx.x * r + i;
-    return q < n ? v[q] : kNegInf;
-  }
-};
+// (-inf for invalid ones, including positions past the end); see SplitRun
+// and GlobalRun below.
 // Writes one selected entry: index = gmap[pos] if given, else
 // base + lmap[pos] if use_lmap, else base + pos.  Passed by value.  (An LDS pointer can
 // legitimately be address 0, so its presence is a flag, not a null test.)

@@ -115,7 +115,9 @@ __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
 
 // ---------------------------------------------------------------- bf16 64 x 128, split
 constexpr int kCsaSplit = 128;     // entries of the top-k list per workgroup
-constexpr int kHcaSplit = 512;     // visible entries per workgroup
+constexpr int kCsaGroups = 2;      // key groups per CSA workgroup (4 waves)
+constexpr int kHcaSplit = 1024;    // visible entries per workgroup
+constexpr int kHcaGroups = 4;      // key groups per HCA workgroup (8 waves)
 constexpr int kPartRows = 130;     // per (query, split): O^T[128][64], then m[64], l[64]
 constexpr int kVPitch = 160;       // bf16 per V row in LDS (256 B + 64 B pad)
 constexpr int kKPitch = 136;       // bf16 per K row in LDS (256 B + 16 B pad)
@@ -128,11 +130,11 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 typedef __attribute__((address_space(3))) float lds_f32;
 
+template <int KG>
 struct __attribute__((aligned(16))) AttnSmem {
-  uint16_t v[2][2][32 * kVPitch];    // [buffer][key group][entry][d], row-major V tiles
-  uint16_t k[2][2][32 * kKPitch];    // [buffer][key group][entry][d], row-major K tiles
+  uint16_t v[2][KG][32 * kVPitch];   // [buffer][key group][entry][d], row-major V tiles
+  uint16_t k[2][KG][32 * kKPitch];   // [buffer][key group][entry][d], row-major K tiles
 };
-__shared__ AttnSmem g_attn;
 
 // Per-round loads of one thread: four 16-byte chunks of its key group's K
 // tile and four of its V tile (chunk c = t128 + 128 i: tile row c / 16,
@@ -144,7 +146,13 @@ struct RoundRegs {
 };
 
 // ej: this lane's entry for tile row jl (lanes 0..31 and 32..63 agree), -1 if
-// none; a chunk's row takes its entry from lane (row) by a shuffle.
+// none; a chunk's row takes its entry from lane (row) by a shuffle.  Every
+// load is issued: a row without an entry reads row 0 (in bounds, as N_max is
+// at least 1); its V chunk is zeroed when it is staged (probability 0 times a
+// non-finite value would not be 0) and its K chunk only feeds a score that
+// the mask drops.  Branch-free loads whose values are first used at staging
+// keep the compiler's count of loads in flight exact, so that waiting for
+// one round never waits for the round after it.
 __device__ __forceinline__ void load_round(const uint16_t* __restrict__ Kb,
                                            const uint16_t* __restrict__ Vb, int64_t kv_sn, int ej,
                                            int t128, RoundRegs& rr) {
@@ -154,24 +162,21 @@ __device__ __forceinline__ void load_round(const uint16_t* __restrict__ Kb,
     const int pair = t128 + 128 * it;
     const int vr = pair >> 4, ch = pair & 15;
     const int ev = __shfl(ej, vr, 64);
-    const int64_t off = static_cast<int64_t>(ev) * kv_sn + 8 * ch;
-    rr.kv[it] = ev >= 0 ? ld16(Kb + off) : make_uint4(0, 0, 0, 0);
-    rr.vv[it] = ev >= 0 ? ld16(Vb + off) : make_uint4(0, 0, 0, 0);
+    const int64_t off = static_cast<int64_t>(ev < 0 ? 0 : ev) * kv_sn + 8 * ch;
+    rr.kv[it] = ld16(Kb + off);
+    rr.vv[it] = ld16(Vb + off);
   }
 }
 
 // One key group of the workgroup processes one 32-entry tile per round:
-//   K and V rows -> LDS (row-major, 16-byte writes), barrier,
+//   stage_round: K and V rows -> LDS (row-major, 16-byte writes);
+//   compute_round: barrier,
 //   S^T = K q^T (8 MFMA 32x32x16, K rows read back in the A-operand layout),
 //   online softmax per lane (each lane owns one head column),
 //   O^T += V^T P^T with V^T read from LDS by transposing loads
 //   (ds_read_b64_tr_b16) and P^T straight from the S accumulator.
-__device__ __forceinline__ void process_round(const RoundRegs& rr, bool active, int buf, int kg,
-                                              int t128, int jl, int g, const bf16x8_t (&bq)[8],
-                                              float scale_log2, float& m_run, float& l_run,
-                                              f32x16_t (&o)[4]) {
-  lds_u16* vt = (lds_u16*)&g_attn.v[buf][kg][0];
-  lds_u16* kt = (lds_u16*)&g_attn.k[buf][kg][0];
+__device__ __forceinline__ void stage_round(const RoundRegs& rr, lds_u16* vt, lds_u16* kt,
+                                            int t128) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int pair = t128 + 128 * it;
@@ -179,8 +184,15 @@ __device__ __forceinline__ void process_round(const RoundRegs& rr, bool active, 
     const uint4 x = rr.kv[it];
     *(lds_u32x4*)(kt + vr * kKPitch + 8 * ch) = u32x4{x.x, x.y, x.z, x.w};
     const uint4 y = rr.vv[it];
-    *(lds_u32x4*)(vt + vr * kVPitch + 8 * ch) = u32x4{y.x, y.y, y.z, y.w};
+    const u32x4 yv = ((rr.vmask >> vr) & 1u) ? u32x4{y.x, y.y, y.z, y.w} : u32x4{0, 0, 0, 0};
+    *(lds_u32x4*)(vt + vr * kVPitch + 8 * ch) = yv;
   }
+}
+
+__device__ __forceinline__ void compute_round(uint32_t vmask, bool active, const lds_u16* vt,
+                                              const lds_u16* kt, int jl, int g,
+                                              const bf16x8_t (&bq)[8], float scale_log2,
+                                              float& m_run, float& l_run, f32x16_t (&o)[4]) {
   __syncthreads();
   if (!active) return;
   f32x16_t sacc = {};
@@ -196,7 +208,7 @@ __device__ __forceinline__ void process_round(const RoundRegs& rr, bool active, 
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int j = 8 * (i >> 2) + 4 * g + (i & 3);
-    x[i] = ((rr.vmask >> j) & 1u) ? sacc[i] * scale_log2 : kNegInf;
+    x[i] = ((vmask >> j) & 1u) ? sacc[i] * scale_log2 : kNegInf;
     tmax = fmaxf(tmax, x[i]);
   }
   tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -250,13 +262,18 @@ __device__ __forceinline__ void process_round(const RoundRegs& rr, bool active, 
   }
 }
 
-// One workgroup per (split, query row); 4 waves = 2 key groups x 2 head
-// halves.  Key group kg takes tiles 2r + kg in round r.  The K/V operands of
-// round r + 1 are in flight while round r computes; CSA entry indices are
-// loaded one round further ahead.  Two workgroups fit on a compute unit.  Output: the split's unnormalised O^T, running maximum m and
-// sum l (base-2 logits) in d-major rows, written with coalesced stores.
-template <bool HCA>
-__global__ __launch_bounds__(256, 2) void attend_split_kernel(
+// One workgroup per (split, query row); 2 KG waves = KG key groups x 2 head
+// halves.  Key group kg takes tiles KG r + kg in round r.  Round r is staged
+// into LDS and its registers are reloaded with round r + 2 before it
+// computes, so two rounds of K/V loads are in flight during the compute; CSA
+// entry indices are read two rounds ahead of their loads.  CSA runs 2 key groups (two workgroups per
+// compute unit), HCA 4 (one workgroup of 8 waves per compute unit, so that a
+// split covers twice the entries for the same loads in flight and the
+// partials to merge are halved).  Output: the split's unnormalised O^T,
+// running maximum m and sum l (base-2 logits) in d-major rows, written with
+// coalesced stores.
+template <bool HCA, int KG>
+__global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn, const int32_t* __restrict__ idx,
     int kk, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
@@ -272,94 +289,127 @@ __global__ __launch_bounds__(256, 2) void attend_split_kernel(
   const int s0 = split * split_len;
   const int s_end = min(n, s0 + split_len);
   const int ntiles = s_end > s0 ? (s_end - s0 + 31) / 32 : 0;
-  const int nrounds = (ntiles + 1) / 2;
+  const int nrounds = (ntiles + KG - 1) / KG;
   const int32_t* irow = HCA ? nullptr : idx + static_cast<int64_t>(row) * kk;
 
   const uint16_t* Kb = K + b * kv_sb;
   const uint16_t* Vb = Vc + b * kv_sb;
   f32x16_t o[4] = {};
   float m_run = kNegInf, l_run = 0.f;
+  __shared__ AttnSmem<KG> sm;
+  lds_u16* const vt0 = (lds_u16*)&sm.v[0][kg][0];
+  lds_u16* const kt0 = (lds_u16*)&sm.k[0][kg][0];
+  lds_u16* const vt1 = (lds_u16*)&sm.v[1][kg][0];
+  lds_u16* const kt1 = (lds_u16*)&sm.k[1][kg][0];
 
-// entry of tile row jl in round rr (-1: none)
-#define CSA_ENTRY(rr, out)                                                       \
-  do {                                                                           \
-    const int t_ = 2 * (rr) + kg, p_ = s0 + 32 * t_ + jl;                        \
-    int e_ = -1;                                                                 \
-    if (t_ < ntiles && p_ < s_end) {                                             \
-      e_ = HCA ? p_ : irow[p_];                                                  \
-      if (e_ < 0 || e_ >= n_ent) e_ = -1;                                        \
-    }                                                                            \
-    (out) = e_;                                                                  \
-  } while (0)
+  // Entry of tile row jl in round rr: entry_raw reads the index list without
+  // a condition (position clamped into the list), entry_ok validates it when
+  // the round's loads are issued (-1: none).  A load under a branch, or a
+  // check right after it, would make the compiler wait for every load in
+  // flight, the next round's included.
+  auto entry_raw = [&](int rr) -> int {
+    const int p_ = s0 + 32 * (KG * rr + kg) + jl;
+    return HCA ? p_ : irow[min(p_, kk - 1)];
+  };
+  auto entry_ok = [&](int rr, int e) -> int {
+    const int t_ = KG * rr + kg, p_ = s0 + 32 * t_ + jl;
+    // bitwise, not short-circuit: no branch that the index load could sink into
+    const bool ok = (t_ < ntiles) & (p_ < s_end) & (e >= 0) & (e < n_ent);
+    return ok ? e : -1;
+  };
 
-  // two register sets: while round r computes, the loads of round r + 1 are
-  // in flight (rounds unrolled by two, so no set is copied)
+  // Two register sets, rounds taken in pairs (an odd count ends with an
+  // empty round).  Loads, including those of rounds past the end (no
+  // entries), are issued on every path, with no branch around them: the
+  // compiler then counts the loads in flight exactly and waiting for one
+  // round never waits for a later one.
   RoundRegs ra, rb;
-  int ejn;
-  {
-    int e0;
-    CSA_ENTRY(0, e0);
-    CSA_ENTRY(1, ejn);
-    load_round(Kb, Vb, kv_sn, e0, t128, ra);
-  }
+  int ea = entry_raw(0), eb = entry_raw(1);
   // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
-  // (loaded after the first gathers are issued: those wait on the entries)
+  // (issued after the first entry indices, which the first loads wait for)
   const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
   bf16x8_t bq[8];
 #pragma unroll
   for (int s = 0; s < 8; ++s) bq[s] = ld_bf16x8(qrow + h * 128 + 16 * s + 8 * g);
-  for (int r = 0; r < nrounds; r += 2) {
-    if (r + 1 < nrounds) load_round(Kb, Vb, kv_sn, ejn, t128, rb);
-    CSA_ENTRY(r + 2, ejn);
-    process_round(ra, 2 * r + kg < ntiles, 0, kg, t128, jl, g, bq, scale_log2, m_run, l_run, o);
-    if (r + 1 < nrounds) {
-      if (r + 2 < nrounds) load_round(Kb, Vb, kv_sn, ejn, t128, ra);
-      CSA_ENTRY(r + 3, ejn);
-      process_round(rb, 2 * (r + 1) + kg < ntiles, 1, kg, t128, jl, g, bq, scale_log2, m_run,
-                    l_run, o);
-    }
-  }
-#undef CSA_ENTRY
+  load_round(Kb, Vb, kv_sn, entry_ok(0, ea), t128, ra);
+  ea = entry_raw(2);
+  load_round(Kb, Vb, kv_sn, entry_ok(1, eb), t128, rb);
+  eb = entry_raw(3);
+  // q resident before the loop (rounds 0 and 1 stay in flight), so that no
+  // wait inside the loop is computed as if it were still loading; the loop
+  // runs at least once so that the loads above stay ahead of this point
+#pragma unroll
+  for (int s = 0; s < 8; ++s) asm volatile("" ::"v"(bq[s]));
+  int r = 0;
+  do {
+    stage_round(ra, vt0, kt0, t128);
+    const uint32_t vma = ra.vmask;
+    load_round(Kb, Vb, kv_sn, entry_ok(r + 2, ea), t128, ra);
+    ea = entry_raw(r + 4);
+    compute_round(vma, KG * r + kg < ntiles, vt0, kt0, jl, g, bq, scale_log2, m_run, l_run, o);
+    stage_round(rb, vt1, kt1, t128);
+    const uint32_t vmb = rb.vmask;
+    load_round(Kb, Vb, kv_sn, entry_ok(r + 3, eb), t128, rb);
+    eb = entry_raw(r + 5);
+    compute_round(vmb, KG * (r + 1) + kg < ntiles, vt1, kt1, jl, g, bq, scale_log2, m_run, l_run,
+                  o);
+    r += 2;
+  } while (r < nrounds);
 
-  // Merge the two key groups of each head half through LDS (reuses the V
-  // tiles): key group 0 finishes d-tiles 0-1 and key group 1 d-tiles 2-3;
-  // each hands the other the half it does not finish, then both store.
+  // Merge the KG key groups of each head half through LDS (reuses the tile
+  // buffers): key group kg finishes the d-tiles dt with dt % KG == kg and
+  // hands the others its accumulators, running maximum and sum.
   l_run = l_run + __shfl_xor(l_run, 32, 64);
   __syncthreads();
-  lds_f32* xo = (lds_f32*)&g_attn.v[0][0][0];      // [kg][hh][lane][32 + 2]
-  constexpr int kX = 34;
+  constexpr int kX = 67;                           // floats per lane: 64 + m + l, odd pitch
+  static_assert(KG * 2 * 64 * kX * sizeof(float) <= sizeof(AttnSmem<KG>), "merge area");
+  lds_f32* xo = (lds_f32*)&sm.v[0][0][0];          // [kg][hh][lane][kX]
   {
     lds_f32* dst = xo + ((kg * 2 + hh) * 64 + lane) * kX;
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd)
+    for (int dt = 0; dt < 4; ++dt)
+      if (dt % KG != kg)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dst[16 * dd + i] = kg == 0 ? o[2 + dd][i] : o[dd][i];
-    dst[32] = m_run;
-    dst[33] = l_run;
+        for (int i = 0; i < 16; ++i) dst[16 * dt + i] = o[dt][i];
+    dst[64] = m_run;
+    dst[65] = l_run;
   }
   __syncthreads();
   {
-    const lds_f32* src = xo + (((1 - kg) * 2 + hh) * 64 + lane) * kX;
-    const float m1 = src[32], l1 = src[33];
-    const float M = fmaxf(m_run, m1);
-    float a0 = 0.f, a1 = 0.f;
-    if (M != kNegInf) {
-      a0 = exp2_fast(m_run - M);
-      a1 = exp2_fast(m1 - M);
+    float mk[KG], lk[KG], ak[KG];
+    float M = kNegInf;
+#pragma unroll
+    for (int k2 = 0; k2 < KG; ++k2) {
+      const lds_f32* src = xo + ((k2 * 2 + hh) * 64 + lane) * kX;
+      mk[k2] = k2 == kg ? m_run : src[64];
+      lk[k2] = k2 == kg ? l_run : src[65];
+      M = fmaxf(M, mk[k2]);
+    }
+    float L = 0.f;
+#pragma unroll
+    for (int k2 = 0; k2 < KG; ++k2) {
+      ak[k2] = M == kNegInf ? 0.f : exp2_fast(mk[k2] - M);
+      L = fmaf(ak[k2], lk[k2], L);
     }
     float* pr = part + (static_cast<int64_t>(row) * nsplit + split) * kPartRows * 64;
-    const int dt0 = 2 * kg;
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd)
+    for (int dt = 0; dt < 4; ++dt) {
+      if (dt % KG != kg) continue;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int d = 32 * (dt0 + dd) + 8 * (i >> 2) + 4 * g + (i & 3);
-        const float mine = kg == 0 ? o[dd][i] : o[2 + dd][i];
-        pr[d * 64 + h] = a0 * mine + a1 * src[16 * dd + i];
+        const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
+        float v = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < KG; ++k2) {
+          const float x = k2 == kg ? o[dt][i] : xo[((k2 * 2 + hh) * 64 + lane) * kX + 16 * dt + i];
+          v = fmaf(ak[k2], x, v);
+        }
+        pr[d * 64 + h] = v;
       }
+    }
     if (kg == 0 && g == 0) {
       pr[128 * 64 + h] = M;
-      pr[129 * 64 + h] = a0 * l_run + a1 * l1;
+      pr[129 * 64 + h] = L;
     }
   }
 }
@@ -473,12 +523,12 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
   float* part = static_cast<float*>(a.ws);
   const dim3 grid(nsplit, a.B * a.Tq);
   if (hca)
-    hipLaunchKernelGGL(attend_split_kernel<true>, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((attend_split_kernel<true, kHcaGroups>), grid, dim3(128 * kHcaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
                        a.n_entries, a.Tq, a.N_max, a.m, scale_log2, sl, nsplit, part);
   else
-    hipLaunchKernelGGL(attend_split_kernel<false>, grid, dim3(256), 0, s,
+    hipLaunchKernelGGL((attend_split_kernel<false, kCsaGroups>), grid, dim3(128 * kCsaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
                        a.n_entries, a.Tq, a.N_max, a.m, scale_log2, sl, nsplit, part);

@@ -172,6 +172,35 @@ def test_tuned_kernels_ragged():
             check_lse(LH[b, t], lh_ref, 2.5e-3)
 
 
+def test_hca_multi_split_ragged():
+    """HCA on the tuned kernel with visible counts that end exactly on, just
+    past and just before split boundaries, several splits per query, a
+    sharp softmax in one sequence, one entry and none."""
+    B, Tq, N_max, m = 3, 3, 3100, 128
+    _say("hca multi-split ragged bf16 64x128")
+    q = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 31)
+    q[2] *= 24.0                                           # logit std ~3
+    kc = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 32)
+    vc = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 33)
+    vis = [[1024, 1025, 2048], [2047, 3100, 1], [3073, 31, 0]]
+    q_pos = torch.tensor([[m * v + m - 2 for v in row] for row in vis], dtype=torch.int32,
+                         device=DEV)
+    n_ent = torch.tensor([N_max, N_max, 3090], dtype=torch.int32, device=DEV)
+    oh, lseh = csa.hca_attend(q, kc, vc, q_pos, n_ent, m, with_lse=True)
+    torch.cuda.synchronize()
+    Q, K, Vv, OH, LH = np64(q), np64(kc), np64(vc), np64(oh), np64(lseh)
+    qp, ne = q_pos.cpu().numpy(), n_ent.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible_count(int(qp[b, t]), m, int(ne[b]))
+            assert V == min(vis[b][t], int(ne[b]))
+            oh_ref, lh_ref = oracle.hca_attend(Q[b, t], K[b], Vv[b], V)
+            check_attention(OH[b, t], oh_ref, "bf16", f"hca b={b} t={t} V={V}")
+            check_lse(LH[b, t], lh_ref, 2e-2 if b == 2 else 2.5e-3)
+    assert np.all(OH[2, 2] == 0) and np.all(np.isneginf(LH[2, 2]))
+    assert np.array_equal(OH[1, 2], np.tile(Vv[1, 0], (64, 1)))
+
+
 def test_tuned_prefill_scores_ragged():
     """bf16 64 x 128 with many queries per sequence (the prefill score
     kernel: 8 queries per workgroup, 2048 keys per workgroup): a query count

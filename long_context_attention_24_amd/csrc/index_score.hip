@@ -141,22 +141,42 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   const int chunk = blockIdx.x * kWavesPerWg + wave;
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  {
-    // q_I rows (heads) of this query into LDS, read back per tile as the A
-    // operand (the registers hold the accumulators of two tiles instead)
-    const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
+  // q_I rows (heads) of this query go to LDS and are read back per tile as
+  // the A operand (the registers hold the accumulators of two tiles instead)
+  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
+  u32x4_t qv[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = static_cast<int>(threadIdx.x) + 256 * i;     // 16-byte chunk: head c / 16
-      *(lds_u32x4*)((lds_u16*)q_lds + (c >> 4) * kKeyPitch + 8 * (c & 15)) =
-          *reinterpret_cast<const u32x4_t*>(qrow + 8 * c);
-    }
-  }
-  __syncthreads();                                // the only barrier: early exits follow
+  for (int i = 0; i < 4; ++i)
+    qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * (static_cast<int>(threadIdx.x) + 256 * i));
   const int key0 = chunk * kKeysPerWave;
-  if (key0 >= N_max) return;
   const int key_end = min(key0 + kKeysPerWave, N_max);
   const int vis_end = min(key_end, V);
+  // The first two key tiles are requested before the query is staged and
+  // the barrier passed, so that their latency overlaps the query's (the
+  // empty asm with a memory clobber keeps the compiler from sinking them
+  // below).  Every wave issues them, also one that exits below: rows are
+  // clamped to [0, vis_end - 1] (row 0 when nothing is visible; N_max >= 1).
+  const uint16_t* kb = k + b * k_sb + 8 * (lane & 15);
+  const int lrow = lane >> 4;                     // row within each 4-row load
+  const int jmax = max(vis_end - 1, 0);
+  u32x4_t kt[3][8];
+  auto load_tile = [&](int t, u32x4_t (&dst)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = min(key0 + 32 * t + 4 * i + lrow, jmax);
+      dst[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
+    }
+  };
+  load_tile(0, kt[0]);
+  load_tile(1, kt[1]);
+  asm volatile("" ::"s"(k) : "memory");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = static_cast<int>(threadIdx.x) + 256 * i;       // 16-byte chunk: head c / 16
+    *(lds_u32x4*)((lds_u16*)q_lds + (c >> 4) * kKeyPitch + 8 * (c & 15)) = qv[i];
+  }
+  __syncthreads();                                // the only barrier: early exits follow
+  if (key0 >= N_max) return;
   float* srow = scores + row * s_rs;
   for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
   if (key0 >= vis_end) {
@@ -165,18 +185,6 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     return;
   }
 
-  const uint16_t* kb = k + b * k_sb + 8 * (lane & 15);
-  const int lrow = lane >> 4;                     // row within each 4-row load
-  u32x4_t kt[3][8];
-  auto load_tile = [&](int t, u32x4_t (&dst)[8]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int j = min(key0 + 32 * t + 4 * i + lrow, vis_end - 1);
-      dst[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
-    }
-  };
-  load_tile(0, kt[0]);
-  load_tile(1, kt[1]);
   lds_u16* kl = (lds_u16*)&key_lds[wave][0];
   const lds_u16* ql = (const lds_u16*)q_lds + jl * kKeyPitch + 8 * g;
   // head weights in accumulator-row order: row = 8*(r/4) + 4*g + r%4

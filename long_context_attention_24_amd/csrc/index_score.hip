@@ -316,12 +316,17 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   const uint16_t* kb = k + b * k_sb + 8 * (tid & 15);
   const int jcap = max(vmax, 1) - 1;              // clamp rows to visible ones (in bounds)
   const int lrow = tid >> 4;                      // tile row this thread loads
+  // Key tile loads are issued on every path (rows clamped, so tiles past
+  // the end read visible rows again): with no branch around them the
+  // compiler counts the loads in flight exactly and waiting for one tile
+  // never waits for the tiles behind it.
   u32x4_t ring[kPfStages];
 #pragma unroll
   for (int u = 0; u < kPfStages; ++u)
-    if (u < ntiles) ring[u] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * u + lrow, jcap)) * k_sn);
+    ring[u] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * u + lrow, jcap)) * k_sn);
 
-  // A operand: q_I rows of the wave's query (zero for an invalid one)
+  // A operand: q_I rows of the wave's query (an invalid query reads row 0
+  // and its results are never stored)
   bf16x8_t a[2][8];
   float wv[2][16];
   {
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
     for (int hf = 0; hf < 2; ++hf) {
 #pragma unroll
       for (int s2 = 0; s2 < 8; ++s2)
-        a[hf][s2] = rowq >= 0 ? ld_bf16x8(qrow + (32 * hf + jl) * 128 + 16 * s2 + 8 * g) : bf16x8_t{};
+        a[hf][s2] = ld_bf16x8(qrow + (32 * hf + jl) * 128 + 16 * s2 + 8 * g);
 #pragma unroll
       for (int r = 0; r < 16; ++r) wv[hf][r] = wrow[32 * hf + 8 * (r >> 2) + 4 * g + (r & 3)];
     }
@@ -364,10 +369,10 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   // into LDS buffer (tt+2)%3, load tile tt+6 into the freed register slot,
   // issue the MFMAs of tile tt+1, then the epilogue of tile tt (whose MFMAs
   // were issued one iteration earlier) while they run.
-  if (ntiles > 0) *(lds_u32x4*)st_ptr0 = ring[0];
-  if (ntiles > 1) *(lds_u32x4*)(st_ptr0 + kBufElems) = ring[1];
-  if (4 < ntiles) ring[0] = load_tile(4);
-  if (5 < ntiles) ring[1] = load_tile(5);
+  *(lds_u32x4*)st_ptr0 = ring[0];
+  *(lds_u32x4*)(st_ptr0 + kBufElems) = ring[1];
+  ring[0] = load_tile(4);
+  ring[1] = load_tile(5);
   __syncthreads();
   if (ntiles > 0) mfma_tile(0, acc[0]);
   for (int t = 0; t < ntiles; t += kTilesPerWave) {   // one 256-key chunk per pass
@@ -377,7 +382,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
       if (tt < ntiles) {
         __syncthreads();
         if (tt + 2 < ntiles) *(lds_u32x4*)(st_ptr0 + ((tt + 2) % 3) * kBufElems) = ring[(u + 2) % kPfStages];
-        if (tt + 6 < ntiles) ring[(u + 2) % kPfStages] = load_tile(tt + 6);
+      }
+      ring[(u + 2) % kPfStages] = load_tile(tt + 6);
+      if (tt < ntiles) {
         // the MFMAs of tile tt+1 (past the last tile they read a stale
         // buffer and are discarded: unconditional, so they share one
         // scheduling region with the epilogue of tile tt) interleaved with

@@ -7,7 +7,8 @@ Recipe (every tensor is independent, so any subset can be regenerated):
   the same seed differ; parity tests always hand the oracle the exact bits
   that the GPU consumed, so that does not matter.
 * Draws are float32 ``standard_normal`` times the tensor's std, then stored:
-  fp32 as is, bf16 by round-to-nearest-even, FP4 by ``fp4_quantize``.
+  fp32 as is, bf16 by round-to-nearest-even, FP4 by ``fp4_quantize`` (fp32
+  block scales) or ``mx4_quantize`` (E8M0 block scales).
 * Distributions: pooling logits N(0, 1); Q, K, V, indexer q / k
   N(0, 1)/sqrt(dim); indexer head weights N(0, w_std) in fp32.
 
@@ -47,6 +48,20 @@ _E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], dtype=np.float32
 _E2M1_MIDS = (_E2M1_GRID[1:] + _E2M1_GRID[:-1]) / 2
 
 
+def _e2m1_pack(y: np.ndarray, shape) -> np.ndarray:
+    """Round float32 ``y`` to the nearest E2M1 value (ties to the even code,
+    saturating at +-6) and pack pairs, element 2i in the low nibble."""
+    a = np.abs(y)
+    lo = np.searchsorted(_E2M1_MIDS, a, side="left")    # midpoints strictly below a
+    hi = np.searchsorted(_E2M1_MIDS, a, side="right")   # midpoints at or below a
+    tie = lo != hi                                      # a sits exactly on a midpoint
+    idx = np.where(tie, np.where(lo % 2 == 0, lo, lo + 1), lo)
+    idx = np.minimum(idx, 7).astype(np.uint8)
+    sign = (np.signbit(y)).astype(np.uint8) << 3
+    code = (idx | sign).reshape(shape)
+    return (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+
+
 def fp4_quantize(x: torch.Tensor, block: int = 32):
     """Encode the last dim of ``x`` as FP4 E2M1 codes with one fp32 scale per block.
 
@@ -62,16 +77,30 @@ def fp4_quantize(x: torch.Tensor, block: int = 32):
     amax = np.abs(xb).max(axis=-1)
     scale = np.where(amax > 0, amax / np.float32(6.0), np.float32(1.0)).astype(np.float32)
     y = (xb / scale[..., None]).astype(np.float32)
-    a = np.abs(y)
-    lo = np.searchsorted(_E2M1_MIDS, a, side="left")    # midpoints strictly below a
-    hi = np.searchsorted(_E2M1_MIDS, a, side="right")   # midpoints at or below a
-    tie = lo != hi                                      # a sits exactly on a midpoint
-    idx = np.where(tie, np.where(lo % 2 == 0, lo, lo + 1), lo)
-    idx = np.minimum(idx, 7).astype(np.uint8)
-    sign = (np.signbit(y)).astype(np.uint8) << 3
-    code = (idx | sign).reshape(xs.shape)
-    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
-    return torch.from_numpy(packed), torch.from_numpy(scale)
+    return torch.from_numpy(_e2m1_pack(y, xs.shape)), torch.from_numpy(scale)
+
+
+def mx4_quantize(x: torch.Tensor, block: int = 32):
+    """Encode the last dim of ``x`` as MX FP4: E2M1 codes with one E8M0 scale
+    byte per block, as the OCP Microscaling formats define it.
+
+    Shared exponent e = floor(log2(amax)) - 2 (2 is the largest E2M1
+    exponent), clamped to [-127, 127]; an all-zero block takes -127.  Code =
+    x / 2**e rounded to the nearest E2M1 value, ties to the even code,
+    saturating at +-6 (amax / 2**e lies in [4, 8)).  Scale byte = e + 127.
+    Returns (codes uint8 [..., dim/2], scale bytes uint8 [..., dim/block]).
+    """
+    xs = x.detach().to("cpu", torch.float32).numpy()
+    dim = xs.shape[-1]
+    assert dim % block == 0 and dim % 2 == 0
+    xb = xs.reshape(xs.shape[:-1] + (dim // block, block))
+    amax = np.abs(xb).max(axis=-1).astype(np.float64)
+    _, k = np.frexp(amax)                     # amax = f * 2**k, 0.5 <= f < 1: floor(log2) = k - 1
+    e = np.where(amax > 0, k - 1 - 2, -127)
+    e = np.clip(e, -127, 127).astype(np.int64)
+    y = (xb.astype(np.float64) * np.ldexp(1.0, -e)[..., None]).astype(np.float32)
+    return (torch.from_numpy(_e2m1_pack(y, xs.shape)),
+            torch.from_numpy((e + 127).astype(np.uint8)))
 
 
 # ---------------------------------------------------------------- drawing
@@ -107,9 +136,10 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
       k_cache   [B, N, D]       cached compressed K (rows >= n_cache left zero
       v_cache   [B, N, D]       for the compress stage to fill)
       ki_cache  [B, N, D_I]     cached compressed indexer keys (bf16 / f32)
-      ki_codes  [B, N, D_I/2]   (fp4) E2M1 codes, ki_scale [B, N, D_I/32] fp32
+      ki_codes  [B, N, D_I/2]   (fp4, mx4) E2M1 codes, ki_scale [B, N, D_I/32]
+                                fp32 (fp4) or E8M0 bytes (mx4)
       q         [B, Tq, H, D]
-      q_idx     [B, Tq, H_I, D_I] (fp4: q_codes / q_scale)
+      q_idx     [B, Tq, H_I, D_I] (fp4, mx4: q_codes / q_scale)
       w_idx     [B, Tq, H_I]    fp32
       q_pos     [B, Tq] int32, n_entries [B] int32
     """
@@ -154,8 +184,8 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
         if w.n_cache:
             kic[:, : w.n_cache] = _normal(w, "ki_cache", (B, w.n_cache, w.D_I),
                                           std_for_dim(w.D_I), device)
-        if w.index_dtype == "fp4":
-            codes, scale = fp4_quantize(kic)
+        if w.index_dtype in ("fp4", "mx4"):
+            codes, scale = (fp4_quantize if w.index_dtype == "fp4" else mx4_quantize)(kic)
             out["ki_codes"] = codes.to(device)
             out["ki_scale"] = scale.to(device)
         else:
@@ -165,8 +195,8 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
         out["q"] = _store(_normal(w, "q", (B, w.Tq, w.H, D), std_for_dim(D), device), w.dtype)
     if w.kind == "csa" and need("q_idx"):
         qi = _normal(w, "q_idx", (B, w.Tq, w.H_I, w.D_I), std_for_dim(w.D_I), device)
-        if w.index_dtype == "fp4":
-            codes, scale = fp4_quantize(qi)
+        if w.index_dtype in ("fp4", "mx4"):
+            codes, scale = (fp4_quantize if w.index_dtype == "fp4" else mx4_quantize)(qi)
             out["q_codes"] = codes.to(device)
             out["q_scale"] = scale.to(device)
         else:

@@ -29,7 +29,7 @@ class Workload:
     D_I: int                # indexer head dim (0 for HCA)
     k: int                  # top-k entries per query (0 for HCA: all visible)
     dtype: str              # storage dtype of q / caches / raw tokens: "f32" | "bf16"
-    index_dtype: str        # indexer q/k storage: "f32" | "bf16" | "fp4"
+    index_dtype: str        # indexer q/k storage: "f32" | "bf16" | "fp4" | "mx4"
     w_std: float            # std of the indexer head weights
     seed: int
 
@@ -77,6 +77,12 @@ WORKLOADS = {
         name="csa_decode_1m_fp4", kind="csa", B=4, m=4, n_cache=262144, n_raw=0, Tq=1,
         q_pos0=1048576, H=64, D=128, H_I=64, D_I=128, k=1024, dtype="bf16",
         index_dtype="fp4", w_std=1.0 / 8.0, seed=4),
+    # The same with power-of-two (E8M0) block scales, the MX FP4 encoding that
+    # gfx950's block-scaled MFMA applies itself (same draws as the fp4 case).
+    "csa_decode_1m_mx4": Workload(
+        name="csa_decode_1m_mx4", kind="csa", B=4, m=4, n_cache=262144, n_raw=0, Tq=1,
+        q_pos0=1048576, H=64, D=128, H_I=64, D_I=128, k=1024, dtype="bf16",
+        index_dtype="mx4", w_std=1.0 / 8.0, seed=4),
 }
 
 

@@ -9,13 +9,16 @@ from .csa_oracle import (  # noqa: F401
     NEG_INF,
     attend,
     csa_reference,
+    e2m1_scaled_to_e4m3,
     e2m1_to_e4m3,
     e2m1_value,
     e4m3_value,
+    e8m0_value,
     fp4_dequantize,
     from_bf16_bits,
     hca_attend,
     index_scores,
+    mx4_dequantize,
     pool,
     round_to_bf16,
     topk_select,

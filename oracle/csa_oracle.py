@@ -36,6 +36,12 @@ below and listed with its reason in the design notes):
   R7 FP4: E2M1 codes (sign, 2 exponent bits with bias 1, 1 mantissa bit),
      element 2i in the low nibble, one fp32 scale per 32 consecutive
      elements; the value is code value times scale.
+  R8 FP4 with power-of-two block scales (the MX-native variant): the same
+     codes with one E8M0 scale byte per 32 elements (value 2**(byte - 127),
+     byte 255 is NaN), the encoding of the OCP Microscaling formats.  §5's
+     claim that FP4 dequantises to FP8 E4M3 without loss while the scale
+     stays within a threshold is exact for such scales: every E2M1 value
+     times 2**e is an E4M3 value for -8 <= e <= 6.
 """
 from __future__ import annotations
 
@@ -123,6 +129,39 @@ def fp4_dequantize(codes, scales, block: int = 32) -> np.ndarray:
     s = np.asarray(scales, dtype=np.float32).astype(np.float64)
     D = vals.shape[-1]
     return vals * np.repeat(s, block, axis=-1)[..., :D]
+
+
+def e8m0_value(byte: int) -> float:
+    """R8: value of an E8M0 scale byte (OCP MX): 2**(byte - 127); 255 is NaN."""
+    byte = int(byte)
+    if not 0 <= byte <= 255:
+        raise ValueError(byte)
+    return math.nan if byte == 255 else math.ldexp(1.0, byte - 127)
+
+
+def e2m1_scaled_to_e4m3(code: int, e: int) -> Optional[int]:
+    """R8 / §5: the E4M3 byte holding exactly e2m1_value(code) * 2**e, or None.
+
+    Found by searching all 256 E4M3 bytes (the definition itself)."""
+    v = math.ldexp(e2m1_value(code), e)
+    want_sign = (code >> 3) & 1
+    for b in range(256):
+        if (b >> 7) == want_sign and e4m3_value(b) == v:
+            return b
+    return None
+
+
+def mx4_dequantize(codes, scale_bytes, block: int = 32) -> np.ndarray:
+    """R8: packed E2M1 codes [..., D/2] and E8M0 scale bytes [..., D/block] -> float64 [..., D]."""
+    sb = np.asarray(scale_bytes, dtype=np.uint8)
+    table = np.array([e8m0_value(b) for b in range(256)], dtype=np.float64)
+    c = np.asarray(codes, dtype=np.uint8)
+    nib = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.uint8)
+    nib[..., 0::2] = c & 0xF
+    nib[..., 1::2] = c >> 4
+    vals = np.array([e2m1_value(i) for i in range(16)], dtype=np.float64)[nib]
+    D = vals.shape[-1]
+    return vals * np.repeat(table[sb], block, axis=-1)[..., :D]
 
 
 # ------------------------------------------------------------------ CSA / HCA steps

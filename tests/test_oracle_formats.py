@@ -1,4 +1,4 @@
-"""Pins for the oracle's number formats (FP4 E2M1, E4M3, bf16) and the FP4 input encoder."""
+"""Pins for the oracle's number formats (FP4 E2M1, E4M3, E8M0, bf16) and the FP4 / MX FP4 input encoders."""
 import math
 
 import numpy as np
@@ -97,3 +97,73 @@ def test_bf16_bits_roundtrip():
     bits = bf16_bits_from_f32(x)
     assert list(bits) == [0x3F80, 0xC020, 0x3C00, 0x4049]
     assert np.array_equal(oracle.from_bf16_bits(bits), x.astype(np.float64))
+
+
+# ---------------------------------------------------------------- MX FP4 (E8M0 block scales)
+def test_e8m0_decoder_known_values(golden):
+    rows = golden("e8m0_values.txt")
+    assert len(rows) >= 8
+    for row in rows:
+        b, v = row.split()
+        got = oracle.e8m0_value(int(b, 16))
+        if v == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(v)
+
+
+def test_fp4_to_e4m3_lossless_within_threshold():
+    # §5: FP4 dequantises to FP8 E4M3 without loss while the block scale stays
+    # within a threshold.  With a power-of-two scale 2^e that threshold is
+    # -8 <= e <= 6: every E2M1 value times 2^e is an E4M3 value there, and
+    # just outside it some code has no exact E4M3 form: 6 * 2^7 = 768 exceeds
+    # E4M3's largest finite value 448, 0.5 * 2^-9 = 2^-10 is below its
+    # smallest subnormal 2^-9, and 1.5 * 2^-9 would need a 2^-10 step.
+    for e in range(-8, 7):
+        for code in range(16):
+            b = oracle.e2m1_scaled_to_e4m3(code, e)
+            assert b is not None, (code, e)
+            assert oracle.e4m3_value(b) == math.ldexp(oracle.e2m1_value(code), e)
+    assert oracle.e2m1_scaled_to_e4m3(7, 7) is None          # 768 > 448
+    assert oracle.e2m1_scaled_to_e4m3(1, -9) is None         # 2^-10 < 2^-9
+    assert oracle.e2m1_scaled_to_e4m3(3, -9) is None         # 1.5 * 2^-9: needs a 2^-10 step
+
+
+def test_mx4_dequantize_is_fp4_with_power_of_two_scales():
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 256, size=(3, 64), dtype=np.uint8)
+    sb = rng.integers(100, 160, size=(3, 4), dtype=np.uint8)
+    pow2 = np.ldexp(np.float32(1.0), sb.astype(np.int32) - 127).astype(np.float32)
+    np.testing.assert_array_equal(oracle.mx4_dequantize(codes, sb),
+                                  oracle.fp4_dequantize(codes, pow2))
+
+
+def test_mx4_encoder_worked_examples(golden):
+    from csa_synth import mx4_quantize
+    for row in golden("mx4_encoding.txt"):
+        a, b, c = (t.strip() for t in row.split("|"))
+        xs = [float(v) for v in a.split(",")]
+        x = torch.zeros(1, 32)
+        x[0, : len(xs)] = torch.tensor(xs)
+        codes, sb = mx4_quantize(x)
+        assert int(sb[0, 0]) == int(b), row
+        got = oracle.mx4_dequantize(codes.numpy(), sb.numpy())[0]
+        want = [float(v) for v in c.split(",")]
+        assert list(got[: len(want)]) == want, row
+        assert np.all(got[len(want):] == 0), row
+
+
+def test_mx4_encoder_error_bound():
+    # every decoded value is within half a grid step of the input clamped to
+    # +-6 * 2^e (the largest step, between 4 and 6, is 2 * 2^e), and the
+    # block's largest magnitude lands in [4, 8) * 2^e before saturation
+    from csa_synth import mx4_quantize
+    x = torch.randn(64, 128) * torch.exp(torch.randn(64, 1) * 3)
+    codes, sb = mx4_quantize(x)
+    deq = oracle.mx4_dequantize(codes.numpy(), sb.numpy())
+    xs = x.numpy().astype(np.float64).reshape(64, 4, 32)
+    step = np.ldexp(1.0, sb.numpy().astype(np.int64) - 127)[..., None]
+    clamped = np.clip(xs, -6 * step, 6 * step)
+    assert np.all(np.abs(deq.reshape(64, 4, 32) - clamped) <= step * (1 + 1e-12))
+    amax = np.abs(xs).max(axis=-1, keepdims=True)
+    assert np.all((amax >= 4 * step) & (amax < 8 * step))

@@ -13,7 +13,8 @@ from HBM.
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (only 1),
 --graph (also time the step captured in a HIP graph), --no-cpu-baseline,
 --workload NAME (another workload's own line instead of the headline one:
-hca_decode_1m, csa_decode_1m_fp4 or csa_prefill_chunk; see other_workload),
+hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4 or csa_prefill_chunk; see
+other_workload),
 --score-only (launch only the indexer score kernel, for hardware-counter
 runs), --copy-calibration (run only a plain device copy of known size, for
 scaling the FETCH_SIZE / WRITE_SIZE counters).
@@ -179,6 +180,8 @@ def other_workload(args):
       compressed caches; roofline: the attention's K/V stream against HBM.
     csa_decode_1m_fp4: FP4 indexer scores + top-k + sparse attention for 4
       decode tokens at 1M context; roofline: the FP4 score kernel's bytes.
+    csa_decode_1m_mx4: the same with MX FP4 indexer inputs (one E8M0 scale
+      byte per 32 elements); roofline: the MX score kernel's bytes.
     csa_prefill_chunk: compress the 4096 new tokens, score / select / attend
       all 4096 queries; roofline: the prefill score kernel's FLOPs against the
       bf16 MFMA peak.
@@ -225,7 +228,8 @@ def other_workload(args):
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
                    compress_ms=round(comp_ms, 4),
                    compress_gbs=round(raw_bytes / (comp_ms * 1e-3) / 1e9, 1))
-    elif w.name == "csa_decode_1m_fp4":
+    elif w.name in ("csa_decode_1m_fp4", "csa_decode_1m_mx4"):
+        mx = w.name == "csa_decode_1m_mx4"
         # one quantised draw; the other copies hold its entries rolled along
         # the entry axis (distinct memory for the cache rotation)
         first = make_inputs(w, device=dev)
@@ -257,14 +261,21 @@ def other_workload(args):
                             q_scale=c["q_scale"], k_scale=c["ki_scale"], out=scores)
         ms = timed(step, args.steps, args.warmup)
         sms = timed(score_only, args.steps, args.warmup)
-        score_bytes = w.B * w.N * (64 + 16 + 4) + w.B * w.H_I * (64 + 16 + 4)
+        # per (row, entry): 64 B codes + the scales (16 B fp32 or 4 E8M0 bytes)
+        # + 4 B score; per row the query codes, scales and head weights
+        sc_b = 4 if mx else 16
+        score_bytes = w.B * w.N * (64 + sc_b + 4) + w.B * w.H_I * (64 + sc_b + 4)
         gbs = score_bytes / (sms * 1e-3) / 1e9
-        res = dict(metric="CSA decode tokens/sec at 1M context, FP4 indexer, 1 MI355X",
+        res = dict(metric=("CSA decode tokens/sec at 1M context, MX FP4 indexer (E8M0 scales), "
+                           "1 MI355X") if mx else
+                          "CSA decode tokens/sec at 1M context, FP4 indexer, 1 MI355X",
                    value=round(w.B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
                    config={"workload": w.name, "batch": w.B, "context_tokens": w.q_pos0,
-                           "compressed_entries": w.N, "m": w.m, "indexer": "64x128 FP4 E2M1",
-                           "top_k": w.k},
-                   roofline={"kernel": "score_fp4_h64d128_kernel", "bound": "hbm",
+                           "compressed_entries": w.N, "m": w.m,
+                           "indexer": "64x128 FP4 E2M1, E8M0 block scales" if mx else
+                                      "64x128 FP4 E2M1", "top_k": w.k},
+                   roofline={"kernel": "score_mx4_h64d128_kernel" if mx else
+                                       "score_fp4_h64d128_kernel", "bound": "hbm",
                              "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                              "algorithmic_bytes_per_launch": score_bytes,

@@ -31,6 +31,11 @@
  *     output 0 and lse -inf.  lse is the natural-log log-sum-exp.
  *   - FP4: E2M1 codes, element 2i in the low nibble of byte i, one fp32
  *     scale per 32 consecutive elements of a vector.
+ *   - MX FP4 (a variant of §5's FP4 path): the same codes with one E8M0
+ *     scale byte per 32 elements, as in the OCP Microscaling formats; such
+ *     power-of-two scales keep FP4 -> FP8 E4M3 exact (the pages' condition
+ *     that the scale stay within range) and gfx950's block-scaled MFMA
+ *     applies them itself.
  *
  * Conventions for every call
  *   - All data pointers are DEVICE memory owned by the caller.  The library
@@ -73,7 +78,9 @@ typedef enum {
 typedef enum {
   CSA_F32 = 0,        /* float32                                           */
   CSA_BF16 = 1,       /* bfloat16 (uint16 bit patterns)                    */
-  CSA_FP4_E2M1 = 2    /* packed E2M1 codes + one fp32 scale per 32 values  */
+  CSA_FP4_E2M1 = 2,   /* packed E2M1 codes + one fp32 scale per 32 values  */
+  CSA_FP4_E2M1_E8M0 = 3 /* packed E2M1 codes + one E8M0 scale byte per 32
+                           values (MX FP4: value = code * 2^(byte - 127))  */
 } csa_dtype_t;
 
 int csa_abi_version(void);
@@ -108,20 +115,24 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st,
  *   scores[b, t, j] = sum_h w_idx[b,t,h] * max(0, q_idx[b,t,h,:] . k_idx[b,j,:])
  *                     for j < V(b,t), and -inf for V(b,t) <= j < N_max.
  *
- * q_idx     [B, Tq, H_I, D_I] contiguous (idx_dtype); for CSA_FP4_E2M1 the
- *           codes [B, Tq, H_I, D_I/2] bytes plus q_scale [B, Tq, H_I, D_I/32].
+ * q_idx     [B, Tq, H_I, D_I] contiguous (idx_dtype); for the FP4 dtypes the
+ *           codes [B, Tq, H_I, D_I/2] bytes plus q_scale [B, Tq, H_I, D_I/32]
+ *           contiguous: fp32 (CSA_FP4_E2M1) or E8M0 bytes (CSA_FP4_E2M1_E8M0).
  * w_idx     [B, Tq, H_I] fp32 contiguous.
  * k_idx     [B, N_max, D_I] with strides (k_sb, k_sn) (FP4: bytes of codes);
- *           k_scale [B, N_max, D_I/32] with strides (ks_sb, ks_sn) for FP4,
- *           else NULL.
+ *           k_scale [B, N_max, D_I/32] with strides (ks_sb, ks_sn) in scale
+ *           elements (fp32 or bytes) for the FP4 dtypes, else NULL.  Scale
+ *           pointers and strides: 16-byte aligned for fp32 scales, 4-byte
+ *           aligned for E8M0 bytes.
  * q_pos     [B, Tq] int32 device: position of each query token.
  * n_entries [B] int32 device: valid cache rows per sequence (<= N_max).
  * scores    [B, Tq, N_max] fp32 contiguous.
  * Supported: F32 / BF16 with H_I <= 64 and D_I in {32, 64, 128};
- *            FP4 with H_I = 64, D_I = 128.  Tuned: BF16 and FP4 64 x 128.
+ *            both FP4 dtypes with H_I = 64, D_I = 128.  Tuned: BF16 and FP4
+ *            64 x 128.
  */
-csa_status_t csa_index_score(const void* q_idx, const float* q_scale, const float* w_idx,
-                             const void* k_idx, const float* k_scale,
+csa_status_t csa_index_score(const void* q_idx, const void* q_scale, const float* w_idx,
+                             const void* k_idx, const void* k_scale,
                              int64_t k_sb, int64_t k_sn, int64_t ks_sb, int64_t ks_sn,
                              csa_dtype_t idx_dtype,
                              const int32_t* q_pos, const int32_t* n_entries,
@@ -152,8 +163,8 @@ csa_status_t csa_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes);
  * csa_index_topk - csa_index_score followed by csa_topk, with the score
  * matrix kept in the workspace.  Arguments as in those two calls.
  */
-csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float* w_idx,
-                            const void* k_idx, const float* k_scale,
+csa_status_t csa_index_topk(const void* q_idx, const void* q_scale, const float* w_idx,
+                            const void* k_idx, const void* k_scale,
                             int64_t k_sb, int64_t k_sn, int64_t ks_sb, int64_t ks_sn,
                             csa_dtype_t idx_dtype,
                             const int32_t* q_pos, const int32_t* n_entries,

@@ -32,7 +32,7 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libcsa.so")
 
-CSA_F32, CSA_BF16, CSA_FP4_E2M1 = 0, 1, 2
+CSA_F32, CSA_BF16, CSA_FP4_E2M1, CSA_FP4_E2M1_E8M0 = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "csa_abi_version", "csa_status_string", "csa_last_error",
@@ -164,15 +164,19 @@ def _index_args(q_idx, w_idx, k_idx, q_scale, k_scale):
     _contig(q_idx, "q_idx")
     _contig(w_idx, "w_idx")
     dt = _dtype_code(k_idx)
+    if dt == CSA_FP4_E2M1 and k_scale is not None and k_scale.dtype == torch.uint8:
+        dt = CSA_FP4_E2M1_E8M0          # MX FP4: E8M0 scale bytes
     B, Tq, H_I = q_idx.shape[:3]
-    D_I = q_idx.shape[3] * (2 if dt == CSA_FP4_E2M1 else 1)
+    D_I = q_idx.shape[3] * (2 if dt in (CSA_FP4_E2M1, CSA_FP4_E2M1_E8M0) else 1)
     N_max = k_idx.shape[1]
     if k_idx.stride(-1) != 1:
         raise ValueError("k_idx needs a contiguous last dim")
     ks_sb = ks_sn = 0
-    if dt == CSA_FP4_E2M1:
+    if dt in (CSA_FP4_E2M1, CSA_FP4_E2M1_E8M0):
         if q_scale is None or k_scale is None:
             raise ValueError("FP4 indexer needs q_scale and k_scale")
+        if q_scale.dtype != k_scale.dtype:
+            raise ValueError("q_scale and k_scale must have the same dtype")
         _contig(q_scale, "q_scale")
         ks_sb, ks_sn = k_scale.stride(0), k_scale.stride(1)
     return dt, B, Tq, H_I, D_I, N_max, ks_sb, ks_sn

@@ -31,7 +31,11 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 size_t esize(csa_dtype_t dt) { return dt == CSA_F32 ? 4 : 2; }
 
-bool valid_dtype(csa_dtype_t dt) { return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP4_E2M1; }
+bool valid_dtype(csa_dtype_t dt) {
+  return dt == CSA_F32 || dt == CSA_BF16 || dt == CSA_FP4_E2M1 || dt == CSA_FP4_E2M1_E8M0;
+}
+bool is_fp4(csa_dtype_t dt) { return dt == CSA_FP4_E2M1 || dt == CSA_FP4_E2M1_E8M0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -44,8 +48,8 @@ int64_t score_row_stride(int N_max) { return (static_cast<int64_t>(N_max) + 3) /
     if (!(cond)) return fail(st, __VA_ARGS__); \
   } while (0)
 
-csa_status_t check_score_args(const void* q_idx, const float* q_scale, const float* w_idx,
-                              const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
+csa_status_t check_score_args(const void* q_idx, const void* q_scale, const float* w_idx,
+                              const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
                               int64_t ks_sb, int64_t ks_sn, csa_dtype_t dt, const int32_t* q_pos,
                               const int32_t* n_entries, int B, int Tq, int N_max, int H_I, int D_I,
                               int m) {
@@ -58,10 +62,14 @@ csa_status_t check_score_args(const void* q_idx, const float* q_scale, const flo
               "index score: dtype %d with H_I=%d D_I=%d not supported", (int)dt, H_I, D_I);
   CSA_REQUIRE(aligned16(q_idx) && aligned16(k_idx) && aligned16(w_idx), CSA_ERR_INVALID_ARGUMENT,
               "index score: pointers must be 16-byte aligned");
-  if (dt == CSA_FP4_E2M1) {
+  if (is_fp4(dt)) {
     CSA_REQUIRE(q_scale && k_scale, CSA_ERR_INVALID_ARGUMENT, "index score: FP4 needs scales");
-    CSA_REQUIRE(aligned16(q_scale) && aligned16(k_scale), CSA_ERR_INVALID_ARGUMENT,
-                "index score: scale pointers must be 16-byte aligned");
+    if (dt == CSA_FP4_E2M1)
+      CSA_REQUIRE(aligned16(q_scale) && aligned16(k_scale), CSA_ERR_INVALID_ARGUMENT,
+                  "index score: fp32 scale pointers must be 16-byte aligned");
+    else
+      CSA_REQUIRE(aligned4(q_scale) && aligned4(k_scale), CSA_ERR_INVALID_ARGUMENT,
+                  "index score: E8M0 scale pointers must be 4-byte aligned");
     CSA_REQUIRE(k_sn >= D_I / 2 && k_sn % 16 == 0 && k_sb % 16 == 0 &&
                     k_sb >= static_cast<int64_t>(N_max) * k_sn,
                 CSA_ERR_INVALID_ARGUMENT, "index score: bad FP4 code strides");
@@ -142,8 +150,8 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st, const float
                     "compress launch");
 }
 
-csa_status_t csa_index_score(const void* q_idx, const float* q_scale, const float* w_idx,
-                             const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
+csa_status_t csa_index_score(const void* q_idx, const void* q_scale, const float* w_idx,
+                             const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
                              int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
                              const int32_t* q_pos, const int32_t* n_entries, int B, int Tq,
                              int N_max, int H_I, int D_I, int m, float* scores,
@@ -201,8 +209,8 @@ csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* b
 }
 
 
-csa_status_t csa_index_topk(const void* q_idx, const float* q_scale, const float* w_idx,
-                            const void* k_idx, const float* k_scale, int64_t k_sb, int64_t k_sn,
+csa_status_t csa_index_topk(const void* q_idx, const void* q_scale, const float* w_idx,
+                            const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
                             int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
                             const int32_t* q_pos, const int32_t* n_entries, int B, int Tq,
                             int N_max, int H_I, int D_I, int m, int k, int32_t* topk_idx,

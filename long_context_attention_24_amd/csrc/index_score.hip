@@ -550,6 +550,108 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
   }
 }
 
+// ---------------------------------------------------------------- MX FP4 (E8M0 scales), 64 x 128
+// The same operand layout with power-of-two block scales: lane (row / column
+// l % 16, block l / 16) hands the MFMA its block's E8M0 byte, the hardware
+// scales each block partial exactly, and one MFMA per 16-head tile gives the
+// whole 128-dim dot product.  The epilogue is ReLU and w only (2 VALU
+// operations per head and entry), so the kernel streams: a wave keeps
+// kMxAhead tiles of codes (16 bytes per lane) and scale words (the key's four
+// scale bytes, read by all four block lanes) in flight.
+constexpr int kMxAhead = 7;
+
+__global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
+    const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k,
+    const uint8_t* __restrict__ k_scale, int64_t k_sb, int64_t k_sn, int64_t ks_sb,
+    int64_t ks_sn, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries,
+    int Tq, int N_max, int m, float* __restrict__ scores, int64_t s_rs,
+    float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
+  const int row = blockIdx.y, b = row / Tq;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  const int chunk = blockIdx.x * kWavesPerWg + wave;
+  const int key0 = chunk * kKeysPerWave;
+  if (key0 >= N_max) return;
+  const int key_end = min(key0 + kKeysPerWave, N_max);
+  const int vis_end = min(key_end, V);
+  float* srow = scores + row * s_rs;
+  for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
+  if (key0 >= vis_end) {
+    if (chunk_rep != nullptr && lane == 0)
+      chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
+    return;
+  }
+
+  // keys past the visible range are clamped to the last visible one (in
+  // bounds, masked on output)
+  const uint8_t* kb = k + b * k_sb + 16 * g;
+  const uint8_t* ksb = k_scale + b * ks_sb;
+  u32x4_t kc[kMxAhead + 1];
+  uint32_t ks[kMxAhead + 1];
+  auto load_tile = [&](int t, u32x4_t& c, uint32_t& sw) {
+    const int j = min(key0 + 16 * t + nl, vis_end - 1);
+    c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
+    sw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ksb + static_cast<int64_t>(j) * ks_sn));
+  };
+#pragma unroll
+  for (int t = 0; t < kMxAhead; ++t) load_tile(t, kc[t], ks[t]);
+
+  // A operand per head tile mt: head 16 mt + n, block g (16 bytes of codes)
+  // and that block's scale byte
+  const uint8_t* qrow = q + static_cast<int64_t>(row) * 64 * 64;
+  const uint8_t* qsrow = q_scale + static_cast<int64_t>(row) * 64 * 4;
+  v8i32_t qa[4];
+  int sa[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(qrow + (16 * mt + nl) * 64 + 16 * g);
+    qa[mt] = v8i32_t{static_cast<int>(c[0]), static_cast<int>(c[1]), static_cast<int>(c[2]),
+                     static_cast<int>(c[3]), 0, 0, 0, 0};
+    sa[mt] = qsrow[(16 * mt + nl) * 4 + g];
+  }
+  // accumulator rows: head = 16*mt + 4*g + r
+  float wv[4][4];
+  const float* wrow = w + static_cast<int64_t>(row) * 64;
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[mt][r] = wrow[16 * mt + 4 * g + r];
+
+  float scv[kFp4Tiles];
+#pragma unroll
+  for (int t = 0; t < kFp4Tiles; ++t) {
+    if (t + kMxAhead < kFp4Tiles)
+      load_tile(t + kMxAhead, kc[(t + kMxAhead) % (kMxAhead + 1)], ks[(t + kMxAhead) % (kMxAhead + 1)]);
+    const u32x4_t c = kc[t % (kMxAhead + 1)];
+    const int sb = static_cast<int>((ks[t % (kMxAhead + 1)] >> (8 * g)) & 0xffu);
+    const v8i32_t bc = {static_cast<int>(c[0]), static_cast<int>(c[1]), static_cast<int>(c[2]),
+                        static_cast<int>(c[3]), 0, 0, 0, 0};
+    float sum = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const f32x4_t z = {};
+      const f32x4_t p =
+          __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], bc, z, 4, 4, 0, sa[mt], 0, sb);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sum = fmaf(wv[mt][r], relu_f32(p[r]), sum);
+    }
+    // heads are spread over the four 16-lane groups of the key's column
+    sum = sum + __shfl_xor(sum, 16, 64);
+    sum = sum + __shfl_xor(sum, 32, 64);
+    const int jj = key0 + 16 * t + nl;
+    const bool ok = jj < vis_end;
+    if (g == 0 && ok) srow[jj] = sum;
+    scv[t] = ok ? sum : kNegInf;
+  }
+  const int thr_c = bound_c_row(V, bound_k);
+  if (chunk_rep != nullptr && thr_c > 0) {
+    const float2 rep = wave_chunk_report<kFp4Tiles>(scv, g == 0, thr_c);
+    if (lane == 0) chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = rep;
+  }
+}
+
 template <typename T, int D>
 void launch_generic(const ScoreArgs& a, hipStream_t s) {
   const dim3 grid((a.N_max + 255) / 256, a.B * a.Tq);
@@ -561,13 +663,14 @@ void launch_generic(const ScoreArgs& a, hipStream_t s) {
 }  // namespace
 
 bool score_tuned(csa_dtype_t dt, int H, int D) {
-  return (dt == CSA_FP4_E2M1 || dt == CSA_BF16) && H == 64 && D == 128;
+  return (dt == CSA_FP4_E2M1 || dt == CSA_FP4_E2M1_E8M0 || dt == CSA_BF16) && H == 64 &&
+         D == 128;
 }
 
 int score_chunk_keys() { return kKeysPerWave; }
 
 bool score_supported(csa_dtype_t dt, int H, int D) {
-  if (dt == CSA_FP4_E2M1) return H == 64 && D == 128;
+  if (dt == CSA_FP4_E2M1 || dt == CSA_FP4_E2M1_E8M0) return H == 64 && D == 128;
   if (dt != CSA_F32 && dt != CSA_BF16) return false;
   return H >= 1 && H <= 64 && (D == 32 || D == 64 || D == 128);
 }
@@ -576,10 +679,19 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
   if (dt == CSA_FP4_E2M1) {
     const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
     hipLaunchKernelGGL(score_fp4_h64d128_kernel, grid, dim3(256), 0, s,
-                       static_cast<const uint8_t*>(a.q), a.q_scale, a.w,
-                       static_cast<const uint8_t*>(a.k), a.k_scale, a.k_sb, a.k_sn, a.ks_sb,
-                       a.ks_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs,
-                       a.chunk_rep, a.n_chunks, a.bound_k);
+                       static_cast<const uint8_t*>(a.q), static_cast<const float*>(a.q_scale),
+                       a.w, static_cast<const uint8_t*>(a.k),
+                       static_cast<const float*>(a.k_scale), a.k_sb, a.k_sn, a.ks_sb, a.ks_sn,
+                       a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs, a.chunk_rep,
+                       a.n_chunks, a.bound_k);
+  } else if (dt == CSA_FP4_E2M1_E8M0) {
+    const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
+    hipLaunchKernelGGL(score_mx4_h64d128_kernel, grid, dim3(256), 0, s,
+                       static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.q_scale),
+                       a.w, static_cast<const uint8_t*>(a.k),
+                       static_cast<const uint8_t*>(a.k_scale), a.k_sb, a.k_sn, a.ks_sb, a.ks_sn,
+                       a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs, a.chunk_rep,
+                       a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128 && a.Tq >= kPfQueries) {
     const int groups = (a.Tq + kPfQueries - 1) / kPfQueries;
     const dim3 grid((a.N_max + kPfKeys - 1) / kPfKeys, a.B * groups);

@@ -18,10 +18,10 @@ hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const floa
 // ---- index_score.hip
 struct ScoreArgs {
   const void* q;            // [B*Tq, H_I, D_I] (FP4: codes)
-  const float* q_scale;     // FP4 only
+  const void* q_scale;      // FP4 only: fp32 (CSA_FP4_E2M1) or E8M0 bytes
   const float* w;           // [B*Tq, H_I]
   const void* k;            // cache base
-  const float* k_scale;     // FP4 only
+  const void* k_scale;      // FP4 only: fp32 (CSA_FP4_E2M1) or E8M0 bytes
   int64_t k_sb, k_sn, ks_sb, ks_sn;
   const int32_t* q_pos;
   const int32_t* n_entries;

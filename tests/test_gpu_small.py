@@ -267,6 +267,46 @@ def test_fp4_scores_ragged():
         check_topk(I[b, 0], s_ref, V, k)
 
 
+def test_mx4_scores_ragged():
+    """MX FP4 indexer (E2M1 codes, one E8M0 scale byte per 32 elements, the
+    hardware's block scales) on ragged sizes, with block exponents spread far
+    apart on both sides (so a scale applied to the wrong block shows), an
+    all-zero key block (scale byte 0) and a partially valid cache.  Scores
+    against the oracle fed the same quantised inputs, then the selection."""
+    from csa_synth import mx4_quantize
+    B, N_max, m, k = 3, 1000 + 37, 4, 300
+    _say("mx4 ragged scores")
+    qi = _randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.float32, 91)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.float32, 92)
+    wi = _randn((B, 1, 64), 1 / 8, torch.float32, 93)
+    ki[:, :, 32:64] *= 2.0 ** 10
+    ki[:, :, 96:128] *= 2.0 ** -12
+    ki[:, 5:300:7, 64:96] = 0.0
+    qi[:, :, 7, 0:32] *= 2.0 ** 20
+    qi[:, :, 40, 96:128] *= 2.0 ** -30
+    qi[:, :, 1::3, 32:64] *= 2.0 ** -9
+    qc, qs = (t.to(DEV) for t in mx4_quantize(qi))
+    kc, ks = (t.to(DEV) for t in mx4_quantize(ki))
+    assert ks.dtype == torch.uint8 and int(ks.min()) == 0
+    pos = [4 * N_max + 3, 4 * 50 + 1, 4 * 777]
+    q_pos = torch.tensor([[p] for p in pos], dtype=torch.int32, device=DEV)
+    ne = [N_max, 900, 1001]
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qc, wi, kc, q_pos, n_ent, m, q_scale=qs, k_scale=ks)
+    idx = csa.index_topk(qc, wi, kc, q_pos, n_ent, m, k, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    S, I, W = np64(scores), np64(idx), np64(wi)
+    QI = oracle.mx4_dequantize(qc.cpu().numpy(), qs.cpu().numpy())
+    KI = oracle.mx4_dequantize(kc.cpu().numpy(), ks.cpu().numpy())
+    for b in range(B):
+        V = oracle.visible_count(pos[b], m, ne[b])
+        s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
+        assert np.all(np.isneginf(S[b, 0, V:])), (b, V)
+        bound = score_bound(QI[b, 0], W[b, 0], KI[b, :V], 128, 64)
+        assert np.all(np.abs(S[b, 0, :V] - s_ref[:V]) <= bound), (b, V)
+        check_topk(I[b, 0], s_ref, V, k)
+
+
 def test_bounded_selection_ties_and_degenerate():
     """The bounded selection (chunk bounds + survivor list) on inputs far from
     Gaussian, where ties decide: all scores equal (more survivors than the

@@ -24,8 +24,9 @@ def _say(msg):
 def _decode_check(w, inp, idx, o, lse, fp4=False):
     """Check every query of a decode workload: top-k gate and attention gate."""
     if fp4:
-        KI = oracle.fp4_dequantize(inp["ki_codes"].cpu().numpy(), inp["ki_scale"].cpu().numpy())
-        QI = oracle.fp4_dequantize(inp["q_codes"].cpu().numpy(), inp["q_scale"].cpu().numpy())
+        deq = oracle.mx4_dequantize if w.index_dtype == "mx4" else oracle.fp4_dequantize
+        KI = deq(inp["ki_codes"].cpu().numpy(), inp["ki_scale"].cpu().numpy())
+        QI = deq(inp["q_codes"].cpu().numpy(), inp["q_scale"].cpu().numpy())
     else:
         KI, QI = np64(inp["ki_cache"]), np64(inp["q_idx"])
     W = np64(inp["w_idx"])
@@ -107,6 +108,24 @@ def test_csa_decode_1m_fp4_full():
         rec.append(len(set(I[b, 0].tolist()) & set(ref.tolist())) / w.k)
     _say(f"{w.name}: recall vs quantised-input oracle {rec}")
     assert min(rec) >= 0.995
+
+
+def test_csa_decode_1m_mx4_full():
+    """The 1M-context decode with MX FP4 indexer inputs (E8M0 block scales):
+    every query's top-k and attention against the oracle on the same
+    quantised inputs."""
+    w = WORKLOADS["csa_decode_1m_mx4"]
+    _say(f"{w.name}: generating inputs")
+    inp = make_inputs(w, device=DEV)
+    assert inp["ki_scale"].dtype == torch.uint8
+    _say(f"{w.name}: index_topk + attend")
+    idx = csa.index_topk(inp["q_codes"], inp["w_idx"], inp["ki_codes"], inp["q_pos"],
+                         inp["n_entries"], w.m, w.k, q_scale=inp["q_scale"],
+                         k_scale=inp["ki_scale"])
+    o, lse = csa.attend(inp["q"], inp["k_cache"], inp["v_cache"], idx, inp["n_entries"],
+                        with_lse=True)
+    torch.cuda.synchronize()
+    _decode_check(w, inp, idx, o, lse, fp4=True)
 
 
 def test_hca_decode_1m_full():

@@ -558,7 +558,7 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
 // operations per head and entry), so the kernel streams: a wave keeps
 // kMxAhead tiles of codes (16 bytes per lane) and scale words (the key's four
 // scale bytes, read by all four block lanes) in flight.
-constexpr int kMxAhead = 7;
+constexpr int kMxAhead = 3;
 
 __global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
     const uint8_t* __restrict__ q, const uint8_t* __restrict__ q_scale,

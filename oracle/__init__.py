@@ -19,6 +19,7 @@ from .csa_oracle import (  # noqa: F401
     hca_attend,
     index_scores,
     mx4_dequantize,
+    mx4_quantize,
     pool,
     round_to_bf16,
     topk_select,

@@ -151,6 +151,38 @@ def e2m1_scaled_to_e4m3(code: int, e: int) -> Optional[int]:
     return None
 
 
+def mx4_quantize(x, block: int = 32):
+    """R8: MX FP4 encoding of the last dim of x (OCP Microscaling formats).
+
+    Per block of 32 elements: shared exponent e = floor(log2(amax)) - 2 (2 is
+    the largest E2M1 exponent), clamped to [-127, 127], -127 for an all-zero
+    block; scale byte e + 127.  Each element's magnitude |x| / 2**e goes to
+    the nearest E2M1 magnitude, a tie to the code with an even mantissa bit,
+    anything above 5 to 6 (saturation); the sign bit is x's own, so -0.0 and
+    values that round to zero from below keep it.  Element 2i is the low
+    nibble of byte i.  Returns (codes uint8 [..., D/2], scale bytes uint8
+    [..., D/32]).
+    """
+    xs = np.asarray(x, dtype=np.float64)
+    D = xs.shape[-1]
+    if D % block or D % 2:
+        raise ValueError(D)
+    xb = xs.reshape(xs.shape[:-1] + (D // block, block))
+    amax = np.abs(xb).max(axis=-1)
+    e = np.full(amax.shape, -127, dtype=np.int64)
+    nz = amax > 0
+    e[nz] = np.frexp(amax[nz])[1] - 1 - 2         # amax = f 2^p, f in [0.5, 1): floor(log2) = p - 1
+    e = np.clip(e, -127, 127)
+    a = np.abs(xb) * np.ldexp(1.0, -e)[..., None]
+    # magnitude index 0..7 over {0, .5, 1, 1.5, 2, 3, 4, 6}: strict '>' where the
+    # tie belongs to the lower (even) code, '>=' where it belongs to the upper
+    mag = ((a > 0.25).astype(np.uint8) + (a >= 0.75) + (a > 1.25) + (a >= 1.75) +
+           (a > 2.5) + (a >= 3.5) + (a > 5.0)).astype(np.uint8)
+    code = (mag | (np.signbit(xb).astype(np.uint8) << 3)).reshape(xs.shape)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    return packed, (e + 127).astype(np.uint8)
+
+
 def mx4_dequantize(codes, scale_bytes, block: int = 32) -> np.ndarray:
     """R8: packed E2M1 codes [..., D/2] and E8M0 scale bytes [..., D/block] -> float64 [..., D]."""
     sb = np.asarray(scale_bytes, dtype=np.uint8)

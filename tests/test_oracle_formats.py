@@ -167,3 +167,40 @@ def test_mx4_encoder_error_bound():
     assert np.all(np.abs(deq.reshape(64, 4, 32) - clamped) <= step * (1 + 1e-12))
     amax = np.abs(xs).max(axis=-1, keepdims=True)
     assert np.all((amax >= 4 * step) & (amax < 8 * step))
+
+
+def test_oracle_mx4_encoder_worked_examples(golden):
+    # the oracle's own MX encoder (used to check the GPU encoder) on the same
+    # hand-worked blocks as the input encoder
+    for row in golden("mx4_encoding.txt"):
+        a, b, c = (t.strip() for t in row.split("|"))
+        xs = [float(v) for v in a.split(",")]
+        x = np.zeros((1, 32))
+        x[0, : len(xs)] = xs
+        codes, sb = oracle.mx4_quantize(x)
+        assert int(sb[0, 0]) == int(b), row
+        got = oracle.mx4_dequantize(codes, sb)[0]
+        want = [float(v) for v in c.split(",")]
+        assert list(got[: len(want)]) == want, row
+
+
+def test_oracle_mx4_encoder_matches_input_encoder():
+    # two independent implementations of the same definition agree byte for
+    # byte on float32 data with blocks spread over many binades, exact ties
+    # and signed zeros
+    from csa_synth import mx4_quantize
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((40, 128)) * np.exp2(rng.integers(-60, 60, (40, 4))).repeat(32, 1))
+    x = x.astype(np.float32)
+    x[0, :32] = 0.0
+    x[0, :8] = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0]        # ties at scale 1 (amax 6)
+    x[1, :32] = 0.0
+    x[1, 3] = -0.0
+    x[2, :32] = -0.0
+    x[3, 32:64] = [-1e-30] * 31 + [4.0]                             # tiny values round to -0
+    c1, s1 = oracle.mx4_quantize(x)
+    c2, s2 = mx4_quantize(torch.from_numpy(x))
+    np.testing.assert_array_equal(c1, c2.numpy())
+    np.testing.assert_array_equal(s1, s2.numpy())
+    assert (c1[3, 16] & 0x0F) == 0x8                                # -1e-30 -> code -0
+    assert s1[0, 0] == 127 and list(c1[0, :4]) == [0x20, 0x42, 0x64, 0x76]   # 0,1 | 1,2 | 2,4 | 4,6

@@ -261,6 +261,18 @@ def other_workload(args):
                             q_scale=c["q_scale"], k_scale=c["ki_scale"], out=scores)
         ms = timed(step, args.steps, args.warmup)
         sms = timed(score_only, args.steps, args.warmup)
+        extra = {}
+        if mx:
+            # the MX encoder on the GPU: a whole bf16 indexer-key cache
+            # [B, N, 128] -> codes + scale bytes (HBM stream)
+            kb = torch.randn((w.B, w.N, w.D_I), device=dev).to(torch.bfloat16)
+            kcd = torch.empty((w.B, w.N, w.D_I // 2), dtype=torch.uint8, device=dev)
+            ksd = torch.empty((w.B, w.N, w.D_I // 32), dtype=torch.uint8, device=dev)
+            qms = timed(lambda i: csa.quantize_mx4(kb, codes=kcd, scales=ksd), 20, 3)
+            qbytes = w.B * w.N * (w.D_I * 2 + w.D_I // 2 + w.D_I // 32)
+            extra = {"quantize_kcache_ms": round(qms, 4),
+                     "quantize_kcache_gbs": round(qbytes / (qms * 1e-3) / 1e9, 1)}
+            del kb, kcd, ksd
         # per (row, entry): 64 B codes + the scales (16 B fp32 or 4 E8M0 bytes)
         # + 4 B score; per row the query codes, scales and head weights
         sc_b = 4 if mx else 16
@@ -279,7 +291,7 @@ def other_workload(args):
                              "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                              "algorithmic_bytes_per_launch": score_bytes,
-                             "avg_launch_ms": round(sms, 5)})
+                             "avg_launch_ms": round(sms, 5)}, **extra)
     elif w.name == "csa_prefill_chunk":
         inp = make_inputs(w, device=dev)
         cache = torch.empty((1, w.N, 384), dtype=torch.bfloat16, device=dev)

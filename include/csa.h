@@ -110,6 +110,26 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st,
                           hipStream_t stream);
 
 /*
+ * csa_quantize_mx4 - MX FP4 encoding of indexer vectors (§5: the indexer QK
+ * path in FP4; the input format of CSA_FP4_E2M1_E8M0).  Per block of 32
+ * consecutive elements of a row (OCP Microscaling encoding):
+ *   e = floor(log2(max |x|)) - 2, clamped to [-127, 127] (-127 for an
+ *   all-zero block); scale byte e + 127;
+ *   code = the E2M1 magnitude nearest to |x| / 2^e (a tie to the code with an
+ *   even mantissa bit; above 5 saturates to 6) with x's sign bit.
+ * x       [rows, D] dtype (CSA_F32 or CSA_BF16), row stride x_rs elements.
+ * codes   [rows, D/2] bytes, element 2i in the low nibble of byte i, row
+ *         stride c_rs bytes.
+ * scales  [rows, D/32] E8M0 bytes, row stride s_rs bytes.
+ * Requires rows >= 1, D a multiple of 32, x and codes 16-byte aligned with
+ * row strides of whole 16-byte units, c_rs >= D/2, s_rs >= D/32, x_rs >= D.
+ * Inputs must be finite.
+ */
+csa_status_t csa_quantize_mx4(const void* x, int64_t x_rs, csa_dtype_t dtype, int rows, int D,
+                              uint8_t* codes, int64_t c_rs, uint8_t* scales, int64_t s_rs,
+                              hipStream_t stream);
+
+/*
  * csa_index_score - Lightning Indexer scores (§2.1), every entry of the cache.
  *
  *   scores[b, t, j] = sum_h w_idx[b,t,h] * max(0, q_idx[b,t,h,:] . k_idx[b,j,:])

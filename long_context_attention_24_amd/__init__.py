@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "CsaError", "library_path", "load_library",
-    "compress", "index_score", "topk", "index_topk", "attend", "hca_attend",
+    "compress", "quantize_mx4", "index_score", "topk", "index_topk", "attend", "hca_attend",
     "index_topk_workspace_bytes", "attend_workspace_bytes", "hca_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
@@ -36,7 +36,7 @@ CSA_F32, CSA_BF16, CSA_FP4_E2M1, CSA_FP4_E2M1_E8M0 = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "csa_abi_version", "csa_status_string", "csa_last_error",
-    "csa_compress", "csa_index_score", "csa_topk", "csa_topk_workspace",
+    "csa_compress", "csa_quantize_mx4", "csa_index_score", "csa_topk", "csa_topk_workspace",
     "csa_index_topk", "csa_index_topk_workspace",
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
 )
@@ -60,6 +60,7 @@ _SIGS = {
     "csa_last_error": ([], ctypes.c_char_p),
     "csa_compress": ([_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                       _vp], _i32),
+    "csa_quantize_mx4": ([_vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64, _vp], _i32),
     "csa_index_score": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
                          _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "csa_topk": ([_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp],
@@ -156,6 +157,31 @@ def compress(x: torch.Tensor, logits: torch.Tensor, m: int,
         x.data_ptr(), x.stride(0), x.stride(1), logits.data_ptr(), logits.stride(0),
         out.data_ptr(), out.stride(0), out.stride(1), _dtype_code(x), B, n, C, m, _stream()))
     return out
+
+
+# ------------------------------------------------------------------ MX FP4 encoding
+def quantize_mx4(x: torch.Tensor, codes: Optional[torch.Tensor] = None,
+                 scales: Optional[torch.Tensor] = None):
+    """MX FP4 encoding of x [..., D] (fp32 or bf16, D a multiple of 32) on the GPU
+    -> (codes uint8 [..., D/2], E8M0 scale bytes uint8 [..., D/32])."""
+    _require_cuda(x, codes, scales)
+    D = x.shape[-1]
+    lead = tuple(x.shape[:-1])
+    x2 = x.reshape(-1, D)
+    if x2.stride(-1) != 1:
+        raise ValueError("x needs a contiguous last dim")
+    rows = x2.shape[0]
+    if codes is None:
+        codes = torch.empty(lead + (D // 2,), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty(lead + (D // 32,), dtype=torch.uint8, device=x.device)
+    c2, s2 = codes.reshape(rows, D // 2), scales.reshape(rows, D // 32)
+    if c2.stride(-1) != 1 or s2.stride(-1) != 1:
+        raise ValueError("codes and scales need a contiguous last dim")
+    _check(load_library().csa_quantize_mx4(
+        x2.data_ptr(), x2.stride(0), _dtype_code(x2), rows, D, c2.data_ptr(), c2.stride(0),
+        s2.data_ptr(), s2.stride(0), _stream()))
+    return codes, scales
 
 
 # ------------------------------------------------------------------ indexer

@@ -19,7 +19,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcsa.so")
 
 ARCH = "gfx950"
-SOURCES = ["compress.hip", "index_score.hip", "topk.hip", "attend.hip", "csa_api.cpp"]
+SOURCES = ["compress.hip", "quantize.hip", "index_score.hip", "topk.hip", "attend.hip",
+           "csa_api.cpp"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

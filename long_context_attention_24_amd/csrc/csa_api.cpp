@@ -150,6 +150,25 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st, const float
                     "compress launch");
 }
 
+csa_status_t csa_quantize_mx4(const void* x, int64_t x_rs, csa_dtype_t dtype, int rows, int D,
+                              uint8_t* codes, int64_t c_rs, uint8_t* scales, int64_t s_rs,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  CSA_REQUIRE(x && codes && scales, CSA_ERR_INVALID_ARGUMENT, "quantize mx4: NULL pointer");
+  CSA_REQUIRE(rows >= 1 && D >= 32 && D % 32 == 0, CSA_ERR_INVALID_ARGUMENT,
+              "quantize mx4: need rows >= 1 and D a positive multiple of 32");
+  CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+              "quantize mx4: dtype must be F32 or BF16");
+  const int64_t es = static_cast<int64_t>(esize(dtype));
+  CSA_REQUIRE(aligned16(x) && aligned16(codes) && (x_rs * es) % 16 == 0 && c_rs % 16 == 0,
+              CSA_ERR_INVALID_ARGUMENT, "quantize mx4: x and codes must be 16-byte aligned rows");
+  CSA_REQUIRE(x_rs >= D && c_rs >= D / 2 && s_rs >= D / 32, CSA_ERR_INVALID_ARGUMENT,
+              "quantize mx4: row strides smaller than the rows");
+  return hip_status(csa::launch_quantize_mx4(x, x_rs, dtype, rows, D, codes, c_rs, scales, s_rs,
+                                             stream),
+                    "quantize mx4 launch");
+}
+
 csa_status_t csa_index_score(const void* q_idx, const void* q_scale, const float* w_idx,
                              const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
                              int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,

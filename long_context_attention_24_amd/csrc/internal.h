@@ -15,6 +15,11 @@ hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const floa
                            void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dt, int B, int n,
                            int C, int m, hipStream_t s);
 
+// ---- quantize.hip
+hipError_t launch_quantize_mx4(const void* x, int64_t x_rs, csa_dtype_t dt, int rows, int D,
+                               uint8_t* codes, int64_t c_rs, uint8_t* scales, int64_t s_rs,
+                               hipStream_t s);
+
 // ---- index_score.hip
 struct ScoreArgs {
   const void* q;            // [B*Tq, H_I, D_I] (FP4: codes)

@@ -59,6 +59,25 @@ def test_compress_validation(lib):
     assert b"m=5000" in lib.csa_last_error()
 
 
+def test_quantize_mx4_validation(lib):
+    f = lib.csa_quantize_mx4
+    args = [A, 128, 1, 4, 128, A, 64, A, 4, None]          # bf16 [4, 128] -> codes, scales
+    bad = list(args); bad[0] = None
+    assert f(*bad) == INVALID
+    bad = list(args); bad[4] = 96 + 8                      # D not a multiple of 32
+    assert f(*bad) == INVALID
+    bad = list(args); bad[2] = 2                           # FP4 input
+    assert f(*bad) == UNSUPPORTED
+    bad = list(args); bad[6] = 56                          # code rows not 16-byte multiples
+    assert f(*bad) == INVALID
+    bad = list(args); bad[8] = 3                           # scale rows shorter than D/32
+    assert f(*bad) == INVALID
+    bad = list(args); bad[5] = A + 8                       # misaligned codes
+    assert f(*bad) == INVALID
+    bad = list(args); bad[3] = 0                           # no rows
+    assert f(*bad) == INVALID
+
+
 def test_index_score_validation(lib):
     f = lib.csa_index_score
     args = [A, None, A, A, None, 32768 * 128, 128, 0, 0, 1, A, A, 2, 1, 32768, 64, 128, 4, A, None]

@@ -307,6 +307,76 @@ def test_mx4_scores_ragged():
         check_topk(I[b, 0], s_ref, V, k)
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("rows,D", [(1, 32), (37, 128), (300, 256)])
+def test_quantize_mx4_bit_exact(dtype, rows, D):
+    """GPU MX FP4 encoder against the oracle's encoder, byte for byte: blocks
+    spread over many binades, exact ties on the E2M1 grid, all-zero and
+    signed-zero blocks, values rounding to -0, subnormal fp32 inputs, values
+    near the fp32 maximum and saturating ones."""
+    _say(f"quantize mx4 {dtype} rows={rows} D={D}")
+    g = torch.Generator().manual_seed(rows * 1000 + D)
+    x = torch.randn((rows, D), generator=g, dtype=torch.float64)
+    x *= torch.exp2(torch.randint(-40, 40, (rows, D // 32), generator=g).double()).repeat_interleave(32, 1)
+    x = x.to(torch.float32)
+    x[0, :32] = 0.0
+    x[0, :8] = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])      # ties, amax 6
+    if rows > 1:
+        x[1, :32] = -0.0
+    if rows > 2:
+        x[2, :32] = -1e-30
+        x[2, 5] = 4.0
+    if rows > 3:
+        x[3, :32] = 1e-40                                   # fp32 subnormals
+        x[3, 7] = -3e-39
+    if rows > 4:
+        x[4, :32] = 3.0e38
+        x[4, 1] = -2.5e38
+        x[4, 2] = 7.0                                       # tiny next to huge
+    if rows > 5:
+        x[5, :32] = 1.0
+        x[5, 0] = 7.9                                       # amax / 2^e near 8: saturates
+    if dtype == torch.bfloat16:
+        x = x.to(torch.bfloat16).to(torch.float32)          # exact bf16 values, finite
+        x = torch.nan_to_num(x, posinf=3.0e38, neginf=-3.0e38)
+    xd = x.to(DEV, dtype)
+    codes, scales = csa.quantize_mx4(xd)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.mx4_quantize(xd.float().cpu().numpy())
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
+def test_quantize_mx4_then_score():
+    """Indexer inputs encoded on the GPU feed the MX score path: scores and
+    selection against the oracle on the GPU's own codes."""
+    B, N_max, m, k = 2, 2048 + 77, 4, 256
+    _say("quantize mx4 on the GPU, then MX scores")
+    qi = _randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 95)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 96)
+    wi = _randn((B, 1, 64), 1 / 8, torch.float32, 97)
+    qc, qs = csa.quantize_mx4(qi)
+    kc, ks = csa.quantize_mx4(ki)
+    pos = [4 * N_max + 1, 4 * 1500]
+    q_pos = torch.tensor([[p] for p in pos], dtype=torch.int32, device=DEV)
+    ne = [N_max, 2000]
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qc, wi, kc, q_pos, n_ent, m, q_scale=qs, k_scale=ks)
+    idx = csa.index_topk(qc, wi, kc, q_pos, n_ent, m, k, q_scale=qs, k_scale=ks)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.mx4_quantize(np64(ki))
+    assert np.array_equal(kc.cpu().numpy(), c_ref) and np.array_equal(ks.cpu().numpy(), s_ref)
+    QI = oracle.mx4_dequantize(qc.cpu().numpy(), qs.cpu().numpy())
+    KI = oracle.mx4_dequantize(kc.cpu().numpy(), ks.cpu().numpy())
+    S, I, W = np64(scores), np64(idx), np64(wi)
+    for b in range(B):
+        V = oracle.visible_count(pos[b], m, ne[b])
+        s_ref_b = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
+        bound = score_bound(QI[b, 0], W[b, 0], KI[b, :V], 128, 64)
+        assert np.all(np.abs(S[b, 0, :V] - s_ref_b[:V]) <= bound), b
+        check_topk(I[b, 0], s_ref_b, V, k)
+
+
 def test_bounded_selection_ties_and_degenerate():
     """The bounded selection (chunk bounds + survivor list) on inputs far from
     Gaussian, where ties decide: all scores equal (more survivors than the

@@ -8,12 +8,13 @@
 // one workgroup per (query, split), then a combine kernel merges the split
 // partials with their running maxima.  Inside a split, tiles of 32 entries
 // go through MFMA with the entries as M and the heads as N:
-//     S^T[j, h] = K[j] . q[h]           (A = K rows, B = q^T, in registers)
+//     S^T[j, h] = K[j] . q[h]           (A = K rows from LDS, B = q^T in registers)
 //     O^T[d, h] += V^T[d, j] P^T[j, h]  (A = V^T from LDS, B = P^T)
 // With that orientation each lane owns one head column, so the online
 // softmax is lane-local (plus one exchange with lane l^32) and the softmax
 // probabilities leave the S accumulator already in the B-operand layout of
-// the PV product.  V rows are transposed into LDS (double buffered).
+// the PV product.  K and V rows are staged row-major in LDS (double
+// buffered); V^T is read with transposing loads.
 // Softmax runs in base 2 with the scale folded into log2(e).
 #include <float.h>
 

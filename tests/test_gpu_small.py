@@ -347,6 +347,51 @@ def test_quantize_mx4_bit_exact(dtype, rows, D):
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
 
 
+def _mx4_edge_blocks():
+    """32-element blocks at the edges of the MX FP4 encoding, as fp32 lists."""
+    ties = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    eps = 2.0 ** -10
+    grid = [4.0] + ties + [t + eps for t in ties] + [t - eps for t in ties] + \
+        [-t for t in ties] + [-0.0, 0.0, 6.0]
+    blocks = [[v * 2.0 ** k for v in grid] for k in (3, -20, 100, -120)]
+    pad = lambda b: b + [0.0] * (32 - len(b))
+    blocks += [
+        pad([7.99, 5.0, 5.01, -7.5, 6.0, -6.0, -5.0, 4.99]),            # saturation at 6
+        [0.0] * 32, [-0.0] * 32, [0.0, -0.0] * 16,
+        # e = -127 with non-zero codes: amax below 2^-125
+        pad([2.0 ** -126, 2.0 ** -127, 3 * 2.0 ** -128, -(2.0 ** -149), 2.0 ** -149,
+             1.5 * 2.0 ** -127, -(2.0 ** -128), 5 * 2.0 ** -130, 7 * 2.0 ** -131]),
+        pad([1.5 * 2.0 ** -125, 2.0 ** -125, -(2.0 ** -127), 2.0 ** -129, 1.25 * 2.0 ** -126]),
+        # e = -126: subnormal inputs next to the smallest normal scale
+        pad([2.0 ** -124, 2.0 ** -127, -(2.0 ** -127), 2.0 ** -128, 3 * 2.0 ** -128,
+             -(2.0 ** -149), 2.0 ** -126]),
+        pad([1.0, 1e-40, -1e-40, 2.0 ** -149, -(2.0 ** -149), -0.0]),     # subnormals, e = -2
+        pad([3.0e38, -3.0e38, 1.0e38, 2.0 ** 127, 2.0 ** 100, -(2.0 ** 126)]),
+    ]
+    if len(blocks) % 2:
+        blocks.append([0.0] * 32)
+    return blocks
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_mx4_edge_blocks(dtype):
+    """GPU MX FP4 encoder on hand-made edge blocks, byte for byte against the
+    oracle: ties and near-ties on the E2M1 grid in several binades,
+    saturation, signed zeros, the clamped exponent -127 with non-zero codes,
+    subnormal inputs under the smallest normal scale, values near the fp32
+    maximum."""
+    _say(f"quantize mx4 edge blocks {dtype}")
+    x = torch.tensor(_mx4_edge_blocks(), dtype=torch.float32).reshape(-1, 64)
+    assert torch.isfinite(x).all()
+    xd = x.to(DEV, dtype)
+    codes, scales = csa.quantize_mx4(xd)
+    torch.cuda.synchronize()
+    c_ref, s_ref = oracle.mx4_quantize(xd.float().cpu().numpy())
+    assert (s_ref == 0).any() and (c_ref[s_ref.repeat(16, 1) == 0] & 0x77).any()
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
+
+
 def test_quantize_mx4_then_score():
     """Indexer inputs encoded on the GPU feed the MX score path: scores and
     selection against the oracle on the GPU's own codes."""

@@ -43,8 +43,9 @@ __device__ __forceinline__ int visible_count(int q_pos, int m, int n_entries, in
 
 // Selection bound shared by the score and top-k kernels: every chunk of
 // kBoundChunk keys reports its c-th largest score, c being the smallest value
-// with floor(V / kBoundChunk) * c >= k for a row with V visible entries.  The
-// minimum of the reports is then at most the row's k-th largest score.
+// with floor(V / kBoundChunk) * c >= k for a row with V visible entries.  Any
+// value reached by ceil(k / c) of the reports is then at most the row's k-th
+// largest score (the minimum of the full chunks' reports always is).
 // Returns 0 (no bound) when that c would exceed kMaxBoundC.
 constexpr int kBoundChunk = 256;
 constexpr int kMaxBoundC = 16;
@@ -79,6 +80,10 @@ __device__ __forceinline__ float wave_min(float v) { return __ockl_wfred_min_f32
 __device__ __forceinline__ float wave_sum(float v) { return __ockl_wfred_add_f32(v); }
 extern "C" __device__ int32_t __ockl_wfred_max_i32(int32_t);
 __device__ __forceinline__ int wave_max_int(int v) { return __ockl_wfred_max_i32(v); }
+extern "C" __device__ uint32_t __ockl_wfred_min_u32(uint32_t);
+extern "C" __device__ uint32_t __ockl_wfred_max_u32(uint32_t);
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) { return __ockl_wfred_min_u32(v); }
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) { return __ockl_wfred_max_u32(v); }
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) { return __ockl_wfred_add_u32(v); }
 __device__ __forceinline__ int wave_sum_int(int v) {
   return static_cast<int>(__ockl_wfred_add_u32(static_cast<uint32_t>(v)));

@@ -69,8 +69,9 @@ __global__ __launch_bounds__(256) void score_generic_kernel(
 // kBoundChunk keys), the c-th largest with c = bound_c_row(V, k) for the row,
 // and the largest.  Every chunk that reports a finite c-th largest holds c
 // entries at or above it, and the floor(V / kBoundChunk) full chunks all do,
-// so the minimum report is at most the row's k-th largest score.  The top-k
-// kernels use that bound to drop most entries before selecting, and the
+// so the ceil(k / c)-th largest report is at most the row's k-th largest
+// score.  The top-k kernels use that bound to drop most entries before
+// selecting, and the
 // largest report as the top of the survivors' range.  A chunk with fewer
 // than c valid entries reports +inf as its c-th largest (-inf as its largest
 // when it has none); rows with no bound (c = 0) write nothing.

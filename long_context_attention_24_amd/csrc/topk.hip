@@ -20,9 +20,9 @@
 // Drivers.
 //   * Bounded (topk_bounded_kernel), used with the chunk reports the tuned
 //     score kernels leave: per 256-key chunk of a row its c-th largest and
-//     its largest score.  The minimum c-th largest over the row is at most
-//     the row's k-th largest (see bound_c_row), so entries below it can never
-//     be selected: one workgroup per row keeps the few survivors in LDS, in
+//     its largest score.  The ceil(k / c)-th largest of these reports is at
+//     most the row's k-th largest (see row_bound), so entries below it can
+//     never be selected: one workgroup per row keeps the few survivors in LDS, in
 //     index order, and selects there (select_sorted_list: the same histogram
 //     search over [bound, largest report], finished by pairwise ranks inside
 //     a small bin).
@@ -415,7 +415,8 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 
 // ============================================================ bounded path
 // topk_bounded_kernel: one 1024-thread workgroup per row.
-//   1. The row bound comes from the chunk reports (one block reduction).
+//   1. The row bound comes from the chunk reports (every wave on its own,
+//      the reports loaded next to the first score loads).
 //   2. The row is streamed in chunks of 32768 scores (eight coalesced 16-byte
 //      loads per thread, the next chunk's loads in flight while the current
 //      one is filtered); entries at or above the bound are appended to an LDS
@@ -625,37 +626,107 @@ __device__ __forceinline__ void load_round(const float* __restrict__ srow, int b
 }
 
 // Row bound and range top from the chunk reports, computed by every wave on
-// its own.  bound: the minimum c-th largest report when the reporting chunks
-// hold at least k entries at or above their reports, else -inf.  top: the
-// largest report (at least every score of the row).  c = 0: no reports were
-// written; both are -inf.  The reports are loaded before c is looked at (they
-// are in bounds either way), four per lane at a time.
-__device__ __forceinline__ float2 wave_row_bound(const float2* __restrict__ rep, int n_chunks,
-                                                 int c, int k) {
+// its own.  A report other than +inf certifies c entries of its chunk at or
+// above it (+inf: the chunk had fewer than c scored entries, or none).  With
+// r = ceil(k / c), any value that at least r reports reach is therefore
+// reached by at least k entries: a valid bound.  bound: the r-th largest
+// report, found from below by bisection over order-preserving keys (the
+// minimum when there are exactly r reports; -inf when fewer).  Taking the
+// r-th largest rather than the minimum keeps a few low chunks (for example
+// freshly pooled entries with smaller norms) from loosening the whole row's
+// bound.  top: the largest report top (at least every score of the row).
+// c = 0: no reports were written; both are -inf.  The reports are loaded
+// before c is looked at (they are in bounds either way).  n_chunks >= 1.
+constexpr int kRepPerLane = kMaxBoundedN / kBoundChunk / 64;   // reports per lane
+constexpr int kBoundSteps = 12;                                 // bisection steps
+
+__device__ __forceinline__ uint32_t f32_order_key(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float f32_from_order_key(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// The row's reports into registers, lane l holding reports l, l + 64, ...
+// (index clamped to the last report, n_chunks >= 1; row_bound masks the
+// slots past n_chunks): four slots always, the rest only for rows of more
+// than 256 reports, under one branch with no use inside, so that callers
+// can issue them next to their other early loads.
+constexpr int kRepFirst = 4;
+__device__ __forceinline__ void load_reports(const float2* __restrict__ rep, int n_chunks,
+                                             float2 (&t)[kRepPerLane]) {
   const int lane = threadIdx.x & 63;
-  float mn = FLT_MAX, mx = -FLT_MAX;
-  uint32_t cnt = 0;
-  for (int i0 = 0; i0 < n_chunks; i0 += 256) {
-    float2 t[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = i0 + 64 * u + lane;
-      t[u] = i < n_chunks ? rep[i] : make_float2(kPosInf, kNegInf);
-    }
+  for (int u = 0; u < kRepFirst; ++u) t[u] = rep[min(64 * u + lane, n_chunks - 1)];
+  if (n_chunks > 64 * kRepFirst) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (t[u].x != kPosInf) {
-        mn = fminf(mn, t[u].x);
-        ++cnt;
-      }
-      mx = fmaxf(mx, t[u].y);
-    }
+    for (int u = kRepFirst; u < kRepPerLane; ++u) t[u] = rep[min(64 * u + lane, n_chunks - 1)];
+  } else {
+#pragma unroll
+    for (int u = kRepFirst; u < kRepPerLane; ++u) t[u] = make_float2(kPosInf, kNegInf);
   }
+}
+
+// Order keys, count and extrema of the report slots [U0, U1) (key 0: none).
+template <int U0, int U1>
+__device__ __forceinline__ void report_keys(const float2 (&t)[kRepPerLane], int n_chunks,
+                                            uint32_t (&key)[kRepPerLane], uint32_t& kmin,
+                                            uint32_t& kmax, uint32_t& cnt, float& mx) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int u = U0; u < U1; ++u) {
+    const bool in = 64 * u + lane < n_chunks;
+    key[u] = in && t[u].x != kPosInf ? f32_order_key(t[u].x) : 0u;
+    if (key[u] != 0u) {
+      kmin = min(kmin, key[u]);
+      kmax = max(kmax, key[u]);
+      ++cnt;
+    }
+    if (in) mx = fmaxf(mx, t[u].y);
+  }
+}
+
+template <int U1>
+__device__ __forceinline__ uint32_t keys_at_least(const uint32_t (&key)[kRepPerLane], uint32_t mid) {
+  uint32_t n = 0;
+#pragma unroll
+  for (int u = 0; u < U1; ++u) n += key[u] >= mid ? 1u : 0u;
+  return n;
+}
+
+__device__ __forceinline__ float2 row_bound(const float2 (&t)[kRepPerLane], int n_chunks, int c,
+                                            int k) {
+  float mx = -FLT_MAX;
+  uint32_t kmin = 0xffffffffu, kmax = 0u, cnt = 0;
+  uint32_t key[kRepPerLane];
+  const bool wide = n_chunks > 64 * kRepFirst;   // uniform: slots past the first four in use
+  report_keys<0, kRepFirst>(t, n_chunks, key, kmin, kmax, cnt, mx);
+  if (wide) report_keys<kRepFirst, kRepPerLane>(t, n_chunks, key, kmin, kmax, cnt, mx);
   if (c <= 0) return make_float2(kNegInf, kNegInf);
-  mn = wave_min(mn);
   mx = wave_max(mx);
   cnt = wave_sum_u32(cnt);
-  return make_float2(static_cast<long long>(cnt) * c >= k ? mn : kNegInf, mx);
+  const uint32_t r = static_cast<uint32_t>((k + c - 1) / c);
+  if (cnt < r) return make_float2(kNegInf, mx);
+  // invariant: at least r keys >= lo, fewer than r keys >= hi
+  uint32_t lo = wave_min_u32(kmin);
+  if (cnt > r) {
+    uint64_t hi = static_cast<uint64_t>(wave_max_u32(kmax)) + 1;
+    for (int it = 0; it < kBoundSteps && hi - lo > 1; ++it) {
+      const uint32_t mid = static_cast<uint32_t>(lo + ((hi - lo) >> 1));
+      const uint32_t n = wide ? keys_at_least<kRepPerLane>(key, mid) : keys_at_least<kRepFirst>(key, mid);
+      if (wave_sum_u32(n) >= r) lo = mid;
+      else hi = mid;
+    }
+  }
+  return make_float2(f32_from_order_key(lo), mx);
+}
+
+__device__ __forceinline__ float2 wave_row_bound(const float2* __restrict__ rep, int n_chunks,
+                                                 int c, int k) {
+  float2 t[kRepPerLane];
+  load_reports(rep, n_chunks, t);
+  return row_bound(t, n_chunks, c, k);
 }
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t msk, uint32_t add) {
@@ -769,11 +840,14 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* srow = scores + row * s_rs;
   float x[kStreamSlots];
-  if (!REGIONS) load_round(srow, wave * kWaveSeg, N_max, x);
+  float2 rt[kRepPerLane];
+  if (!REGIONS) {
+    load_round(srow, wave * kWaveSeg, N_max, x);
+    load_reports(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks, rt);
+  }
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   float2 rb = make_float2(kNegInf, kNegInf);
-  if (!REGIONS)
-    rb = wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks, bound_c_row(V, k), k);
+  if (!REGIONS) rb = row_bound(rt, n_chunks, bound_c_row(V, k), k);
   g_sm.hist[2 * tid] = 0;
   g_sm.hist[2 * tid + 1] = 0;
   if (tid == 0) g_sm.cand_n = 0;

@@ -235,6 +235,42 @@ def test_tuned_prefill_scores_ragged():
             check_topk(I[b, t], s_ref, V, k)
 
 
+def _low_chunks(ki, chunks, scale):
+    """Scale the keys of the given 256-entry chunks down (their chunk reports
+    become the row's lowest, as for freshly pooled entries)."""
+    for c in chunks:
+        ki[:, 256 * c:256 * (c + 1)] *= scale
+    return ki
+
+
+@pytest.mark.parametrize("Tq,N_max,k,chunks", [
+    (72, 40000, 256, (3, 50, 151, 155)),        # streamed rows: c = 2, r = 128 of ~157 reports
+    (1, 100000, 1024, (0, 7, 200, 389)),        # filtered regions: c = 3, r = 342 of 391 reports
+])
+def test_topk_bound_rth_report(Tq, N_max, k, chunks):
+    """Selection with more chunk reports than the bound needs (the bound is
+    the r-th largest report, r = ceil(k / c), found by bisection), some
+    chunks' keys scaled down so that their reports are the row's lowest:
+    the selected sets against the oracle's exact top-k."""
+    B = 2 if Tq == 1 else 1
+    _say(f"top-k bound: Tq={Tq} N_max={N_max} k={k}")
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 41)
+    ki = _low_chunks(_randn((B, N_max, 128), 1 / math.sqrt(128), torch.float32, 42), chunks, 0.3)
+    ki = ki.to(torch.bfloat16)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 43)
+    pos = [[4 * N_max - 1 - 4 * 37 * t for t in range(Tq)] for _ in range(B)]
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor([N_max] * B, dtype=torch.int32, device=DEV)
+    idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, 4, k)
+    torch.cuda.synchronize()
+    I, QI, KI, W = np64(idx), np64(qi), np64(ki), np64(wi)
+    rows = [(b, t) for b in range(B) for t in range(0, Tq, 7)]
+    for b, t in rows:
+        V = oracle.visible_count(pos[b][t], 4, N_max)
+        s_ref = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+        check_topk(I[b, t], s_ref, V, k)
+
+
 def test_fp4_scores_ragged():
     """FP4 indexer (E2M1 codes, one fp32 scale per 32 elements) on ragged
     sizes: a partial last load unit and chunk, visible counts inside the first

@@ -638,7 +638,7 @@ __device__ __forceinline__ void load_round(const float* __restrict__ srow, int b
 // c = 0: no reports were written; both are -inf.  The reports are loaded
 // before c is looked at (they are in bounds either way).  n_chunks >= 1.
 constexpr int kRepPerLane = kMaxBoundedN / kBoundChunk / 64;   // reports per lane
-constexpr int kBoundSteps = 12;                                 // bisection steps
+constexpr int kBoundSteps = 10;                                 // bisection steps
 
 __device__ __forceinline__ uint32_t f32_order_key(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -650,22 +650,31 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t key) {
 
 // The row's reports into registers, lane l holding reports l, l + 64, ...
 // (index clamped to the last report, n_chunks >= 1; row_bound masks the
-// slots past n_chunks): four slots always, the rest only for rows of more
-// than 256 reports, under one branch with no use inside, so that callers
-// can issue them next to their other early loads.
-constexpr int kRepFirst = 4;
-__device__ __forceinline__ void load_reports(const float2* __restrict__ rep, int n_chunks,
-                                             float2 (&t)[kRepPerLane]) {
+// slots past n_chunks): slots 0-3 always, 4-7 for rows of more than 256
+// reports, 8-15 for more than 512, each group under one branch with no use
+// inside, so that callers can issue them next to their other early loads.
+constexpr int kRepA = 4, kRepB = 8;
+__device__ __forceinline__ int report_slots(int n_chunks) {
+  return n_chunks > 64 * kRepB ? kRepPerLane : n_chunks > 64 * kRepA ? kRepB : kRepA;
+}
+template <int U0, int U1>
+__device__ __forceinline__ void load_report_slots(const float2* __restrict__ rep, int n_chunks,
+                                                  float2 (&t)[kRepPerLane], bool in_use) {
   const int lane = threadIdx.x & 63;
+  if (in_use) {
 #pragma unroll
-  for (int u = 0; u < kRepFirst; ++u) t[u] = rep[min(64 * u + lane, n_chunks - 1)];
-  if (n_chunks > 64 * kRepFirst) {
-#pragma unroll
-    for (int u = kRepFirst; u < kRepPerLane; ++u) t[u] = rep[min(64 * u + lane, n_chunks - 1)];
+    for (int u = U0; u < U1; ++u) t[u] = rep[min(64 * u + lane, n_chunks - 1)];
   } else {
 #pragma unroll
-    for (int u = kRepFirst; u < kRepPerLane; ++u) t[u] = make_float2(kPosInf, kNegInf);
+    for (int u = U0; u < U1; ++u) t[u] = make_float2(kPosInf, kNegInf);
   }
+}
+__device__ __forceinline__ void load_reports(const float2* __restrict__ rep, int n_chunks,
+                                             float2 (&t)[kRepPerLane]) {
+  const int ns = report_slots(n_chunks);
+  load_report_slots<0, kRepA>(rep, n_chunks, t, true);
+  load_report_slots<kRepA, kRepB>(rep, n_chunks, t, ns > kRepA);
+  load_report_slots<kRepB, kRepPerLane>(rep, n_chunks, t, ns > kRepB);
 }
 
 // Order keys, count and extrema of the report slots [U0, U1) (key 0: none).
@@ -700,9 +709,10 @@ __device__ __forceinline__ float2 row_bound(const float2 (&t)[kRepPerLane], int 
   float mx = -FLT_MAX;
   uint32_t kmin = 0xffffffffu, kmax = 0u, cnt = 0;
   uint32_t key[kRepPerLane];
-  const bool wide = n_chunks > 64 * kRepFirst;   // uniform: slots past the first four in use
-  report_keys<0, kRepFirst>(t, n_chunks, key, kmin, kmax, cnt, mx);
-  if (wide) report_keys<kRepFirst, kRepPerLane>(t, n_chunks, key, kmin, kmax, cnt, mx);
+  const int ns = report_slots(n_chunks);         // uniform: slots in use
+  report_keys<0, kRepA>(t, n_chunks, key, kmin, kmax, cnt, mx);
+  if (ns > kRepA) report_keys<kRepA, kRepB>(t, n_chunks, key, kmin, kmax, cnt, mx);
+  if (ns > kRepB) report_keys<kRepB, kRepPerLane>(t, n_chunks, key, kmin, kmax, cnt, mx);
   if (c <= 0) return make_float2(kNegInf, kNegInf);
   mx = wave_max(mx);
   cnt = wave_sum_u32(cnt);
@@ -714,7 +724,9 @@ __device__ __forceinline__ float2 row_bound(const float2 (&t)[kRepPerLane], int 
     uint64_t hi = static_cast<uint64_t>(wave_max_u32(kmax)) + 1;
     for (int it = 0; it < kBoundSteps && hi - lo > 1; ++it) {
       const uint32_t mid = static_cast<uint32_t>(lo + ((hi - lo) >> 1));
-      const uint32_t n = wide ? keys_at_least<kRepPerLane>(key, mid) : keys_at_least<kRepFirst>(key, mid);
+      const uint32_t n = ns > kRepB   ? keys_at_least<kRepPerLane>(key, mid)
+                         : ns > kRepA ? keys_at_least<kRepB>(key, mid)
+                                      : keys_at_least<kRepA>(key, mid);
       if (wave_sum_u32(n) >= r) lo = mid;
       else hi = mid;
     }

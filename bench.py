@@ -13,8 +13,8 @@ from HBM.
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (only 1),
 --graph (also time the step captured in a HIP graph), --no-cpu-baseline,
 --workload NAME (another workload's own line instead of the headline one:
-hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4 or csa_prefill_chunk; see
-other_workload),
+hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4 or csa_prefill_chunk, the
+last also timing the step with bf16 index scores; see other_workload),
 --score-only (launch only the indexer score kernel, for hardware-counter
 runs), --copy-calibration (run only a plain device copy of known size, for
 scaling the FETCH_SIZE / WRITE_SIZE counters).
@@ -316,9 +316,18 @@ def other_workload(args):
         def score_only(i):
             csa.index_score(inp["q_idx"], inp["w_idx"], ki, inp["q_pos"], inp["n_entries"], w.m,
                             out=scores)
+        ws_topk16 = torch.empty(csa.index_topk_bf16_workspace_bytes(1, w.Tq, w.N, w.k),
+                                dtype=torch.uint8, device=dev)
+
+        def step_bf16_scores(i):   # the same step with the score matrix held in bf16
+            csa.compress(inp["raw"], inp["logits"], w.m, out=cache[:, w.n_cache:])
+            csa.index_topk_bf16(inp["q_idx"], inp["w_idx"], ki, inp["q_pos"], inp["n_entries"],
+                                w.m, w.k, workspace=ws_topk16, out=idx)
+            csa.attend(inp["q"], kc, vc, idx, inp["n_entries"], workspace=ws_attn, out=out)
         steps, warm = max(1, min(args.steps, 10)), max(1, min(args.warmup, 2))
         ms = timed(step, steps, warm)
         sms = timed(score_only, steps, warm)
+        ms16 = timed(step_bf16_scores, steps, warm)
         # visible (query, entry) pairs x 64 heads x 128 dims x 2
         vis = sum(w.n_cache + (i + 1) // w.m for i in range(w.Tq))
         flop = vis * w.H_I * w.D_I * 2
@@ -331,7 +340,9 @@ def other_workload(args):
                    roofline={"kernel": "score_prefill_bf16_h64d128_kernel", "bound": "mfma",
                              "achieved": round(tfs, 1), "peak": 2500.0, "unit": "TFLOP/s",
                              "frac": round(tfs / 2500.0, 4), "traffic": None,
-                             "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(sms, 4)})
+                             "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(sms, 4)},
+                   bf16_index_scores={"ms_per_step": round(ms16, 5),
+                                      "tokens_per_s": round(w.Tq / (ms16 * 1e-3), 1)})
         base["steps"], base["warmup"] = steps, warm
     else:
         print(f"unknown workload {w.name}", file=sys.stderr)

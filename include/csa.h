@@ -194,6 +194,30 @@ csa_status_t csa_index_topk(const void* q_idx, const void* q_scale, const float*
 csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes);
 
 /*
+ * csa_index_topk_bf16 - csa_index_topk with the score matrix held in BF16
+ * ("DeepSeek-V4 点评总结", 主要观点, the FP4 quantisation-aware-training
+ * point: index scores stored in BF16 instead of FP32, reported as 2x faster
+ * inference at 99.7 % KV recall).
+ *
+ *   Each fp32 score is rounded to BF16 (nearest, ties to even) when it is
+ *   stored; the selection is the exact top-k of the rounded scores (ties to
+ *   the lower index, ascending index order, -1 padding), so it can differ
+ *   from the fp32 selection only where rounding merges or reorders scores.
+ * Arguments as in csa_index_topk for the BF16 64 x 128 indexer (q_idx
+ * [B, Tq, 64, 128], k_idx [B, N_max, 128] with strides (k_sb, k_sn)); no
+ * scale arguments.  topk_score returns the rounded scores (fp32) or is NULL.
+ * Workspace: csa_index_topk_bf16_workspace bytes, 16-byte aligned.
+ * Supported: N_max <= 262144 and k as for csa_topk; else CSA_ERR_UNSUPPORTED.
+ */
+csa_status_t csa_index_topk_bf16(const void* q_idx, const float* w_idx, const void* k_idx,
+                                 int64_t k_sb, int64_t k_sn,
+                                 const int32_t* q_pos, const int32_t* n_entries,
+                                 int B, int Tq, int N_max, int m, int k,
+                                 int32_t* topk_idx, float* topk_score,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t csa_index_topk_bf16_workspace(int B, int Tq, int N_max, int k, size_t* bytes);
+
+/*
  * csa_attend - core attention over the selected entries only (§2.1).
  *
  *   o[b,t,h,:] = sum_{j in S} softmax_j(scale * q[b,t,h,:] . K[b,j,:]) V[b,j,:]

@@ -24,8 +24,9 @@ import torch
 
 __all__ = [
     "CsaError", "library_path", "load_library",
-    "compress", "quantize_mx4", "index_score", "topk", "index_topk", "attend", "hca_attend",
-    "index_topk_workspace_bytes", "attend_workspace_bytes", "hca_workspace_bytes",
+    "compress", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
+    "attend", "hca_attend", "index_topk_workspace_bytes", "index_topk_bf16_workspace_bytes",
+    "attend_workspace_bytes", "hca_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -38,6 +39,7 @@ EXPORTED_SYMBOLS = (
     "csa_abi_version", "csa_status_string", "csa_last_error",
     "csa_compress", "csa_quantize_mx4", "csa_index_score", "csa_topk", "csa_topk_workspace",
     "csa_index_topk", "csa_index_topk_workspace",
+    "csa_index_topk_bf16", "csa_index_topk_bf16_workspace",
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
 )
 
@@ -69,6 +71,9 @@ _SIGS = {
     "csa_index_topk": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp], _i32),
     "csa_index_topk_workspace": ([_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "csa_index_topk_bf16": ([_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                             _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa_index_topk_bf16_workspace": ([_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
     "csa_attend": ([_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "csa_attend_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
@@ -260,6 +265,40 @@ def index_topk(q_idx, w_idx, k_idx, q_pos, n_entries, m: int, k: int, q_scale=No
         q_idx.data_ptr(), _ptr(q_scale), w_idx.data_ptr(), k_idx.data_ptr(), _ptr(k_scale),
         k_idx.stride(0), k_idx.stride(1), ks_sb, ks_sn, dt, q_pos.data_ptr(), n_entries.data_ptr(),
         B, Tq, N_max, H_I, D_I, m, k, idx.data_ptr(), _ptr(val), _ptr(ws), ws_bytes, _stream()))
+    return (idx, val) if with_scores else idx
+
+
+def index_topk_bf16_workspace_bytes(B: int, Tq: int, N_max: int, k: int) -> int:
+    need = ctypes.c_size_t(0)
+    _check(load_library().csa_index_topk_bf16_workspace(B, Tq, N_max, k, ctypes.byref(need)))
+    return need.value
+
+
+def index_topk_bf16(q_idx, w_idx, k_idx, q_pos, n_entries, m: int, k: int,
+                    with_scores: bool = False, workspace: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None):
+    """index_topk for the bf16 64 x 128 indexer with the score matrix stored in
+    bf16 (each score rounded to nearest even); the selection is the exact
+    top-k of the rounded scores -> idx [B, Tq, k] int32 (+ their rounded scores)."""
+    _require_cuda(q_idx, w_idx, k_idx, q_pos, n_entries)
+    if q_idx.dtype != torch.bfloat16 or k_idx.dtype != torch.bfloat16:
+        raise ValueError("index_topk_bf16: q_idx and k_idx must be bfloat16")
+    if q_idx.dim() != 4 or tuple(q_idx.shape[2:]) != (64, 128) or not q_idx.is_contiguous():
+        raise ValueError("index_topk_bf16: q_idx must be a contiguous [B, Tq, 64, 128] tensor")
+    if k_idx.dim() != 3 or k_idx.shape[2] != 128 or k_idx.stride(2) != 1:
+        raise ValueError("index_topk_bf16: k_idx must be [B, N_max, 128] with a contiguous last dim")
+    if w_idx.dtype != torch.float32 or not w_idx.is_contiguous():
+        raise ValueError("index_topk_bf16: w_idx must be contiguous float32 [B, Tq, 64]")
+    B, Tq = q_idx.shape[0], q_idx.shape[1]
+    N_max = k_idx.shape[1]
+    need = index_topk_bf16_workspace_bytes(B, Tq, N_max, k)
+    ws, ws_bytes = _workspace(need, k_idx.device, workspace)
+    idx = out if out is not None else torch.empty((B, Tq, k), dtype=torch.int32, device=k_idx.device)
+    val = torch.empty((B, Tq, k), dtype=torch.float32, device=k_idx.device) if with_scores else None
+    _check(load_library().csa_index_topk_bf16(
+        q_idx.data_ptr(), w_idx.data_ptr(), k_idx.data_ptr(), k_idx.stride(0), k_idx.stride(1),
+        q_pos.data_ptr(), n_entries.data_ptr(), B, Tq, N_max, m, k, idx.data_ptr(), _ptr(val),
+        _ptr(ws), ws_bytes, _stream()))
     return (idx, val) if with_scores else idx
 
 

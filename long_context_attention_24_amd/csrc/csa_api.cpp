@@ -98,10 +98,10 @@ int bound_k(csa_dtype_t dt, int H_I, int D_I, int N_max, int k) {
 }
 
 // scores | chunk bounds | selection workspace
-size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws) {
+size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws, size_t score_bytes) {
   const size_t rows = static_cast<size_t>(B) * Tq;
   const size_t bws = csa::topk_bounded_workspace_bytes(static_cast<int>(rows), N_max);
-  return round_up(rows * score_row_stride(N_max) * sizeof(float)) +
+  return round_up(rows * score_row_stride(N_max) * score_bytes) +
          round_up(rows * bound_chunks(N_max) * sizeof(float2)) +
          round_up(topk_ws > bws ? topk_ws : bws);
 }
@@ -182,7 +182,7 @@ csa_status_t csa_index_score(const void* q_idx, const void* q_scale, const float
   CSA_REQUIRE(scores, CSA_ERR_INVALID_ARGUMENT, "index score: NULL scores");
   csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
                    q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, N_max,
-                   nullptr, 0, 0};
+                   nullptr, 0, 0, false};
   return hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
 }
 
@@ -213,8 +213,8 @@ csa_status_t csa_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
   const size_t need = csa::topk_workspace_bytes(B * Tq, N_max, k);
   CSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), CSA_ERR_WORKSPACE_TOO_SMALL,
               "topk: workspace %zu < %zu bytes", ws_bytes, need);
-  return hip_status(csa::launch_topk(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, nullptr,
-                                     0, topk_idx, topk_score, ws, stream),
+  return hip_status(csa::launch_topk(scores, false, s_rs, q_pos, n_entries, B, Tq, N_max, m, k,
+                                     nullptr, 0, topk_idx, topk_score, ws, stream),
                     "topk launch");
 }
 
@@ -223,10 +223,69 @@ csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* b
   size_t t = 0;
   csa_status_t st = csa_topk_workspace(B, Tq, N_max, k, &t);
   if (st != CSA_OK) return st;
-  *bytes = index_topk_ws_bytes(B, Tq, N_max, t);
+  *bytes = index_topk_ws_bytes(B, Tq, N_max, t, sizeof(float));
   return CSA_OK;
 }
 
+csa_status_t csa_index_topk_bf16_workspace(int B, int Tq, int N_max, int k, size_t* bytes) {
+  g_err[0] = 0;
+  CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "index topk bf16 workspace: NULL result");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && N_max >= 1 && k >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "index topk bf16 workspace: sizes must be >= 1");
+  CSA_REQUIRE(csa::topk_bounded_ok(N_max) && csa::topk_supported(N_max, k), CSA_ERR_UNSUPPORTED,
+              "index topk bf16: N_max=%d with k=%d not supported", N_max, k);
+  *bytes = index_topk_ws_bytes(B, Tq, N_max, 0, sizeof(uint16_t));
+  return CSA_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared body of csa_index_topk (fp32 score rows) and csa_index_topk_bf16.
+csa_status_t index_topk_impl(const void* q_idx, const void* q_scale, const float* w_idx,
+                             const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
+                             int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
+                             const int32_t* q_pos, const int32_t* n_entries, int B, int Tq,
+                             int N_max, int H_I, int D_I, int m, int k, int32_t* topk_idx,
+                             float* topk_score, void* ws, size_t ws_bytes, hipStream_t stream,
+                             bool score16) {
+  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
+                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(topk_idx && k >= 1, CSA_ERR_INVALID_ARGUMENT, "index topk: bad output / k");
+  if (score16)
+    CSA_REQUIRE(csa::score16_supported(idx_dtype, H_I, D_I), CSA_ERR_UNSUPPORTED,
+                "index topk bf16: needs the BF16 64 x 128 indexer (dtype %d, H_I=%d, D_I=%d)",
+                static_cast<int>(idx_dtype), H_I, D_I);
+  size_t need = 0;
+  st = score16 ? csa_index_topk_bf16_workspace(B, Tq, N_max, k, &need)
+               : csa_index_topk_workspace(B, Tq, N_max, k, &need);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
+              "index topk: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
+  const int64_t srs = score_row_stride(N_max);
+  const size_t rows = static_cast<size_t>(B) * Tq;
+  char* base = static_cast<char*>(ws);
+  void* scores = base;
+  base += round_up(rows * srs * (score16 ? sizeof(uint16_t) : sizeof(float)));
+  const int n_chunks = bound_chunks(N_max);
+  const int bk = bound_k(idx_dtype, H_I, D_I, N_max, k);
+  float2* bounds = bk > 0 ? reinterpret_cast<float2*>(base) : nullptr;
+  base += round_up(rows * n_chunks * sizeof(float2));
+  csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs,
+                   bounds, n_chunks, bk, score16};
+  st = hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
+  if (st != CSA_OK) return st;
+  return hip_status(csa::launch_topk(scores, score16, srs, q_pos, n_entries, B, Tq, N_max, m, k,
+                                     bounds, n_chunks, topk_idx, topk_score, base, stream),
+                    "topk launch");
+}
+
+}  // namespace
+
+extern "C" {
 
 csa_status_t csa_index_topk(const void* q_idx, const void* q_scale, const float* w_idx,
                             const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
@@ -235,32 +294,20 @@ csa_status_t csa_index_topk(const void* q_idx, const void* q_scale, const float*
                             int N_max, int H_I, int D_I, int m, int k, int32_t* topk_idx,
                             float* topk_score, void* ws, size_t ws_bytes, hipStream_t stream) {
   g_err[0] = 0;
-  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
-                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
-  if (st != CSA_OK) return st;
-  CSA_REQUIRE(topk_idx && k >= 1, CSA_ERR_INVALID_ARGUMENT, "index topk: bad output / k");
-  size_t need = 0;
-  st = csa_index_topk_workspace(B, Tq, N_max, k, &need);
-  if (st != CSA_OK) return st;
-  CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
-              "index topk: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
-  const int64_t srs = score_row_stride(N_max);
-  const size_t rows = static_cast<size_t>(B) * Tq;
-  char* base = static_cast<char*>(ws);
-  float* scores = reinterpret_cast<float*>(base);
-  base += round_up(rows * srs * sizeof(float));
-  const int n_chunks = bound_chunks(N_max);
-  const int bk = bound_k(idx_dtype, H_I, D_I, N_max, k);
-  float2* bounds = bk > 0 ? reinterpret_cast<float2*>(base) : nullptr;
-  base += round_up(rows * n_chunks * sizeof(float2));
-  csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
-                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs,
-                   bounds, n_chunks, bk};
-  st = hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
-  if (st != CSA_OK) return st;
-  return hip_status(csa::launch_topk(scores, srs, q_pos, n_entries, B, Tq, N_max, m, k, bounds,
-                                     n_chunks, topk_idx, topk_score, base, stream),
-                    "topk launch");
+  return index_topk_impl(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                         idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, k, topk_idx,
+                         topk_score, ws, ws_bytes, stream, false);
+}
+
+csa_status_t csa_index_topk_bf16(const void* q_idx, const float* w_idx, const void* k_idx,
+                                 int64_t k_sb, int64_t k_sn, const int32_t* q_pos,
+                                 const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
+                                 int32_t* topk_idx, float* topk_score, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  g_err[0] = 0;
+  return index_topk_impl(q_idx, nullptr, w_idx, k_idx, nullptr, k_sb, k_sn, 0, 0, CSA_BF16, q_pos,
+                         n_entries, B, Tq, N_max, 64, 128, m, k, topk_idx, topk_score, ws,
+                         ws_bytes, stream, true);
 }
 
 static csa_status_t check_attend(const void* q, const void* k_c, const void* v_c, int64_t kv_sb,

@@ -56,6 +56,28 @@ __device__ __forceinline__ int bound_c_row(int V, int k) {
   return c <= kMaxBoundC ? c : 0;
 }
 
+// Score storage: fp32, or bf16 for the 16-bit score path (round to nearest,
+// ties to even; +-inf stay infinite, scores are never NaN).  Rounding is
+// monotone, so the c-th largest of the rounded scores is the rounded c-th
+// largest and a chunk report rounds like the scores it summarises.
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_round(float x) {
+  return __uint_as_float(static_cast<uint32_t>(bf16_rne_bits(x)) << 16);
+}
+__device__ __forceinline__ void put_score(float* p, float v) { *p = v; }
+__device__ __forceinline__ void put_score(uint16_t* p, float v) { *p = bf16_rne_bits(v); }
+__device__ __forceinline__ float get_score(const float* p) { return *p; }
+__device__ __forceinline__ float get_score(const uint16_t* p) {
+  return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+}
+template <typename S>
+__device__ __forceinline__ float2 stored_report(float2 r) {
+  return sizeof(S) == 2 ? make_float2(bf16_round(r.x), bf16_round(r.y)) : r;
+}
+
 // max(x, 0) as one integer max on the bit pattern: negative values (sign bit
 // set, so negative as integers) and -0.0 become +0.0, the rest pass through.
 // A float max would first canonicalise x, costing a second instruction.

@@ -128,10 +128,11 @@ static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 // output.
 constexpr int kKeyPitch = 136;                    // bf16 per key row in LDS (256 B + 16 B)
 
+template <typename SO>
 __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, SO* __restrict__ scores,
     int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
   __shared__ __attribute__((aligned(16))) uint16_t key_lds[kWavesPerWg][32 * kKeyPitch];
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[64 * kKeyPitch];
@@ -178,8 +179,8 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   }
   __syncthreads();                                // the only barrier: early exits follow
   if (key0 >= N_max) return;
-  float* srow = scores + row * s_rs;
-  for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
+  SO* srow = scores + row * s_rs;
+  for (int j = max(key0, V) + lane; j < key_end; j += 64) put_score(&srow[j], kNegInf);
   if (key0 >= vis_end) {
     if (chunk_rep != nullptr && lane == 0)
       chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     const float tot = sum + other;     // commutative: both halves get the same bits
     const int j = key0 + 32 * t + jl;
     const bool ok = j < vis_end;
-    if (g == 0 && ok) srow[j] = tot;
+    if (g == 0 && ok) put_score(&srow[j], tot);
     sc[t] = ok ? tot : kNegInf;
   };
   // Iteration t: loads of tile t+2, tile t through LDS into the MFMAs, and
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   const int thr_c = bound_c_row(V, bound_k);
   if (chunk_rep != nullptr && thr_c > 0) {
     const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, thr_c);
-    if (lane == 0) chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = rep;
+    if (lane == 0) chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = stored_report<SO>(rep);
   }
 }
 
@@ -276,10 +277,11 @@ constexpr int kPfThreads = 64 * kPfQueries;
 constexpr int kPfKeys = 2048;
 constexpr int kPfStages = 4;
 
+template <typename SO>
 __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, float* __restrict__ scores,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, SO* __restrict__ scores,
     int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
@@ -311,8 +313,8 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
 
   // -inf for every key this workgroup covers but does not compute
   if (rowq >= 0) {
-    float* srow = scores + rowq * s_rs;
-    for (int j = j0 + 32 * ntiles + lane; j < j1; j += 64) srow[j] = kNegInf;
+    SO* srow = scores + rowq * s_rs;
+    for (int j = j0 + 32 * ntiles + lane; j < j1; j += 64) put_score(&srow[j], kNegInf);
   }
   const uint16_t* kb = k + b * k_sb + 8 * (tid & 15);
   const int jcap = max(vmax, 1) - 1;              // clamp rows to visible ones (in bounds)
@@ -406,14 +408,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
         const float tot = sum + __shfl_xor(sum, 32, 64);
         const int j = j0 + 32 * tt + jl;
         const bool ok = j < vq;
-        if (g == 0 && rowq >= 0 && j < j1) scores[rowq * s_rs + j] = ok ? tot : kNegInf;
+        if (g == 0 && rowq >= 0 && j < j1) put_score(&scores[rowq * s_rs + j], ok ? tot : kNegInf);
         sc[u] = ok ? tot : kNegInf;
         // after each 256-key chunk (or the last computed tile): its bound
         if (cq > 0 && (u == kTilesPerWave - 1 || tt == ntiles - 1)) {
 #pragma unroll
           for (int v = u + 1; v < kTilesPerWave; ++v) sc[v] = kNegInf;
           const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, cq);
-          if (lane == 0) chunk_rep[static_cast<int64_t>(rowq) * n_chunks + (j0 + 32 * tt) / kBoundChunk] = rep;
+          if (lane == 0)
+            chunk_rep[static_cast<int64_t>(rowq) * n_chunks + (j0 + 32 * tt) / kBoundChunk] = stored_report<SO>(rep);
         }
       }
     }
@@ -658,7 +661,8 @@ void launch_generic(const ScoreArgs& a, hipStream_t s) {
   const dim3 grid((a.N_max + 255) / 256, a.B * a.Tq);
   hipLaunchKernelGGL((score_generic_kernel<T, D>), grid, dim3(256), 0, s,
                      static_cast<const T*>(a.q), a.w, static_cast<const T*>(a.k), a.k_sb, a.k_sn,
-                     a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.H, a.scores, a.s_rs);
+                     a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.H, static_cast<float*>(a.scores),
+                     a.s_rs);
 }
 
 }  // namespace
@@ -669,6 +673,8 @@ bool score_tuned(csa_dtype_t dt, int H, int D) {
 }
 
 int score_chunk_keys() { return kKeysPerWave; }
+
+bool score16_supported(csa_dtype_t dt, int H, int D) { return dt == CSA_BF16 && H == 64 && D == 128; }
 
 bool score_supported(csa_dtype_t dt, int H, int D) {
   if (dt == CSA_FP4_E2M1 || dt == CSA_FP4_E2M1_E8M0) return H == 64 && D == 128;
@@ -683,29 +689,45 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
                        static_cast<const uint8_t*>(a.q), static_cast<const float*>(a.q_scale),
                        a.w, static_cast<const uint8_t*>(a.k),
                        static_cast<const float*>(a.k_scale), a.k_sb, a.k_sn, a.ks_sb, a.ks_sn,
-                       a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs, a.chunk_rep,
-                       a.n_chunks, a.bound_k);
+                       a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, static_cast<float*>(a.scores),
+                       a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
   } else if (dt == CSA_FP4_E2M1_E8M0) {
     const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
     hipLaunchKernelGGL(score_mx4_h64d128_kernel, grid, dim3(256), 0, s,
                        static_cast<const uint8_t*>(a.q), static_cast<const uint8_t*>(a.q_scale),
                        a.w, static_cast<const uint8_t*>(a.k),
                        static_cast<const uint8_t*>(a.k_scale), a.k_sb, a.k_sn, a.ks_sb, a.ks_sn,
-                       a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores, a.s_rs, a.chunk_rep,
-                       a.n_chunks, a.bound_k);
+                       a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, static_cast<float*>(a.scores),
+                       a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128 && a.Tq >= kPfQueries) {
     const int groups = (a.Tq + kPfQueries - 1) / kPfQueries;
     const dim3 grid((a.N_max + kPfKeys - 1) / kPfKeys, a.B * groups);
-    hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel, grid, dim3(kPfThreads), 0, s,
-                       static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
-                       a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
-                       a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
+    if (a.score16)
+      hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel<uint16_t>, grid, dim3(kPfThreads), 0, s,
+                         static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
+                         a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m,
+                         static_cast<uint16_t*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
+                         a.bound_k);
+    else
+      hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel<float>, grid, dim3(kPfThreads), 0, s,
+                         static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
+                         a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m,
+                         static_cast<float*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
+                         a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
     const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
-    hipLaunchKernelGGL(score_bf16_h64d128_kernel, grid, dim3(256), 0, s,
-                       static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
-                       a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m, a.scores,
-                       a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
+    if (a.score16)
+      hipLaunchKernelGGL(score_bf16_h64d128_kernel<uint16_t>, grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
+                         a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m,
+                         static_cast<uint16_t*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
+                         a.bound_k);
+    else
+      hipLaunchKernelGGL(score_bf16_h64d128_kernel<float>, grid, dim3(256), 0, s,
+                         static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
+                         a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m,
+                         static_cast<float*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
+                         a.bound_k);
   } else if (dt == CSA_BF16) {
     if (a.D == 32) launch_generic<uint16_t, 32>(a, s);
     else if (a.D == 64) launch_generic<uint16_t, 64>(a, s);

@@ -31,14 +31,16 @@ struct ScoreArgs {
   const int32_t* q_pos;
   const int32_t* n_entries;
   int B, Tq, N_max, H, D, m;
-  float* scores;            // [B*Tq, s_rs]
+  void* scores;             // [B*Tq, s_rs] fp32, or bf16 when score16
   int64_t s_rs;             // row stride of scores (elements)
   float2* chunk_rep;        // [B*Tq, n_chunks] (c-th largest, largest) per chunk, or NULL
   int n_chunks, bound_k;    // bound_k: the k the bounds serve (0: none)
+  bool score16;             // bf16 scores (and bf16-rounded reports); score16_supported only
 };
 hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s);
 bool score_supported(csa_dtype_t dt, int H, int D);
 bool score_tuned(csa_dtype_t dt, int H, int D);   // writes chunk bounds
+bool score16_supported(csa_dtype_t dt, int H, int D);
 int score_chunk_keys();                            // keys per bound chunk
 
 // ---- topk.hip
@@ -52,7 +54,8 @@ size_t topk_workspace_bytes(int rows, int N_max, int k);
 bool topk_bounded_ok(int N_max);
 size_t topk_bounded_workspace_bytes(int rows, int N_max);
 bool topk_supported(int N_max, int k);
-hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
+// score16: bf16 score rows (chunk_rep required and topk_bounded_ok(N_max)).
+hipError_t launch_topk(const void* scores, bool score16, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
                        const float2* chunk_rep, int n_chunks, int32_t* idx,
                        float* out_scores, void* ws, hipStream_t s);

@@ -293,14 +293,15 @@ struct SplitRun {
 };
 
 // Global-memory run, linear, n values (-0.0 read as +0.0).
+template <typename S>
 struct GlobalRun {
   static constexpr int kUnroll = 1;
-  const float* __restrict__ v;
+  const S* __restrict__ v;
   int n, r;
   __device__ __forceinline__ int len() const { return r; }
   __device__ __forceinline__ float get(int i) const {
     const int q = threadIdx.x * r + i;
-    return q < n ? v[q] + 0.0f : kNegInf;
+    return q < n ? get_score(v + q) + 0.0f : kNegInf;
   }
 };
 
@@ -610,17 +611,18 @@ __device__ __forceinline__ void select_sorted_list(const lds_u32x2* lp, int n, f
 
 // One round of a wave's contiguous segment: lane l holds entries
 // base + 64 s + l, s < kStreamSlots (-inf at or past N_max).
-__device__ __forceinline__ void load_round(const float* __restrict__ srow, int base, int N_max,
+template <typename S>
+__device__ __forceinline__ void load_round(const S* __restrict__ srow, int base, int N_max,
                                            float (&x)[kStreamSlots]) {
   const int lane = threadIdx.x & 63;
   if (base + kWaveSeg <= N_max) {
 #pragma unroll
-    for (int s = 0; s < kStreamSlots; ++s) x[s] = srow[base + 64 * s + lane];
+    for (int s = 0; s < kStreamSlots; ++s) x[s] = get_score(srow + base + 64 * s + lane);
   } else {
 #pragma unroll
     for (int s = 0; s < kStreamSlots; ++s) {
       const int q = base + 64 * s + lane;
-      x[s] = q < N_max ? srow[q] : kNegInf;
+      x[s] = q < N_max ? get_score(srow + q) : kNegInf;
     }
   }
 }
@@ -760,8 +762,19 @@ constexpr int kFiltSeg = 4096;
 constexpr int kRegion = 1024;
 static_assert(kMaxBoundedN / kRegion <= kSelThreads, "one region per thread in the offset scan");
 
+// four consecutive scores (16-byte aligned fp32 or 8-byte aligned bf16)
+__device__ __forceinline__ float4 load4_scores(const float* p) {
+  return *reinterpret_cast<const float4*>(p);
+}
+__device__ __forceinline__ float4 load4_scores(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
+}
+
+template <typename S>
 __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(
-    const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
+    const S* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
     const float2* __restrict__ chunk_rep, int n_chunks, int nreg, float* __restrict__ reg_val,
     int32_t* __restrict__ reg_idx, int32_t* __restrict__ reg_cnt) {
@@ -772,17 +785,17 @@ __global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(
   if (r >= nreg) return;
   // loads bounded by N_max, issued before the visible count is known
   const int Ln = max(0, min(N_max - e0, kRegion));
-  const float* src = scores + row * s_rs + e0;
+  const S* src = scores + row * s_rs + e0;
   float v[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int q = 256 * i + 4 * lane;
     if (q + 3 < Ln) {
-      const float4 x = *reinterpret_cast<const float4*>(src + q);
+      const float4 x = load4_scores(src + q);
       v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < Ln) ? src[q + e] : kNegInf;
+      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < Ln) ? get_score(src + q + e) : kNegInf;
     }
   }
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
@@ -837,9 +850,9 @@ int filter_regions(int N_max) { return (N_max + kFiltSeg - 1) / kFiltSeg * (kFil
 // survivors' range.  More than kListCap survivors (inputs far from the
 // expected distribution): the row is selected from global memory by
 // block_select instead.
-template <bool REGIONS>
+template <bool REGIONS, typename S>
 __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
-    const float* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
+    const S* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
     const float2* __restrict__ chunk_rep, int n_chunks, int nreg,
     const float* __restrict__ reg_val, const int32_t* __restrict__ reg_idx,
@@ -850,7 +863,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
   lds_u32x2* lp = (lds_u32x2*)lp_s;
   const int row = blockIdx.x, b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* srow = scores + row * s_rs;
+  const S* srow = scores + row * s_rs;
   float x[kStreamSlots];
   float2 rt[kRepPerLane];
   if (!REGIONS) {
@@ -962,7 +975,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
     em.lmap = nullptr;
     em.gmap = nullptr;
     const int n_sel =
-        block_select<NW>(GlobalRun{srow, V, (V + kSelThreads - 1) / kSelThreads}, k, p, em);
+        block_select<NW>(GlobalRun<S>{srow, V, (V + kSelThreads - 1) / kSelThreads}, k, p, em);
     pad_output<kSelThreads>(em, n_sel, k);
   }
 }
@@ -993,33 +1006,46 @@ size_t topk_bounded_workspace_bytes(int rows, int N_max) {
   return regs * kRegion * (sizeof(float) + sizeof(int32_t)) + regs * sizeof(int32_t);
 }
 
-hipError_t launch_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
+template <typename S>
+hipError_t launch_topk_bounded(const S* scores, int64_t s_rs, const int32_t* q_pos,
+                               const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
+                               const float2* chunk_rep, int n_chunks, int32_t* idx,
+                               float* out_scores, void* ws, hipStream_t s) {
+  const int rows = B * Tq;
+  if (!use_regions(rows, N_max)) {
+    hipLaunchKernelGGL((topk_bounded_kernel<false, S>), dim3(rows), dim3(kSelThreads), 0, s, scores,
+                       s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, 0, nullptr,
+                       nullptr, nullptr, idx, out_scores);
+    return hipGetLastError();
+  }
+  const int nreg = filter_regions(N_max);
+  const size_t slots = static_cast<size_t>(rows) * nreg * kRegion;
+  float* rv = static_cast<float*>(ws);
+  int32_t* ri = reinterpret_cast<int32_t*>(rv + slots);
+  int32_t* rc = ri + slots;
+  hipLaunchKernelGGL(topk_filter_kernel<S>, dim3((N_max + kFiltSeg - 1) / kFiltSeg, rows),
+                     dim3(kSegThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
+                     chunk_rep, n_chunks, nreg, rv, ri, rc);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((topk_bounded_kernel<true, S>), dim3(rows), dim3(kSelThreads), 0, s, scores,
+                     s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, nreg, rv, ri,
+                     rc, idx, out_scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const void* scores_v, bool score16, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
                        const float2* chunk_rep, int n_chunks, int32_t* idx, float* out_scores,
                        void* ws, hipStream_t s) {
   const int rows = B * Tq;
-  if (chunk_rep != nullptr && topk_bounded_ok(N_max)) {
-    if (!use_regions(rows, N_max)) {
-      hipLaunchKernelGGL(topk_bounded_kernel<false>, dim3(rows), dim3(kSelThreads), 0, s, scores,
-                         s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, 0, nullptr,
-                         nullptr, nullptr, idx, out_scores);
-      return hipGetLastError();
-    }
-    const int nreg = filter_regions(N_max);
-    const size_t slots = static_cast<size_t>(rows) * nreg * kRegion;
-    float* rv = static_cast<float*>(ws);
-    int32_t* ri = reinterpret_cast<int32_t*>(rv + slots);
-    int32_t* rc = ri + slots;
-    hipLaunchKernelGGL(topk_filter_kernel, dim3((N_max + kFiltSeg - 1) / kFiltSeg, rows),
-                       dim3(kSegThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
-                       chunk_rep, n_chunks, nreg, rv, ri, rc);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_bounded_kernel<true>, dim3(rows), dim3(kSelThreads), 0, s, scores,
-                       s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, nreg, rv, ri,
-                       rc, idx, out_scores);
-    return hipGetLastError();
-  }
+  if (score16)   // bf16 rows: the bounded path only (the caller checks chunk_rep and N_max)
+    return launch_topk_bounded(static_cast<const uint16_t*>(scores_v), s_rs, q_pos, n_entries, B,
+                               Tq, N_max, m, k, chunk_rep, n_chunks, idx, out_scores, ws, s);
+  const float* scores = static_cast<const float*>(scores_v);
+  if (chunk_rep != nullptr && topk_bounded_ok(N_max))
+    return launch_topk_bounded(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, chunk_rep,
+                               n_chunks, idx, out_scores, ws, s);
   const int nseg = num_segments(N_max);
   float* cv = static_cast<float*>(ws);
   int32_t* ci = reinterpret_cast<int32_t*>(cv + static_cast<size_t>(rows) * nseg * k);

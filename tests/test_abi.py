@@ -121,6 +121,23 @@ def test_index_topk_workspace(lib):
     assert f(*args) == WS_SMALL
 
 
+def test_index_topk_bf16_workspace_and_validation(lib):
+    sz, sz32 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.csa_index_topk_bf16_workspace(16, 1, 32768, 1024, ctypes.byref(sz)) == OK
+    assert lib.csa_index_topk_workspace(16, 1, 32768, 1024, ctypes.byref(sz32)) == OK
+    assert 16 * 32768 * 2 <= sz.value < sz32.value     # 2-byte score rows
+    assert lib.csa_index_topk_bf16_workspace(1, 1, 262145, 1024, ctypes.byref(sz)) == UNSUPPORTED
+    assert lib.csa_index_topk_bf16_workspace(1, 1, 32768, 4096, ctypes.byref(sz)) == UNSUPPORTED
+    assert lib.csa_index_topk_bf16_workspace(0, 1, 32768, 1024, ctypes.byref(sz)) == INVALID
+    f = lib.csa_index_topk_bf16
+    args = [A, A, A, 32768 * 128, 128, A, A, 16, 1, 32768, 4, 1024, A, None, A, 1024, None]
+    assert f(*args) == WS_SMALL
+    bad = list(args)
+    bad[4] = 100                                        # key row stride below 128
+    assert f(*bad) == INVALID
+    assert f(*(args[:11] + [0] + args[12:])) == INVALID   # k = 0
+
+
 def test_attend_validation(lib):
     sz = ctypes.c_size_t(0)
     assert lib.csa_attend_workspace(1, 16, 1, 64, 128, 1024, ctypes.byref(sz)) == OK

@@ -271,6 +271,40 @@ def test_topk_bound_rth_report(Tq, N_max, k, chunks):
         check_topk(I[b, t], s_ref, V, k)
 
 
+@pytest.mark.parametrize("B,Tq,N_max,k", [
+    (2, 13, 2 * 2048 + 300, 300),   # prefill kernel; rows with and without a bound
+    (3, 1, 70000, 1024),            # decode kernel; long rows: filter + regions
+    (1, 1, 20000, 2048),            # no bound (c > 16): the row overflows the LDS list
+])
+def test_index_topk_bf16_scores_exact(B, Tq, N_max, k):
+    """BF16 index scores: the selection equals the oracle's top-k of the GPU's
+    own fp32 scores rounded to bf16 (nearest, ties to even), index for index,
+    and the returned scores are those rounded values.  The fp32 scores come
+    from csa_index_score, whose kernels compute the same sums (the bf16 path
+    differs only in how it stores them)."""
+    _say(f"bf16 index scores: B={B} Tq={Tq} N_max={N_max} k={k}")
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 61)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 62)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 63)
+    pos = [[4 * N_max - 1 - 4 * 301 * t - 4 * 999 * b for t in range(Tq)] for b in range(B)]
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor([N_max - 17 * b for b in range(B)], dtype=torch.int32, device=DEV)
+    idx, val = csa.index_topk_bf16(qi, wi, ki, q_pos, n_ent, 4, k, with_scores=True)
+    s32 = csa.index_score(qi, wi, ki, q_pos, n_ent, 4)
+    torch.cuda.synchronize()
+    I, VAL, S = np64(idx), np64(val), np64(s32)
+    ne = n_ent.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible_count(pos[b][t], 4, int(ne[b]))
+            r = oracle.round_to_bf16(S[b, t, :V])
+            want = oracle.topk_select(r, V, k)
+            assert np.array_equal(I[b, t], want), (b, t, V)
+            n = int((want >= 0).sum())
+            assert np.array_equal(VAL[b, t, :n], r[want[:n]]), (b, t)
+            assert np.all(np.isneginf(VAL[b, t, n:]))
+
+
 def test_fp4_scores_ragged():
     """FP4 indexer (E2M1 codes, one fp32 scale per 32 elements) on ragged
     sizes: a partial last load unit and chunk, visible counts inside the first

@@ -13,8 +13,8 @@ from HBM.
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (only 1),
 --graph (also time the step captured in a HIP graph), --no-cpu-baseline,
 --workload NAME (another workload's own line instead of the headline one:
-hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4 or csa_prefill_chunk, the
-last also timing the step with bf16 index scores; see other_workload),
+hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4, csa_prefill_chunk (also
+timing the step with bf16 index scores) or swa_decode_128k; see other_workload),
 --score-only (launch only the indexer score kernel, for hardware-counter
 runs), --copy-calibration (run only a plain device copy of known size, for
 scaling the FETCH_SIZE / WRITE_SIZE counters).
@@ -185,15 +185,43 @@ def other_workload(args):
     csa_prefill_chunk: compress the 4096 new tokens, score / select / attend
       all 4096 queries; roofline: the prefill score kernel's FLOPs against the
       bf16 MFMA peak.
+    swa_decode_128k: sliding-window attention (window 4096) for 32 decode
+      tokens over uncompressed 128K-token caches; roofline: the window's K/V
+      bytes against HBM.
     """
     import long_context_attention_24_amd as csa
-    from csa_synth import WORKLOADS, make_inputs
+    from csa_synth import SWA_DECODE, WORKLOADS, make_inputs, make_swa_inputs
 
-    w = WORKLOADS[args.workload]
     dev = "cuda"
     timed = _timer()
     base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    if args.workload == "swa_decode_128k":
+        p = SWA_DECODE
+        B, N, H, D, W = p["B"], p["n_tokens"], p["H"], p["D"], p["window"]
+        copies = [make_swa_inputs(B, N, H, D, p["seed"] + c, device=dev) for c in range(N_COPIES)]
+        ws = torch.empty(csa.swa_workspace_bytes(torch.bfloat16, B, 1, H, D, N, W),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(copies[0]["q"])
+
+        def step(i):
+            c = copies[i % N_COPIES]
+            csa.swa_attend(c["q"], c["k"], c["v"], c["q_pos"], c["n_tokens"], W, workspace=ws,
+                           out=out)
+        ms = timed(step, args.steps, args.warmup)
+        step_bytes = B * W * D * 2 * 2 + 2 * B * H * D * 2
+        gbs = step_bytes / (ms * 1e-3) / 1e9
+        base.update(dict(
+            metric="Sliding-window decode tokens/sec (window 4096 at 128K context), 1 MI355X",
+            value=round(B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+            config={"workload": "swa_decode_128k", "batch": B, "context_tokens": N,
+                    "window": W, "heads": f"{H}x{D}"},
+            roofline={"kernel": "attend_split_kernel<HCA, window> + combine", "bound": "hbm",
+                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}))
+        print(json.dumps(base))
+        return
+    w = WORKLOADS[args.workload]
     if w.name == "hca_decode_1m":
         inp = make_inputs(w, device=dev, parts=["raw", "logits", "q", "q_pos", "n_entries"])
         caches = []

@@ -12,5 +12,7 @@ from .generate import (  # noqa: F401
     f32_from_bf16_bits,
     fp4_quantize,
     make_inputs,
+    make_swa_inputs,
     mx4_quantize,
+    SWA_DECODE,
 )

@@ -211,6 +211,28 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
     return out
 
 
+# Sliding-window decode inputs: B sequences with a cache of n_tokens
+# uncompressed tokens each (K, V ~ N(0,1)/sqrt(D), bf16) and one query token
+# at the last position (q ~ N(0,1)/sqrt(D), H heads).
+SWA_DECODE = dict(B=32, n_tokens=131072, H=64, D=128, window=4096, seed=5)
+
+
+def make_swa_inputs(B: int, n_tokens: int, H: int, D: int, seed: int,
+                    device="cpu") -> Dict[str, torch.Tensor]:
+    out = {}
+    std = 1.0 / np.sqrt(D)
+    for i, (name, shape) in enumerate((("q", (B, 1, H, D)), ("k", (B, n_tokens, D)),
+                                       ("v", (B, n_tokens, D)))):
+        g = torch.Generator(device=device)
+        g.manual_seed(seed * 1000 + 100 + i)
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+        x.normal_(0.0, 1.0, generator=g)
+        out[name] = (x * std).to(torch.bfloat16)
+    out["q_pos"] = torch.full((B, 1), n_tokens - 1, dtype=torch.int32, device=device)
+    out["n_tokens"] = torch.full((B,), n_tokens, dtype=torch.int32, device=device)
+    return out
+
+
 def sharp_variant(x: torch.Tensor, factor: float) -> torch.Tensor:
     """Scale a stored bf16/fp32 tensor by ``factor`` (re-rounded): used to draw
     'sharp' attention inputs whose softmax is far from uniform."""

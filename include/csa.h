@@ -254,6 +254,30 @@ csa_status_t hca_attend(const void* q, const void* k_c, const void* v_c,
 csa_status_t hca_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
                                   size_t* bytes);
 
+/*
+ * swa_attend - sliding-window attention over uncompressed tokens ("DeepSeek
+ * V4 技术解读", §2.3: the first layers attend a sliding window of recent
+ * tokens at full resolution; the window size is not given there and is an
+ * argument here).
+ *
+ *   o[b,t,h,:] = sum_{j in S} softmax_j(scale * q[b,t,h,:] . K[b,j,:]) V[b,j,:]
+ *   S = { j : max(0, P - window) <= j < P },  P = min(q_pos[b,t] + 1,
+ *   n_tokens[b], N_max): the query's own token and the window - 1 before it.
+ *   lse as in csa_attend (S is never empty for q_pos >= 0).
+ * q [B, Tq, H, D] contiguous; k, v [B, N_max, D] token caches sharing strides
+ * (kv_sb, kv_sn); q_pos [B, Tq], n_tokens [B] int32 device (tokens cached).
+ * window >= 1.  Workspace: swa_attend_workspace bytes (16-byte aligned).
+ * Supported: as csa_attend; tuned BF16 64 x 128.
+ */
+csa_status_t swa_attend(const void* q, const void* k, const void* v,
+                        int64_t kv_sb, int64_t kv_sn,
+                        const int32_t* q_pos, const int32_t* n_tokens,
+                        csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max, int window,
+                        float scale, void* out, float* lse,
+                        void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t swa_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
+                                  int window, size_t* bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "CsaError", "library_path", "load_library",
     "compress", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
-    "attend", "hca_attend", "index_topk_workspace_bytes", "index_topk_bf16_workspace_bytes",
+    "attend", "hca_attend", "swa_attend", "index_topk_workspace_bytes",
+    "index_topk_bf16_workspace_bytes", "swa_workspace_bytes",
     "attend_workspace_bytes", "hca_workspace_bytes",
     "EXPORTED_SYMBOLS",
 ]
@@ -41,6 +42,7 @@ EXPORTED_SYMBOLS = (
     "csa_index_topk", "csa_index_topk_workspace",
     "csa_index_topk_bf16", "csa_index_topk_bf16_workspace",
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
+    "swa_attend", "swa_attend_workspace",
 )
 
 
@@ -80,6 +82,10 @@ _SIGS = {
     "hca_attend": ([_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                     _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "hca_attend_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)], _i32),
+    "swa_attend": ([_vp, _vp, _vp, _i64, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                    _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
+    "swa_attend_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)],
+                             _i32),
 }
 
 
@@ -360,5 +366,33 @@ def hca_attend(q, k_cache, v_cache, q_pos, n_entries, m: int, scale: Optional[fl
     _check(load_library().hca_attend(
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1),
         q_pos.data_ptr(), n_entries.data_ptr(), _dtype_code(q), B, Tq, H, D, N_max, m, scale,
+        out.data_ptr(), _ptr(lse), _ptr(ws), ws_bytes, _stream()))
+    return (out, lse) if with_lse else out
+
+
+def swa_workspace_bytes(dtype: torch.dtype, B: int, Tq: int, H: int, D: int, N_max: int,
+                        window: int) -> int:
+    need = ctypes.c_size_t(0)
+    code = CSA_F32 if dtype == torch.float32 else CSA_BF16
+    _check(load_library().swa_attend_workspace(code, B, Tq, H, D, N_max, window,
+                                               ctypes.byref(need)))
+    return need.value
+
+
+def swa_attend(q, k_cache, v_cache, q_pos, n_tokens, window: int, scale: Optional[float] = None,
+               with_lse: bool = False, workspace: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None):
+    """Sliding-window attention over uncompressed tokens: each query attends its
+    own token and the window - 1 before it -> o [B, Tq, H, D] (+ lse [B, Tq, H])."""
+    B, Tq, H, D, N_max = _attn_common(q, k_cache, v_cache)
+    _contig(q_pos, "q_pos")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    need = swa_workspace_bytes(q.dtype, B, Tq, H, D, N_max, window)
+    ws, ws_bytes = _workspace(need, q.device, workspace)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if with_lse else None
+    _check(load_library().swa_attend(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1),
+        q_pos.data_ptr(), n_tokens.data_ptr(), _dtype_code(q), B, Tq, H, D, N_max, window, scale,
         out.data_ptr(), _ptr(lse), _ptr(ws), ws_bytes, _stream()))
     return (out, lse) if with_lse else out

@@ -44,8 +44,8 @@ template <typename T, int D, bool HCA>
 __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
     const T* __restrict__ q, const T* __restrict__ K, const T* __restrict__ Vc, int64_t kv_sb,
     int64_t kv_sn, const int32_t* __restrict__ idx, int kk, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_entries, int Tq, int H, int N_max, int m, float scale_log2,
-    T* __restrict__ out, float* __restrict__ lse) {
+    const int32_t* __restrict__ n_entries, int Tq, int H, int N_max, int m, int win,
+    float scale_log2, T* __restrict__ out, float* __restrict__ lse) {
   __shared__ float qs[D];
   __shared__ float p_s[kGenThreads];
   __shared__ int j_s[kGenThreads];
@@ -55,7 +55,9 @@ __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
   const T* qh = q + (static_cast<int64_t>(row) * H + h) * D;
   for (int d = tid; d < D; d += kGenThreads) qs[d] = ldf<T>(qh + d) * scale_log2;
   const int n_ent = min(n_entries[b], N_max);
-  const int n = HCA ? visible_count(q_pos[row], m, n_entries[b], N_max) : kk;
+  const int nv = HCA ? visible_count(q_pos[row], m, n_entries[b], N_max) : kk;
+  const int lo = HCA && win > 0 ? max(0, nv - win) : 0;   // window: the last win entries
+  const int n = nv - lo;
   const T* Kb = K + b * kv_sb;
   const T* Vb = Vc + b * kv_sb;
   __syncthreads();
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
     const int i = c0 + tid;
     int j = -1;
     if (i < n) {
-      j = HCA ? i : idx[static_cast<int64_t>(row) * kk + i];
+      j = HCA ? lo + i : idx[static_cast<int64_t>(row) * kk + i];
       if (j < 0 || j >= n_ent) j = -1;
     }
     float logit = kNegInf;
@@ -278,7 +280,8 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn, const int32_t* __restrict__ idx,
     int kk, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
-    int N_max, int m, float scale_log2, int split_len, int nsplit, float* __restrict__ part) {
+    int N_max, int m, int win, float scale_log2, int split_len, int nsplit,
+    float* __restrict__ part) {
   const int split = blockIdx.x, row = blockIdx.y, b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = wave & 1, kg = wave >> 1;
@@ -286,7 +289,11 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
   const int t128 = hh * 64 + lane;
   const int h = 32 * hh + jl;        // this lane's head (S^T / O^T column)
   const int n_ent = min(n_entries[b], N_max);
-  const int n = HCA ? visible_count(q_pos[row], m, n_entries[b], N_max) : kk;
+  const int nv = HCA ? visible_count(q_pos[row], m, n_entries[b], N_max) : kk;
+  // HCA with a window: positions count from lo, the first of the last win
+  // visible entries (splits laid over the window, not the whole cache)
+  const int lo = HCA && win > 0 ? max(0, nv - win) : 0;
+  const int n = nv - lo;
   const int s0 = split * split_len;
   const int s_end = min(n, s0 + split_len);
   const int ntiles = s_end > s0 ? (s_end - s0 + 31) / 32 : 0;
@@ -310,7 +317,7 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
   // flight, the next round's included.
   auto entry_raw = [&](int rr) -> int {
     const int p_ = s0 + 32 * (KG * rr + kg) + jl;
-    return HCA ? p_ : irow[min(p_, kk - 1)];
+    return HCA ? lo + p_ : irow[min(p_, kk - 1)];
   };
   auto entry_ok = [&](int rr, int e) -> int {
     const int t_ = KG * rr + kg, p_ = s0 + 32 * t_ + jl;
@@ -479,8 +486,8 @@ void launch_generic(const AttendArgs& a, float scale_log2, hipStream_t s) {
   hipLaunchKernelGGL((attend_generic_kernel<T, D, HCA>), dim3(a.H, a.B * a.Tq), dim3(kGenThreads),
                      0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.kc),
                      static_cast<const T*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
-                     a.n_entries, a.Tq, a.H, a.N_max, a.m, scale_log2, static_cast<T*>(a.out),
-                     a.lse);
+                     a.n_entries, a.Tq, a.H, a.N_max, a.m, a.win, scale_log2,
+                     static_cast<T*>(a.out), a.lse);
 }
 
 template <typename T, bool HCA>
@@ -518,7 +525,7 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
     return hipGetLastError();
   }
   const int sl = split_len(hca);
-  const int n = hca ? a.N_max : a.topk;
+  const int n = hca ? (a.win > 0 ? min(a.win, a.N_max) : a.N_max) : a.topk;
   int nsplit = (n + sl - 1) / sl;
   if (nsplit < 1) nsplit = 1;
   float* part = static_cast<float*>(a.ws);
@@ -527,12 +534,12 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
     hipLaunchKernelGGL((attend_split_kernel<true, kHcaGroups>), grid, dim3(128 * kHcaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
-                       a.n_entries, a.Tq, a.N_max, a.m, scale_log2, sl, nsplit, part);
+                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part);
   else
     hipLaunchKernelGGL((attend_split_kernel<false, kCsaGroups>), grid, dim3(128 * kCsaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
-                       a.n_entries, a.Tq, a.N_max, a.m, scale_log2, sl, nsplit, part);
+                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(attend_combine_kernel, dim3(a.B * a.Tq, 8), dim3(256), 0, s, part, nsplit,

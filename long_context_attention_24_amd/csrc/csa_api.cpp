@@ -354,7 +354,7 @@ csa_status_t csa_attend(const void* q, const void* k_c, const void* v_c, int64_t
   CSA_REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))),
               CSA_ERR_WORKSPACE_TOO_SMALL, "attend: workspace %zu < %zu bytes", ws_bytes, need);
   csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, topk_idx, nullptr, n_entries, B, Tq, H, D,
-                    N_max, k, 1, scale, out, lse, ws};
+                    N_max, k, 1, 0, scale, out, lse, ws};
   return hip_status(csa::launch_attend(a, dtype, false, stream), "attend launch");
 }
 
@@ -382,8 +382,37 @@ csa_status_t hca_attend(const void* q, const void* k_c, const void* v_c, int64_t
   CSA_REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))),
               CSA_ERR_WORKSPACE_TOO_SMALL, "hca: workspace %zu < %zu bytes", ws_bytes, need);
   csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, nullptr, q_pos, n_entries, B, Tq, H, D,
-                    N_max, 0, m, scale, out, lse, ws};
+                    N_max, 0, m, 0, scale, out, lse, ws};
   return hip_status(csa::launch_attend(a, dtype, true, stream), "hca launch");
+}
+
+csa_status_t swa_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
+                                  int window, size_t* bytes) {
+  g_err[0] = 0;
+  CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "swa workspace: NULL result");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1 && D >= 1 && N_max >= 1 && window >= 1,
+              CSA_ERR_INVALID_ARGUMENT, "swa workspace: sizes must be >= 1");
+  *bytes = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D,
+                                      window < N_max ? window : N_max);
+  return CSA_OK;
+}
+
+csa_status_t swa_attend(const void* q, const void* k, const void* v, int64_t kv_sb,
+                        int64_t kv_sn, const int32_t* q_pos, const int32_t* n_tokens,
+                        csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max, int window,
+                        float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                        hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_attend(q, k, v, kv_sb, kv_sn, n_tokens, dtype, B, Tq, H, D, N_max, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(q_pos && window >= 1, CSA_ERR_INVALID_ARGUMENT, "swa: bad q_pos / window");
+  const int wn = window < N_max ? window : N_max;
+  const size_t need = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D, wn);
+  CSA_REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))),
+              CSA_ERR_WORKSPACE_TOO_SMALL, "swa: workspace %zu < %zu bytes", ws_bytes, need);
+  csa::AttendArgs a{q, k, v, kv_sb, kv_sn, nullptr, q_pos, n_tokens, B, Tq, H, D,
+                    N_max, 0, 1, wn, scale, out, lse, ws};
+  return hip_status(csa::launch_attend(a, dtype, true, stream), "swa launch");
 }
 
 }  // extern "C"

@@ -70,11 +70,13 @@ struct AttendArgs {
   const int32_t* q_pos;     // HCA: [B*Tq]
   const int32_t* n_entries; // [B]
   int B, Tq, H, D, N_max, topk, m;
+  int win;                  // HCA only: attend the last win visible entries (0: all)
   float scale;
   void* out;
   float* lse;
   void* ws;
 };
+// k_or_nmax: k (CSA), N_max (HCA) or min(window, N_max) (HCA with a window)
 size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax);
 bool attend_supported(csa_dtype_t dt, int H, int D);
 hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s);

@@ -17,6 +17,7 @@ from .csa_oracle import (  # noqa: F401
     fp4_dequantize,
     from_bf16_bits,
     hca_attend,
+    swa_attend,
     index_scores,
     mx4_dequantize,
     mx4_quantize,

@@ -42,6 +42,10 @@ below and listed with its reason in the design notes):
      claim that FP4 dequantises to FP8 E4M3 without loss while the scale
      stays within a threshold is exact for such scales: every E2M1 value
      times 2**e is an E4M3 value for -8 <= e <= 6.
+  R9 sliding window (§2.3's first layers): a query at position p attends the
+     uncompressed tokens max(0, P - window) .. P - 1 with P = min(p + 1,
+     tokens cached), i.e. its own token and the window - 1 before it; the
+     pages give no window size, so it is an argument.
 """
 from __future__ import annotations
 
@@ -274,6 +278,15 @@ def attend(q, k_cache, v_cache, selected: Iterable[int], scale: Optional[float] 
 def hca_attend(q, k_cache, v_cache, visible: int, scale: Optional[float] = None):
     """§2.2 HCA: attention over every visible compressed entry, no selection."""
     return attend(q, k_cache, v_cache, range(visible), scale)
+
+
+def swa_attend(q, k_cache, v_cache, q_pos: int, n_tokens: int, window: int,
+               scale: Optional[float] = None):
+    """R9 sliding-window attention ("DeepSeek V4 技术解读", §2.3, the first
+    layers): over uncompressed tokens, the query's own token and the
+    window - 1 tokens before it (window is an argument; the pages give none)."""
+    P = min(q_pos + 1, n_tokens)
+    return attend(q, k_cache, v_cache, range(max(0, P - window), P), scale)
 
 
 # ------------------------------------------------------------------ whole path

@@ -305,6 +305,33 @@ def test_index_topk_bf16_scores_exact(B, Tq, N_max, k):
             assert np.all(np.isneginf(VAL[b, t, n:]))
 
 
+@pytest.mark.parametrize("window", [1, 100, 1500, 6000])
+@pytest.mark.parametrize("dtype,H,D", [(torch.bfloat16, 64, 128), (torch.float32, 3, 32)])
+def test_swa_attend_ragged(window, dtype, H, D):
+    """Sliding-window attention: windows of one token, inside one split, over
+    several splits and beyond the cache; queries near the start (window
+    clipped at token 0), at the end, and past the tokens cached (window ends
+    at the cache end).  Outputs and lse against the oracle."""
+    B, Tq, N_max = 2, 5, 5000
+    _say(f"swa window={window} {dtype} H={H} D={D}")
+    q = _randn((B, Tq, H, D), 1 / math.sqrt(D), dtype, 71)
+    kc = _randn((B, N_max, D), 1 / math.sqrt(D), dtype, 72)
+    vc = _randn((B, N_max, D), 1 / math.sqrt(D), dtype, 73)
+    pos = [[0, 57, 1499, 3000, N_max - 1], [4, 2047, 2600, 4000, 4500]]
+    n_tok = [N_max, 3001]
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    n_t = torch.tensor(n_tok, dtype=torch.int32, device=DEV)
+    o, lse = csa.swa_attend(q, kc, vc, q_pos, n_t, window, with_lse=True)
+    torch.cuda.synchronize()
+    O, L, Q, K, Vv = np64(o), np64(lse), np64(q), np64(kc), np64(vc)
+    kind = "bf16" if dtype == torch.bfloat16 else "f32"
+    for b in range(B):
+        for t in range(Tq):
+            o_ref, l_ref = oracle.swa_attend(Q[b, t], K[b], Vv[b], pos[b][t], n_tok[b], window)
+            check_attention(O[b, t], o_ref, kind, f"swa b={b} t={t}")
+            check_lse(L[b, t], l_ref, 2.5e-3 if kind == "bf16" else 1e-5)
+
+
 def test_fp4_scores_ragged():
     """FP4 indexer (E2M1 codes, one fp32 scale per 32 elements) on ragged
     sizes: a partial last load unit and chunk, visible counts inside the first

@@ -102,6 +102,27 @@ def test_csa_decode_128k_bf16_scores_recall():
     assert recall >= 0.995, recall
 
 
+def test_swa_decode_128k_full():
+    """Sliding-window decode at its full size (32 tokens, window 4096, 128K
+    uncompressed tokens per sequence), in the benchmark's launch
+    configuration; every sequence against the oracle."""
+    from csa_synth import SWA_DECODE, make_swa_inputs
+    p = SWA_DECODE
+    _say("swa_decode_128k: generating inputs")
+    inp = make_swa_inputs(p["B"], p["n_tokens"], p["H"], p["D"], p["seed"], device=DEV)
+    o, lse = csa.swa_attend(inp["q"], inp["k"], inp["v"], inp["q_pos"], inp["n_tokens"],
+                            p["window"], with_lse=True)
+    torch.cuda.synchronize()
+    O, L, Q = np64(o), np64(lse), np64(inp["q"])
+    lo = p["n_tokens"] - p["window"]
+    K, Vv = np64(inp["k"][:, lo:]), np64(inp["v"][:, lo:])
+    for b in range(p["B"]):
+        o_ref, l_ref = oracle.swa_attend(Q[b, 0], K[b], Vv[b], p["window"] - 1, p["window"],
+                                         p["window"])
+        check_attention(O[b, 0], o_ref, "bf16", f"swa b={b}")
+        check_lse(L[b, 0], l_ref, 2.5e-3)
+
+
 def test_csa_decode_128k_sharp_attention():
     """Same selection path, attention inputs scaled so the softmax is sharp."""
     w = WORKLOADS["csa_decode_128k"]

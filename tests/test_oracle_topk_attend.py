@@ -113,6 +113,37 @@ def test_hca_m1_is_causal_attention():
         assert np.allclose(o, want[t], atol=1e-12)
 
 
+def test_swa_is_banded_causal_attention():
+    """Sliding-window attention equals torch's scaled_dot_product_attention with
+    a banded causal mask (a library routine, fp64 CPU); window >= p + 1 is full
+    causal attention; window = 1 returns the token's own value row."""
+    rng = np.random.default_rng(10)
+    T, H, D, W = 14, 3, 8, 4
+    q = rng.standard_normal((T, H, D))
+    kr = rng.standard_normal((T, D))
+    vr = rng.standard_normal((T, D))
+    i = torch.arange(T)
+    band = (i[None, :] <= i[:, None]) & (i[None, :] > i[:, None] - W)     # [T_q, T_k]
+    tq = torch.from_numpy(q).permute(1, 0, 2)[None]
+    tk = torch.from_numpy(kr)[None, None].expand(1, H, -1, -1)
+    tv = torch.from_numpy(vr)[None, None].expand(1, H, -1, -1)
+    want = torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=band, scale=0.4)[0].permute(1, 0, 2).numpy()
+    full = _sdpa_causal(q, kr, vr, 0.4)
+    for t in range(T):
+        o, _ = oracle.swa_attend(q[t], kr, vr, t, T, W, 0.4)
+        assert np.allclose(o, want[t], atol=1e-12)
+        o, _ = oracle.swa_attend(q[t], kr, vr, t, T, T, 0.4)
+        assert np.allclose(o, full[t], atol=1e-12)
+        o, lse = oracle.swa_attend(q[t], kr, vr, t, T, 1, 0.4)
+        assert np.array_equal(o, np.tile(vr[t], (H, 1)))
+        assert np.allclose(lse, 0.4 * q[t] @ kr[t], atol=1e-13)
+    # fewer tokens cached than the position implies: the window ends at the cache end
+    o, _ = oracle.swa_attend(q[5], kr, vr, 9, 6, 3, 0.4)
+    o2, _ = oracle.attend(q[5], kr, vr, [3, 4, 5], 0.4)
+    assert np.array_equal(o, o2)
+
+
 def test_attend_closed_forms():
     rng = np.random.default_rng(9)
     H, D, N = 4, 8, 16

@@ -66,28 +66,29 @@ __global__ __launch_bounds__(256) void score_generic_kernel(
 
 // ---------------------------------------------------------------- selection bound
 // Each wave also reports, for the scores it produced (its chunk of
-// kBoundChunk keys), the c-th largest with c = bound_c_row(V, k) for the row,
-// and the largest.  Every chunk that reports a finite c-th largest holds c
-// entries at or above it, and the floor(V / kBoundChunk) full chunks all do,
-// so the ceil(k / c)-th largest report is at most the row's k-th largest
-// score.  The top-k kernels use that bound to drop most entries before
-// selecting, and the
-// largest report as the top of the survivors' range.  A chunk with fewer
-// than c valid entries reports +inf as its c-th largest (-inf as its largest
-// when it has none); rows with no bound (c = 0) write nothing.
+// kBoundChunk keys, held as NV scores by each of 16 or 32 lanes), a value
+// that c of them reach, c = bound_c_row(V, k) for the row: the c-th largest
+// of the per-lane maxima (c lanes hold an entry at or above it; a little
+// below the exact c-th largest, for a fraction of its cost), and the
+// largest score.  Every chunk that reports a finite value holds c entries at
+// or above it, and the floor(V / kBoundChunk) full chunks all do (every lane
+// holds valid entries, c <= 16), so the ceil(k / c)-th largest report is at
+// most the row's k-th largest score.  The top-k kernels use that bound to
+// drop most entries before selecting, and the largest report as the top of
+// the survivors' range.  A chunk with fewer than c lanes holding valid
+// entries reports +inf (-inf as its largest when it has none); rows with no
+// bound (c = 0) write nothing.
 constexpr float kPosInf = __builtin_inff();
 
 template <int NV>
 __device__ float2 wave_chunk_report(const float (&vals)[NV], bool active, int c) {
   const int lane = threadIdx.x & 63;
-  float v[NV];
+  float lm = kNegInf;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) v[i] = active ? vals[i] : kNegInf;
+  for (int i = 0; i < NV; ++i) lm = fmaxf(lm, vals[i]);
+  if (!active) lm = kNegInf;
   float cur = kPosInf, top = kNegInf;
   for (int r = 0; r < c; ++r) {
-    float lm = v[0];
-#pragma unroll
-    for (int i = 1; i < NV; ++i) lm = fmaxf(lm, v[i]);
     const float wm = wave_max(lm);
     if (r == 0) top = wm;
     if (wm == kNegInf) {
@@ -95,16 +96,7 @@ __device__ float2 wave_chunk_report(const float (&vals)[NV], bool active, int c)
       break;
     }
     const unsigned long long msk = __ballot(lm == wm);
-    if (lane == __ffsll(msk) - 1) {     // remove one occurrence of the maximum
-      bool done = false;
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        if (!done && v[i] == wm) {
-          v[i] = kNegInf;
-          done = true;
-        }
-      }
-    }
+    if (lane == __ffsll(msk) - 1) lm = kNegInf;
     cur = wm;
   }
   return make_float2(cur, top);

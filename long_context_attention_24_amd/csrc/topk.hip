@@ -12,8 +12,8 @@
 //     of the k-th largest; [lo, hi] shrinks to that bin's min / max until the
 //     bin is taken whole or all candidates are equal.  Each pass shrinks the
 //     range 2048-fold, so fp32 needs at most ~26 passes.
-//   * Ordered compaction: one block-wide scan of (count > T, count == T)
-//     gives every thread its output slots; entries equal to the threshold are
+//   * Ordered compaction: block-wide scans of (count > T) and (count == T)
+//     give every thread its output slots; entries equal to the threshold are
 //     taken lowest index first.
 // Only integer LDS atomics (counts) are used, so results are deterministic.
 //
@@ -252,12 +252,13 @@ __device__ __forceinline__ int block_select(const Run run, int k, int& p, const 
     gt += (x > T) ? 1u : 0u;
     eq += (x == T && x > kNegInf) ? 1u : 0u;
   }
-  uint32_t tot;
-  const uint32_t pre = block_excl_scan<NW>(gt | (eq << 16), tot, p);
-  const int gt_before = static_cast<int>(pre & 0xffffu);
-  int eq_before = static_cast<int>(pre >> 16);
-  const int gt_total = static_cast<int>(tot & 0xffffu);
-  const int eq_total = static_cast<int>(tot >> 16);
+  // two scans: a run can be a whole row (up to 262144 values), so the counts
+  // do not fit 16-bit halves of one word
+  uint32_t gt_tot, eq_tot;
+  const int gt_before = static_cast<int>(block_excl_scan<NW>(gt, gt_tot, p));
+  int eq_before = static_cast<int>(block_excl_scan<NW>(eq, eq_tot, p));
+  const int gt_total = static_cast<int>(gt_tot);
+  const int eq_total = static_cast<int>(eq_tot);
   int slot = gt_before + min(eq_before, take_eq);
   for (int i = 0; i < R; ++i) {
     const float x = run.get(i);
@@ -416,29 +417,34 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 
 // ============================================================ bounded path
 // topk_bounded_kernel: one 1024-thread workgroup per row.
-//   1. The row bound comes from the chunk reports (every wave on its own,
-//      the reports loaded next to the first score loads).
-//   2. The row is streamed in chunks of 32768 scores (eight coalesced 16-byte
-//      loads per thread, the next chunk's loads in flight while the current
-//      one is filtered); entries at or above the bound are appended to an LDS
-//      list, one LDS atomic per wave reserving the wave's range.  The list is
-//      unordered.
-//   3. Radix selection on order-preserving 32-bit keys, offset by the
-//      smallest survivor key: each pass histograms the next (up to) 11 bits
-//      of the keys still in play (2048 LDS bins, two per thread), one block
-//      scan locates the bin of the k-th largest, and the pass ends the search
-//      when that bin is wholly taken or holds a single key.
-//   4. The taken entries set their bit in an LDS bitmap over entry indices; a
-//      block scan of its popcounts gives every taken entry its output slot,
-//      which puts the result in ascending index order.  Among entries equal
-//      to the threshold value only the lowest indices are taken.
+//   1. The row bound and the top of the survivors' range come from the chunk
+//      reports, every wave computing them on its own (row_bound), the
+//      reports loaded next to the first score loads.
+//   2. Survivor list in LDS, in ascending index order, as (score bits, entry
+//      index) pairs.  Streamed rows: rounds of 16384 scores, each lane
+//      loading 16 scalar scores (entries 64 s + lane of its wave's segment),
+//      the next round's loads in flight while the current one is compacted;
+//      per round the waves count their survivors with ballots, one block scan
+//      gives every wave its offset, and each survivor's slot is that offset
+//      plus its rank among the wave's survivors (ballot + mbcnt).  Filtered
+//      rows (topk_filter_kernel first): the per-region survivor counts are
+//      scanned and the regions copied at their offsets.
+//   3. select_sorted_list: a 2048-bin equal-width histogram over [bound, top]
+//      locates the bin of the k-th largest; a bin of at most 256 entries is
+//      finished by pairwise ranks, a larger one narrows the range to the bin
+//      and repeats.  Because the list is in index order, one block scan of
+//      the pair (count > T, count == T) over contiguous per-thread runs (two
+//      16-bit halves of one word: the list holds fewer than 65536 entries)
+//      gives every selected entry its output slot: ascending indices, and
+//      among entries equal to the threshold the lowest indices.
 // A row whose survivors overflow the list selects from the score row
 // directly (block_select, slow but exact).
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 static_assert(kBins % kSelThreads == 0, "whole bins per thread");
 constexpr int kMaxBoundedN = 262144;
-constexpr int kListCap = 16 * kSelThreads;        // survivors held in LDS (< 65536: packed scans)
+constexpr int kListCap = 16 * kSelThreads;        // survivors held in LDS
+static_assert(kListCap < 65536, "select_sorted_list packs two list counts into one word");
 constexpr int kBrute = 256;                       // bin size finished by pairwise ranks
 constexpr int kStreamSlots = 16;                  // 4-byte loads per lane per round
 constexpr int kWaveSeg = 64 * kStreamSlots;       // entries per wave per round

@@ -88,11 +88,19 @@ def check_attention(o_gpu: np.ndarray, o_ref: np.ndarray, dtype: str, what: str 
     return max_abs, mean_abs, worst
 
 
+# bf16 attention sums the softmax probabilities after rounding each to bf16
+# (relative error at most 2^-9 per term, so at most 2^-9 for the sum: one term
+# dominates a sharp softmax), and lse = max + log(sum); logits come from exact
+# bf16 products accumulated in fp32 (error ~1e-4 at the sharp inputs' scale).
+LSE_TOL_BF16 = 2.0 ** -8
+
+
 def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, tol: float):
-    both_inf = np.isneginf(lse_gpu) & np.isneginf(lse_ref)
-    assert np.array_equal(np.isneginf(lse_gpu), np.isneginf(lse_ref)), "empty-set rows differ"
-    d = np.abs(np.where(both_inf, 0.0, lse_gpu - lse_ref))
-    assert d.max() <= tol, f"lse error {d.max()}"
+    lse_gpu, lse_ref = np.asarray(lse_gpu), np.asarray(lse_ref)
+    empty = np.isneginf(lse_gpu)
+    assert np.array_equal(empty, np.isneginf(lse_ref)), "empty-set rows differ"
+    d = np.abs(lse_gpu[~empty] - lse_ref[~empty])
+    assert d.size == 0 or d.max() <= tol, f"lse error {d.max()}"
 
 
 def check_compress(out_gpu: np.ndarray, x64: np.ndarray, z64: np.ndarray, m: int, dtype: str):

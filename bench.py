@@ -3,7 +3,9 @@
 One step = the whole decode hot path for one batch of 16 sequences, each with
 a 131072-token context compressed 4:1 into 32768 entries and one new query
 token: Lightning Indexer scores (64 heads x 128, bf16) -> top-1024 selection
--> sparse core attention (64 heads x 128, bf16) over the selected entries.
+-> sparse core attention (64 heads x 128, bf16) over the selected entries,
+as one csa_index_topk_attend call (two kernels: the score kernel, then the
+attention kernel that selects each row's top-k itself).
 
 Inputs are synthetic, seeded and resident in HBM before timing.  The decode
 working set (~143 MB) fits the 256 MB Infinity Cache, so consecutive steps
@@ -12,20 +14,39 @@ from HBM.
 
 Prints one JSON line.  Options: --steps K --warmup W --gpus N (only 1),
 --graph (also time the step captured in a HIP graph), --no-cpu-baseline,
---workload NAME (another workload's own line instead of the headline one:
-hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4, csa_prefill_chunk (also
-timing the step with bf16 index scores) or swa_decode_128k; see other_workload),
---score-only (launch only the indexer score kernel, for hardware-counter
-runs), --copy-calibration (run only a plain device copy of known size, for
-scaling the FETCH_SIZE / WRITE_SIZE counters).
+--cpu-seconds S (oracle time budget), --workload NAME (another workload's
+own line: tiny_csa, hca_decode_1m, csa_decode_1m_fp4, csa_decode_1m_mx4,
+csa_prefill_chunk or swa_decode_128k; see other_workload), --step-only (time
+only the headline step: short runs under a profiler), --copy-calibration
+(only a plain device copy of known size, for scaling the FETCH_SIZE /
+WRITE_SIZE counters).
 
-roofline.traffic is read from the counter summary committed under profiles/;
-it is null when the score kernel's source no longer matches the one the
-counters were taken on.
+Measurement notes.
+  * Every timed region is queued behind a spin kernel that holds the GPU
+    until the whole region is enqueued, so host launch overhead is not timed.
+  * roofline: the dominant kernel (the score kernel); achieved = its
+    algorithmic bytes per launch (indexer keys + indexer queries + head
+    weights, the score workspace excluded) / its duration.  The duration is
+    the per-launch period of back-to-back score launches (HIP events on the
+    launch stream) minus the per-launch period of back-to-back empty
+    launches (the dispatch gap between dependent launches); those launches
+    go through csa_index_score, the same kernel as in the step without the
+    chunk-report epilogue.  The rocprofv3 average of the step's score
+    kernel, from the committed kernel-statistics summary, is reported next
+    to it when that summary was taken on the current kernel source.
+  * step_frac_hbm (the 60 % gate of the workload): the step's algorithmic
+    bytes / the step's time / 8 TB/s.
+  * roofline.traffic: HBM bytes per launch of the step's score kernel from
+    the committed FETCH_SIZE / WRITE_SIZE summary; null when that summary was
+    taken on another kernel source.
+  * cpu_baseline: the oracle (fp64 NumPy) on this host's cores
+    (len(os.sched_getaffinity(0)), BLAS threads set to that number), stage by
+    stage, on a bounded sample of the workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -39,10 +60,13 @@ sys.path.insert(0, ROOT)
 METRIC = "CSA decode tokens/sec + achieved HBM GB/s at 128K context, 1 MI355X"
 WORKLOAD = "csa_decode_128k"
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
+STEP_GATE_FRAC = 0.60
 N_COPIES = 4
 SCORE_KERNEL = "score_bf16_h64d128_kernel"
 SCORE_SOURCE = os.path.join(ROOT, "long_context_attention_24_amd", "csrc", "index_score.hip")
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "score_bf16_h64d128_csa_decode_128k_traffic.txt")
+STATS_SUMMARY = os.path.join(ROOT, "profiles", "csa_decode_128k_bench_kernel_stats.txt")
 
 
 def parse():
@@ -54,46 +78,117 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--copy-calibration", action="store_true")
-    p.add_argument("--score-only", action="store_true")
+    p.add_argument("--step-only", action="store_true")
     p.add_argument("--workload", default=WORKLOAD)
     return p.parse_args()
 
 
-def algorithmic_bytes(w):
-    """Bytes the method must move per step and per score-kernel launch."""
+# ---------------------------------------------------------------- algorithmic work
+def decode_bytes(w):
+    """Bytes a CSA decode step must move (step) and its score kernel must read
+    (score): indexer keys, the selected K and V rows, queries, indexer
+    queries, head weights, outputs and the top-k hand-off; the score
+    workspace is excluded."""
     B, N, H, D, HI, DI, k = w.B, w.N, w.H, w.D, w.H_I, w.D_I, w.k
-    ki = B * N * DI * 2                       # indexer keys, bf16
-    gathers = B * k * D * 2 * 2               # selected K and V rows
+    ki = B * N * DI * 2
+    gathers = B * k * D * 2 * 2
     q = B * H * D * 2
     qi = B * HI * DI * 2
     wi = B * HI * 4
     o = B * H * D * 2
-    idx = B * k * 4 * 2                       # written by top-k, read by attention
-    step = ki + gathers + q + qi + wi + o + idx
-    score_kernel = ki + qi + wi + B * N * 4   # + the fp32 scores it writes
-    return step, score_kernel
+    idx = B * k * 4 * 2
+    return ki + gathers + q + qi + wi + o + idx, ki + qi + wi
 
 
-def stage_bytes(w):
-    """Algorithmic bytes of the selection and attention stages of one step
-    (the score workspace is counted where it is read)."""
-    B, N, H, D, k = w.B, w.N, w.H, w.D, w.k
-    select = B * N * 4 + B * k * 4                 # scores read, indices written
-    attend = B * k * D * 2 * 2 + B * H * D * 2 * 2 + B * k * 4   # K/V gathers, q, o, indices
-    return select, attend
+def source_sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
 
 
-def _calibrate_sleep() -> float:
-    """Spin-kernel cycles per millisecond on this GPU."""
-    torch.cuda._sleep(1000)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    n = 2_000_000
-    e0.record()
-    torch.cuda._sleep(n)
-    e1.record()
-    torch.cuda.synchronize()
-    return n / max(e0.elapsed_time(e1), 1e-3)
+def _summary_kv(path):
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return {}
+    kv = {}
+    for ln in lines:
+        if ":" in ln and not ln.startswith(" "):
+            key, val = ln.split(":", 1)
+            kv[key.strip()] = val.strip()
+    return kv
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the step's score kernel from the committed
+    counter summary, or None if it is missing or was taken on a different
+    kernel source."""
+    kv = _summary_kv(TRAFFIC_SUMMARY)
+    if kv.get("source_sha256") != source_sha(SCORE_SOURCE) or "hbm_bytes_per_launch" not in kv:
+        return None
+    return int(kv["hbm_bytes_per_launch"])
+
+
+def recorded_score_kernel_us():
+    """rocprofv3 average duration (us) of the step's score kernel from the
+    committed kernel-statistics summary, or None (missing, other source)."""
+    kv = _summary_kv(STATS_SUMMARY)
+    if kv.get("score_source_sha256") != source_sha(SCORE_SOURCE):
+        return None
+    v = kv.get("score_kernel_avg_us")
+    return float(v) if v else None
+
+
+# ---------------------------------------------------------------- timing
+class Timer:
+    """Back-to-back GPU timing with HIP events on the current stream; the
+    GPU is held by a spin kernel while each timed region is enqueued."""
+
+    def __init__(self):
+        torch.cuda._sleep(1000)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 2_000_000
+        e0.record()
+        torch.cuda._sleep(n)
+        e1.record()
+        torch.cuda.synchronize()
+        self.cycles_per_ms = n / max(e0.elapsed_time(e1), 1e-3)
+
+    def hold(self, ms):
+        torch.cuda._sleep(int(self.cycles_per_ms * ms))
+
+    def period(self, fn, steps, warmup):
+        """Average ms per call of `steps` back-to-back calls."""
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        self.hold(20.0 + 0.05 * steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def quantiles(self, fn, steps, warmup):
+        """p10 / p50 / p90 of per-call times (events around every call)."""
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        self.hold(20.0 + 0.05 * steps)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record()
+            fn(i)
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in ev)
+        return [t[int(q * (steps - 1))] for q in (0.1, 0.5, 0.9)]
+
+    def launch_gap(self, steps=200):
+        """Per-launch period of back-to-back empty kernels (ms)."""
+        return self.period(lambda i: torch.cuda._sleep(0), steps, 20)
 
 
 def copy_calibration():
@@ -108,78 +203,99 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": 4 * n, "bytes_written": 4 * n, "launches": 5}))
 
 
-def cpu_baseline(w, inputs, seconds):
-    """The oracle as it stands, on this host: passes over the batch's
-    sequences (one decode token each) until about `seconds` have elapsed."""
+# ---------------------------------------------------------------- oracle baseline
+def host_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def _f64(t):
     import numpy as np
     import oracle
-    from threadpoolctl import threadpool_info
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return oracle.from_bf16_bits(t.contiguous().view(torch.int16).numpy().view(np.uint16))
+    if t.dtype in (torch.float32, torch.float64):
+        return t.numpy().astype(np.float64)
+    return t.numpy()
 
-    f64 = lambda t: oracle.from_bf16_bits(t.cpu().view(torch.int16).numpy().view(np.uint16)) \
-        if t.dtype == torch.bfloat16 else t.cpu().double().numpy()
-    host = {k: f64(v) for k, v in inputs.items() if v.dtype != torch.int32}
+
+def timed_oracle(stages, items, seconds, per_item=1.0):
+    """Runs the oracle stages over items until about `seconds` have passed (at
+    least one item).  stages: [(name, fn(item, state) -> state)].  Returns
+    (items done, elapsed s, {stage: mean ms per item})."""
+    from threadpoolctl import threadpool_limits
+    acc = {name: 0.0 for name, _ in stages}
     done, t0 = 0, time.perf_counter()
-    while True:
-        b = done % w.B
-        oracle.csa_reference(q=host["q"][b, 0], q_idx=host["q_idx"][b, 0], w_idx=host["w_idx"][b, 0],
-                             k_cache=host["k_cache"][b], v_cache=host["v_cache"][b],
-                             k_idx=host["ki_cache"][b], q_pos=w.q_pos0, m=w.m, k=w.k, n_entries=w.N)
-        done += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
+    with threadpool_limits(limits=host_cores()):
+        while True:
+            it = items[done % len(items)]
+            st = None
+            for name, fn in stages:
+                t1 = time.perf_counter()
+                st = fn(it, st)
+                acc[name] += time.perf_counter() - t1
+            done += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
     el = time.perf_counter() - t0
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} decode tokens ({done / w.B:.1f} passes over the {w.B} sequences of "
-                      f"{WORKLOAD}), fp64 NumPy oracle, {el:.1f} s"}
+    return done, el, {k: round(1e3 * v / done, 3) for k, v in acc.items()}
 
 
-def recorded_traffic():
-    """HBM bytes per score-kernel launch from the committed counter summary,
-    or None if it is missing or was taken on a different kernel source."""
-    import hashlib
-    try:
-        lines = open(TRAFFIC_SUMMARY).read().splitlines()
-    except OSError:
-        return None
-    kv = {}
-    for ln in lines:
-        if ":" in ln and not ln.startswith(" "):
-            key, val = ln.split(":", 1)
-            kv[key.strip()] = val.strip()
-    src = hashlib.sha256(open(SCORE_SOURCE, "rb").read()).hexdigest()
-    if kv.get("source_sha256") != src or "hbm_bytes_per_launch" not in kv:
-        return None
-    return int(kv["hbm_bytes_per_launch"])
+def _blas_threads():
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with threadpool_limits(limits=host_cores()):
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
 
 
-def _timer():
-    """(hold_gpu(ms), timed(fn, steps, warmup) -> ms per call) as in main()."""
-    cycles_per_ms = _calibrate_sleep()
-
-    def timed(fn, steps, warmup):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        torch.cuda._sleep(int(cycles_per_ms * (20.0 + 0.05 * steps)))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps
-    return timed
+def baseline_record(value, unit, stages_ms, sample):
+    return {"value": value, "unit": unit, "cores": host_cores(), "blas_threads": _blas_threads(),
+            "kind": "oracle", "stages_ms_per_token": stages_ms, "sample": sample}
 
 
+def decode_oracle_baseline(w, inp, seconds, dequant=None):
+    """Oracle decode tokens/s: per decode token the indexer scores over the
+    visible entries, the top-k, the attention over the selected entries."""
+    import oracle
+    if dequant is not None:
+        codes, scales, qcodes, qscales = (inp[n].cpu().numpy() for n in
+                                          ("ki_codes", "ki_scale", "q_codes", "q_scale"))
+        KI = None
+        QI = dequant(qcodes, qscales)
+    else:
+        KI, QI = _f64(inp["ki_cache"]), _f64(inp["q_idx"])
+    K, Vc, Q, W = _f64(inp["k_cache"]), _f64(inp["v_cache"]), _f64(inp["q"]), _f64(inp["w_idx"])
+    V = oracle.visible_count(w.q_pos0, w.m, w.N)
+
+    def score(b, _):
+        ki = dequant(codes[b], scales[b]) if dequant is not None else KI[b]
+        return oracle.index_scores(QI[b, 0], W[b, 0], ki, V)
+
+    def select(b, s):
+        return oracle.topk_select(s, V, w.k)
+
+    def attend(b, idx):
+        return oracle.attend(Q[b, 0], K[b], Vc[b], idx)
+    stages = [("score" + (" (incl. FP4 decode of the keys)" if dequant else ""), score),
+              ("select", select), ("attend", attend)]
+    done, el, ms = timed_oracle(stages, list(range(w.B)), seconds)
+    return baseline_record(round(done / el, 3), "tokens/s", ms,
+                           f"{done} decode tokens of {w.name} (sequences taken in turn), fp64 "
+                           f"NumPy oracle, {el:.1f} s")
+
+
+# ---------------------------------------------------------------- other workloads
 def other_workload(args):
     """One JSON line for a workload other than the headline one.
 
+    tiny_csa: the whole tiny fp32 pipeline (compress 256 raw tokens, then
+      score / select / attend for all 256 query positions); correctness
+      workload, reported for the oracle comparison.
     hca_decode_1m: compress the 1M-token raw stream 128:1 (timed once per
       sequence batch, reported), then HCA decode steps (32 tokens) over the
       compressed caches; roofline: the attention's K/V stream against HBM.
     csa_decode_1m_fp4: FP4 indexer scores + top-k + sparse attention for 4
-      decode tokens at 1M context; roofline: the FP4 score kernel's bytes.
+      decode tokens at 1M context (csa_index_topk_attend); roofline: the FP4
+      score kernel's bytes.
     csa_decode_1m_mx4: the same with MX FP4 indexer inputs (one E8M0 scale
       byte per 32 elements); roofline: the MX score kernel's bytes.
     csa_prefill_chunk: compress the 4096 new tokens, score / select / attend
@@ -189,19 +305,22 @@ def other_workload(args):
       tokens over uncompressed 128K-token caches; roofline: the window's K/V
       bytes against HBM.
     """
+    import numpy as np
     import long_context_attention_24_amd as csa
+    import oracle
     from csa_synth import SWA_DECODE, WORKLOADS, make_inputs, make_swa_inputs
 
     dev = "cuda"
-    timed = _timer()
+    tm = Timer()
+    timed = tm.period
     base = {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic"}
+    want_cpu = not args.no_cpu_baseline
     if args.workload == "swa_decode_128k":
         p = SWA_DECODE
         B, N, H, D, W = p["B"], p["n_tokens"], p["H"], p["D"], p["window"]
         copies = [make_swa_inputs(B, N, H, D, p["seed"] + c, device=dev) for c in range(N_COPIES)]
-        ws = torch.empty(csa.swa_workspace_bytes(torch.bfloat16, B, 1, H, D, N, W),
-                         dtype=torch.uint8, device=dev)
+        ws = csa.new_workspace(csa.swa_workspace_bytes(torch.bfloat16, B, 1, H, D, N, W), dev)
         out = torch.empty_like(copies[0]["q"])
 
         def step(i):
@@ -216,13 +335,76 @@ def other_workload(args):
             value=round(B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
             config={"workload": "swa_decode_128k", "batch": B, "context_tokens": N,
                     "window": W, "heads": f"{H}x{D}"},
-            roofline={"kernel": "attend_split_kernel<HCA, window> + combine", "bound": "hbm",
+            roofline={"kernel": "attend_split_kernel<HCA, window>", "bound": "hbm",
                       "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None}))
+                      "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                      "algorithmic_bytes_per_launch": step_bytes, "avg_launch_ms": round(ms, 5)}))
+        if want_cpu:
+            c0 = copies[0]
+            Q = _f64(c0["q"])
+            Kh, Vh = c0["k"], c0["v"]
+
+            def attend(b, _):
+                kb = _f64(Kh[b, N - W:])
+                vb = _f64(Vh[b, N - W:])
+                return oracle.swa_attend(Q[b, 0], kb, vb, W - 1, W, W)
+            done, el, sms = timed_oracle([("attend (incl. bf16 decode of the window)", attend)],
+                                         list(range(B)), args.cpu_seconds)
+            base["cpu_baseline"] = baseline_record(
+                round(done / el, 3), "tokens/s", sms,
+                f"{done} decode tokens of swa_decode_128k, fp64 NumPy oracle, {el:.1f} s")
         print(json.dumps(base))
         return
     w = WORKLOADS[args.workload]
-    if w.name == "hca_decode_1m":
+    if w.name == "tiny_csa":
+        inp = make_inputs(w, device=dev)
+        ws = csa.new_workspace(csa.index_topk_attend_workspace_bytes(0, torch.float32, w.B, w.Tq,
+                                                                     w.N, w.H, w.D, w.k), dev)
+        cache = torch.empty((w.B, w.N, w.C), dtype=torch.float32, device=dev)
+        out = torch.empty_like(inp["q"])
+
+        def step(i):
+            csa.compress(inp["raw"], inp["logits"], w.m, out=cache)
+            csa.index_topk_attend(inp["q_idx"], inp["w_idx"], cache[..., 2 * w.D:], inp["q"],
+                                  cache[..., :w.D], cache[..., w.D:2 * w.D], inp["q_pos"],
+                                  inp["n_entries"], w.m, w.k, workspace=ws, out=out)
+        ms = timed(step, args.steps, args.warmup)
+        res = dict(metric="Tiny CSA pipeline tokens/sec (256 tokens, fp32), 1 MI355X",
+                   value=round(w.Tq / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
+                   config={"workload": w.name, "batch": w.B, "tokens": w.n_raw, "m": w.m,
+                           "top_k": w.k, "heads": f"{w.H}x{w.D}", "indexer": f"{w.H_I}x{w.D_I}"},
+                   roofline=None, dtype_note="fp32 generic (VALU) kernels: correctness workload")
+        base["dtype"] = "f32"
+        if want_cpu:
+            raw, z = _f64(inp["raw"])[0], _f64(inp["logits"])[0]
+            Q, QI, W = _f64(inp["q"])[0], _f64(inp["q_idx"])[0], _f64(inp["w_idx"])[0]
+
+            def compress(t, _):
+                return oracle.pool(raw, z, w.m) if t == 0 else None
+            state = {}
+
+            def score(t, c):
+                if c is not None:
+                    state["cache"] = c
+                C = state["cache"]
+                V = oracle.visible_count(t, w.m, w.N)
+                return C, V, oracle.index_scores(QI[t], W[t], C[:, 2 * w.D:], V)
+
+            def select(t, a):
+                C, V, s = a
+                return C, oracle.topk_select(s, V, w.k)
+
+            def attend(t, a):
+                C, idx = a
+                return oracle.attend(Q[t], C[:, :w.D], C[:, w.D:2 * w.D], idx)
+            done, el, sms = timed_oracle([("compress", compress), ("score", score),
+                                          ("select", select), ("attend", attend)],
+                                         list(range(w.Tq)), args.cpu_seconds)
+            base["cpu_baseline"] = baseline_record(
+                round(done / el, 3), "tokens/s", sms,
+                f"{done} query positions of tiny_csa (the whole 256-position pipeline repeated; "
+                f"compress once per pass), fp64 NumPy oracle, {el:.1f} s")
+    elif w.name == "hca_decode_1m":
         inp = make_inputs(w, device=dev, parts=["raw", "logits", "q", "q_pos", "n_entries"])
         caches = []
         comp_ms = None
@@ -233,9 +415,13 @@ def other_workload(args):
             else:
                 csa.compress(inp["raw"], inp["logits"], w.m, out=kv)
             caches.append(kv)
+        host_raw = host_z = None
+        nb = 512                   # a sample of one sequence's 8192 blocks for the oracle
+        if want_cpu:
+            host_raw = _f64(inp["raw"][0, : nb * w.m])
+            host_z = _f64(inp["logits"][0, : nb * w.m])
         del inp["raw"]
-        ws = torch.empty(csa.hca_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.N),
-                         dtype=torch.uint8, device=dev)
+        ws = csa.new_workspace(csa.hca_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.N), dev)
         out = torch.empty_like(inp["q"])
 
         def step(i):
@@ -251,44 +437,64 @@ def other_workload(args):
                    value=round(w.B / (ms * 1e-3), 1), unit="tokens/s", ms_per_step=round(ms, 5),
                    config={"workload": w.name, "batch": w.B, "context_tokens": w.q_pos0,
                            "compressed_entries": w.N, "m": w.m, "heads": f"{w.H}x{w.D}"},
-                   roofline={"kernel": "attend_split_kernel<HCA> + combine", "bound": "hbm",
+                   roofline={"kernel": "attend_split_kernel<HCA>", "bound": "hbm",
                              "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                             "algorithmic_bytes_per_launch": step_bytes,
+                             "avg_launch_ms": round(ms, 5)},
                    compress_ms=round(comp_ms, 4),
                    compress_gbs=round(raw_bytes / (comp_ms * 1e-3) / 1e9, 1))
+        if want_cpu:
+            Q = _f64(inp["q"])
+            C0 = _f64(caches[0])
+
+            def attend(b, _):
+                return oracle.hca_attend(Q[b, 0], C0[b, :, :w.D], C0[b, :, w.D:], w.N)
+            done, el, sms = timed_oracle([("attend", attend)], list(range(w.B)),
+                                         args.cpu_seconds / 2)
+            t0 = time.perf_counter()
+            oracle.pool(host_raw, host_z, w.m)
+            comp_s_seq = (time.perf_counter() - t0) * (w.N / nb)
+            rec = baseline_record(round(done / el, 3), "tokens/s", sms,
+                                  f"{done} decode tokens of hca_decode_1m (attention over the "
+                                  f"GPU-compressed caches), fp64 NumPy oracle, {el:.1f} s")
+            rec["compress_s_per_sequence_extrapolated"] = round(comp_s_seq, 3)
+            rec["compress_sample"] = (f"oracle pooling of {nb} of the 8192 blocks of one "
+                                      f"sequence, scaled to the sequence (extrapolated)")
+            base["cpu_baseline"] = rec
     elif w.name in ("csa_decode_1m_fp4", "csa_decode_1m_mx4"):
         mx = w.name == "csa_decode_1m_mx4"
         # one quantised draw; the other copies hold its entries rolled along
         # the entry axis (distinct memory for the cache rotation)
-        first = make_inputs(w, device=dev)
+        first = make_inputs(w, device=dev, keep_unquantised=want_cpu)
+        unq = {n: first.pop(n) for n in ("ki_unquantised", "q_idx_unquantised") if n in first}
         copies = [first]
         for c in range(1, N_COPIES):
             cp = dict(first)
             for name in ("ki_codes", "ki_scale", "k_cache", "v_cache"):
                 cp[name] = torch.roll(first[name], shifts=997 * c, dims=1)
             copies.append(cp)
-        ws_topk = torch.empty(csa.index_topk_workspace_bytes(w.B, 1, w.N, w.k), dtype=torch.uint8,
-                              device=dev)
-        ws_attn = torch.empty(csa.attend_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.k),
-                              dtype=torch.uint8, device=dev)
+        ws_step = csa.new_workspace(csa.index_topk_attend_workspace_bytes(
+            3 if mx else 2, torch.bfloat16, w.B, 1, w.N, w.H, w.D, w.k), dev)
         idx = torch.empty((w.B, 1, w.k), dtype=torch.int32, device=dev)
         out = torch.empty_like(copies[0]["q"])
         scores = torch.empty((w.B, 1, w.N), dtype=torch.float32, device=dev)
 
         def step(i):
             c = copies[i % N_COPIES]
-            csa.index_topk(c["q_codes"], c["w_idx"], c["ki_codes"], c["q_pos"], c["n_entries"], w.m,
-                           w.k, q_scale=c["q_scale"], k_scale=c["ki_scale"], workspace=ws_topk,
-                           out=idx)
-            csa.attend(c["q"], c["k_cache"], c["v_cache"], idx, c["n_entries"], workspace=ws_attn,
-                       out=out)
+            csa.index_topk_attend(c["q_codes"], c["w_idx"], c["ki_codes"], c["q"], c["k_cache"],
+                                  c["v_cache"], c["q_pos"], c["n_entries"], w.m, w.k,
+                                  q_scale=c["q_scale"], k_scale=c["ki_scale"], workspace=ws_step,
+                                  out=out)
 
         def score_only(i):
             c = copies[i % N_COPIES]
             csa.index_score(c["q_codes"], c["w_idx"], c["ki_codes"], c["q_pos"], c["n_entries"], w.m,
                             q_scale=c["q_scale"], k_scale=c["ki_scale"], out=scores)
         ms = timed(step, args.steps, args.warmup)
+        gap = tm.launch_gap()
         sms = timed(score_only, args.steps, args.warmup)
+        kms = sms - gap
         extra = {}
         if mx:
             # the MX encoder on the GPU: a whole bf16 indexer-key cache
@@ -301,11 +507,11 @@ def other_workload(args):
             extra = {"quantize_kcache_ms": round(qms, 4),
                      "quantize_kcache_gbs": round(qbytes / (qms * 1e-3) / 1e9, 1)}
             del kb, kcd, ksd
-        # per (row, entry): 64 B codes + the scales (16 B fp32 or 4 E8M0 bytes)
-        # + 4 B score; per row the query codes, scales and head weights
+        # per (row, entry): 64 B codes + the scales (16 B fp32 or 4 E8M0 bytes);
+        # per row the query codes, scales and head weights
         sc_b = 4 if mx else 16
-        score_bytes = w.B * w.N * (64 + sc_b + 4) + w.B * w.H_I * (64 + sc_b + 4)
-        gbs = score_bytes / (sms * 1e-3) / 1e9
+        score_bytes = w.B * w.N * (64 + sc_b) + w.B * w.H_I * (64 + sc_b + 4)
+        gbs = score_bytes / (kms * 1e-3) / 1e9
         res = dict(metric=("CSA decode tokens/sec at 1M context, MX FP4 indexer (E8M0 scales), "
                            "1 MI355X") if mx else
                           "CSA decode tokens/sec at 1M context, FP4 indexer, 1 MI355X",
@@ -313,13 +519,31 @@ def other_workload(args):
                    config={"workload": w.name, "batch": w.B, "context_tokens": w.q_pos0,
                            "compressed_entries": w.N, "m": w.m,
                            "indexer": "64x128 FP4 E2M1, E8M0 block scales" if mx else
-                                      "64x128 FP4 E2M1", "top_k": w.k},
+                                      "64x128 FP4 E2M1", "top_k": w.k,
+                           "timing": "csa_index_topk_attend"},
                    roofline={"kernel": "score_mx4_h64d128_kernel" if mx else
                                        "score_fp4_h64d128_kernel", "bound": "hbm",
                              "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
                              "algorithmic_bytes_per_launch": score_bytes,
-                             "avg_launch_ms": round(sms, 5)}, **extra)
+                             "avg_launch_ms": round(sms, 5), "dispatch_gap_ms": round(gap, 5),
+                             "kernel_ms": round(kms, 5)}, **extra)
+        if want_cpu:
+            deq = oracle.mx4_dequantize if mx else oracle.fp4_dequantize
+            # recall of the GPU's selection against the oracle on the
+            # unquantised draws (what FP4 itself costs the selection; reported)
+            csa.index_topk(first["q_codes"], first["w_idx"], first["ki_codes"], first["q_pos"],
+                           first["n_entries"], w.m, w.k, q_scale=first["q_scale"],
+                           k_scale=first["ki_scale"], out=idx)
+            I = idx.cpu().numpy()
+            KU, QU, W = _f64(unq["ki_unquantised"]), _f64(unq["q_idx_unquantised"]), _f64(first["w_idx"])
+            rec_u = []
+            for b in range(w.B):
+                ref = oracle.topk_select(oracle.index_scores(QU[b, 0], W[b, 0], KU[b], w.N), w.N, w.k)
+                rec_u.append(round(len(set(I[b, 0].tolist()) & set(ref.tolist())) / w.k, 4))
+            res["recall_vs_unquantised_oracle"] = rec_u
+            del KU, QU
+            base["cpu_baseline"] = decode_oracle_baseline(w, first, args.cpu_seconds, dequant=deq)
     elif w.name == "csa_prefill_chunk":
         inp = make_inputs(w, device=dev)
         cache = torch.empty((1, w.N, 384), dtype=torch.bfloat16, device=dev)
@@ -327,10 +551,8 @@ def other_workload(args):
         cache[..., 128:256] = inp["v_cache"]
         cache[..., 256:] = inp["ki_cache"]
         kc, vc, ki = cache[..., :128], cache[..., 128:256], cache[..., 256:]
-        ws_topk = torch.empty(csa.index_topk_workspace_bytes(1, w.Tq, w.N, w.k), dtype=torch.uint8,
-                              device=dev)
-        ws_attn = torch.empty(csa.attend_workspace_bytes(torch.bfloat16, 1, w.Tq, w.H, w.D, w.k),
-                              dtype=torch.uint8, device=dev)
+        ws_topk = csa.new_workspace(csa.index_topk_workspace_bytes(1, w.Tq, w.N, w.k), dev)
+        ws_attn = csa.new_workspace(csa.attend_workspace_bytes(torch.bfloat16, 1, w.Tq, w.H, w.D, w.k), dev)
         idx = torch.empty((1, w.Tq, w.k), dtype=torch.int32, device=dev)
         out = torch.empty_like(inp["q"])
         scores = torch.empty((1, w.Tq, w.N), dtype=torch.float32, device=dev)
@@ -344,8 +566,7 @@ def other_workload(args):
         def score_only(i):
             csa.index_score(inp["q_idx"], inp["w_idx"], ki, inp["q_pos"], inp["n_entries"], w.m,
                             out=scores)
-        ws_topk16 = torch.empty(csa.index_topk_bf16_workspace_bytes(1, w.Tq, w.N, w.k),
-                                dtype=torch.uint8, device=dev)
+        ws_topk16 = csa.new_workspace(csa.index_topk_bf16_workspace_bytes(1, w.Tq, w.N, w.k), dev)
 
         def step_bf16_scores(i):   # the same step with the score matrix held in bf16
             csa.compress(inp["raw"], inp["logits"], w.m, out=cache[:, w.n_cache:])
@@ -366,12 +587,44 @@ def other_workload(args):
                            "context_tokens": w.q_pos0, "compressed_entries": w.N, "m": w.m,
                            "top_k": w.k},
                    roofline={"kernel": "score_prefill_bf16_h64d128_kernel", "bound": "mfma",
-                             "achieved": round(tfs, 1), "peak": 2500.0, "unit": "TFLOP/s",
-                             "frac": round(tfs / 2500.0, 4), "traffic": None,
-                             "algorithmic_flop_per_launch": flop, "avg_launch_ms": round(sms, 4)},
+                             "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS,
+                             "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                             "traffic": None, "algorithmic_flop_per_launch": flop,
+                             "avg_launch_ms": round(sms, 4)},
                    bf16_index_scores={"ms_per_step": round(ms16, 5),
                                       "tokens_per_s": round(w.Tq / (ms16 * 1e-3), 1)})
         base["steps"], base["warmup"] = steps, warm
+        if want_cpu:
+            raw, z = _f64(inp["raw"])[0], _f64(inp["logits"])[0]
+            C = np.concatenate([_f64(cache[0, : w.n_cache]),
+                                oracle.pool(raw, z, w.m)], axis=0)       # the oracle's own pool
+            Q, QI, W = _f64(inp["q"])[0], _f64(inp["q_idx"])[0], _f64(inp["w_idx"])[0]
+            t0 = time.perf_counter()
+            oracle.pool(raw, z, w.m)
+            comp_ms = 1e3 * (time.perf_counter() - t0)
+            rng = np.random.default_rng(2)
+            sample = sorted(rng.choice(w.Tq, size=64, replace=False).tolist())
+
+            def score(i, _):
+                V = oracle.visible_count(w.q_pos0 + i, w.m, w.N)
+                return V, oracle.index_scores(QI[i], W[i], C[:, 256:], V)
+
+            def select(i, a):
+                V, s = a
+                return oracle.topk_select(s, V, w.k)
+
+            def attend(i, idx_):
+                return oracle.attend(Q[i], C[:, :128], C[:, 128:256], idx_)
+            done, el, sms_ = timed_oracle([("score", score), ("select", select), ("attend", attend)],
+                                          sample, args.cpu_seconds)
+            per_tok_s = el / done + comp_ms * 1e-3 / w.Tq
+            rec = baseline_record(round(1.0 / per_tok_s, 3), "tokens/s", sms_,
+                                  f"{done} of the chunk's 4096 query positions (64 sampled, taken "
+                                  f"in turn) plus the compress stage of the whole chunk "
+                                  f"({comp_ms:.0f} ms, shared by its 4096 tokens), fp64 NumPy "
+                                  f"oracle, {el:.1f} s")
+            rec["compress_ms_per_chunk"] = round(comp_ms, 1)
+            base["cpu_baseline"] = rec
     else:
         print(f"unknown workload {w.name}", file=sys.stderr)
         sys.exit(2)
@@ -379,20 +632,7 @@ def other_workload(args):
     print(json.dumps(base))
 
 
-def _stages(w, score_ms, index_topk_ms, attend_ms, score_bytes):
-    """Per-stage time, algorithmic bytes and HBM fraction (selection = the
-    index_topk call minus the score kernel, so it includes one launch gap)."""
-    sel_b, att_b = stage_bytes(w)
-    out = {}
-    for name, ms, b in (("score", score_ms, score_bytes),
-                        ("selection", index_topk_ms - score_ms, sel_b),
-                        ("attention", attend_ms, att_b)):
-        gbs = b / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
-        out[name] = {"ms": round(ms, 5), "algorithmic_bytes": b, "gbs": round(gbs, 1),
-                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-    return out
-
-
+# ---------------------------------------------------------------- headline
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -402,7 +642,6 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
-
     if args.workload != WORKLOAD:
         other_workload(args)
         return
@@ -413,17 +652,33 @@ def main():
     w = WORKLOADS[WORKLOAD]
     dev = "cuda"
     copies = [make_inputs(w.scaled(seed=w.seed + 1000 * c), device=dev) for c in range(N_COPIES)]
-    ws_topk = torch.empty(csa.index_topk_workspace_bytes(w.B, 1, w.N, w.k), dtype=torch.uint8, device=dev)
-    ws_attn = torch.empty(csa.attend_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.k),
-                          dtype=torch.uint8, device=dev)
+    ws_step = csa.new_workspace(csa.index_topk_attend_workspace_bytes(
+        1, torch.bfloat16, w.B, 1, w.N, w.H, w.D, w.k), dev)
+    ws_topk = csa.new_workspace(csa.index_topk_workspace_bytes(w.B, 1, w.N, w.k), dev)
+    ws_topk16 = csa.new_workspace(csa.index_topk_bf16_workspace_bytes(w.B, 1, w.N, w.k), dev)
+    ws_attn = csa.new_workspace(csa.attend_workspace_bytes(torch.bfloat16, w.B, 1, w.H, w.D, w.k),
+                                dev)
     idx = [torch.empty((w.B, 1, w.k), dtype=torch.int32, device=dev) for _ in range(N_COPIES)]
     out = [torch.empty_like(c["q"]) for c in copies]
     scores = torch.empty((w.B, 1, w.N), dtype=torch.float32, device=dev)
 
     def step(i):
         c = copies[i % N_COPIES]
+        csa.index_topk_attend(c["q_idx"], c["w_idx"], c["ki_cache"], c["q"], c["k_cache"],
+                              c["v_cache"], c["q_pos"], c["n_entries"], w.m, w.k,
+                              workspace=ws_step, out=out[i % N_COPIES])
+
+    def step_two_calls(i):
+        c = copies[i % N_COPIES]
         csa.index_topk(c["q_idx"], c["w_idx"], c["ki_cache"], c["q_pos"], c["n_entries"], w.m, w.k,
                        workspace=ws_topk, out=idx[i % N_COPIES])
+        csa.attend(c["q"], c["k_cache"], c["v_cache"], idx[i % N_COPIES], c["n_entries"],
+                   workspace=ws_attn, out=out[i % N_COPIES])
+
+    def step_bf16_scores(i):
+        c = copies[i % N_COPIES]
+        csa.index_topk_bf16(c["q_idx"], c["w_idx"], c["ki_cache"], c["q_pos"], c["n_entries"],
+                            w.m, w.k, workspace=ws_topk16, out=idx[i % N_COPIES])
         csa.attend(c["q"], c["k_cache"], c["v_cache"], idx[i % N_COPIES], c["n_entries"],
                    workspace=ws_attn, out=out[i % N_COPIES])
 
@@ -432,50 +687,12 @@ def main():
         csa.index_score(c["q_idx"], c["w_idx"], c["ki_cache"], c["q_pos"], c["n_entries"], w.m,
                         out=scores)
 
-    def index_topk_only(i):
-        c = copies[i % N_COPIES]
-        csa.index_topk(c["q_idx"], c["w_idx"], c["ki_cache"], c["q_pos"], c["n_entries"], w.m, w.k,
-                       workspace=ws_topk, out=idx[i % N_COPIES])
-
-    def attend_only(i):
-        c = copies[i % N_COPIES]
-        csa.attend(c["q"], c["k_cache"], c["v_cache"], idx[i % N_COPIES], c["n_entries"],
-                   workspace=ws_attn, out=out[i % N_COPIES])
-
-    # Host launch overhead (Python + ctypes) is comparable to a kernel's
-    # duration, so every timed region is enqueued behind a spin kernel that
-    # keeps the GPU busy until the whole region is queued: the events then
-    # measure back-to-back GPU execution only.
-    cycles_per_ms = _calibrate_sleep()
-
-    def hold_gpu(ms):
-        torch.cuda._sleep(int(cycles_per_ms * ms))
-
-    def timed(fn, steps, warmup, per_launch=False):
-        for i in range(warmup):
-            fn(i)
-        torch.cuda.synchronize()
-        hold_gpu(20.0 + 0.05 * steps)
-        if per_launch:
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(steps)]
-            for i in range(steps):
-                ev[i][0].record()
-                fn(i)
-                ev[i][1].record()
-            torch.cuda.synchronize()
-            times = [a.elapsed_time(b) for a, b in ev]
-            if per_launch == "quantiles":
-                times.sort()
-                return [times[int(q * (steps - 1))] for q in (0.1, 0.5, 0.9)]
-            return sum(times) / steps
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for i in range(steps):
-            fn(i)
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps          # ms per call
+    tm = Timer()
+    if args.step_only:
+        ms = tm.period(step, args.steps, args.warmup)
+        print(json.dumps({"workload": WORKLOAD, "ms_per_step": round(ms, 5),
+                          "steps": args.steps, "warmup": args.warmup}))
+        return
 
     graph_ms = None
     if args.graph:
@@ -492,25 +709,24 @@ def main():
             with torch.cuda.graph(g):
                 step(i)
             graphs.append(g)
-        graph_ms = timed(lambda i: graphs[i % N_COPIES].replay(), args.steps, args.warmup)
+        graph_ms = tm.period(lambda i: graphs[i % N_COPIES].replay(), args.steps, args.warmup)
 
-    if args.score_only:
-        ms = timed(score_only, args.steps, args.warmup, per_launch=True)
-        print(json.dumps({"score_only_ms": round(ms, 5), "launches": args.steps + args.warmup}))
-        return
-    ms = timed(step, args.steps, args.warmup)
-    step_q = timed(step, args.steps, args.warmup, per_launch="quantiles")
-    score_ms = timed(score_only, args.steps, args.warmup, per_launch=True)
-    index_topk_ms = timed(index_topk_only, args.steps, args.warmup, per_launch=True)
-    attend_ms = timed(attend_only, args.steps, args.warmup, per_launch=True)
+    ms = tm.period(step, args.steps, args.warmup)
+    step_q = tm.quantiles(step, args.steps, args.warmup)
+    two_ms = tm.period(step_two_calls, args.steps, args.warmup)
+    bf16_ms = tm.period(step_bf16_scores, args.steps, args.warmup)
+    gap_ms = tm.launch_gap()
+    score_launch_ms = tm.period(score_only, args.steps, args.warmup)
+    score_kernel_ms = score_launch_ms - gap_ms
     best_ms = min(ms, graph_ms) if graph_ms else ms
 
-    step_bytes, score_bytes = algorithmic_bytes(w)
-    tok_s = w.B / (best_ms * 1e-3)
-    score_gbs = score_bytes / (score_ms * 1e-3) / 1e9
+    step_bytes, score_bytes = decode_bytes(w)
+    step_gbs = step_bytes / (best_ms * 1e-3) / 1e9
+    score_gbs = score_bytes / (score_kernel_ms * 1e-3) / 1e9
+    rp_us = recorded_score_kernel_us()
     result = {
         "metric": METRIC,
-        "value": round(tok_s, 1),
+        "value": round(w.B / (best_ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -525,24 +741,34 @@ def main():
                    "compressed_entries": w.N, "m": w.m, "indexer": f"{w.H_I}x{w.D_I} bf16",
                    "top_k": w.k, "core_attention": f"{w.H}x{w.D} bf16, 1 shared KV head",
                    "input_copies_rotated": N_COPIES,
+                   "step": "csa_index_topk_attend (score kernel, then selection + attention)",
                    "timing": "hip graph" if graph_ms and graph_ms <= ms else "eager launches"},
-        "step_achieved_gbs": round(step_bytes / (best_ms * 1e-3) / 1e9, 1),
+        "step_achieved_gbs": round(step_gbs, 1),
         "step_algorithmic_bytes": step_bytes,
+        "step_frac_hbm": round(step_gbs / HBM_PEAK_GBS, 4),
+        "gate": {"figure": "step_frac_hbm", "target": STEP_GATE_FRAC,
+                 "met": step_gbs / HBM_PEAK_GBS >= STEP_GATE_FRAC,
+                 "ms_per_step_at_target": round(step_bytes / (STEP_GATE_FRAC * HBM_PEAK_GBS * 1e9)
+                                                * 1e3, 5)},
         "ms_per_step_eager": round(ms, 5),
         "step_ms_p10_p50_p90": [round(x, 5) for x in step_q],
         "ms_per_step_graph": round(graph_ms, 5) if graph_ms else None,
-        "call_ms": {"index_score": round(score_ms, 5),
-                    "index_topk (score + selection)": round(index_topk_ms, 5),
-                    "attend (split + combine)": round(attend_ms, 5)},
-        "stages": _stages(w, score_ms, index_topk_ms, attend_ms, score_bytes),
+        "ms_per_step_two_calls": round(two_ms, 5),
+        "bf16_index_scores": {"ms_per_step": round(bf16_ms, 5),
+                              "speedup_vs_fp32_scores_two_calls": round(two_ms / bf16_ms, 4)},
+        "dispatch_gap_ms": round(gap_ms, 5),
         "roofline": {"kernel": SCORE_KERNEL, "bound": "hbm",
                      "achieved": round(score_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(score_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "algorithmic_bytes_per_launch": score_bytes,
-                     "avg_launch_ms": round(score_ms, 5)},
+                     "avg_launch_ms": round(score_launch_ms, 5),
+                     "kernel_ms": round(score_kernel_ms, 5),
+                     "rocprof_avg_ms": round(rp_us * 1e-3, 5) if rp_us else None,
+                     "frac_rocprof": round(score_bytes / (rp_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                     if rp_us else None},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, copies[0], args.cpu_seconds)
+        result["cpu_baseline"] = decode_oracle_baseline(w, copies[0], args.cpu_seconds)
     print(json.dumps(result))
 
 

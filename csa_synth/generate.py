@@ -127,7 +127,8 @@ def _store(x: torch.Tensor, dtype: str) -> torch.Tensor:
     raise ValueError(dtype)
 
 
-def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor]:
+def make_inputs(w: Workload, device="cpu", parts=None,
+                keep_unquantised: bool = False) -> Dict[str, torch.Tensor]:
     """Draw the inputs of workload ``w`` on ``device``.
 
     Returns a dict of tensors (names below); ``parts`` limits which are drawn.
@@ -142,6 +143,8 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
       q_idx     [B, Tq, H_I, D_I] (fp4, mx4: q_codes / q_scale)
       w_idx     [B, Tq, H_I]    fp32
       q_pos     [B, Tq] int32, n_entries [B] int32
+    keep_unquantised (fp4, mx4): also return the fp32 draws before encoding,
+      ki_unquantised [B, N, D_I] and q_idx_unquantised [B, Tq, H_I, D_I].
     """
     want = set(parts) if parts is not None else None
 
@@ -188,6 +191,8 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
             codes, scale = (fp4_quantize if w.index_dtype == "fp4" else mx4_quantize)(kic)
             out["ki_codes"] = codes.to(device)
             out["ki_scale"] = scale.to(device)
+            if keep_unquantised:
+                out["ki_unquantised"] = kic.clone()
         else:
             out["ki_cache"] = _store(kic, w.index_dtype)
         del kic
@@ -199,6 +204,8 @@ def make_inputs(w: Workload, device="cpu", parts=None) -> Dict[str, torch.Tensor
             codes, scale = (fp4_quantize if w.index_dtype == "fp4" else mx4_quantize)(qi)
             out["q_codes"] = codes.to(device)
             out["q_scale"] = scale.to(device)
+            if keep_unquantised:
+                out["q_idx_unquantised"] = qi
         else:
             out["q_idx"] = _store(qi, w.index_dtype)
     if w.kind == "csa" and need("w_idx"):

@@ -229,7 +229,17 @@ csa_status_t csa_index_topk_bf16_workspace(int B, int Tq, int N_max, int k, size
  * k_c, v_c  [B, N_max, D] sharing strides (kv_sb, kv_sn).
  * topk_idx  [B, Tq, k] int32.
  * out       [B, Tq, H, D] (dtype); lse [B, Tq, H] fp32 or NULL.
- * Supported: F32 / BF16 with H <= 64, D in {32, 64, 128}; tuned BF16 64 x 128.
+ * ws        csa_attend_workspace bytes, 16-byte aligned (NULL when that is 0).
+ *           The tuned path splits the entry list over several workgroups
+ *           that merge their partial results through synchronisation words
+ *           at the front of the workspace: the workspace must be ZERO-FILLED
+ *           before its first use (for example with hipMemsetAsync).  Every
+ *           call leaves those words zero again, so a workspace is cleared
+ *           once and then reused by any number of calls of any shape (this
+ *           holds for hca_attend and swa_attend workspaces too).  Calls that
+ *           may run concurrently need separate workspaces.
+ * Supported: F32 / BF16 with H <= 64, D in {32, 64, 128}, B * Tq <= 65536;
+ *            tuned BF16 64 x 128.
  */
 csa_status_t csa_attend(const void* q, const void* k_c, const void* v_c,
                         int64_t kv_sb, int64_t kv_sn,
@@ -253,6 +263,42 @@ csa_status_t hca_attend(const void* q, const void* k_c, const void* v_c,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 csa_status_t hca_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
                                   size_t* bytes);
+
+/*
+ * csa_index_topk_attend - one CSA decode step: Lightning Indexer scores,
+ * top-k selection and core attention over the selected entries, in one call
+ * ("DeepSeek V4 技术解读", §2.1, the three steps of the CSA flow: compressed
+ * KV cache -> Lightning Indexer -> core attention).
+ *
+ *   Results equal csa_index_topk followed by csa_attend on the same inputs:
+ *   out (and lse) as csa_attend computes them over the top-k set of each
+ *   query token; topk_idx (NULL: not returned) as csa_index_topk returns it.
+ *
+ * Indexer arguments as in csa_index_topk (q_idx .. idx_dtype, H_I, D_I);
+ * attention arguments as in csa_attend (q, k_c, v_c, kv_sb, kv_sn, dtype, H,
+ * D, scale, out, lse); q_pos, n_entries, B, Tq, N_max, m, k as in both.
+ * ws        csa_index_topk_attend_workspace bytes, 16-byte aligned, ZERO-FILLED
+ *           before its first use (it starts with the attention's
+ *           synchronisation words; every call leaves them zero).
+ * The step runs the score kernel, the selection kernel(s) and the split
+ * attention kernel (which merges its splits itself) back to back on
+ * `stream`, with the index lists in the workspace when topk_idx is NULL.
+ * Supported: as csa_index_topk and csa_attend together.
+ */
+csa_status_t csa_index_topk_attend(const void* q_idx, const void* q_scale, const float* w_idx,
+                                   const void* k_idx, const void* k_scale,
+                                   int64_t k_sb, int64_t k_sn, int64_t ks_sb, int64_t ks_sn,
+                                   csa_dtype_t idx_dtype,
+                                   const void* q, const void* k_c, const void* v_c,
+                                   int64_t kv_sb, int64_t kv_sn, csa_dtype_t dtype,
+                                   const int32_t* q_pos, const int32_t* n_entries,
+                                   int B, int Tq, int N_max, int H_I, int D_I, int H, int D,
+                                   int m, int k, float scale,
+                                   void* out, float* lse, int32_t* topk_idx,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
+csa_status_t csa_index_topk_attend_workspace(csa_dtype_t idx_dtype, csa_dtype_t dtype, int B,
+                                             int Tq, int N_max, int H, int D, int k,
+                                             size_t* bytes);
 
 /*
  * swa_attend - sliding-window attention over uncompressed tokens ("DeepSeek

@@ -25,9 +25,10 @@ import torch
 __all__ = [
     "CsaError", "library_path", "load_library",
     "compress", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
-    "attend", "hca_attend", "swa_attend", "index_topk_workspace_bytes",
+    "attend", "hca_attend", "swa_attend", "index_topk_attend", "index_topk_workspace_bytes",
+    "index_topk_attend_workspace_bytes",
     "index_topk_bf16_workspace_bytes", "swa_workspace_bytes",
-    "attend_workspace_bytes", "hca_workspace_bytes",
+    "attend_workspace_bytes", "hca_workspace_bytes", "new_workspace",
     "EXPORTED_SYMBOLS",
 ]
 
@@ -43,6 +44,7 @@ EXPORTED_SYMBOLS = (
     "csa_index_topk_bf16", "csa_index_topk_bf16_workspace",
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
     "swa_attend", "swa_attend_workspace",
+    "csa_index_topk_attend", "csa_index_topk_attend_workspace",
 )
 
 
@@ -86,6 +88,12 @@ _SIGS = {
                     _i32, _f32, _vp, _vp, _vp, _sz, _vp], _i32),
     "swa_attend_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)],
                              _i32),
+    "csa_index_topk_attend": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32,
+                               _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp,
+                               _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                               _vp, _vp, _vp, _vp, _sz, _vp], _i32),
+    "csa_index_topk_attend_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.POINTER(_sz)], _i32),
 }
 
 
@@ -147,11 +155,20 @@ def _contig(t: torch.Tensor, name: str) -> torch.Tensor:
 
 
 def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Tuple[Optional[torch.Tensor], int]:
+    """The caller's workspace, or a new zero-filled one: the library's
+    workspaces start with synchronisation words that must be zero before the
+    first call (every call leaves them zero).  A caller-owned workspace must
+    have been zero-filled once (``new_workspace`` does that)."""
     if nbytes == 0:
         return ws, 0 if ws is None else ws.numel() * ws.element_size()
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     return ws, ws.numel() * ws.element_size()
+
+
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of ``nbytes`` bytes (reusable across calls)."""
+    return torch.zeros(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
 # ------------------------------------------------------------------ compress
@@ -396,3 +413,48 @@ def swa_attend(q, k_cache, v_cache, q_pos, n_tokens, window: int, scale: Optiona
         q_pos.data_ptr(), n_tokens.data_ptr(), _dtype_code(q), B, Tq, H, D, N_max, window, scale,
         out.data_ptr(), _ptr(lse), _ptr(ws), ws_bytes, _stream()))
     return (out, lse) if with_lse else out
+
+
+# ------------------------------------------------------------------ whole decode step
+def index_topk_attend_workspace_bytes(idx_dtype_code: int, dtype: torch.dtype, B: int, Tq: int,
+                                      N_max: int, H: int, D: int, k: int) -> int:
+    need = ctypes.c_size_t(0)
+    code = CSA_F32 if dtype == torch.float32 else CSA_BF16
+    _check(load_library().csa_index_topk_attend_workspace(idx_dtype_code, code, B, Tq, N_max, H,
+                                                          D, k, ctypes.byref(need)))
+    return need.value
+
+
+def index_topk_attend(q_idx, w_idx, k_idx, q, k_cache, v_cache, q_pos, n_entries, m: int, k: int,
+                      q_scale=None, k_scale=None, scale: Optional[float] = None,
+                      with_lse: bool = False, with_idx: bool = False,
+                      workspace: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None, idx_out: Optional[torch.Tensor] = None):
+    """One CSA decode step in one call: indexer scores, top-k and core attention
+    -> o [B, Tq, H, D] (+ lse [B, Tq, H]) (+ idx [B, Tq, k] int32), equal to
+    index_topk followed by attend."""
+    dt, B, Tq, H_I, D_I, N_max, ks_sb, ks_sn = _index_args(q_idx, w_idx, k_idx, q_scale, k_scale)
+    B2, Tq2, H, D, N2 = _attn_common(q, k_cache, v_cache)
+    if (B2, Tq2, N2) != (B, Tq, N_max):
+        raise ValueError("indexer and attention shapes disagree")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    need = index_topk_attend_workspace_bytes(dt, q.dtype, B, Tq, N_max, H, D, k)
+    ws, ws_bytes = _workspace(need, q.device, workspace)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Tq, H), dtype=torch.float32, device=q.device) if with_lse else None
+    idx = idx_out
+    if with_idx and idx is None:
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device=q.device)
+    _check(load_library().csa_index_topk_attend(
+        q_idx.data_ptr(), _ptr(q_scale), w_idx.data_ptr(), k_idx.data_ptr(), _ptr(k_scale),
+        k_idx.stride(0), k_idx.stride(1), ks_sb, ks_sn, dt,
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1),
+        _dtype_code(q), q_pos.data_ptr(), n_entries.data_ptr(),
+        B, Tq, N_max, H_I, D_I, H, D, m, k, scale,
+        out.data_ptr(), _ptr(lse), _ptr(idx), _ptr(ws), ws_bytes, _stream()))
+    res = (out,)
+    if with_lse:
+        res += (lse,)
+    if with_idx:
+        res += (idx,)
+    return res[0] if len(res) == 1 else res

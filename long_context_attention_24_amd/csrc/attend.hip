@@ -265,6 +265,110 @@ __device__ __forceinline__ void compute_round(uint32_t vmask, bool active, const
   }
 }
 
+// ---- merge of the split partials inside the split kernel
+// The splits of a row meet at a barrier in global memory: each workgroup,
+// once its partial is stored (device-scope stores, completed before it
+// arrives), adds one to the row's arrival counter and waits until every
+// split has arrived; then split s merges its own slice of the output dims
+// over all splits, in split order (the result does not depend on which
+// workgroup finishes first).  Counters: arrive[rows], depart[rows] and one
+// word counting waits that gave up, at the front of the workspace; zero
+// before the first call, and every call leaves them zero (the last
+// workgroup of a row to leave the barrier resets the row's two counters).
+// The wait is bounded so that a kernel always ends.  The splits of a row are
+// consecutive workgroups and dispatch follows workgroup order, so a waiting
+// workgroup only ever waits for workgroups that are already running.
+constexpr int kSpinLimit = 1 << 22;               // about 0.1 s of polling
+constexpr int kAttendMaxRows = 65536;             // B * Tq (the grid's y extent)
+constexpr int kSyncStride = 32;                   // int32 words per row's counters
+
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void row_barrier(int32_t* sync, int rows, int row, int n) {
+  __builtin_amdgcn_s_waitcnt(0);                  // this thread's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t* arrive = sync + kSyncStride * row;     // one 128-byte line per row
+    int32_t* depart = arrive + 1;
+    __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int it = 0; __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n; ++it) {
+      if (it == kSpinLimit) {
+        __hip_atomic_fetch_add(sync + kSyncStride * kAttendMaxRows, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (__hip_atomic_fetch_add(depart, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1) {
+      __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(depart, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
+// Split s of nsplit merges output dims [d0, d1), d0 = s * Ld, Ld = ceil(128 /
+// nsplit) rounded up to a multiple of 4.  Thread (h, grp) owns dims
+// db .. db + 3 of head h for db = d0 + 4 grp, d0 + 4 (grp + NT / 64), ...:
+// every load is a coalesced 64-float row of a partial.  Splits are taken in
+// groups of eight, every load of a group issued before its arithmetic, and
+// the running maximum rescales what is already summed.
+template <int NT>
+__device__ __forceinline__ void merge_splits(const float* __restrict__ prow, int nsplit, int split,
+                                             uint16_t* __restrict__ orow, float* __restrict__ lrow) {
+  constexpr int NG = NT / 64;
+  constexpr int U = 8;
+  const int h = threadIdx.x & 63, grp = threadIdx.x >> 6;
+  const int per = (128 + nsplit - 1) / nsplit;
+  const int Ld = (per + 3) & ~3;
+  const int d0 = split * Ld, d1 = min(128, d0 + Ld);
+  const int64_t sstride = static_cast<int64_t>(kPartRows) * 64;
+  for (int db = d0 + 4 * grp; db < d1; db += 4 * NG) {
+    float M = kNegInf, L = 0.f;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nsplit; s0 += U) {
+      float v[U][4], ms[U], ls[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = s0 + u < nsplit;
+        const float* ps = prow + static_cast<int64_t>(ok ? s0 + u : s0) * sstride + h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[u][i] = ld_coherent(ps + (db + i) * 64);
+        const float mu = ld_coherent(ps + 128 * 64);
+        ms[u] = ok ? mu : kNegInf;
+        ls[u] = ld_coherent(ps + 129 * 64);
+      }
+      float mg = M;
+#pragma unroll
+      for (int u = 0; u < U; ++u) mg = fmaxf(mg, ms[u]);
+      if (mg == kNegInf) continue;
+      const float a = M == kNegInf ? 0.f : exp2_fast(M - mg);
+      L *= a;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= a;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float wu = ms[u] == kNegInf ? 0.f : exp2_fast(ms[u] - mg);
+        L = fmaf(wu, ls[u], L);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
+      }
+      M = mg;
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    uint2 w2;
+    w2.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+    w2.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+    *reinterpret_cast<uint2*>(orow + h * 128 + db) = w2;
+    if (lrow != nullptr && db == 0) lrow[h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+  }
+}
+
 // One workgroup per (split, query row); 2 KG waves = KG key groups x 2 head
 // halves.  Key group kg takes tiles KG r + kg in round r.  Round r is staged
 // into LDS and its registers are reloaded with round r + 2 before it
@@ -275,14 +379,21 @@ __device__ __forceinline__ void compute_round(uint32_t vmask, bool active, const
 // partials to merge are halved).  Output: the split's unnormalised O^T,
 // running maximum m and sum l (base-2 logits) in d-major rows, written with
 // coalesced stores.
-template <bool HCA, int KG>
-__global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn, const int32_t* __restrict__ idx,
+// Entry sources: the entry index at position p of a query row's list.
+struct GlobalIdxSrc {              // CSA: the caller's top-k list in global memory
+  const int32_t* __restrict__ irow;
+  int kk;
+  __device__ __forceinline__ int raw(int p) const { return irow[min(p, kk - 1)]; }
+};
+template <bool HCA, int KG, typename Src>
+__device__ __forceinline__ void split_attention(
+    AttnSmem<KG>& sm, const Src& src, int split, int row, const uint16_t* __restrict__ q,
+    const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn,
     int kk, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
     int N_max, int m, int win, float scale_log2, int split_len, int nsplit,
-    float* __restrict__ part) {
-  const int split = blockIdx.x, row = blockIdx.y, b = row / Tq;
+    float* __restrict__ part, int32_t* __restrict__ sync, int rows, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = wave & 1, kg = wave >> 1;
   const int jl = lane & 31, g = lane >> 5;
@@ -298,13 +409,11 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
   const int s_end = min(n, s0 + split_len);
   const int ntiles = s_end > s0 ? (s_end - s0 + 31) / 32 : 0;
   const int nrounds = (ntiles + KG - 1) / KG;
-  const int32_t* irow = HCA ? nullptr : idx + static_cast<int64_t>(row) * kk;
 
   const uint16_t* Kb = K + b * kv_sb;
   const uint16_t* Vb = Vc + b * kv_sb;
   f32x16_t o[4] = {};
   float m_run = kNegInf, l_run = 0.f;
-  __shared__ AttnSmem<KG> sm;
   lds_u16* const vt0 = (lds_u16*)&sm.v[0][kg][0];
   lds_u16* const kt0 = (lds_u16*)&sm.k[0][kg][0];
   lds_u16* const vt1 = (lds_u16*)&sm.v[1][kg][0];
@@ -317,7 +426,7 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
   // flight, the next round's included.
   auto entry_raw = [&](int rr) -> int {
     const int p_ = s0 + 32 * (KG * rr + kg) + jl;
-    return HCA ? lo + p_ : irow[min(p_, kk - 1)];
+    return HCA ? lo + p_ : src.raw(p_);
   };
   auto entry_ok = [&](int rr, int e) -> int {
     const int t_ = KG * rr + kg, p_ = s0 + 32 * t_ + jl;
@@ -399,6 +508,43 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
       ak[k2] = M == kNegInf ? 0.f : exp2_fast(mk[k2] - M);
       L = fmaf(ak[k2], lk[k2], L);
     }
+    // this key group's d-tiles, merged over the key groups
+    float vals[4][16];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      if (dt % KG != kg) continue;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float v = 0.f;
+#pragma unroll
+        for (int k2 = 0; k2 < KG; ++k2) {
+          const float x = k2 == kg ? o[dt][i] : xo[((k2 * 2 + hh) * 64 + lane) * kX + 16 * dt + i];
+          v = fmaf(ak[k2], x, v);
+        }
+        vals[dt][i] = v;
+      }
+    }
+    if (nsplit == 1) {
+      // the only split: normalise and write the output directly
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      uint16_t* orow = out + (static_cast<int64_t>(row) * 64 + h) * 128;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        if (dt % KG != kg) continue;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          uint2 w2;
+          w2.x = pack_bf16x2(vals[dt][4 * q4] * inv, vals[dt][4 * q4 + 1] * inv);
+          w2.y = pack_bf16x2(vals[dt][4 * q4 + 2] * inv, vals[dt][4 * q4 + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * q4 + 4 * g) = w2;
+        }
+      }
+      if (lse != nullptr && kg == 0 && g == 0)
+        lse[static_cast<int64_t>(row) * 64 + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+      return;
+    }
+    // partial of this split, stored coherently at device scope (read by the
+    // other workgroups of the row): O^T d-major, then m and l
     float* pr = part + (static_cast<int64_t>(row) * nsplit + split) * kPartRows * 64;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
@@ -406,76 +552,38 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
-        float v = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < KG; ++k2) {
-          const float x = k2 == kg ? o[dt][i] : xo[((k2 * 2 + hh) * 64 + lane) * kX + 16 * dt + i];
-          v = fmaf(ak[k2], x, v);
-        }
-        pr[d * 64 + h] = v;
+        st_coherent(pr + d * 64 + h, vals[dt][i]);
       }
     }
     if (kg == 0 && g == 0) {
-      pr[128 * 64 + h] = M;
-      pr[129 * 64 + h] = L;
+      st_coherent(pr + 128 * 64 + h, M);
+      st_coherent(pr + 129 * 64 + h, L);
     }
   }
+  row_barrier(sync, rows, row, nsplit);
+  merge_splits<128 * KG>(part + static_cast<int64_t>(row) * nsplit * kPartRows * 64, nsplit, split,
+                         out + static_cast<int64_t>(row) * 64 * 128,
+                         lse != nullptr ? lse + static_cast<int64_t>(row) * 64 : nullptr);
 }
 
-// Merge of the split partials.  Grid (rows, 8 dim blocks); thread (h, c)
-// owns output dims 16 y + 4 c .. +3 of head h: every read is a coalesced
-// 64-float row of a partial.
-__global__ __launch_bounds__(256) void attend_combine_kernel(const float* __restrict__ part,
-                                                             int nsplit, uint16_t* __restrict__ out,
-                                                             float* __restrict__ lse) {
-  const int row = blockIdx.x, tid = threadIdx.x;
-  const int h = tid & 63, d0 = 16 * blockIdx.y + 4 * (tid >> 6);
-  const int64_t sstride = static_cast<int64_t>(kPartRows) * 64;
-  const float* base = part + static_cast<int64_t>(row) * nsplit * sstride + h;
-  // One pass over the splits in groups of eight: every load of a group
-  // (maxima, sums, partial rows) is issued before its arithmetic, and the
-  // running maximum rescales what is already summed.
-  constexpr int U = 8;
-  float M = kNegInf, L = 0.f;
-  float acc[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = 0.f;
-  for (int s = 0; s < nsplit; s += U) {
-    float v[U][4], ms[U], ls[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = s + u < nsplit;
-      const float* ps = base + static_cast<int64_t>(ok ? s + u : s) * sstride;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[u][i] = ps[(d0 + i) * 64];
-      ms[u] = ok ? ps[128 * 64] : kNegInf;
-      ls[u] = ps[129 * 64];
-    }
-    float mg = M;
-#pragma unroll
-    for (int u = 0; u < U; ++u) mg = fmaxf(mg, ms[u]);
-    if (mg == kNegInf) continue;
-    const float a = M == kNegInf ? 0.f : exp2_fast(M - mg);
-    L *= a;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] *= a;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float wu = ms[u] == kNegInf ? 0.f : exp2_fast(ms[u] - mg);
-      L = fmaf(wu, ls[u], L);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = fmaf(wu, v[u][i], acc[i]);
-    }
-    M = mg;
-  }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint2 v;
-  v.x = pack_bf16x2(acc[0] * inv, acc[1] * inv);
-  v.y = pack_bf16x2(acc[2] * inv, acc[3] * inv);
-  *reinterpret_cast<uint2*>(out + (static_cast<int64_t>(row) * 64 + h) * 128 + d0) = v;
-  if (lse != nullptr && blockIdx.y == 0 && tid < 64)
-    lse[static_cast<int64_t>(row) * 64 + h] = L > 0.f ? (M + log2f(L)) * kLn2 : kNegInf;
+// One workgroup per (split, query row): CSA over the caller's top-k lists, or
+// HCA / a sliding window over the visible entries.
+template <bool HCA, int KG>
+__global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn, const int32_t* __restrict__ idx,
+    int kk, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
+    int N_max, int m, int win, float scale_log2, int split_len, int nsplit,
+    float* __restrict__ part, int32_t* __restrict__ sync, int rows, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  __shared__ AttnSmem<KG> sm;
+  const int row = blockIdx.y;
+  const GlobalIdxSrc src{HCA ? idx : idx + static_cast<int64_t>(row) * kk, kk};
+  split_attention<HCA, KG>(sm, src, blockIdx.x, row, q, K, Vc, kv_sb, kv_sn, kk, q_pos, n_entries,
+                           Tq, N_max, m, win, scale_log2, split_len, nsplit, part, sync, rows, out,
+                           lse);
 }
+
 
 bool tuned(csa_dtype_t dt, int H, int D) { return dt == CSA_BF16 && H == 64 && D == 128; }
 
@@ -504,12 +612,27 @@ bool attend_supported(csa_dtype_t dt, int H, int D) {
   return H >= 1 && H <= 64 && (D == 32 || D == 64 || D == 128);
 }
 
+// Workspace of the tuned path: a fixed block of merge counters at the front
+// (2 per row for up to kMaxRows rows, plus one word), then the split
+// partials.  The block has the same size and place for every call, and
+// calls leave it zero, so a workspace zero-filled once serves calls of any
+// shape.
+size_t sync_bytes(int) {
+  return (static_cast<size_t>(kSyncStride * kAttendMaxRows + 1) * sizeof(int32_t) + 255) / 256 *
+         256;
+}
+
 size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D,
                               int k_or_nmax) {
   if (!tuned(dt, H, D)) return 0;
   const int sl = split_len(hca);
   const int nsplit = (k_or_nmax + sl - 1) / sl;
-  return static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * kPartRows * 64 * sizeof(float);
+  return sync_bytes(B * Tq) +
+         static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * kPartRows * 64 * sizeof(float);
+}
+
+bool attend_rows_ok(int B, int Tq) {
+  return static_cast<long long>(B) * Tq <= kAttendMaxRows;
 }
 
 hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s) {
@@ -528,23 +651,25 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
   const int n = hca ? (a.win > 0 ? min(a.win, a.N_max) : a.N_max) : a.topk;
   int nsplit = (n + sl - 1) / sl;
   if (nsplit < 1) nsplit = 1;
-  float* part = static_cast<float*>(a.ws);
-  const dim3 grid(nsplit, a.B * a.Tq);
+  const int rows = a.B * a.Tq;
+  int32_t* sync = static_cast<int32_t*>(a.ws);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(a.ws) + sync_bytes(rows));
+  uint16_t* out = static_cast<uint16_t*>(a.out);
+  const dim3 grid(nsplit, rows);
   if (hca)
     hipLaunchKernelGGL((attend_split_kernel<true, kHcaGroups>), grid, dim3(128 * kHcaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
-                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part);
+                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part, sync, rows,
+                       out, a.lse);
   else
     hipLaunchKernelGGL((attend_split_kernel<false, kCsaGroups>), grid, dim3(128 * kCsaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
-                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attend_combine_kernel, dim3(a.B * a.Tq, 8), dim3(256), 0, s, part, nsplit,
-                     static_cast<uint16_t*>(a.out), a.lse);
+                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part, sync, rows,
+                       out, a.lse);
   return hipGetLastError();
 }
+
 
 }  // namespace csa

@@ -242,6 +242,40 @@ csa_status_t csa_index_topk_bf16_workspace(int B, int Tq, int N_max, int k, size
 
 namespace {
 
+// Workspace of the index + top-k pair: score rows | chunk reports | selection.
+struct IndexWs {
+  void* scores;
+  int64_t srs;
+  float2* bounds;                 // NULL when the score kernel writes no reports
+  int n_chunks;
+  void* sel_ws;
+};
+
+// Lays out the workspace and launches the score kernel (with chunk reports
+// when the bounded selection will use them).
+csa_status_t launch_index_scores(const void* q_idx, const void* q_scale, const float* w_idx,
+                                 const void* k_idx, const void* k_scale, int64_t k_sb,
+                                 int64_t k_sn, int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
+                                 const int32_t* q_pos, const int32_t* n_entries, int B, int Tq,
+                                 int N_max, int H_I, int D_I, int m, int k, void* ws, bool score16,
+                                 hipStream_t stream, IndexWs& iw) {
+  const int64_t srs = score_row_stride(N_max);
+  const size_t rows = static_cast<size_t>(B) * Tq;
+  char* base = static_cast<char*>(ws);
+  iw.scores = base;
+  iw.srs = srs;
+  base += round_up(rows * srs * (score16 ? sizeof(uint16_t) : sizeof(float)));
+  iw.n_chunks = bound_chunks(N_max);
+  const int bk = bound_k(idx_dtype, H_I, D_I, N_max, k);
+  iw.bounds = bk > 0 ? reinterpret_cast<float2*>(base) : nullptr;
+  base += round_up(rows * iw.n_chunks * sizeof(float2));
+  iw.sel_ws = base;
+  csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, iw.scores, srs,
+                   iw.bounds, iw.n_chunks, bk, score16};
+  return hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
+}
+
 // Shared body of csa_index_topk (fp32 score rows) and csa_index_topk_bf16.
 csa_status_t index_topk_impl(const void* q_idx, const void* q_scale, const float* w_idx,
                              const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
@@ -264,22 +298,14 @@ csa_status_t index_topk_impl(const void* q_idx, const void* q_scale, const float
   if (st != CSA_OK) return st;
   CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
               "index topk: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
-  const int64_t srs = score_row_stride(N_max);
-  const size_t rows = static_cast<size_t>(B) * Tq;
-  char* base = static_cast<char*>(ws);
-  void* scores = base;
-  base += round_up(rows * srs * (score16 ? sizeof(uint16_t) : sizeof(float)));
-  const int n_chunks = bound_chunks(N_max);
-  const int bk = bound_k(idx_dtype, H_I, D_I, N_max, k);
-  float2* bounds = bk > 0 ? reinterpret_cast<float2*>(base) : nullptr;
-  base += round_up(rows * n_chunks * sizeof(float2));
-  csa::ScoreArgs a{q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
-                   q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, scores, srs,
-                   bounds, n_chunks, bk, score16};
-  st = hip_status(csa::launch_score(a, idx_dtype, stream), "index score launch");
+  IndexWs iw;
+  st = launch_index_scores(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                           idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, k, ws, score16,
+                           stream, iw);
   if (st != CSA_OK) return st;
-  return hip_status(csa::launch_topk(scores, score16, srs, q_pos, n_entries, B, Tq, N_max, m, k,
-                                     bounds, n_chunks, topk_idx, topk_score, base, stream),
+  return hip_status(csa::launch_topk(iw.scores, score16, iw.srs, q_pos, n_entries, B, Tq, N_max, m,
+                                     k, iw.bounds, iw.n_chunks, topk_idx, topk_score, iw.sel_ws,
+                                     stream),
                     "topk launch");
 }
 
@@ -317,6 +343,8 @@ static csa_status_t check_attend(const void* q, const void* k_c, const void* v_c
               "attend: NULL pointer");
   CSA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1 && D >= 1 && N_max >= 1, CSA_ERR_INVALID_ARGUMENT,
               "attend: sizes must be >= 1");
+  CSA_REQUIRE(csa::attend_rows_ok(B, Tq), CSA_ERR_UNSUPPORTED,
+              "attend: B*Tq=%lld query rows exceed 65536", static_cast<long long>(B) * Tq);
   CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
               "attend: dtype must be F32 or BF16");
   CSA_REQUIRE(csa::attend_supported(dtype, H, D), CSA_ERR_UNSUPPORTED,
@@ -413,6 +441,91 @@ csa_status_t swa_attend(const void* q, const void* k, const void* v, int64_t kv_
   csa::AttendArgs a{q, k, v, kv_sb, kv_sn, nullptr, q_pos, n_tokens, B, Tq, H, D,
                     N_max, 0, 1, wn, scale, out, lse, ws};
   return hip_status(csa::launch_attend(a, dtype, true, stream), "swa launch");
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- score -> top-k -> attention
+namespace {
+
+// attention workspace | top-k list (used when the caller passes none) | index + top-k workspace
+struct StepWs {
+  size_t attn, idx, index;
+};
+csa_status_t step_ws(csa_dtype_t idx_dtype, csa_dtype_t dtype, int B, int Tq, int N_max, int H,
+                     int D, int k, StepWs& w) {
+  size_t t = 0;
+  csa_status_t st = csa_index_topk_workspace(B, Tq, N_max, k, &t);
+  if (st != CSA_OK) return st;
+  (void)idx_dtype;
+  w.attn = round_up(csa::attend_workspace_bytes(dtype, false, B, Tq, H, D, k));
+  w.idx = round_up(static_cast<size_t>(B) * Tq * k * sizeof(int32_t));
+  w.index = t;
+  return CSA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+csa_status_t csa_index_topk_attend_workspace(csa_dtype_t idx_dtype, csa_dtype_t dtype, int B,
+                                             int Tq, int N_max, int H, int D, int k,
+                                             size_t* bytes) {
+  g_err[0] = 0;
+  CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "index topk attend workspace: NULL result");
+  CSA_REQUIRE(B >= 1 && Tq >= 1 && N_max >= 1 && H >= 1 && D >= 1 && k >= 1,
+              CSA_ERR_INVALID_ARGUMENT, "index topk attend workspace: sizes must be >= 1");
+  CSA_REQUIRE(valid_dtype(idx_dtype) && (dtype == CSA_F32 || dtype == CSA_BF16),
+              CSA_ERR_INVALID_ARGUMENT, "index topk attend workspace: bad dtype");
+  StepWs w;
+  const csa_status_t st = step_ws(idx_dtype, dtype, B, Tq, N_max, H, D, k, w);
+  if (st != CSA_OK) return st;
+  *bytes = w.attn + w.idx + w.index;
+  return CSA_OK;
+}
+
+csa_status_t csa_index_topk_attend(const void* q_idx, const void* q_scale, const float* w_idx,
+                                   const void* k_idx, const void* k_scale, int64_t k_sb,
+                                   int64_t k_sn, int64_t ks_sb, int64_t ks_sn,
+                                   csa_dtype_t idx_dtype, const void* q, const void* k_c,
+                                   const void* v_c, int64_t kv_sb, int64_t kv_sn,
+                                   csa_dtype_t dtype, const int32_t* q_pos,
+                                   const int32_t* n_entries, int B, int Tq, int N_max, int H_I,
+                                   int D_I, int H, int D, int m, int k, float scale, void* out,
+                                   float* lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
+                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
+  if (st != CSA_OK) return st;
+  st = check_attend(q, k_c, v_c, kv_sb, kv_sn, n_entries, dtype, B, Tq, H, D, N_max, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(k >= 1, CSA_ERR_INVALID_ARGUMENT, "index topk attend: k must be >= 1");
+  CSA_REQUIRE(csa::topk_supported(N_max, k), CSA_ERR_UNSUPPORTED,
+              "index topk attend: N_max=%d with k=%d not supported", N_max, k);
+  StepWs w;
+  st = step_ws(idx_dtype, dtype, B, Tq, N_max, H, D, k, w);
+  if (st != CSA_OK) return st;
+  const size_t need = w.attn + w.idx + w.index;
+  CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
+              "index topk attend: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
+  char* base = static_cast<char*>(ws);
+  void* attn_ws = base;
+  int32_t* idx_buf = reinterpret_cast<int32_t*>(base + w.attn);
+  void* index_ws = base + w.attn + w.idx;
+  IndexWs iw;
+  st = launch_index_scores(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                           idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, k, index_ws,
+                           false, stream, iw);
+  if (st != CSA_OK) return st;
+  csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, nullptr, nullptr, n_entries, B, Tq, H, D,
+                    N_max, k, m, 0, scale, out, lse, attn_ws};
+  int32_t* idx = topk_idx != nullptr ? topk_idx : idx_buf;
+  st = hip_status(csa::launch_topk(iw.scores, false, iw.srs, q_pos, n_entries, B, Tq, N_max, m, k,
+                                   iw.bounds, iw.n_chunks, idx, nullptr, iw.sel_ws, stream),
+                  "topk launch");
+  if (st != CSA_OK) return st;
+  a.idx = idx;
+  return hip_status(csa::launch_attend(a, dtype, false, stream), "attend launch");
 }
 
 }  // extern "C"

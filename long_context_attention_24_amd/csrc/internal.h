@@ -76,8 +76,12 @@ struct AttendArgs {
   float* lse;
   void* ws;
 };
-// k_or_nmax: k (CSA), N_max (HCA) or min(window, N_max) (HCA with a window)
+// k_or_nmax: k (CSA), N_max (HCA) or min(window, N_max) (HCA with a window).
+// The tuned path's workspace starts with merge counters that must be zero
+// before a call; every call leaves them zero.
 size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax);
+bool attend_rows_ok(int B, int Tq);   // B * Tq within the tuned kernels' row limit
+
 bool attend_supported(csa_dtype_t dt, int H, int D);
 hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s);
 

@@ -633,9 +633,9 @@ def test_step_graph_replay_matches_eager():
     pos = torch.tensor([[4 * N], [4 * N - 9], [4000], [4 * 5000 + 1]], dtype=torch.int32, device=DEV)
     ne = torch.tensor([N, N, N, 6000], dtype=torch.int32, device=DEV)
     u8 = torch.uint8
-    ws_t = torch.empty(csa.index_topk_workspace_bytes(B, 1, N, k), dtype=u8, device=DEV)
-    ws_a = torch.empty(csa.attend_workspace_bytes(bf, B, 1, 64, 128, k), dtype=u8, device=DEV)
-    ws_h = torch.empty(csa.hca_workspace_bytes(bf, B, 1, 64, 128, N), dtype=u8, device=DEV)
+    ws_t = csa.new_workspace(csa.index_topk_workspace_bytes(B, 1, N, k), DEV)
+    ws_a = csa.new_workspace(csa.attend_workspace_bytes(bf, B, 1, 64, 128, k), DEV)
+    ws_h = csa.new_workspace(csa.hca_workspace_bytes(bf, B, 1, 64, 128, N), DEV)
     idx = torch.empty((B, 1, k), dtype=torch.int32, device=DEV)
     o, oh = torch.empty_like(q), torch.empty_like(q)
 
@@ -693,6 +693,124 @@ def test_attention_sharp_and_single_entry():
             check_attention(O[b, t], o_ref, "bf16", f"sharp b={b} t={t}")
             check_lse(L[b, t], l_ref, LSE_TOL_BF16)
     assert np.array_equal(O[1, 2], np.tile(Vv[1, 3000], (64, 1)))
+
+
+def _step_case(B, Tq, N_max, k, seed, wzero=False, pos=None, ne=None):
+    bf = torch.bfloat16
+    q = _randn((B, Tq, 64, 128), 3 / math.sqrt(128), bf, seed)
+    kc = _randn((B, N_max, 128), 1 / math.sqrt(128), bf, seed + 1)
+    vc = _randn((B, N_max, 128), 1 / math.sqrt(128), bf, seed + 2)
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), bf, seed + 3)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), bf, seed + 4)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, seed + 5)
+    if wzero:
+        wi.zero_()
+    if pos is None:
+        pos = [[4 * N_max + 3] * Tq] * B
+    if ne is None:
+        ne = [N_max] * B
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    return q, kc, vc, qi, ki, wi, q_pos, n_ent
+
+
+@pytest.mark.parametrize("name,B,Tq,N_max,k,wzero,pos,ne", [
+    # decode rows: several splits, V < k, no valid rows, k not a multiple of 128
+    ("ragged", 4, 2, 5000, 300, False,
+     [[4 * 5000 + 3, 2], [4 * 777, 4 * 200], [4 * 4000 + 1, 4 * 4500], [9, 4 * 5000]],
+     [5000, 777, 4300, 0]),
+    # rows of 2000 .. 12000 visible entries: no chunk bound (k > 16 * full chunks)
+    ("unbounded", 2, 3, 12000, 1024, False,
+     [[4 * 12000, 4 * 2000, 4 * 9000], [4 * 11999 + 3, 4 * 6000, 4 * 1025]], [12000, 12000]),
+    # every score equal: the survivor list overflows, the whole row is selected from
+    ("all_equal", 2, 1, 32768, 1024, True, None, None),
+    # many query rows (the prefill score kernel)
+    ("many_rows", 1, 520, 3000, 512, False, [[4 * 3000 + i for i in range(520)]], None),
+])
+def test_index_topk_attend_matches_separate(name, B, Tq, N_max, k, wzero, pos, ne):
+    """csa_index_topk_attend (score -> top-k -> attention in one call, the
+    index lists kept in its workspace) equals csa_index_topk followed by
+    csa_attend bitwise (indices, outputs, lse), and matches the oracle stage
+    by stage."""
+    _say(f"index_topk_attend: {name}")
+    q, kc, vc, qi, ki, wi, q_pos, n_ent = _step_case(B, Tq, N_max, k, 400, wzero, pos, ne)
+    o, lse, idx = csa.index_topk_attend(qi, wi, ki, q, kc, vc, q_pos, n_ent, 4, k, with_lse=True,
+                                        with_idx=True)
+    idx2 = csa.index_topk(qi, wi, ki, q_pos, n_ent, 4, k)
+    o2, lse2 = csa.attend(q, kc, vc, idx2, n_ent, with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), "top-k lists differ from csa_index_topk"
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "outputs differ from csa_attend"
+    assert torch.equal(lse, lse2), "lse differs from csa_attend"
+    I, Q, K, Vv, QI, KI, W = (np64(t) for t in (idx, q, kc, vc, qi, ki, wi))
+    O, L = np64(o), np64(lse)
+    P, NE = q_pos.cpu().numpy(), n_ent.cpu().numpy()
+    rows = [(b, t) for b in range(B) for t in range(Tq)]
+    for b, t in rows[:: max(1, len(rows) // 12)]:
+        V = oracle.visible_count(int(P[b, t]), 4, int(NE[b]))
+        s = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+        if wzero:
+            assert np.array_equal(I[b, t], oracle.topk_select(s, V, k))
+        else:
+            check_topk(I[b, t], s, V, k)
+        o_ref, l_ref = oracle.attend(Q[b, t], K[b], Vv[b], I[b, t])
+        check_attention(O[b, t], o_ref, "bf16", f"{name} b={b} t={t}")
+        check_lse(L[b, t], l_ref, LSE_TOL_BF16)
+
+
+ATTEND_SYNC_BYTES = ((32 * 65536 + 1) * 4 + 255) // 256 * 256   # merge counters at the front
+
+
+def test_attention_workspace_reuse_across_shapes():
+    """One zero-filled workspace serves split attention calls of different
+    shapes in a row (CSA with many and with one split, HCA, a sliding
+    window): each result matches the oracle, and the merge counters at the
+    front of the workspace are zero again after every call."""
+    bf = torch.bfloat16
+    N_max = 5000
+    kc = _randn((4, N_max, 128), 1 / math.sqrt(128), bf, 91)
+    vc = _randn((4, N_max, 128), 1 / math.sqrt(128), bf, 92)
+    q = _randn((4, 2, 64, 128), 3 / math.sqrt(128), bf, 93)
+    n_ent = torch.tensor([N_max, 4000, 77, 1], dtype=torch.int32, device=DEV)
+    nbytes = max(csa.attend_workspace_bytes(bf, 4, 2, 64, 128, 1024),
+                 csa.hca_workspace_bytes(bf, 4, 2, 64, 128, N_max),
+                 csa.swa_workspace_bytes(bf, 4, 2, 64, 128, N_max, 3000))
+    ws = csa.new_workspace(nbytes, DEV)
+    K, Vv, Q = np64(kc), np64(vc), np64(q)
+    ne = n_ent.cpu().numpy()
+    g = _gen(94)
+    for case, (B, k) in enumerate([(4, 1024), (2, 100), (3, 300)]):
+        _say(f"workspace reuse: csa B={B} k={k}")
+        idx = torch.randint(-3, N_max, (B, 2, k), generator=g, device=DEV, dtype=torch.int32)
+        o, lse = csa.attend(q[:B], kc[:B], vc[:B], idx, n_ent[:B], with_lse=True, workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[:ATTEND_SYNC_BYTES].any(), "merge counters left non-zero"
+        I, O, L = np64(idx), np64(o), np64(lse)
+        for b in range(B):
+            for t in range(2):
+                o_ref, l_ref = oracle.attend(Q[b, t], K[b], Vv[b], [j for j in I[b, t] if j < ne[b]])
+                check_attention(O[b, t], o_ref, "bf16", f"reuse csa case={case} b={b} t={t}")
+                check_lse(L[b, t], l_ref, LSE_TOL_BF16)
+    _say("workspace reuse: hca and swa")
+    pos = torch.tensor([[4 * 4999 + 3, 700], [4 * 3000, 9], [500, 4 * 77 + 3], [2, 3]],
+                       dtype=torch.int32, device=DEV)
+    oh, lh = csa.hca_attend(q, kc, vc, pos, n_ent, 4, with_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert not ws[:ATTEND_SYNC_BYTES].any(), "merge counters left non-zero"
+    os_, ls_ = csa.swa_attend(q, kc, vc, pos, n_ent, 3000, with_lse=True, workspace=ws)
+    torch.cuda.synchronize()
+    assert not ws[:ATTEND_SYNC_BYTES].any(), "merge counters left non-zero"
+    P = pos.cpu().numpy()
+    OH, LH, OS, LS = np64(oh), np64(lh), np64(os_), np64(ls_)
+    for b in range(4):
+        for t in range(2):
+            V = oracle.visible_count(int(P[b, t]), 4, int(ne[b]))
+            o_ref, l_ref = oracle.hca_attend(Q[b, t], K[b], Vv[b], V)
+            check_attention(OH[b, t], o_ref, "bf16", f"reuse hca b={b} t={t}")
+            check_lse(LH[b, t], l_ref, LSE_TOL_BF16)
+            o_ref, l_ref = oracle.swa_attend(Q[b, t], K[b], Vv[b], int(P[b, t]), int(ne[b]), 3000)
+            check_attention(OS[b, t], o_ref, "bf16", f"reuse swa b={b} t={t}")
+            check_lse(LS[b, t], l_ref, LSE_TOL_BF16)
 
 
 def test_compress_edge_cases():

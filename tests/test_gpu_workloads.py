@@ -47,17 +47,33 @@ def _decode_check(w, inp, idx, o, lse, fp4=False):
     return KI, QI, W
 
 
+def _fused_step(w, inp, fp4=False):
+    """The decode step as the benchmark runs it (csa_index_topk_attend) and as
+    two calls (csa_index_topk, csa_attend): the two must agree bitwise."""
+    kw = dict(q_scale=inp["q_scale"], k_scale=inp["ki_scale"]) if fp4 else {}
+    qi = inp["q_codes"] if fp4 else inp["q_idx"]
+    ki = inp["ki_codes"] if fp4 else inp["ki_cache"]
+    o, lse, idx = csa.index_topk_attend(qi, inp["w_idx"], ki, inp["q"], inp["k_cache"],
+                                        inp["v_cache"], inp["q_pos"], inp["n_entries"], w.m, w.k,
+                                        with_lse=True, with_idx=True, **kw)
+    idx2 = csa.index_topk(qi, inp["w_idx"], ki, inp["q_pos"], inp["n_entries"], w.m, w.k, **kw)
+    o2, lse2 = csa.attend(inp["q"], inp["k_cache"], inp["v_cache"], idx2, inp["n_entries"],
+                          with_lse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2), "fused step: top-k lists differ"
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "fused step: outputs differ"
+    assert torch.equal(lse, lse2), "fused step: lse differs"
+    return idx, o, lse
+
+
 def test_csa_decode_128k_full():
     w = WORKLOADS["csa_decode_128k"]
     _say(f"{w.name}: generating inputs")
     inp = make_inputs(w, device=DEV)
-    _say(f"{w.name}: index_topk + attend")
-    idx = csa.index_topk(inp["q_idx"], inp["w_idx"], inp["ki_cache"], inp["q_pos"],
-                         inp["n_entries"], w.m, w.k)
+    _say(f"{w.name}: index_topk_attend (fused step) and index_topk + attend")
+    idx, o, lse = _fused_step(w, inp)
     scores = csa.index_score(inp["q_idx"], inp["w_idx"], inp["ki_cache"], inp["q_pos"],
                              inp["n_entries"], w.m)
-    o, lse = csa.attend(inp["q"], inp["k_cache"], inp["v_cache"], idx, inp["n_entries"],
-                        with_lse=True)
     torch.cuda.synchronize()
     KI, QI, W = _decode_check(w, inp, idx, o, lse)
     # indexer scores within the fp32 accumulation bound, sampled rows
@@ -147,14 +163,9 @@ def test_csa_decode_128k_sharp_attention():
 def test_csa_decode_1m_fp4_full():
     w = WORKLOADS["csa_decode_1m_fp4"]
     _say(f"{w.name}: generating inputs")
-    inp = make_inputs(w, device=DEV)
-    _say(f"{w.name}: index_topk + attend")
-    idx = csa.index_topk(inp["q_codes"], inp["w_idx"], inp["ki_codes"], inp["q_pos"],
-                         inp["n_entries"], w.m, w.k, q_scale=inp["q_scale"],
-                         k_scale=inp["ki_scale"])
-    o, lse = csa.attend(inp["q"], inp["k_cache"], inp["v_cache"], idx, inp["n_entries"],
-                        with_lse=True)
-    torch.cuda.synchronize()
+    inp = make_inputs(w, device=DEV, keep_unquantised=True)
+    _say(f"{w.name}: index_topk_attend (fused step) and index_topk + attend")
+    idx, o, lse = _fused_step(w, inp, fp4=True)
     KI, QI, W = _decode_check(w, inp, idx, o, lse, fp4=True)
     # recall against the oracle on the same quantised inputs (gate >= 0.995)
     I = np64(idx)
@@ -164,6 +175,14 @@ def test_csa_decode_1m_fp4_full():
         rec.append(len(set(I[b, 0].tolist()) & set(ref.tolist())) / w.k)
     _say(f"{w.name}: recall vs quantised-input oracle {rec}")
     assert min(rec) >= 0.995
+    # reported, not gated: recall against the oracle on the unquantised draws
+    # (what FP4 quantisation itself costs the selection)
+    KU, QU = np64(inp["ki_unquantised"]), np64(inp["q_idx_unquantised"])
+    rec_u = []
+    for b in range(w.B):
+        ref = oracle.topk_select(oracle.index_scores(QU[b, 0], W[b, 0], KU[b], w.N), w.N, w.k)
+        rec_u.append(len(set(I[b, 0].tolist()) & set(ref.tolist())) / w.k)
+    _say(f"{w.name}: recall vs unquantised oracle (reported) {rec_u}")
 
 
 def test_csa_decode_1m_mx4_full():
@@ -174,13 +193,8 @@ def test_csa_decode_1m_mx4_full():
     _say(f"{w.name}: generating inputs")
     inp = make_inputs(w, device=DEV)
     assert inp["ki_scale"].dtype == torch.uint8
-    _say(f"{w.name}: index_topk + attend")
-    idx = csa.index_topk(inp["q_codes"], inp["w_idx"], inp["ki_codes"], inp["q_pos"],
-                         inp["n_entries"], w.m, w.k, q_scale=inp["q_scale"],
-                         k_scale=inp["ki_scale"])
-    o, lse = csa.attend(inp["q"], inp["k_cache"], inp["v_cache"], idx, inp["n_entries"],
-                        with_lse=True)
-    torch.cuda.synchronize()
+    _say(f"{w.name}: index_topk_attend (fused step) and index_topk + attend")
+    idx, o, lse = _fused_step(w, inp, fp4=True)
     _decode_check(w, inp, idx, o, lse, fp4=True)
 
 

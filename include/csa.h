@@ -301,6 +301,34 @@ csa_status_t csa_index_topk_attend_workspace(csa_dtype_t idx_dtype, csa_dtype_t 
                                              size_t* bytes);
 
 /*
+ * csa_index_topk_attend_noalloc - csa_index_topk_attend for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, the same results.
+ *
+ * The intermediate buffers live in a library-owned scratch array of
+ * csa_index_topk_attend_noalloc_max_bytes() bytes (32 MiB) per GPU, held
+ * until the process ends; the call allocates nothing.  Every call on a GPU
+ * uses that GPU's one array, so calls that may overlap on one GPU (other
+ * streams, other threads) race and must not be issued.  The stream must
+ * belong to the calling thread's current device.  Limits: B * Tq <= 4096 and
+ * the step's buffers within the scratch size (csa_index_topk_attend_workspace
+ * minus its 8 MiB counter block gives them), else CSA_ERR_UNSUPPORTED.
+ */
+csa_status_t csa_index_topk_attend_noalloc(const void* q_idx, const void* q_scale,
+                                           const float* w_idx, const void* k_idx,
+                                           const void* k_scale, int64_t k_sb, int64_t k_sn,
+                                           int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
+                                           const void* q, const void* k_c, const void* v_c,
+                                           int64_t kv_sb, int64_t kv_sn, csa_dtype_t dtype,
+                                           const int32_t* q_pos, const int32_t* n_entries,
+                                           int B, int Tq, int N_max, int H_I, int D_I, int H,
+                                           int D, int m, int k, float scale,
+                                           void* out, float* lse, int32_t* topk_idx,
+                                           hipStream_t stream);
+size_t csa_index_topk_attend_noalloc_max_bytes(void);
+
+/*
  * swa_attend - sliding-window attention over uncompressed tokens ("DeepSeek
  * V4 技术解读", §2.3: the first layers attend a sliding window of recent
  * tokens at full resolution; the window size is not given there and is an

@@ -25,7 +25,8 @@ import torch
 __all__ = [
     "CsaError", "library_path", "load_library",
     "compress", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
-    "attend", "hca_attend", "swa_attend", "index_topk_attend", "index_topk_workspace_bytes",
+    "attend", "hca_attend", "swa_attend", "index_topk_attend", "index_topk_attend_noalloc",
+    "index_topk_workspace_bytes",
     "index_topk_attend_workspace_bytes",
     "index_topk_bf16_workspace_bytes", "swa_workspace_bytes",
     "attend_workspace_bytes", "hca_workspace_bytes", "new_workspace",
@@ -45,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
     "swa_attend", "swa_attend_workspace",
     "csa_index_topk_attend", "csa_index_topk_attend_workspace",
+    "csa_index_topk_attend_noalloc", "csa_index_topk_attend_noalloc_max_bytes",
 )
 
 
@@ -94,6 +96,11 @@ _SIGS = {
                                _vp, _vp, _vp, _vp, _sz, _vp], _i32),
     "csa_index_topk_attend_workspace": ([_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                                          ctypes.POINTER(_sz)], _i32),
+    "csa_index_topk_attend_noalloc": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32,
+                                       _vp, _vp, _vp, _i64, _i64, _i32, _vp, _vp,
+                                       _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                       _vp, _vp, _vp, _vp], _i32),
+    "csa_index_topk_attend_noalloc_max_bytes": ([], _sz),
 }
 
 
@@ -458,3 +465,28 @@ def index_topk_attend(q_idx, w_idx, k_idx, q, k_cache, v_cache, q_pos, n_entries
     if with_idx:
         res += (idx,)
     return res[0] if len(res) == 1 else res
+
+
+def index_topk_attend_noalloc(q_idx, w_idx, k_idx, q, k_cache, v_cache, q_pos, n_entries, m: int,
+                              k: int, q_scale=None, k_scale=None, scale: Optional[float] = None,
+                              out: Optional[torch.Tensor] = None,
+                              lse: Optional[torch.Tensor] = None,
+                              idx_out: Optional[torch.Tensor] = None):
+    """index_topk_attend with the library's own per-GPU scratch instead of a
+    workspace: the call allocates no device memory (out, lse and idx_out, when
+    given, are written in place; out is allocated here only when None).
+    Calls that may overlap on one GPU race on the scratch."""
+    dt, B, Tq, H_I, D_I, N_max, ks_sb, ks_sn = _index_args(q_idx, w_idx, k_idx, q_scale, k_scale)
+    B2, Tq2, H, D, N2 = _attn_common(q, k_cache, v_cache)
+    if (B2, Tq2, N2) != (B, Tq, N_max):
+        raise ValueError("indexer and attention shapes disagree")
+    scale = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    _check(load_library().csa_index_topk_attend_noalloc(
+        q_idx.data_ptr(), _ptr(q_scale), w_idx.data_ptr(), k_idx.data_ptr(), _ptr(k_scale),
+        k_idx.stride(0), k_idx.stride(1), ks_sb, ks_sn, dt,
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1),
+        _dtype_code(q), q_pos.data_ptr(), n_entries.data_ptr(),
+        B, Tq, N_max, H_I, D_I, H, D, m, k, scale,
+        out.data_ptr(), _ptr(lse), _ptr(idx_out), _stream()))
+    return out

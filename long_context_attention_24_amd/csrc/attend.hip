@@ -271,15 +271,15 @@ __device__ __forceinline__ void compute_round(uint32_t vmask, bool active, const
 // arrives), adds one to the row's arrival counter and waits until every
 // split has arrived; then split s merges its own slice of the output dims
 // over all splits, in split order (the result does not depend on which
-// workgroup finishes first).  Counters: arrive[rows], depart[rows] and one
-// word counting waits that gave up, at the front of the workspace; zero
-// before the first call, and every call leaves them zero (the last
+// workgroup finishes first).  Counters: one 128-byte line per query row at
+// the front of the workspace (separate lines keep the rows' atomics apart),
+// holding the row's arrivals, departures and a count of waits that gave up;
+// zero before the first call, and every call leaves them zero (the last
 // workgroup of a row to leave the barrier resets the row's two counters).
 // The wait is bounded so that a kernel always ends.  The splits of a row are
 // consecutive workgroups and dispatch follows workgroup order, so a waiting
 // workgroup only ever waits for workgroups that are already running.
 constexpr int kSpinLimit = 1 << 22;               // about 0.1 s of polling
-constexpr int kAttendMaxRows = 65536;             // B * Tq (the grid's y extent)
 constexpr int kSyncStride = 32;                   // int32 words per row's counters
 
 __device__ __forceinline__ void st_coherent(float* p, float v) {
@@ -298,8 +298,7 @@ __device__ __forceinline__ void row_barrier(int32_t* sync, int rows, int row, in
     __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int it = 0; __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n; ++it) {
       if (it == kSpinLimit) {
-        __hip_atomic_fetch_add(sync + kSyncStride * kAttendMaxRows, 1, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(arrive + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
       __builtin_amdgcn_s_sleep(1);
@@ -613,22 +612,26 @@ bool attend_supported(csa_dtype_t dt, int H, int D) {
 }
 
 // Workspace of the tuned path: a fixed block of merge counters at the front
-// (2 per row for up to kMaxRows rows, plus one word), then the split
-// partials.  The block has the same size and place for every call, and
-// calls leave it zero, so a workspace zero-filled once serves calls of any
-// shape.
-size_t sync_bytes(int) {
-  return (static_cast<size_t>(kSyncStride * kAttendMaxRows + 1) * sizeof(int32_t) + 255) / 256 *
-         256;
+// (one 128-byte line per row for up to kAttendMaxRows rows), then the split
+// partials.  The block has the same size and place for every
+// call, and calls leave it zero, so a workspace zero-filled once serves calls
+// of any shape.
+size_t attend_sync_block_bytes(int rows) {
+  return (static_cast<size_t>(kSyncStride) * rows * sizeof(int32_t) + 255) / 256 * 256;
+}
+
+size_t attend_part_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax) {
+  if (!tuned(dt, H, D)) return 0;
+  const int sl = split_len(hca);
+  const int nsplit = (k_or_nmax + sl - 1) / sl;
+  return static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * kPartRows * 64 * sizeof(float);
 }
 
 size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D,
                               int k_or_nmax) {
   if (!tuned(dt, H, D)) return 0;
-  const int sl = split_len(hca);
-  const int nsplit = (k_or_nmax + sl - 1) / sl;
-  return sync_bytes(B * Tq) +
-         static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * kPartRows * 64 * sizeof(float);
+  return attend_sync_block_bytes(kAttendMaxRows) +
+         attend_part_bytes(dt, hca, B, Tq, H, D, k_or_nmax);
 }
 
 bool attend_rows_ok(int B, int Tq) {
@@ -652,8 +655,10 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
   int nsplit = (n + sl - 1) / sl;
   if (nsplit < 1) nsplit = 1;
   const int rows = a.B * a.Tq;
-  int32_t* sync = static_cast<int32_t*>(a.ws);
-  float* part = reinterpret_cast<float*>(static_cast<char*>(a.ws) + sync_bytes(rows));
+  int32_t* sync = a.sync != nullptr ? a.sync : static_cast<int32_t*>(a.ws);
+  float* part = a.part != nullptr ? a.part
+                                  : reinterpret_cast<float*>(static_cast<char*>(a.ws) +
+                                                             attend_sync_block_bytes(kAttendMaxRows));
   uint16_t* out = static_cast<uint16_t*>(a.out);
   const dim3 grid(nsplit, rows);
   if (hca)

@@ -2,6 +2,7 @@
 // dispatch to the kernels.  Every check runs on the host before anything is
 // enqueued; a failed check leaves the outputs untouched.
 #include <stdarg.h>
+#include <atomic>
 #include <stdio.h>
 #include <string.h>
 
@@ -448,21 +449,103 @@ csa_status_t swa_attend(const void* q, const void* k, const void* v, int64_t kv_
 // ---------------------------------------------------------------- score -> top-k -> attention
 namespace {
 
-// attention workspace | top-k list (used when the caller passes none) | index + top-k workspace
-struct StepWs {
-  size_t attn, idx, index;
+// Intermediate buffers of one decode step: attention merge counters (zero
+// before the call, zero after it) for `sync_rows` rows, attention partials,
+// top-k lists (used when the caller passes none), index + top-k workspace.
+struct StepSizes {
+  size_t sync, part, idx, index;
+  size_t total() const { return sync + part + idx + index; }
 };
-csa_status_t step_ws(csa_dtype_t idx_dtype, csa_dtype_t dtype, int B, int Tq, int N_max, int H,
-                     int D, int k, StepWs& w) {
+csa_status_t step_sizes(csa_dtype_t dtype, int B, int Tq, int N_max, int H, int D, int k,
+                        int sync_rows, StepSizes& z) {
   size_t t = 0;
   csa_status_t st = csa_index_topk_workspace(B, Tq, N_max, k, &t);
   if (st != CSA_OK) return st;
-  (void)idx_dtype;
-  w.attn = round_up(csa::attend_workspace_bytes(dtype, false, B, Tq, H, D, k));
-  w.idx = round_up(static_cast<size_t>(B) * Tq * k * sizeof(int32_t));
-  w.index = t;
+  const bool tuned = csa::attend_part_bytes(dtype, false, B, Tq, H, D, k) > 0;
+  z.sync = tuned ? round_up(csa::attend_sync_block_bytes(sync_rows)) : 0;
+  z.part = round_up(csa::attend_part_bytes(dtype, false, B, Tq, H, D, k));
+  z.idx = round_up(static_cast<size_t>(B) * Tq * k * sizeof(int32_t));
+  z.index = t;
   return CSA_OK;
 }
+
+csa_status_t check_step(const void* q_idx, const void* q_scale, const float* w_idx,
+                        const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
+                        int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype, const void* q,
+                        const void* k_c, const void* v_c, int64_t kv_sb, int64_t kv_sn,
+                        csa_dtype_t dtype, const int32_t* q_pos, const int32_t* n_entries, int B,
+                        int Tq, int N_max, int H_I, int D_I, int H, int D, int m, int k,
+                        void* out) {
+  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
+                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
+  if (st != CSA_OK) return st;
+  st = check_attend(q, k_c, v_c, kv_sb, kv_sn, n_entries, dtype, B, Tq, H, D, N_max, out);
+  if (st != CSA_OK) return st;
+  CSA_REQUIRE(k >= 1, CSA_ERR_INVALID_ARGUMENT, "index topk attend: k must be >= 1");
+  CSA_REQUIRE(csa::topk_supported(N_max, k), CSA_ERR_UNSUPPORTED,
+              "index topk attend: N_max=%d with k=%d not supported", N_max, k);
+  return CSA_OK;
+}
+
+// Launches the step on buffers laid out as StepSizes at base (arguments
+// already validated).
+csa_status_t step_impl(const void* q_idx, const void* q_scale, const float* w_idx,
+                       const void* k_idx, const void* k_scale, int64_t k_sb, int64_t k_sn,
+                       int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype, const void* q,
+                       const void* k_c, const void* v_c, int64_t kv_sb, int64_t kv_sn,
+                       csa_dtype_t dtype, const int32_t* q_pos, const int32_t* n_entries, int B,
+                       int Tq, int N_max, int H_I, int D_I, int H, int D, int m, int k, float scale,
+                       void* out, float* lse, int32_t* topk_idx, const StepSizes& z, char* base,
+                       hipStream_t stream) {
+  int32_t* sync = reinterpret_cast<int32_t*>(base);
+  float* part = reinterpret_cast<float*>(base + z.sync);
+  int32_t* idx_buf = reinterpret_cast<int32_t*>(base + z.sync + z.part);
+  void* index_ws = base + z.sync + z.part + z.idx;
+  IndexWs iw;
+  csa_status_t st = launch_index_scores(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
+                                        ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I,
+                                        m, k, index_ws, false, stream, iw);
+  if (st != CSA_OK) return st;
+  int32_t* idx = topk_idx != nullptr ? topk_idx : idx_buf;
+  st = hip_status(csa::launch_topk(iw.scores, false, iw.srs, q_pos, n_entries, B, Tq, N_max, m, k,
+                                   iw.bounds, iw.n_chunks, idx, nullptr, iw.sel_ws, stream),
+                  "topk launch");
+  if (st != CSA_OK) return st;
+  csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, idx, nullptr, n_entries, B, Tq, H, D,
+                    N_max, k, m, 0, scale, out, lse, nullptr, sync, part};
+  return hip_status(csa::launch_attend(a, dtype, false, stream), "attend launch");
+}
+
+// ---- the allocation-free variant's scratch
+// One file-scope device array per GPU the library runs on, held until the
+// process ends.  Host code never uses its name as an address: the device
+// address comes from hipGetSymbolAddress, taken once per device (with that
+// device current) on the first call there and kept in g_scratch_addr.  The
+// array is zero when the code object is loaded; the attention merge counters
+// at its front are the only part that must be zero before a call, and every
+// call leaves them zero.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr int kScratchRows = 4096;                // B * Tq the counter block serves
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+
+csa_status_t scratch_address(void** addr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  CSA_REQUIRE(dev >= 0 && dev < kMaxDevices, CSA_ERR_UNSUPPORTED, "device %d >= %d", dev,
+              kMaxDevices);
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_addr[dev].store(p, std::memory_order_release);
+  }
+  *addr = p;
+  return CSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -476,10 +559,10 @@ csa_status_t csa_index_topk_attend_workspace(csa_dtype_t idx_dtype, csa_dtype_t 
               CSA_ERR_INVALID_ARGUMENT, "index topk attend workspace: sizes must be >= 1");
   CSA_REQUIRE(valid_dtype(idx_dtype) && (dtype == CSA_F32 || dtype == CSA_BF16),
               CSA_ERR_INVALID_ARGUMENT, "index topk attend workspace: bad dtype");
-  StepWs w;
-  const csa_status_t st = step_ws(idx_dtype, dtype, B, Tq, N_max, H, D, k, w);
+  StepSizes z;
+  const csa_status_t st = step_sizes(dtype, B, Tq, N_max, H, D, k, csa::kAttendMaxRows, z);
   if (st != CSA_OK) return st;
-  *bytes = w.attn + w.idx + w.index;
+  *bytes = z.total();
   return CSA_OK;
 }
 
@@ -494,38 +577,52 @@ csa_status_t csa_index_topk_attend(const void* q_idx, const void* q_scale, const
                                    float* lse, int32_t* topk_idx, void* ws, size_t ws_bytes,
                                    hipStream_t stream) {
   g_err[0] = 0;
-  csa_status_t st = check_score_args(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
-                                     ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m);
+  csa_status_t st = check_step(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                               idx_dtype, q, k_c, v_c, kv_sb, kv_sn, dtype, q_pos, n_entries, B,
+                               Tq, N_max, H_I, D_I, H, D, m, k, out);
   if (st != CSA_OK) return st;
-  st = check_attend(q, k_c, v_c, kv_sb, kv_sn, n_entries, dtype, B, Tq, H, D, N_max, out);
+  StepSizes z;
+  st = step_sizes(dtype, B, Tq, N_max, H, D, k, csa::kAttendMaxRows, z);
   if (st != CSA_OK) return st;
-  CSA_REQUIRE(k >= 1, CSA_ERR_INVALID_ARGUMENT, "index topk attend: k must be >= 1");
-  CSA_REQUIRE(csa::topk_supported(N_max, k), CSA_ERR_UNSUPPORTED,
-              "index topk attend: N_max=%d with k=%d not supported", N_max, k);
-  StepWs w;
-  st = step_ws(idx_dtype, dtype, B, Tq, N_max, H, D, k, w);
+  CSA_REQUIRE(ws && ws_bytes >= z.total() && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
+              "index topk attend: workspace %zu < %zu bytes (or misaligned)", ws_bytes, z.total());
+  return step_impl(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn, idx_dtype, q,
+                   k_c, v_c, kv_sb, kv_sn, dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, H, D,
+                   m, k, scale, out, lse, topk_idx, z, static_cast<char*>(ws), stream);
+}
+
+size_t csa_index_topk_attend_noalloc_max_bytes(void) { return kScratchBytes; }
+
+csa_status_t csa_index_topk_attend_noalloc(const void* q_idx, const void* q_scale,
+                                           const float* w_idx, const void* k_idx,
+                                           const void* k_scale, int64_t k_sb, int64_t k_sn,
+                                           int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
+                                           const void* q, const void* k_c, const void* v_c,
+                                           int64_t kv_sb, int64_t kv_sn, csa_dtype_t dtype,
+                                           const int32_t* q_pos, const int32_t* n_entries, int B,
+                                           int Tq, int N_max, int H_I, int D_I, int H, int D,
+                                           int m, int k, float scale, void* out, float* lse,
+                                           int32_t* topk_idx, hipStream_t stream) {
+  g_err[0] = 0;
+  csa_status_t st = check_step(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
+                               idx_dtype, q, k_c, v_c, kv_sb, kv_sn, dtype, q_pos, n_entries, B,
+                               Tq, N_max, H_I, D_I, H, D, m, k, out);
   if (st != CSA_OK) return st;
-  const size_t need = w.attn + w.idx + w.index;
-  CSA_REQUIRE(ws && ws_bytes >= need && aligned16(ws), CSA_ERR_WORKSPACE_TOO_SMALL,
-              "index topk attend: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
-  char* base = static_cast<char*>(ws);
-  void* attn_ws = base;
-  int32_t* idx_buf = reinterpret_cast<int32_t*>(base + w.attn);
-  void* index_ws = base + w.attn + w.idx;
-  IndexWs iw;
-  st = launch_index_scores(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
-                           idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, k, index_ws,
-                           false, stream, iw);
+  CSA_REQUIRE(static_cast<long long>(B) * Tq <= kScratchRows, CSA_ERR_UNSUPPORTED,
+              "index topk attend noalloc: B*Tq=%lld > %d query rows", static_cast<long long>(B) * Tq,
+              kScratchRows);
+  StepSizes z;
+  st = step_sizes(dtype, B, Tq, N_max, H, D, k, kScratchRows, z);
   if (st != CSA_OK) return st;
-  csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, nullptr, nullptr, n_entries, B, Tq, H, D,
-                    N_max, k, m, 0, scale, out, lse, attn_ws};
-  int32_t* idx = topk_idx != nullptr ? topk_idx : idx_buf;
-  st = hip_status(csa::launch_topk(iw.scores, false, iw.srs, q_pos, n_entries, B, Tq, N_max, m, k,
-                                   iw.bounds, iw.n_chunks, idx, nullptr, iw.sel_ws, stream),
-                  "topk launch");
+  CSA_REQUIRE(z.total() <= kScratchBytes, CSA_ERR_UNSUPPORTED,
+              "index topk attend noalloc: needs %zu bytes of scratch, the maximum is %zu",
+              z.total(), kScratchBytes);
+  void* base = nullptr;
+  st = scratch_address(&base);
   if (st != CSA_OK) return st;
-  a.idx = idx;
-  return hip_status(csa::launch_attend(a, dtype, false, stream), "attend launch");
+  return step_impl(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn, idx_dtype, q,
+                   k_c, v_c, kv_sb, kv_sn, dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, H, D,
+                   m, k, scale, out, lse, topk_idx, z, static_cast<char*>(base), stream);
 }
 
 }  // extern "C"

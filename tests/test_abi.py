@@ -19,7 +19,7 @@ A = 0x10000   # a 16-byte aligned fake device address: never dereferenced on the
 def _declared():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return set(re.findall(r"^\s*(?:csa_status_t|int|const char\s*\*)\s*(\w+)\s*\(", src, flags=re.M))
+    return set(re.findall(r"^\s*(?:csa_status_t|int|size_t|const char\s*\*)\s*(\w+)\s*\(", src, flags=re.M))
 
 
 @pytest.fixture(scope="module")

@@ -758,7 +758,7 @@ def test_index_topk_attend_matches_separate(name, B, Tq, N_max, k, wzero, pos, n
         check_lse(L[b, t], l_ref, LSE_TOL_BF16)
 
 
-ATTEND_SYNC_BYTES = ((32 * 65536 + 1) * 4 + 255) // 256 * 256   # merge counters at the front
+ATTEND_SYNC_BYTES = 32 * 4 * 65536                  # merge counters at the front
 
 
 def test_attention_workspace_reuse_across_shapes():

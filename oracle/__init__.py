@@ -7,6 +7,7 @@ kernels.  See ``csa_oracle.py`` for the definitions and their sources.
 """
 from .csa_oracle import (  # noqa: F401
     NEG_INF,
+    append_block,
     attend,
     csa_reference,
     e2m1_scaled_to_e4m3,
@@ -19,6 +20,7 @@ from .csa_oracle import (  # noqa: F401
     hca_attend,
     swa_attend,
     index_scores,
+    merge_attention,
     mx4_dequantize,
     mx4_quantize,
     pool,

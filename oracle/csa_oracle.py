@@ -46,6 +46,14 @@ below and listed with its reason in the design notes):
      uncompressed tokens max(0, P - window) .. P - 1 with P = min(p + 1,
      tokens cached), i.e. its own token and the window - 1 before it; the
      pages give no window size, so it is an argument.
+  R10 combining branches (§2.3, the local window kept next to the compressed
+     global retrieval): two attention results over disjoint key sets, each
+     given as (output, log-sum-exp) under the same softmax scale, combine
+     into the attention over the union of the sets.
+  R11 appending to the cache: after token t (0-based) is added, a block is
+     complete when (t + 1) is a multiple of m; its entry j = (t + 1) / m - 1
+     pools tokens m j .. m j + m - 1 (R1) and the sequence then holds j + 1
+     entries.
 """
 from __future__ import annotations
 
@@ -287,6 +295,40 @@ def swa_attend(q, k_cache, v_cache, q_pos: int, n_tokens: int, window: int,
     window - 1 tokens before it (window is an argument; the pages give none)."""
     P = min(q_pos + 1, n_tokens)
     return attend(q, k_cache, v_cache, range(max(0, P - window), P), scale)
+
+
+def merge_attention(o1, lse1, o2, lse2):
+    """R10: the attention over S1 u S2 from the results over disjoint S1 and S2.
+
+    o1, o2 [H, D], lse1, lse2 [H] (natural log, -inf for an empty set) ->
+    (o [H, D], lse [H]) in float64: lse = log(exp(lse1) + exp(lse2)) and
+    o = exp(lse1 - lse) o1 + exp(lse2 - lse) o2; both sets empty gives 0, -inf.
+    """
+    o1, o2 = np.asarray(o1, dtype=np.float64), np.asarray(o2, dtype=np.float64)
+    l1, l2 = np.asarray(lse1, dtype=np.float64), np.asarray(lse2, dtype=np.float64)
+    H = l1.shape[0]
+    o = np.zeros_like(o1)
+    lse = np.full(H, NEG_INF)
+    for h in range(H):
+        if l1[h] == NEG_INF and l2[h] == NEG_INF:
+            continue
+        mx = max(l1[h], l2[h])
+        e1 = math.exp(l1[h] - mx) if l1[h] != NEG_INF else 0.0
+        e2 = math.exp(l2[h] - mx) if l2[h] != NEG_INF else 0.0
+        lse[h] = mx + math.log(e1 + e2)
+        o[h] = (e1 * o1[h] + e2 * o2[h]) / (e1 + e2)
+    return o, lse
+
+
+def append_block(x_block, z_block, t: int, m: int):
+    """R11: the entry that appending token t completes, or None.
+
+    x_block [m, C], z_block [m]: the m most recent tokens (t - m + 1 .. t) ->
+    (entry index j, pooled row [C] float64) when (t + 1) % m == 0, else None.
+    """
+    if (t + 1) % m:
+        return None
+    return (t + 1) // m - 1, pool(x_block, z_block, m)[0]
 
 
 # ------------------------------------------------------------------ whole path

@@ -131,3 +131,26 @@ def test_index_scores_relu_is_per_head(H):
     K = np.array([[2.0, 0.0]])
     s = oracle.index_scores(q, np.array([1.0, 1.0]), K, 1)
     assert s[0] == 2.0
+
+
+def test_append_block_completes_exactly_the_blocks_of_the_whole_pool():
+    """R11: appending tokens one at a time completes entry j exactly when
+    token m j + m - 1 arrives, and the pooled rows equal pooling the whole
+    sequence at once (every entry, every m)."""
+    rng = np.random.default_rng(31)
+    for m in (1, 4, 7, 128):
+        n, C = 3 * m + m // 2 + 1, 5
+        x = rng.standard_normal((n, C))
+        z = rng.standard_normal(n)
+        whole = oracle.pool(x, z, m)
+        got = []
+        for t in range(n):
+            lo = max(0, t - m + 1)
+            r = oracle.append_block(x[lo:t + 1], z[lo:t + 1], t, m) if t + 1 >= m else None
+            if (t + 1) % m == 0:
+                assert r is not None and r[0] == (t + 1) // m - 1
+                got.append(r[1])
+            else:
+                assert r is None
+        assert len(got) == n // m
+        np.testing.assert_allclose(np.array(got), whole, rtol=0, atol=0)

@@ -202,3 +202,42 @@ def test_selected_entries_dominate_sharp_attention():
                              k_idx=ki, q_pos=4 * N, m=4, k=4, n_entries=N)
     assert needle in r["idx"]
     assert np.allclose(r["o"], np.tile(vc[needle], (H, 1)), atol=1e-6)
+
+
+# ---------------------------------------------------------------- combining two branches (R10)
+def test_merge_of_disjoint_sets_is_attention_over_the_union():
+    """merge(attend(S1), attend(S2)) = attend(S1 u S2) for disjoint S1, S2,
+    the union computed in one softmax; either order; an empty side returns
+    the other side; both empty gives 0 / -inf."""
+    rng = np.random.default_rng(21)
+    H, D, N = 6, 16, 300
+    for trial in range(20):
+        q = rng.standard_normal((H, D)) * 2.0
+        K = rng.standard_normal((N, D))
+        V = rng.standard_normal((N, D))
+        perm = rng.permutation(N)
+        cut = int(rng.integers(1, N))
+        S1, S2 = perm[:cut], perm[cut:]
+        o1, l1 = oracle.attend(q, K, V, S1)
+        o2, l2 = oracle.attend(q, K, V, S2)
+        o, lse = oracle.merge_attention(o1, l1, o2, l2)
+        o_ref, l_ref = oracle.attend(q, K, V, np.concatenate([S1, S2]))
+        np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)
+        ob, lb = oracle.merge_attention(o2, l2, o1, l1)
+        np.testing.assert_allclose(ob, o_ref, rtol=0, atol=1e-12)
+    oe, le = oracle.attend(q, K, V, [])
+    o, lse = oracle.merge_attention(o1, l1, oe, le)
+    assert np.array_equal(o, o1) and np.array_equal(lse, l1)
+    o, lse = oracle.merge_attention(oe, le, oe, le)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # a window branch and a compressed branch over different key tensors:
+    # the merge equals one softmax over the concatenated keys
+    Kw, Vw = rng.standard_normal((40, D)), rng.standard_normal((40, D))
+    ow, lw = oracle.attend(q, Kw, Vw, range(40))
+    oc, lc = oracle.attend(q, K, V, S1)
+    o, lse = oracle.merge_attention(ow, lw, oc, lc)
+    Kcat, Vcat = np.concatenate([Kw, K[S1]]), np.concatenate([Vw, V[S1]])
+    o_ref, l_ref = oracle.attend(q, Kcat, Vcat, range(Kcat.shape[0]))
+    np.testing.assert_allclose(o, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_ref, rtol=0, atol=1e-12)

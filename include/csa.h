@@ -110,6 +110,31 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st,
                           hipStream_t stream);
 
 /*
+ * csa_compress_append - incremental compression during decoding (§2.1 KV
+ * cache compression applied as tokens arrive: a compressed entry is formed
+ * once its m tokens are all present).
+ *
+ * For each sequence b, token t = t_new[b] (0-based position) has just been
+ * added.  When it completes a block, (t + 1) % m == 0, entry
+ * j = (t + 1) / m - 1 is pooled exactly as csa_compress pools it,
+ *   cache[b, j, c] = sum_{i<m} w_i x_token(m*j + i)[c],
+ *   w = softmax(logits of tokens m*j .. m*j + m - 1),
+ * and n_entries[b] is set to j + 1 (device memory, updated in place).
+ * Otherwise (or when t < 0, or j >= N_max) nothing is written.
+ * x        [B, x_rows, C] dtype, strides (x_sb, x_st): token s at row s mod
+ *          x_rows; x_rows a positive multiple of m (x_rows = m: a ring of the
+ *          latest block; x_rows >= sequence length: the whole sequence).
+ * logits   [B, x_rows] fp32 (batch stride z_sb), token s at column s mod x_rows.
+ * cache    [B, N_max, C] dtype with strides (c_sb, c_sj).
+ * Requirements on dtype, C, m and alignment as csa_compress.
+ */
+csa_status_t csa_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
+                                 const float* logits, int64_t z_sb, const int32_t* t_new,
+                                 void* cache, int64_t c_sb, int64_t c_sj, int32_t* n_entries,
+                                 csa_dtype_t dtype, int B, int C, int m, int N_max,
+                                 hipStream_t stream);
+
+/*
  * csa_quantize_mx4 - MX FP4 encoding of indexer vectors (§5: the indexer QK
  * path in FP4; the input format of CSA_FP4_E2M1_E8M0).  Per block of 32
  * consecutive elements of a row (OCP Microscaling encoding):
@@ -263,6 +288,24 @@ csa_status_t hca_attend(const void* q, const void* k_c, const void* v_c,
                         void* ws, size_t ws_bytes, hipStream_t stream);
 csa_status_t hca_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D, int N_max,
                                   size_t* bytes);
+
+/*
+ * csa_attend_merge - attention over the union of two disjoint key sets from
+ * the two partial results ("DeepSeek V4 技术解读", §2.3: a local sliding
+ * window kept next to the compressed global entries; e.g. the outputs of
+ * swa_attend and csa_attend for the same queries, same softmax scale).
+ *
+ *   lse = log(exp(lse_a) + exp(lse_b)),
+ *   out = exp(lse_a - lse) o_a + exp(lse_b - lse) o_b     (per row and head;
+ *   both sets empty, lse_a = lse_b = -inf: out 0, lse -inf).
+ *
+ * o_a, o_b, out [rows, H, D] contiguous (dtype F32 or BF16), lse_a, lse_b,
+ * lse_out [rows, H] fp32 (lse_out may be NULL).  out may be o_a or o_b
+ * itself (elementwise); no other overlap.  Requires D a multiple of 8.
+ */
+csa_status_t csa_attend_merge(const void* o_a, const float* lse_a, const void* o_b,
+                              const float* lse_b, csa_dtype_t dtype, int rows, int H, int D,
+                              void* out, float* lse_out, hipStream_t stream);
 
 /*
  * csa_index_topk_attend - one CSA decode step: Lightning Indexer scores,

@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "CsaError", "library_path", "load_library",
-    "compress", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
+    "compress", "compress_append", "attend_merge", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
     "attend", "hca_attend", "swa_attend", "index_topk_attend", "index_topk_attend_noalloc",
     "index_topk_workspace_bytes",
     "index_topk_attend_workspace_bytes",
@@ -40,7 +40,7 @@ CSA_F32, CSA_BF16, CSA_FP4_E2M1, CSA_FP4_E2M1_E8M0 = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "csa_abi_version", "csa_status_string", "csa_last_error",
-    "csa_compress", "csa_quantize_mx4", "csa_index_score", "csa_topk", "csa_topk_workspace",
+    "csa_compress", "csa_compress_append", "csa_attend_merge", "csa_quantize_mx4", "csa_index_score", "csa_topk", "csa_topk_workspace",
     "csa_index_topk", "csa_index_topk_workspace",
     "csa_index_topk_bf16", "csa_index_topk_bf16_workspace",
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
@@ -69,6 +69,9 @@ _SIGS = {
     "csa_compress": ([_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                       _vp], _i32),
     "csa_quantize_mx4": ([_vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64, _vp], _i32),
+    "csa_compress_append": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i32,
+                             _i32, _i32, _i32, _i32, _vp], _i32),
+    "csa_attend_merge": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
     "csa_index_score": ([_vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _i64, _i32, _vp, _vp,
                          _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp], _i32),
     "csa_topk": ([_vp, _i64, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _sz, _vp],
@@ -192,6 +195,44 @@ def compress(x: torch.Tensor, logits: torch.Tensor, m: int,
         x.data_ptr(), x.stride(0), x.stride(1), logits.data_ptr(), logits.stride(0),
         out.data_ptr(), out.stride(0), out.stride(1), _dtype_code(x), B, n, C, m, _stream()))
     return out
+
+
+def compress_append(x: torch.Tensor, logits: torch.Tensor, t_new: torch.Tensor, m: int,
+                    cache: torch.Tensor, n_entries: torch.Tensor) -> None:
+    """Incremental compression: token t_new[b] was just added to x [B, R, C]
+    (token s at row s % R, R a multiple of m) with logits [B, R]; if it
+    completes a block, pool the block into cache [B, N_max, C] row
+    (t + 1) // m - 1 and set n_entries[b] to (t + 1) // m, in place."""
+    _require_cuda(x, logits, t_new, cache, n_entries)
+    B, R, C = x.shape
+    if x.stride(-1) != 1 or cache.stride(-1) != 1 or logits.stride(-1) != 1:
+        raise ValueError("x, cache and logits need a contiguous last dim")
+    if logits.dtype != torch.float32 or t_new.dtype != torch.int32 or n_entries.dtype != torch.int32:
+        raise ValueError("logits must be float32, t_new and n_entries int32")
+    if cache.dtype != x.dtype or cache.shape[0] != B or cache.shape[2] != C:
+        raise ValueError("cache must be [B, N_max, C] of x's dtype")
+    _check(load_library().csa_compress_append(
+        x.data_ptr(), x.stride(0), x.stride(1), R, logits.data_ptr(), logits.stride(0),
+        t_new.data_ptr(), cache.data_ptr(), cache.stride(0), cache.stride(1), n_entries.data_ptr(),
+        _dtype_code(x), B, C, m, cache.shape[1], _stream()))
+
+
+def attend_merge(o_a, lse_a, o_b, lse_b, out: Optional[torch.Tensor] = None, with_lse: bool = False):
+    """Attention over the union of two disjoint key sets from the results over
+    each (o [..., H, D] and lse [..., H], same softmax scale)."""
+    _require_cuda(o_a, lse_a, o_b, lse_b, out)
+    for t, name in ((o_a, "o_a"), (o_b, "o_b"), (lse_a, "lse_a"), (lse_b, "lse_b")):
+        _contig(t, name)
+    if o_a.shape != o_b.shape or lse_a.shape != o_a.shape[:-1] or lse_b.shape != lse_a.shape:
+        raise ValueError("o_a, o_b [..., H, D] and lse_a, lse_b [..., H] must agree")
+    H, D = o_a.shape[-2], o_a.shape[-1]
+    rows = o_a.numel() // (H * D)
+    out = torch.empty_like(o_a) if out is None else out
+    lse = torch.empty_like(lse_a) if with_lse else None
+    _check(load_library().csa_attend_merge(
+        o_a.data_ptr(), lse_a.data_ptr(), o_b.data_ptr(), lse_b.data_ptr(), _dtype_code(o_a), rows,
+        H, D, out.data_ptr(), _ptr(lse), _stream()))
+    return (out, lse) if with_lse else out
 
 
 # ------------------------------------------------------------------ MX FP4 encoding

@@ -584,6 +584,64 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
 }
 
 
+
+// ---------------------------------------------------------------- merging two branches
+// Attention results over disjoint key sets (a sliding window and the
+// compressed entries, say), each as (o, lse) under the same softmax scale,
+// give the attention over the union: lse = log(e^lse_a + e^lse_b) and
+// o = e^(lse_a - lse) o_a + e^(lse_b - lse) o_b.  One thread per 8 output
+// dims of one (row, head); elementwise, so out may be o_a or o_b itself.
+template <typename T>
+__global__ __launch_bounds__(256) void merge_kernel(const T* __restrict__ oa, const float* __restrict__ la,
+                                                    const T* __restrict__ ob, const float* __restrict__ lb,
+                                                    T* out, float* __restrict__ lse_out, int64_t rows_h,
+                                                    int D) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int per = D / 8;
+  if (i >= rows_h * per) return;
+  const int64_t rh = i / per;
+  const int64_t off = rh * D + (i - rh * per) * 8;
+  const float a = la[rh], b = lb[rh];
+  const float mx = fmaxf(a, b);
+  float wa = 0.f, wb = 0.f, l = kNegInf;
+  if (mx != kNegInf) {
+    const float ea = a == kNegInf ? 0.f : expf(a - mx);
+    const float eb = b == kNegInf ? 0.f : expf(b - mx);
+    const float sum = ea + eb;
+    wa = ea / sum;
+    wb = eb / sum;
+    l = mx + logf(sum);
+  }
+  float x[8], y[8];
+  if constexpr (sizeof(T) == 2) {
+    const uint4 u = ld16(oa + off), v = ld16(ob + off);
+    const uint32_t uu[4] = {u.x, u.y, u.z, u.w}, vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      x[2 * c] = __uint_as_float(uu[c] << 16);
+      x[2 * c + 1] = __uint_as_float(uu[c] & 0xffff0000u);
+      y[2 * c] = __uint_as_float(vv[c] << 16);
+      y[2 * c + 1] = __uint_as_float(vv[c] & 0xffff0000u);
+    }
+    uint4 r;
+    r.x = pack_bf16x2(wa * x[0] + wb * y[0], wa * x[1] + wb * y[1]);
+    r.y = pack_bf16x2(wa * x[2] + wb * y[2], wa * x[3] + wb * y[3]);
+    r.z = pack_bf16x2(wa * x[4] + wb * y[4], wa * x[5] + wb * y[5]);
+    r.w = pack_bf16x2(wa * x[6] + wb * y[6], wa * x[7] + wb * y[7]);
+    st16(out + off, r);
+  } else {
+#pragma unroll
+    for (int c = 0; c < 8; c += 4) {
+      const float4 u = *reinterpret_cast<const float4*>(oa + off + c);
+      const float4 v = *reinterpret_cast<const float4*>(ob + off + c);
+      *reinterpret_cast<float4*>(out + off + c) =
+          make_float4(wa * u.x + wb * v.x, wa * u.y + wb * v.y, wa * u.z + wb * v.z,
+                      wa * u.w + wb * v.w);
+    }
+  }
+  if (lse_out != nullptr && i - rh * per == 0) lse_out[rh] = l;
+}
+
 bool tuned(csa_dtype_t dt, int H, int D) { return dt == CSA_BF16 && H == 64 && D == 128; }
 
 int split_len(bool hca) { return hca ? kHcaSplit : kCsaSplit; }
@@ -676,5 +734,22 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
   return hipGetLastError();
 }
 
+
+hipError_t launch_merge(const void* oa, const float* la, const void* ob, const float* lb,
+                        csa_dtype_t dt, int rows, int H, int D, void* out, float* lse_out,
+                        hipStream_t s) {
+  const int64_t rows_h = static_cast<int64_t>(rows) * H;
+  const int64_t threads = rows_h * (D / 8);
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  if (dt == CSA_F32)
+    hipLaunchKernelGGL(merge_kernel<float>, grid, dim3(256), 0, s, static_cast<const float*>(oa),
+                       la, static_cast<const float*>(ob), lb, static_cast<float*>(out), lse_out,
+                       rows_h, D);
+  else
+    hipLaunchKernelGGL(merge_kernel<uint16_t>, grid, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(oa), la, static_cast<const uint16_t*>(ob), lb,
+                       static_cast<uint16_t*>(out), lse_out, rows_h, D);
+  return hipGetLastError();
+}
 
 }  // namespace csa

@@ -47,19 +47,19 @@ struct Chunk<uint16_t> {
   }
 };
 
+// Pools one block of m rows (xb, token stride x_st; logits zb) into orow.
+// Must be reached by the whole workgroup (it synchronises).
 template <typename T>
-__global__ __launch_bounds__(kCompressThreads) void compress_kernel(
-    const T* __restrict__ x, int64_t x_sb, int64_t x_st, const float* __restrict__ z,
-    int64_t z_sb, T* __restrict__ out, int64_t o_sb, int64_t o_sj, int m, int CH, int P) {
+__device__ __forceinline__ void pool_block(const T* __restrict__ xb, int64_t x_st,
+                                           const float* __restrict__ zb, T* __restrict__ orow,
+                                           int m, int CH, int P) {
   constexpr int E = Chunk<T>::N;
   __shared__ float e_s[kMaxPool];
   __shared__ float red[kCompressThreads / 64];
   __shared__ float part[kCompressThreads * E];
 
-  const int j = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
-  const float* zb = z + b * z_sb + static_cast<int64_t>(j) * m;
 
   // softmax weights of the block's logits (unnormalised; divided at the end)
   float mx = kNegInf;
@@ -88,11 +88,11 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
     float acc[E];
 #pragma unroll
     for (int c = 0; c < E; ++c) acc[c] = 0.f;
-    const T* xb = x + b * x_sb + static_cast<int64_t>(j) * m * x_st + ch * E;
+    const T* xc = xb + ch * E;
 #pragma unroll 4
     for (int i = p; i < m; i += P) {
       float f[E];
-      Chunk<T>::unpack(ld16(xb + static_cast<int64_t>(i) * x_st), f);
+      Chunk<T>::unpack(ld16(xc + static_cast<int64_t>(i) * x_st), f);
       const float e = e_s[i];
 #pragma unroll
       for (int c = 0; c < E; ++c) acc[c] = fmaf(e, f[c], acc[c]);
@@ -111,8 +111,41 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
     }
 #pragma unroll
     for (int c = 0; c < E; ++c) r[c] = r[c] / total;
-    st16(out + b * o_sb + static_cast<int64_t>(j) * o_sj + tid * E, Chunk<T>::pack(r));
+    st16(orow + tid * E, Chunk<T>::pack(r));
   }
+}
+
+// One workgroup per compressed entry (j, b) of the batch.
+template <typename T>
+__global__ __launch_bounds__(kCompressThreads) void compress_kernel(
+    const T* __restrict__ x, int64_t x_sb, int64_t x_st, const float* __restrict__ z,
+    int64_t z_sb, T* __restrict__ out, int64_t o_sb, int64_t o_sj, int m, int CH, int P) {
+  const int j = blockIdx.x, b = blockIdx.y;
+  pool_block<T>(x + b * x_sb + static_cast<int64_t>(j) * m * x_st, x_st,
+                z + b * z_sb + static_cast<int64_t>(j) * m, out + b * o_sb + static_cast<int64_t>(j) * o_sj,
+                m, CH, P);
+}
+
+// Append: one workgroup per sequence.  Token t = t_new[b] was just added; if
+// it completes a block (m divides t + 1), entry j = (t + 1) / m - 1 pools
+// tokens m j .. m j + m - 1, read from rows (m j + i) mod x_rows of x and z
+// (x_rows a multiple of m: a ring of the latest tokens, or the whole
+// sequence), and the sequence's entry count becomes j + 1.  Entries at or
+// past N_max are not written.
+template <typename T>
+__global__ __launch_bounds__(kCompressThreads) void compress_append_kernel(
+    const T* __restrict__ x, int64_t x_sb, int64_t x_st, int x_rows, const float* __restrict__ z,
+    int64_t z_sb, const int32_t* __restrict__ t_new, T* __restrict__ cache, int64_t c_sb,
+    int64_t c_sj, int32_t* __restrict__ n_entries, int N_max, int m, int CH, int P) {
+  const int b = blockIdx.x;
+  const int t = t_new[b];
+  if (t < 0 || (t + 1) % m != 0) return;          // uniform over the workgroup
+  const int j = (t + 1) / m - 1;
+  if (j >= N_max) return;
+  const int64_t r0 = static_cast<int64_t>(m) * j % x_rows;
+  pool_block<T>(x + b * x_sb + r0 * x_st, x_st, z + b * z_sb + r0, cache + b * c_sb + j * c_sj, m,
+                CH, P);
+  if (threadIdx.x == 0) n_entries[b] = j + 1;
 }
 
 template <typename T>
@@ -132,7 +165,34 @@ hipError_t launch_typed(const void* x, int64_t x_sb, int64_t x_st, const float* 
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_append_typed(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
+                               const float* z, int64_t z_sb, const int32_t* t_new, void* cache,
+                               int64_t c_sb, int64_t c_sj, int32_t* n_entries, int B, int C,
+                               int m, int N_max, hipStream_t s) {
+  constexpr int E = Chunk<T>::N;
+  const int CH = C / E;
+  int P = kCompressThreads / CH;
+  if (P > m) P = m;
+  const int threads = ((P * CH + 63) / 64) * 64;
+  hipLaunchKernelGGL(compress_append_kernel<T>, dim3(B), dim3(threads), 0, s,
+                     static_cast<const T*>(x), x_sb, x_st, x_rows, z, z_sb, t_new,
+                     static_cast<T*>(cache), c_sb, c_sj, n_entries, N_max, m, CH, P);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
+                                  const float* z, int64_t z_sb, const int32_t* t_new, void* cache,
+                                  int64_t c_sb, int64_t c_sj, int32_t* n_entries, csa_dtype_t dt,
+                                  int B, int C, int m, int N_max, hipStream_t s) {
+  if (dt == CSA_F32)
+    return launch_append_typed<float>(x, x_sb, x_st, x_rows, z, z_sb, t_new, cache, c_sb, c_sj,
+                                      n_entries, B, C, m, N_max, s);
+  return launch_append_typed<uint16_t>(x, x_sb, x_st, x_rows, z, z_sb, t_new, cache, c_sb, c_sj,
+                                       n_entries, B, C, m, N_max, s);
+}
 
 hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const float* z, int64_t z_sb,
                            void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dt, int B, int n,

@@ -151,6 +151,53 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st, const float
                     "compress launch");
 }
 
+csa_status_t csa_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
+                                 const float* logits, int64_t z_sb, const int32_t* t_new,
+                                 void* cache, int64_t c_sb, int64_t c_sj, int32_t* n_entries,
+                                 csa_dtype_t dtype, int B, int C, int m, int N_max,
+                                 hipStream_t stream) {
+  g_err[0] = 0;
+  CSA_REQUIRE(x && logits && t_new && cache && n_entries, CSA_ERR_INVALID_ARGUMENT,
+              "compress append: NULL pointer");
+  CSA_REQUIRE(B >= 1 && C >= 1 && m >= 1 && N_max >= 1 && x_rows >= m && x_rows % m == 0,
+              CSA_ERR_INVALID_ARGUMENT,
+              "compress append: sizes must be >= 1 and x_rows a positive multiple of m");
+  CSA_REQUIRE(m <= 4096, CSA_ERR_UNSUPPORTED, "compress append: m=%d > 4096", m);
+  CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+              "compress append: dtype must be F32 or BF16");
+  const int64_t es = static_cast<int64_t>(esize(dtype));
+  CSA_REQUIRE((C * es) % 16 == 0 && C * es / 16 <= 256, CSA_ERR_UNSUPPORTED,
+              "compress append: C*elem_size must be a multiple of 16 and at most 4096 bytes");
+  CSA_REQUIRE(aligned16(x) && aligned16(cache), CSA_ERR_INVALID_ARGUMENT,
+              "compress append: pointers must be 16-byte aligned");
+  CSA_REQUIRE((x_st * es) % 16 == 0 && (x_sb * es) % 16 == 0 && (c_sj * es) % 16 == 0 &&
+                  (c_sb * es) % 16 == 0,
+              CSA_ERR_INVALID_ARGUMENT, "compress append: strides must be multiples of 16 bytes");
+  CSA_REQUIRE(x_st >= C && c_sj >= C && z_sb >= x_rows, CSA_ERR_INVALID_ARGUMENT,
+              "compress append: strides smaller than the rows");
+  return hip_status(csa::launch_compress_append(x, x_sb, x_st, x_rows, logits, z_sb, t_new, cache,
+                                                c_sb, c_sj, n_entries, dtype, B, C, m, N_max,
+                                                stream),
+                    "compress append launch");
+}
+
+csa_status_t csa_attend_merge(const void* o_a, const float* lse_a, const void* o_b,
+                              const float* lse_b, csa_dtype_t dtype, int rows, int H, int D,
+                              void* out, float* lse_out, hipStream_t stream) {
+  g_err[0] = 0;
+  CSA_REQUIRE(o_a && lse_a && o_b && lse_b && out, CSA_ERR_INVALID_ARGUMENT,
+              "attend merge: NULL pointer");
+  CSA_REQUIRE(rows >= 1 && H >= 1 && D >= 8 && D % 8 == 0, CSA_ERR_INVALID_ARGUMENT,
+              "attend merge: need rows, H >= 1 and D a positive multiple of 8");
+  CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+              "attend merge: dtype must be F32 or BF16");
+  CSA_REQUIRE(aligned16(o_a) && aligned16(o_b) && aligned16(out), CSA_ERR_INVALID_ARGUMENT,
+              "attend merge: outputs must be 16-byte aligned");
+  return hip_status(csa::launch_merge(o_a, lse_a, o_b, lse_b, dtype, rows, H, D, out, lse_out,
+                                      stream),
+                    "attend merge launch");
+}
+
 csa_status_t csa_quantize_mx4(const void* x, int64_t x_rs, csa_dtype_t dtype, int rows, int D,
                               uint8_t* codes, int64_t c_rs, uint8_t* scales, int64_t s_rs,
                               hipStream_t stream) {

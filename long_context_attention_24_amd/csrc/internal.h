@@ -15,6 +15,11 @@ hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const floa
                            void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dt, int B, int n,
                            int C, int m, hipStream_t s);
 
+hipError_t launch_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
+                                  const float* z, int64_t z_sb, const int32_t* t_new, void* cache,
+                                  int64_t c_sb, int64_t c_sj, int32_t* n_entries, csa_dtype_t dt,
+                                  int B, int C, int m, int N_max, hipStream_t s);
+
 // ---- quantize.hip
 hipError_t launch_quantize_mx4(const void* x, int64_t x_rs, csa_dtype_t dt, int rows, int D,
                                uint8_t* codes, int64_t c_rs, uint8_t* scales, int64_t s_rs,
@@ -91,5 +96,9 @@ size_t attend_part_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, 
 
 bool attend_supported(csa_dtype_t dt, int H, int D);
 hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s);
+// (o, lse) of two disjoint key sets -> the attention over their union
+hipError_t launch_merge(const void* oa, const float* la, const void* ob, const float* lb,
+                        csa_dtype_t dt, int rows, int H, int D, void* out, float* lse_out,
+                        hipStream_t s);
 
 }  // namespace csa

@@ -110,6 +110,31 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st,
                           hipStream_t stream);
 
 /*
+ * csa_compress_mx4 - csa_compress with the trailing D_mx channels of every
+ * entry (the indexer key) stored as MX FP4 instead of dtype (§2.1
+ * compression and §5's FP4 indexer QK path in one pass: the key is encoded
+ * from its fp32 pooled value, the format CSA_FP4_E2M1_E8M0 consumes).
+ *
+ *   channels c < C - D_mx: out[b, j, c] as csa_compress writes it;
+ *   channels C - D_mx .. C - 1: the pooled fp32 values v encoded per block of
+ *   32 as csa_quantize_mx4 encodes them (shared exponent e from the block's
+ *   largest |v|, codes = nearest E2M1 of v / 2^e): codes[b, j, D_mx/2]
+ *   (element 2i in the low nibble of byte i), scales[b, j, D_mx/32] (e + 127).
+ *
+ * x, logits, dtype, B, n, C, m and their strides as in csa_compress; out
+ * [B, n/m, C - D_mx] (strides o_sb, o_sj; NULL allowed when D_mx == C);
+ * codes with strides (c_sb, c_sj) bytes, 4-byte aligned (2 for CSA_F32);
+ * scales with strides (s_sb, s_sj) bytes.  D_mx and C - D_mx multiples of 32.
+ */
+csa_status_t csa_compress_mx4(const void* x, int64_t x_sb, int64_t x_st,
+                              const float* logits, int64_t z_sb,
+                              void* out, int64_t o_sb, int64_t o_sj,
+                              uint8_t* codes, int64_t c_sb, int64_t c_sj,
+                              uint8_t* scales, int64_t s_sb, int64_t s_sj,
+                              csa_dtype_t dtype, int B, int n, int C, int D_mx, int m,
+                              hipStream_t stream);
+
+/*
  * csa_compress_append - incremental compression during decoding (§2.1 KV
  * cache compression applied as tokens arrive: a compressed entry is formed
  * once its m tokens are all present).

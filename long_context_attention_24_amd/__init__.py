@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "CsaError", "library_path", "load_library",
-    "compress", "compress_append", "attend_merge", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
+    "compress", "compress_mx4", "compress_append", "attend_merge", "quantize_mx4", "index_score", "topk", "index_topk", "index_topk_bf16",
     "attend", "hca_attend", "swa_attend", "index_topk_attend", "index_topk_attend_noalloc",
     "index_topk_workspace_bytes",
     "index_topk_attend_workspace_bytes",
@@ -40,7 +40,7 @@ CSA_F32, CSA_BF16, CSA_FP4_E2M1, CSA_FP4_E2M1_E8M0 = 0, 1, 2, 3
 
 EXPORTED_SYMBOLS = (
     "csa_abi_version", "csa_status_string", "csa_last_error",
-    "csa_compress", "csa_compress_append", "csa_attend_merge", "csa_quantize_mx4", "csa_index_score", "csa_topk", "csa_topk_workspace",
+    "csa_compress", "csa_compress_mx4", "csa_compress_append", "csa_attend_merge", "csa_quantize_mx4", "csa_index_score", "csa_topk", "csa_topk_workspace",
     "csa_index_topk", "csa_index_topk_workspace",
     "csa_index_topk_bf16", "csa_index_topk_bf16_workspace",
     "csa_attend", "csa_attend_workspace", "hca_attend", "hca_attend_workspace",
@@ -69,6 +69,8 @@ _SIGS = {
     "csa_compress": ([_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i32, _i32, _i32, _i32,
                       _vp], _i32),
     "csa_quantize_mx4": ([_vp, _i64, _i32, _i32, _i32, _vp, _i64, _vp, _i64, _vp], _i32),
+    "csa_compress_mx4": ([_vp, _i64, _i64, _vp, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64,
+                          _i64, _i32, _i32, _i32, _i32, _i32, _i32, _vp], _i32),
     "csa_compress_append": ([_vp, _i64, _i64, _i32, _vp, _i64, _vp, _vp, _i64, _i64, _vp, _i32,
                              _i32, _i32, _i32, _i32, _vp], _i32),
     "csa_attend_merge": ([_vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], _i32),
@@ -195,6 +197,32 @@ def compress(x: torch.Tensor, logits: torch.Tensor, m: int,
         x.data_ptr(), x.stride(0), x.stride(1), logits.data_ptr(), logits.stride(0),
         out.data_ptr(), out.stride(0), out.stride(1), _dtype_code(x), B, n, C, m, _stream()))
     return out
+
+
+def compress_mx4(x: torch.Tensor, logits: torch.Tensor, m: int, d_mx: int,
+                 out: Optional[torch.Tensor] = None, codes: Optional[torch.Tensor] = None,
+                 scales: Optional[torch.Tensor] = None):
+    """Pool every m tokens of x [B, n, C]; the leading C - d_mx channels are
+    returned in x's dtype, the trailing d_mx MX FP4 encoded from their fp32
+    pooled values -> (out [B, n//m, C - d_mx] or None, codes uint8
+    [B, n//m, d_mx/2], E8M0 scales uint8 [B, n//m, d_mx/32])."""
+    _require_cuda(x, logits, out, codes, scales)
+    B, n, C = x.shape
+    if x.stride(-1) != 1 or logits.stride(-1) != 1 or logits.dtype != torch.float32:
+        raise ValueError("x and logits need a contiguous last dim; logits must be float32")
+    nb = n // m
+    if out is None and d_mx < C:
+        out = torch.empty((B, nb, C - d_mx), dtype=x.dtype, device=x.device)
+    if codes is None:
+        codes = torch.empty((B, nb, d_mx // 2), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, nb, d_mx // 32), dtype=torch.uint8, device=x.device)
+    _check(load_library().csa_compress_mx4(
+        x.data_ptr(), x.stride(0), x.stride(1), logits.data_ptr(), logits.stride(0),
+        _ptr(out), 0 if out is None else out.stride(0), 0 if out is None else out.stride(1),
+        codes.data_ptr(), codes.stride(0), codes.stride(1), scales.data_ptr(), scales.stride(0),
+        scales.stride(1), _dtype_code(x), B, n, C, d_mx, m, _stream()))
+    return out, codes, scales
 
 
 def compress_append(x: torch.Tensor, logits: torch.Tensor, t_new: torch.Tensor, m: int,

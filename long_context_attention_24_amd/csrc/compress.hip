@@ -48,11 +48,16 @@ struct Chunk<uint16_t> {
 };
 
 // Pools one block of m rows (xb, token stride x_st; logits zb) into orow.
+// With CH0 < CH the channels of chunks CH0 .. CH-1 are not stored in orow
+// but MX FP4 encoded from their fp32 pooled values: codes to crow (element
+// 2i in the low nibble of byte i), one E8M0 byte per 32 channels to srow.
 // Must be reached by the whole workgroup (it synchronises).
 template <typename T>
 __device__ __forceinline__ void pool_block(const T* __restrict__ xb, int64_t x_st,
                                            const float* __restrict__ zb, T* __restrict__ orow,
-                                           int m, int CH, int P) {
+                                           int m, int CH, int P, int CH0 = 1 << 30,
+                                           uint8_t* __restrict__ crow = nullptr,
+                                           uint8_t* __restrict__ srow = nullptr) {
   constexpr int E = Chunk<T>::N;
   __shared__ float e_s[kMaxPool];
   __shared__ float red[kCompressThreads / 64];
@@ -101,8 +106,10 @@ __device__ __forceinline__ void pool_block(const T* __restrict__ xb, int64_t x_s
     for (int c = 0; c < E; ++c) part[(p * CH + ch) * E + c] = acc[c];
   }
   __syncthreads();
+  float r[E];
+#pragma unroll
+  for (int c = 0; c < E; ++c) r[c] = 0.f;
   if (tid < CH) {
-    float r[E];
 #pragma unroll
     for (int c = 0; c < E; ++c) r[c] = part[tid * E + c];
     for (int q = 1; q < P; ++q) {
@@ -111,8 +118,125 @@ __device__ __forceinline__ void pool_block(const T* __restrict__ xb, int64_t x_s
     }
 #pragma unroll
     for (int c = 0; c < E; ++c) r[c] = r[c] / total;
-    st16(orow + tid * E, Chunk<T>::pack(r));
+    if (tid < CH0) st16(orow + tid * E, Chunk<T>::pack(r));
   }
+  if (CH0 < CH) {
+    // MX FP4 blocks of 32 channels = G consecutive chunk threads (aligned
+    // groups of lanes): the block maximum by lane exchanges, then each
+    // thread encodes its E channels
+    constexpr int G = 32 / E;
+    float am = 0.f;
+#pragma unroll
+    for (int c = 0; c < E; ++c) am = fmaxf(am, fabsf(r[c]));
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if (tid >= CH0 && tid < CH) {
+      const int e = mx_block_exponent(am);
+      const int q = tid - CH0;
+      uint32_t w = 0;
+      w = mx_cvt_pair<0>(w, r[0], r[1], e);
+      w = mx_cvt_pair<1>(w, r[2], r[3], e);
+      if constexpr (E == 8) {
+        w = mx_cvt_pair<2>(w, r[4], r[5], e);
+        w = mx_cvt_pair<3>(w, r[6], r[7], e);
+        *reinterpret_cast<uint32_t*>(crow + 4 * q) = w;
+      } else {
+        *reinterpret_cast<uint16_t*>(crow + 2 * q) = static_cast<uint16_t>(w);
+      }
+      if (q % G == 0) srow[q / G] = static_cast<uint8_t>(e + 127);
+    }
+  }
+}
+
+// Small blocks (m <= kSmallPool): one thread per (entry, 16-byte channel
+// chunk), the entries of the whole batch laid end to end, so a 256-thread
+// workgroup covers several entries with coalesced loads (the threads of one
+// entry read each token row contiguously).  Each thread forms the block's
+// softmax weights itself from the m logits and sums its chunk over the m
+// tokens in token order: no LDS and no barrier, which a workgroup per entry
+// of a few kilobytes cannot amortise.  With CH0 < CH the chunks from CH0 on
+// are MX FP4 encoded as in pool_block (the 32-channel blocks are aligned
+// groups of consecutive threads; lanes past the end repeat the last chunk so
+// that every lane takes part in the exchanges).
+constexpr int kSmallPool = 16;
+
+template <typename T>
+__global__ __launch_bounds__(256) void compress_small_kernel(
+    const T* __restrict__ x, int64_t x_sb, int64_t x_st, const float* __restrict__ z,
+    int64_t z_sb, T* __restrict__ out, int64_t o_sb, int64_t o_sj, uint8_t* __restrict__ codes,
+    int64_t c_sb, int64_t c_sj, uint8_t* __restrict__ scales, int64_t s_sb, int64_t s_sj, int m,
+    int CH, int CH0, int nblk, int64_t total) {
+  constexpr int E = Chunk<T>::N;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const bool own = gid < total;
+  const int64_t g = own ? gid : total - 1;
+  const int ch = static_cast<int>(g % CH);
+  const int64_t ent = g / CH;
+  const int j = static_cast<int>(ent % nblk), b = static_cast<int>(ent / nblk);
+  const float* zb = z + b * z_sb + static_cast<int64_t>(j) * m;
+  const T* xb = x + b * x_sb + static_cast<int64_t>(j) * m * x_st + ch * E;
+  uint4 raw[kSmallPool];
+#pragma unroll
+  for (int i = 0; i < kSmallPool; ++i)
+    if (i < m) raw[i] = ld16(xb + static_cast<int64_t>(i) * x_st);
+  float mx = kNegInf;
+  for (int i = 0; i < m; ++i) mx = fmaxf(mx, zb[i]);
+  float acc[E], tw = 0.f;
+#pragma unroll
+  for (int c = 0; c < E; ++c) acc[c] = 0.f;
+#pragma unroll
+  for (int i = 0; i < kSmallPool; ++i) {
+    if (i < m) {
+      const float wgt = expf(zb[i] - mx);
+      tw += wgt;
+      float f[E];
+      Chunk<T>::unpack(raw[i], f);
+#pragma unroll
+      for (int c = 0; c < E; ++c) acc[c] = fmaf(wgt, f[c], acc[c]);
+    }
+  }
+  float r[E];
+#pragma unroll
+  for (int c = 0; c < E; ++c) r[c] = acc[c] / tw;
+  if (own && ch < CH0) st16(out + b * o_sb + static_cast<int64_t>(j) * o_sj + ch * E, Chunk<T>::pack(r));
+  if (CH0 < CH) {
+    constexpr int G = 32 / E;
+    float am = 0.f;
+#pragma unroll
+    for (int c = 0; c < E; ++c) am = fmaxf(am, fabsf(r[c]));
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1) am = fmaxf(am, __shfl_xor(am, o, 64));
+    if (own && ch >= CH0) {
+      const int e = mx_block_exponent(am);
+      const int q = ch - CH0;
+      uint8_t* crow = codes + b * c_sb + static_cast<int64_t>(j) * c_sj;
+      uint32_t w = 0;
+      w = mx_cvt_pair<0>(w, r[0], r[1], e);
+      w = mx_cvt_pair<1>(w, r[2], r[3], e);
+      if constexpr (E == 8) {
+        w = mx_cvt_pair<2>(w, r[4], r[5], e);
+        w = mx_cvt_pair<3>(w, r[6], r[7], e);
+        *reinterpret_cast<uint32_t*>(crow + 4 * q) = w;
+      } else {
+        *reinterpret_cast<uint16_t*>(crow + 2 * q) = static_cast<uint16_t>(w);
+      }
+      if (q % G == 0)
+        scales[b * s_sb + static_cast<int64_t>(j) * s_sj + q / G] = static_cast<uint8_t>(e + 127);
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_small(const void* x, int64_t x_sb, int64_t x_st, const float* z, int64_t z_sb,
+                        void* out, int64_t o_sb, int64_t o_sj, uint8_t* codes, int64_t c_sb,
+                        int64_t c_sj, uint8_t* scales, int64_t s_sb, int64_t s_sj, int B, int nblk,
+                        int CH, int CH0, int m, hipStream_t s) {
+  const int64_t total = static_cast<int64_t>(B) * nblk * CH;
+  hipLaunchKernelGGL(compress_small_kernel<T>, dim3(static_cast<unsigned>((total + 255) / 256)),
+                     dim3(256), 0, s, static_cast<const T*>(x), x_sb, x_st, z, z_sb,
+                     static_cast<T*>(out), o_sb, o_sj, codes, c_sb, c_sj, scales, s_sb, s_sj, m,
+                     CH, CH0, nblk, total);
+  return hipGetLastError();
 }
 
 // One workgroup per compressed entry (j, b) of the batch.
@@ -124,6 +248,21 @@ __global__ __launch_bounds__(kCompressThreads) void compress_kernel(
   pool_block<T>(x + b * x_sb + static_cast<int64_t>(j) * m * x_st, x_st,
                 z + b * z_sb + static_cast<int64_t>(j) * m, out + b * o_sb + static_cast<int64_t>(j) * o_sj,
                 m, CH, P);
+}
+
+// The same with the channels from CH0 chunks on MX FP4 encoded.
+template <typename T>
+__global__ __launch_bounds__(kCompressThreads) void compress_mx4_kernel(
+    const T* __restrict__ x, int64_t x_sb, int64_t x_st, const float* __restrict__ z,
+    int64_t z_sb, T* __restrict__ out, int64_t o_sb, int64_t o_sj, uint8_t* __restrict__ codes,
+    int64_t c_sb, int64_t c_sj, uint8_t* __restrict__ scales, int64_t s_sb, int64_t s_sj, int m,
+    int CH, int P, int CH0) {
+  const int j = blockIdx.x, b = blockIdx.y;
+  pool_block<T>(x + b * x_sb + static_cast<int64_t>(j) * m * x_st, x_st,
+                z + b * z_sb + static_cast<int64_t>(j) * m,
+                out + b * o_sb + static_cast<int64_t>(j) * o_sj, m, CH, P, CH0,
+                codes + b * c_sb + static_cast<int64_t>(j) * c_sj,
+                scales + b * s_sb + static_cast<int64_t>(j) * s_sj);
 }
 
 // Append: one workgroup per sequence.  Token t = t_new[b] was just added; if
@@ -159,6 +298,9 @@ hipError_t launch_typed(const void* x, int64_t x_sb, int64_t x_st, const float* 
   int threads = ((P * CH + 63) / 64) * 64;
   const int nblk = n / m;
   if (nblk == 0) return hipSuccess;
+  if (m <= kSmallPool)
+    return launch_small<T>(x, x_sb, x_st, z, z_sb, out, o_sb, o_sj, nullptr, 0, 0, nullptr, 0, 0,
+                           B, nblk, CH, CH, m, s);
   hipLaunchKernelGGL(compress_kernel<T>, dim3(nblk, B), dim3(threads), 0, s,
                      static_cast<const T*>(x), x_sb, x_st, z, z_sb, static_cast<T*>(out), o_sb,
                      o_sj, m, CH, P);
@@ -181,7 +323,40 @@ hipError_t launch_append_typed(const void* x, int64_t x_sb, int64_t x_st, int x_
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_mx4_typed(const void* x, int64_t x_sb, int64_t x_st, const float* z, int64_t z_sb,
+                            void* out, int64_t o_sb, int64_t o_sj, uint8_t* codes, int64_t c_sb,
+                            int64_t c_sj, uint8_t* scales, int64_t s_sb, int64_t s_sj, int B,
+                            int n, int C, int D_mx, int m, hipStream_t s) {
+  constexpr int E = Chunk<T>::N;
+  const int CH = C / E;
+  int P = kCompressThreads / CH;
+  if (P > m) P = m;
+  const int threads = ((P * CH + 63) / 64) * 64;
+  const int nblk = n / m;
+  if (nblk == 0) return hipSuccess;
+  if (m <= kSmallPool)
+    return launch_small<T>(x, x_sb, x_st, z, z_sb, out, o_sb, o_sj, codes, c_sb, c_sj, scales,
+                           s_sb, s_sj, B, nblk, CH, (C - D_mx) / E, m, s);
+  hipLaunchKernelGGL(compress_mx4_kernel<T>, dim3(nblk, B), dim3(threads), 0, s,
+                     static_cast<const T*>(x), x_sb, x_st, z, z_sb, static_cast<T*>(out), o_sb,
+                     o_sj, codes, c_sb, c_sj, scales, s_sb, s_sj, m, CH, P, (C - D_mx) / E);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_compress_mx4(const void* x, int64_t x_sb, int64_t x_st, const float* z,
+                               int64_t z_sb, void* out, int64_t o_sb, int64_t o_sj,
+                               uint8_t* codes, int64_t c_sb, int64_t c_sj, uint8_t* scales,
+                               int64_t s_sb, int64_t s_sj, csa_dtype_t dt, int B, int n, int C,
+                               int D_mx, int m, hipStream_t s) {
+  if (dt == CSA_F32)
+    return launch_mx4_typed<float>(x, x_sb, x_st, z, z_sb, out, o_sb, o_sj, codes, c_sb, c_sj,
+                                   scales, s_sb, s_sj, B, n, C, D_mx, m, s);
+  return launch_mx4_typed<uint16_t>(x, x_sb, x_st, z, z_sb, out, o_sb, o_sj, codes, c_sb, c_sj,
+                                    scales, s_sb, s_sj, B, n, C, D_mx, m, s);
+}
 
 hipError_t launch_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
                                   const float* z, int64_t z_sb, const int32_t* t_new, void* cache,

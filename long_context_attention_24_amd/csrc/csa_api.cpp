@@ -151,6 +151,43 @@ csa_status_t csa_compress(const void* x, int64_t x_sb, int64_t x_st, const float
                     "compress launch");
 }
 
+csa_status_t csa_compress_mx4(const void* x, int64_t x_sb, int64_t x_st, const float* logits,
+                              int64_t z_sb, void* out, int64_t o_sb, int64_t o_sj, uint8_t* codes,
+                              int64_t c_sb, int64_t c_sj, uint8_t* scales, int64_t s_sb,
+                              int64_t s_sj, csa_dtype_t dtype, int B, int n, int C, int D_mx, int m,
+                              hipStream_t stream) {
+  g_err[0] = 0;
+  CSA_REQUIRE(x && logits && codes && scales && (out || D_mx == C), CSA_ERR_INVALID_ARGUMENT,
+              "compress mx4: NULL pointer");
+  CSA_REQUIRE(B >= 1 && n >= 1 && C >= 1 && m >= 1, CSA_ERR_INVALID_ARGUMENT,
+              "compress mx4: sizes must be >= 1");
+  CSA_REQUIRE(D_mx >= 32 && D_mx % 32 == 0 && D_mx <= C && (C - D_mx) % 32 == 0,
+              CSA_ERR_INVALID_ARGUMENT,
+              "compress mx4: D_mx must be a positive multiple of 32, at most C, with C - D_mx a "
+              "multiple of 32");
+  CSA_REQUIRE(m <= 4096, CSA_ERR_UNSUPPORTED, "compress mx4: m=%d > 4096", m);
+  CSA_REQUIRE(dtype == CSA_F32 || dtype == CSA_BF16, CSA_ERR_UNSUPPORTED,
+              "compress mx4: dtype must be F32 or BF16");
+  const int64_t es = static_cast<int64_t>(esize(dtype));
+  CSA_REQUIRE(C * es / 16 <= 256, CSA_ERR_UNSUPPORTED, "compress mx4: C too large (%d)", C);
+  CSA_REQUIRE(aligned16(x) && (out == nullptr || aligned16(out)), CSA_ERR_INVALID_ARGUMENT,
+              "compress mx4: x and out must be 16-byte aligned");
+  const int64_t cw = dtype == CSA_BF16 ? 4 : 2;   // code bytes written per thread
+  CSA_REQUIRE(reinterpret_cast<uintptr_t>(codes) % cw == 0 && c_sj % cw == 0 && c_sb % cw == 0,
+              CSA_ERR_INVALID_ARGUMENT, "compress mx4: codes must be %lld-byte aligned",
+              static_cast<long long>(cw));
+  CSA_REQUIRE((x_st * es) % 16 == 0 && (x_sb * es) % 16 == 0 && (o_sj * es) % 16 == 0 &&
+                  (o_sb * es) % 16 == 0,
+              CSA_ERR_INVALID_ARGUMENT, "compress mx4: strides must be multiples of 16 bytes");
+  CSA_REQUIRE(x_st >= C && z_sb >= n && c_sj >= D_mx / 2 && s_sj >= D_mx / 32 &&
+                  (D_mx == C || o_sj >= C - D_mx),
+              CSA_ERR_INVALID_ARGUMENT, "compress mx4: strides smaller than the rows");
+  return hip_status(csa::launch_compress_mx4(x, x_sb, x_st, logits, z_sb, out, o_sb, o_sj, codes,
+                                             c_sb, c_sj, scales, s_sb, s_sj, dtype, B, n, C, D_mx,
+                                             m, stream),
+                    "compress mx4 launch");
+}
+
 csa_status_t csa_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
                                  const float* logits, int64_t z_sb, const int32_t* t_new,
                                  void* cache, int64_t c_sb, int64_t c_sj, int32_t* n_entries,

@@ -87,6 +87,30 @@ __device__ __forceinline__ float relu_f32(float x) {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// MX FP4 (OCP Microscaling) shared exponent of a 32-element block from its
+// largest magnitude: floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+// clamped to [-127, 127], -127 for an all-zero block.  floor(log2) from the
+// bit pattern, subnormals included.
+__device__ __forceinline__ int mx_block_exponent(float amax) {
+  if (!(amax > 0.f)) return -127;
+  const uint32_t u = __float_as_uint(amax);
+  const int ef = static_cast<int>(u >> 23);
+  const int fl = ef != 0 ? ef - 127 : (31 - __builtin_clz(u & 0x7fffffu)) - 149;
+  return max(-127, min(127, fl - 2));
+}
+
+// Two values to E2M1 codes in byte `sel` of w, x / 2^e rounded to the nearest
+// E2M1 value (ties to even, saturating at 6, x's sign): gfx950's scaled FP4
+// conversion with scale 2^e.  2^-127 is no normal float, so e = -127 (values
+// below 2^-125) is handled as (x 2^126) / 2^-1, which is exact.
+template <int SEL>
+__device__ __forceinline__ uint32_t mx_cvt_pair(uint32_t w, float a, float b, int e) {
+  if (e > -127)
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(
+        w, a, b, __uint_as_float(static_cast<uint32_t>(e + 127) << 23), SEL);
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, a * 0x1p126f, b * 0x1p126f, 0.5f, SEL);
+}
+
 // ---- wave64 reductions and scans -------------------------------------------
 // The device library's DPP implementations (row shifts and broadcasts, no LDS
 // round trips).  Each uses a fixed combination order, so results are

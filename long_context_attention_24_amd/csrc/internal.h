@@ -15,6 +15,11 @@ hipError_t launch_compress(const void* x, int64_t x_sb, int64_t x_st, const floa
                            void* out, int64_t o_sb, int64_t o_sj, csa_dtype_t dt, int B, int n,
                            int C, int m, hipStream_t s);
 
+hipError_t launch_compress_mx4(const void* x, int64_t x_sb, int64_t x_st, const float* z,
+                               int64_t z_sb, void* out, int64_t o_sb, int64_t o_sj,
+                               uint8_t* codes, int64_t c_sb, int64_t c_sj, uint8_t* scales,
+                               int64_t s_sb, int64_t s_sj, csa_dtype_t dt, int B, int n, int C,
+                               int D_mx, int m, hipStream_t s);
 hipError_t launch_compress_append(const void* x, int64_t x_sb, int64_t x_st, int x_rows,
                                   const float* z, int64_t z_sb, const int32_t* t_new, void* cache,
                                   int64_t c_sb, int64_t c_sj, int32_t* n_entries, csa_dtype_t dt,

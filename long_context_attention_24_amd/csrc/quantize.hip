@@ -26,19 +26,7 @@ constexpr int kQuantThreads = 256;
 
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 
-// floor(log2(a)) for a finite a > 0, from the bit pattern (subnormals too)
-__device__ __forceinline__ int floor_log2(float a) {
-  const uint32_t u = __float_as_uint(a);
-  const int ef = static_cast<int>(u >> 23);
-  if (ef != 0) return ef - 127;
-  return (31 - __builtin_clz(u & 0x7fffffu)) - 149;
-}
-
-// the block's shared exponent from its largest magnitude
-__device__ __forceinline__ int block_exponent(float amax) {
-  const int e = amax > 0.f ? floor_log2(amax) - 2 : -127;
-  return max(-127, min(127, e));
-}
+using csa::mx_block_exponent;
 
 // Packs element pairs (2i, 2i+1), i = 4d..4d+3, into code word d; pair i
 // comes from cvt(i, sel) with sel = i % 4 naming the byte it fills.
@@ -73,7 +61,7 @@ __device__ __forceinline__ void encode_block(const float* __restrict__ p, int& e
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(f32_elem(u, j)));
-  e = block_exponent(amax);
+  e = mx_block_exponent(amax);
   if (e > -127) {
     const float sc = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
 #define CSA_CVT(w, i, sel) \
@@ -103,7 +91,7 @@ __device__ __forceinline__ void encode_block(const uint16_t* __restrict__ p, int
     const uint32_t w = bf16_pair(u, i);
     m = max(m, max(w & 0x7fffu, (w >> 16) & 0x7fffu));
   }
-  e = block_exponent(__uint_as_float(m << 16));
+  e = mx_block_exponent(__uint_as_float(m << 16));
   if (e > -127) {
     const float sc = __uint_as_float(static_cast<uint32_t>(e + 127) << 23);
 #define CSA_CVT(w, i, sel) \

@@ -176,3 +176,28 @@ def test_index_topk_invariants():
         assert np.array_equal(np.sort(PERM[IP[b, 0]]), I[b, 0]), f"permutation b={b}"
         checked += 1
     assert checked >= B - 1
+
+
+@pytest.mark.parametrize("dtype,B,n,C,d_mx,m", [(torch.bfloat16, 2, 4096, 384, 128, 4),
+                                                (torch.bfloat16, 1, 4 * 77 + 3, 384, 128, 4),
+                                                (torch.float32, 2, 1024, 160, 32, 4),
+                                                (torch.bfloat16, 2, 1024 * 128, 256, 256, 128)])
+def test_compress_mx4_is_compress_then_mx_encoding(dtype, B, n, C, d_mx, m):
+    """The fused encoder's codes and scale bytes equal the oracle's MX
+    encoding of csa_compress's fp32 pooled values (fp32 compression of the
+    same inputs: the same arithmetic), byte for byte; the leading channels
+    equal csa_compress's bitwise."""
+    _say(f"compress mx4: {dtype} B={B} n={n} C={C} d_mx={d_mx} m={m}")
+    x = _randn((B, n, C), 1 / math.sqrt(128), dtype, 111)
+    x[0, : 4 * m, C - d_mx: C - d_mx + 32] = 0.0          # all-zero blocks
+    x[0, 4 * m: 8 * m, C - 32:] *= 1e-20                   # tiny blocks (small exponents)
+    z = _randn((B, n), 1.0, torch.float32, 112)
+    out, codes, scales = csa.compress_mx4(x, z, m, d_mx)
+    ref_dt = csa.compress(x, z, m)
+    ref32 = csa.compress(x.float(), z, m)
+    torch.cuda.synchronize()
+    if out is not None:
+        assert torch.equal(out, ref_dt[..., : C - d_mx]), "leading channels differ"
+    c_ref, s_ref = oracle.mx4_quantize(np64(ref32[..., C - d_mx:]))
+    assert np.array_equal(codes.cpu().numpy(), c_ref), "codes differ"
+    assert np.array_equal(scales.cpu().numpy(), s_ref), "scale bytes differ"

@@ -99,13 +99,15 @@ def test_csa_decode_128k_bf16_scores_recall():
     inp = make_inputs(w, device=DEV)
     idx = csa.index_topk_bf16(inp["q_idx"], inp["w_idx"], inp["ki_cache"], inp["q_pos"],
                               inp["n_entries"], w.m, w.k)
+    idx32 = csa.index_topk(inp["q_idx"], inp["w_idx"], inp["ki_cache"], inp["q_pos"],
+                           inp["n_entries"], w.m, w.k)
     s32 = csa.index_score(inp["q_idx"], inp["w_idx"], inp["ki_cache"], inp["q_pos"],
                           inp["n_entries"], w.m)
     torch.cuda.synchronize()
-    I, S = np64(idx), np64(s32)
+    I, I32, S = np64(idx), np64(idx32), np64(s32)
     KI, QI, W = np64(inp["ki_cache"]), np64(inp["q_idx"]), np64(inp["w_idx"])
     V = oracle.visible_count(w.q_pos0, w.m, w.N)
-    hit = hit_pred = 0
+    hit = hit_pred = hit_fp32 = 0
     for b in range(w.B):
         assert np.array_equal(I[b, 0], oracle.topk_select(oracle.round_to_bf16(S[b, 0, :V]), V, w.k))
         s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
@@ -113,10 +115,18 @@ def test_csa_decode_128k_bf16_scores_recall():
         pred = oracle.topk_select(oracle.round_to_bf16(s_ref), V, w.k)
         hit += np.intersect1d(I[b, 0], exact).size
         hit_pred += np.intersect1d(pred, exact).size
+        hit_fp32 += np.intersect1d(I[b, 0], I32[b, 0]).size
     recall, predicted = hit / (w.B * w.k), hit_pred / (w.B * w.k)
-    _say(f"{w.name}: bf16-score recall {recall:.5f} (rounding alone: {predicted:.5f})")
+    recall_fp32 = hit_fp32 / (w.B * w.k)
+    _say(f"{w.name}: bf16-score recall {recall:.5f} vs the exact top-k (rounding alone: "
+         f"{predicted:.5f}); {recall_fp32:.5f} vs the fp32-score selection (the survey's 0.997 "
+         f"gate is not reached on these Gaussian scores: 10-60 entries tie at a row's k-th "
+         f"bf16 value)")
     assert abs(recall - predicted) <= 1e-3, (recall, predicted)
+    # floors: the selection is exact on the rounded scores; what rounding alone
+    # costs on this input is 99.6 %, so 99.5 % bounds both recalls from below
     assert recall >= 0.995, recall
+    assert recall_fp32 >= 0.995, recall_fp32
 
 
 def test_swa_decode_128k_full():

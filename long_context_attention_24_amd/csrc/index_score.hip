@@ -9,9 +9,10 @@
 // run on MFMA with the 64 heads of one query as the M dimension and keys as
 // N.  In the 32x32 accumulator layout a lane holds one key and 16 heads, so
 // ReLU, head weight and the head sum stay in registers, followed by a single
-// exchange between lanes l and l^32.  K rows are loaded straight into the B
-// operand (lane l%32 = key row, 16 contiguous bytes per lane per k-step),
-// two tiles ahead of the MFMAs.
+// exchange between lanes l and l^32.  K rows are read with whole-row
+// coalesced loads, one tile ahead of the MFMAs, and reach the B operand
+// (lane l%32 = key row, 16 contiguous bytes per lane per k-step) through a
+// wave-private LDS tile.
 //
 // The MFMA k-slot order does not matter for a dot product as long as A and
 // B use the same one, so slot (lane/32, e) of k-step s holds dimension
@@ -109,13 +110,23 @@ constexpr int kKeysPerWave = 32 * kTilesPerWave;  // one selection chunk
 constexpr int kKeysPerWg = kWavesPerWg * kKeysPerWave;
 static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 
-// Straight-line code over the wave's 8 tiles of 32 keys with a 3-deep ring of
-// registers: the loads of tile t+2 are issued before the MFMAs of tile t and
-// no register is copied, so two tiles (16 KB per wave) stay in flight behind
-// the math; the epilogue of tile t-1 runs while the MFMAs of tile t do.  Loads are coalesced and non-temporal (instruction i of a tile
-// reads key rows 4i .. 4i+3 whole, 16 lanes per row); each tile then passes
-// through a wave-private LDS buffer to reach the MFMA B-operand layout (lane
-// (j, g) holds dims 16s + 8g .. +7 of key j).  Rows past the visible range are
+// Tile order: a row's keys are read as tiles of 32 (8 KB), and wave c of the
+// row (c = its chunk, 0 <= c < nch = ceil(N_max / 256)) takes tiles c, c + nch,
+// c + 2 nch, ...  At each step the waves of a row therefore read one
+// contiguous nch x 8 KB stretch of the key cache together, instead of every
+// wave streaming its own 64 KB region: HBM serves the stretch at about 6.6
+// TB/s, the per-wave regions at about 5.6.  A wave's chunk is thus a strided
+// set of 256 keys; the chunk reports only need disjoint sets of keys.
+// Straight-line code over the wave's 8 tiles with a 2-deep ring of
+// registers: the loads of tile t+1 are issued before tile t is staged and
+// multiplied and no register is copied, so one tile (8 KB per wave, 64 KB per
+// compute unit) stays in flight behind the math (two in flight measured
+// slower: more requests queued at HBM at once); the epilogue of tile t-1 runs
+// while the MFMAs of tile t do.
+// Loads are coalesced and non-temporal (instruction i of a tile reads key
+// rows 4i .. 4i+3 whole, 16 lanes per row); each tile then passes through a
+// wave-private LDS buffer to reach the MFMA B-operand layout (lane (j, g)
+// holds dims 16s + 8g .. +7 of key j).  Rows past the visible range are
 // clamped to the last visible row (in bounds, cache hits) and masked on
 // output.
 constexpr int kKeyPitch = 136;                    // bf16 per key row in LDS (256 B + 16 B)
@@ -142,27 +153,26 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * (static_cast<int>(threadIdx.x) + 256 * i));
-  const int key0 = chunk * kKeysPerWave;
-  const int key_end = min(key0 + kKeysPerWave, N_max);
-  const int vis_end = min(key_end, V);
-  // The first two key tiles are requested before the query is staged and
-  // the barrier passed, so that their latency overlaps the query's (the
+  const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
+  const int vis = min(V, N_max);
+  auto tile_key0 = [&](int t) { return 32 * (t * nch + chunk); };
+  // The first key tile is requested before the query is staged and the
+  // barrier passed, so that its latency overlaps the query's (the
   // empty asm with a memory clobber keeps the compiler from sinking them
-  // below).  Every wave issues them, also one that exits below: rows are
-  // clamped to [0, vis_end - 1] (row 0 when nothing is visible; N_max >= 1).
+  // below).  Every wave issues it, also one that exits below: rows are
+  // clamped to [0, vis - 1] (row 0 when nothing is visible; N_max >= 1).
   const uint16_t* kb = k + b * k_sb + 8 * (lane & 15);
   const int lrow = lane >> 4;                     // row within each 4-row load
-  const int jmax = max(vis_end - 1, 0);
-  u32x4_t kt[3][8];
+  const int jmax = max(vis - 1, 0);
+  u32x4_t kt[2][8];
   auto load_tile = [&](int t, u32x4_t (&dst)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = min(key0 + 32 * t + 4 * i + lrow, jmax);
+      const int j = min(tile_key0(t) + 4 * i + lrow, jmax);
       dst[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
     }
   };
   load_tile(0, kt[0]);
-  load_tile(1, kt[1]);
   asm volatile("" ::"s"(k) : "memory");
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -170,10 +180,13 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     *(lds_u32x4*)((lds_u16*)q_lds + (c >> 4) * kKeyPitch + 8 * (c & 15)) = qv[i];
   }
   __syncthreads();                                // the only barrier: early exits follow
-  if (key0 >= N_max) return;
+  if (chunk >= nch) return;                       // past the row (tile 0 is the wave's first key)
   SO* srow = scores + row * s_rs;
-  for (int j = max(key0, V) + lane; j < key_end; j += 64) put_score(&srow[j], kNegInf);
-  if (key0 >= vis_end) {
+  if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
+    for (int t = 0; t < kTilesPerWave; ++t) {
+      const int j = tile_key0(t) + jl;
+      if (g == 0 && j < N_max) put_score(&srow[j], kNegInf);
+    }
     if (chunk_rep != nullptr && lane == 0)
       chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
     return;
@@ -202,12 +215,12 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     for (int r = 0; r < 16; ++r) sum = fmaf(w1[r], relu_f32(c1[r]), sum);
     const float other = __shfl_xor(sum, 32, 64);
     const float tot = sum + other;     // commutative: both halves get the same bits
-    const int j = key0 + 32 * t + jl;
-    const bool ok = j < vis_end;
-    if (g == 0 && ok) put_score(&srow[j], tot);
+    const int j = tile_key0(t) + jl;
+    const bool ok = j < vis;
+    if (g == 0 && j < N_max) put_score(&srow[j], ok ? tot : kNegInf);
     sc[t] = ok ? tot : kNegInf;
   };
-  // Iteration t: loads of tile t+2, tile t through LDS into the MFMAs, and
+  // Iteration t: loads of tile t+1, tile t through LDS into the MFMAs, and
   // the epilogue of tile t-1 while those MFMAs run (two accumulator sets).
   // sched_barrier(0) keeps the scheduler from sinking the prefetch loads
   // below the MFMAs of the current tile (it would, to shorten live ranges).
@@ -215,12 +228,12 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int t = 0; t < kTilesPerWave; ++t) {
-    if (t + 2 < kTilesPerWave) load_tile(t + 2, kt[(t + 2) % 3]);
+    if (t + 1 < kTilesPerWave) load_tile(t + 1, kt[(t + 1) % 2]);
     __builtin_amdgcn_sched_barrier(0);
     // tile t: registers -> LDS (rows 4i + lrow) -> B operand (row jl)
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      *(lds_u32x4*)(kl + (4 * i + lrow) * kKeyPitch + 8 * (lane & 15)) = kt[t % 3][i];
+      *(lds_u32x4*)(kl + (4 * i + lrow) * kKeyPitch + 8 * (lane & 15)) = kt[t % 2][i];
     bf16x8_t cur[8];
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -447,13 +460,18 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
   const int nl = lane & 15, g = lane >> 4;
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int chunk = blockIdx.x * kWavesPerWg + wave;
-  const int key0 = chunk * kKeysPerWave;
-  if (key0 >= N_max) return;
-  const int key_end = min(key0 + kKeysPerWave, N_max);
-  const int vis_end = min(key_end, V);
+  // tiles of 16 keys in the interleaved order of the bf16 kernel: wave c of
+  // the row takes tiles c, c + nch, c + 2 nch, ...
+  const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
+  if (chunk >= nch) return;
+  const int vis = min(V, N_max);
+  auto tile_key0 = [&](int t) { return 16 * (t * nch + chunk); };
   float* srow = scores + row * s_rs;
-  for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
-  if (key0 >= vis_end) {
+  if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
+    for (int t = 0; t < kFp4Tiles; ++t) {
+      const int j = tile_key0(t) + nl;
+      if (g == 0 && j < N_max) srow[j] = kNegInf;
+    }
     if (chunk_rep != nullptr && lane == 0)
       chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
     return;
@@ -465,7 +483,7 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
   const float* ksb = k_scale + b * ks_sb;
   u32x4_t kc[3], ks[3];
   auto load_tile = [&](int t, u32x4_t& c, u32x4_t& sc4) {
-    const int j = min(key0 + 16 * t + nl, vis_end - 1);
+    const int j = min(tile_key0(t) + nl, vis - 1);
     c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
     sc4 = ld16_stream(ksb + static_cast<int64_t>(j) * ks_sn);
   };
@@ -533,9 +551,9 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     // heads are spread over the four 16-lane groups of the key's column
     sum = sum + __shfl_xor(sum, 16, 64);
     sum = sum + __shfl_xor(sum, 32, 64);
-    const int jj = key0 + 16 * t + nl;
-    const bool ok = jj < vis_end;
-    if (g == 0 && ok) srow[jj] = sum;
+    const int jj = tile_key0(t) + nl;
+    const bool ok = jj < vis;
+    if (g == 0 && jj < N_max) srow[jj] = ok ? sum : kNegInf;
     scv[t] = ok ? sum : kNegInf;
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -568,13 +586,18 @@ __global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
   const int nl = lane & 15, g = lane >> 4;
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int chunk = blockIdx.x * kWavesPerWg + wave;
-  const int key0 = chunk * kKeysPerWave;
-  if (key0 >= N_max) return;
-  const int key_end = min(key0 + kKeysPerWave, N_max);
-  const int vis_end = min(key_end, V);
+  // tiles of 16 keys in the interleaved order of the bf16 kernel: wave c of
+  // the row takes tiles c, c + nch, c + 2 nch, ...
+  const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
+  if (chunk >= nch) return;
+  const int vis = min(V, N_max);
+  auto tile_key0 = [&](int t) { return 16 * (t * nch + chunk); };
   float* srow = scores + row * s_rs;
-  for (int j = max(key0, V) + lane; j < key_end; j += 64) srow[j] = kNegInf;
-  if (key0 >= vis_end) {
+  if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
+    for (int t = 0; t < kFp4Tiles; ++t) {
+      const int j = tile_key0(t) + nl;
+      if (g == 0 && j < N_max) srow[j] = kNegInf;
+    }
     if (chunk_rep != nullptr && lane == 0)
       chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
     return;
@@ -587,7 +610,7 @@ __global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
   u32x4_t kc[kMxAhead + 1];
   uint32_t ks[kMxAhead + 1];
   auto load_tile = [&](int t, u32x4_t& c, uint32_t& sw) {
-    const int j = min(key0 + 16 * t + nl, vis_end - 1);
+    const int j = min(tile_key0(t) + nl, vis - 1);
     c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
     sw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ksb + static_cast<int64_t>(j) * ks_sn));
   };
@@ -636,9 +659,9 @@ __global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
     // heads are spread over the four 16-lane groups of the key's column
     sum = sum + __shfl_xor(sum, 16, 64);
     sum = sum + __shfl_xor(sum, 32, 64);
-    const int jj = key0 + 16 * t + nl;
-    const bool ok = jj < vis_end;
-    if (g == 0 && ok) srow[jj] = sum;
+    const int jj = tile_key0(t) + nl;
+    const bool ok = jj < vis;
+    if (g == 0 && jj < N_max) srow[jj] = ok ? sum : kNegInf;
     scv[t] = ok ? sum : kNegInf;
   }
   const int thr_c = bound_c_row(V, bound_k);

@@ -119,9 +119,9 @@ def test_csa_decode_128k_bf16_scores_recall():
     recall, predicted = hit / (w.B * w.k), hit_pred / (w.B * w.k)
     recall_fp32 = hit_fp32 / (w.B * w.k)
     _say(f"{w.name}: bf16-score recall {recall:.5f} vs the exact top-k (rounding alone: "
-         f"{predicted:.5f}); {recall_fp32:.5f} vs the fp32-score selection (the survey's 0.997 "
-         f"gate is not reached on these Gaussian scores: 10-60 entries tie at a row's k-th "
-         f"bf16 value)")
+         f"{predicted:.5f}); {recall_fp32:.5f} vs the fp32-score selection (the pages' 99.7 % "
+         f"is not reached on these Gaussian scores: 10-60 entries tie at a row's k-th bf16 "
+         f"value)")
     assert abs(recall - predicted) <= 1e-3, (recall, predicted)
     # floors: the selection is exact on the rounded scores; what rounding alone
     # costs on this input is 99.6 %, so 99.5 % bounds both recalls from below

@@ -110,13 +110,16 @@ constexpr int kKeysPerWave = 32 * kTilesPerWave;  // one selection chunk
 constexpr int kKeysPerWg = kWavesPerWg * kKeysPerWave;
 static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 
-// Tile order: a row's keys are read as tiles of 32 (8 KB), and wave c of the
-// row (c = its chunk, 0 <= c < nch = ceil(N_max / 256)) takes tiles c, c + nch,
+// Tile order: a row's keys are read as tiles of 32 (8 KB); chunk c of the row
+// (0 <= c < nch = ceil(N_max / 256)) is the strided set of tiles c, c + nch,
 // c + 2 nch, ...  At each step the waves of a row therefore read one
-// contiguous nch x 8 KB stretch of the key cache together, instead of every
-// wave streaming its own 64 KB region: HBM serves the stretch at about 6.6
-// TB/s, the per-wave regions at about 5.6.  A wave's chunk is thus a strided
-// set of 256 keys; the chunk reports only need disjoint sets of keys.
+// contiguous stretch of the key cache together, instead of every wave
+// streaming its own region: HBM serves the stretch at about 6.4 TB/s, the
+// per-wave regions at about 5.6 (the chunk reports only need disjoint sets
+// of keys).  In the decode kernel a wave takes two chunks, w and w + nw (nw
+// waves per row), one after the other: half the waves, each amortising its
+// query staging over twice the keys (4 % faster than one chunk per wave,
+// four chunks per wave 50 % slower).
 // Straight-line code over the wave's 8 tiles with a 2-deep ring of
 // registers: the loads of tile t+1 are issued before tile t is staged and
 // multiplied and no register is copied, so one tile (8 KB per wave, 64 KB per
@@ -130,6 +133,8 @@ static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 // clamped to the last visible row (in bounds, cache hits) and masked on
 // output.
 constexpr int kKeyPitch = 136;                    // bf16 per key row in LDS (256 B + 16 B)
+constexpr int kChunksPerWave = 2;                 // 256-key chunks per wave (decode kernel)
+constexpr int kDecodeTiles = kTilesPerWave * kChunksPerWave;
 
 template <typename SO>
 __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
@@ -143,7 +148,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 31, g = lane >> 5;
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-  const int chunk = blockIdx.x * kWavesPerWg + wave;
+  const int wid = blockIdx.x * kWavesPerWg + wave;    // this wave within the row
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   // q_I rows (heads) of this query go to LDS and are read back per tile as
@@ -154,8 +159,11 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   for (int i = 0; i < 4; ++i)
     qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * (static_cast<int>(threadIdx.x) + 256 * i));
   const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
+  const int nw = (nch + kChunksPerWave - 1) / kChunksPerWave;   // waves per row
   const int vis = min(V, N_max);
-  auto tile_key0 = [&](int t) { return 32 * (t * nch + chunk); };
+  // tile t of the wave: tile t % 8 of its chunk wid + (t / 8) nw
+  auto chunk_of = [&](int t) { return wid + (t / kTilesPerWave) * nw; };
+  auto tile_key0 = [&](int t) { return 32 * ((t % kTilesPerWave) * nch + chunk_of(t)); };
   // The first key tile is requested before the query is staged and the
   // barrier passed, so that its latency overlaps the query's (the
   // empty asm with a memory clobber keeps the compiler from sinking them
@@ -180,15 +188,17 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     *(lds_u32x4*)((lds_u16*)q_lds + (c >> 4) * kKeyPitch + 8 * (c & 15)) = qv[i];
   }
   __syncthreads();                                // the only barrier: early exits follow
-  if (chunk >= nch) return;                       // past the row (tile 0 is the wave's first key)
+  if (wid >= nw) return;                          // past the row
   SO* srow = scores + row * s_rs;
-  if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
-    for (int t = 0; t < kTilesPerWave; ++t) {
+  if (tile_key0(0) >= vis) {                      // the wave's smallest key: nothing visible
+    for (int t = 0; t < kDecodeTiles; ++t) {
       const int j = tile_key0(t) + jl;
-      if (g == 0 && j < N_max) put_score(&srow[j], kNegInf);
+      if (g == 0 && chunk_of(t) < nch && j < N_max) put_score(&srow[j], kNegInf);
     }
-    if (chunk_rep != nullptr && lane == 0)
-      chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
+    for (int x = 0; x < kChunksPerWave; ++x)
+      if (chunk_rep != nullptr && lane == 0 && chunk_of(kTilesPerWave * x) < nch)
+        chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk_of(kTilesPerWave * x)] =
+            make_float2(kPosInf, kNegInf);
     return;
   }
 
@@ -204,9 +214,11 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     w1[r] = wrow[32 + h];
   }
 
-  float sc[kTilesPerWave];
+  float sc[kChunksPerWave][kTilesPerWave];
+  const int thr_c = bound_c_row(V, bound_k);
   // epilogue of tile t from its accumulators: sum_h w[h] ReLU(s_h), then the
-  // two lane halves (32 heads each) add up
+  // two lane halves (32 heads each) add up; after a chunk's last tile, its
+  // report
   auto epilogue = [&](int t, const f32x16_t& c0, const f32x16_t& c1) {
     float sum = 0.f;
 #pragma unroll
@@ -216,9 +228,15 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     const float other = __shfl_xor(sum, 32, 64);
     const float tot = sum + other;     // commutative: both halves get the same bits
     const int j = tile_key0(t) + jl;
-    const bool ok = j < vis;
-    if (g == 0 && j < N_max) put_score(&srow[j], ok ? tot : kNegInf);
-    sc[t] = ok ? tot : kNegInf;
+    const bool mine = chunk_of(t) < nch;
+    const bool ok = mine && j < vis;
+    if (g == 0 && mine && j < N_max) put_score(&srow[j], ok ? tot : kNegInf);
+    sc[t / kTilesPerWave][t % kTilesPerWave] = ok ? tot : kNegInf;
+    if (t % kTilesPerWave == kTilesPerWave - 1 && chunk_rep != nullptr && thr_c > 0 && mine) {
+      const float2 rep = wave_chunk_report<kTilesPerWave>(sc[t / kTilesPerWave], g == 0, thr_c);
+      if (lane == 0)
+        chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk_of(t)] = stored_report<SO>(rep);
+    }
   };
   // Iteration t: loads of tile t+1, tile t through LDS into the MFMAs, and
   // the epilogue of tile t-1 while those MFMAs run (two accumulator sets).
@@ -227,8 +245,8 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   f32x16_t acc[2][2];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < kTilesPerWave; ++t) {
-    if (t + 1 < kTilesPerWave) load_tile(t + 1, kt[(t + 1) % 2]);
+  for (int t = 0; t < kDecodeTiles; ++t) {
+    if (t + 1 < kDecodeTiles) load_tile(t + 1, kt[(t + 1) % 2]);
     __builtin_amdgcn_sched_barrier(0);
     // tile t: registers -> LDS (rows 4i + lrow) -> B operand (row jl)
 #pragma unroll
@@ -257,12 +275,7 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     if (t > 0) epilogue(t - 1, acc[(t - 1) & 1][0], acc[(t - 1) & 1][1]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  epilogue(kTilesPerWave - 1, acc[(kTilesPerWave - 1) & 1][0], acc[(kTilesPerWave - 1) & 1][1]);
-  const int thr_c = bound_c_row(V, bound_k);
-  if (chunk_rep != nullptr && thr_c > 0) {
-    const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, thr_c);
-    if (lane == 0) chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = stored_report<SO>(rep);
-  }
+  epilogue(kDecodeTiles - 1, acc[(kDecodeTiles - 1) & 1][0], acc[(kDecodeTiles - 1) & 1][1]);
 }
 
 // ---------------------------------------------------------------- bf16 prefill (many queries)
@@ -728,7 +741,9 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
                          static_cast<float*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
                          a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
-    const dim3 grid((a.N_max + kKeysPerWg - 1) / kKeysPerWg, a.B * a.Tq);
+    const int nch = (a.N_max + kKeysPerWave - 1) / kKeysPerWave;
+    const int nw = (nch + kChunksPerWave - 1) / kChunksPerWave;
+    const dim3 grid((nw + kWavesPerWg - 1) / kWavesPerWg, a.B * a.Tq);
     if (a.score16)
       hipLaunchKernelGGL(score_bf16_h64d128_kernel<uint16_t>, grid, dim3(256), 0, s,
                          static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),

@@ -451,7 +451,7 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
 // in memory order (element 2i in the low nibble of byte i).  Its E8M0 block
 // scales hold only powers of two, so they stay at 1 and the fp32 scales of
 // the pages' recipe are applied in the epilogue: each block's partial dot
-// product comes from an MFMA whose B operand keeps only that block's lanes
+// product comes from an MFMA whose A operand keeps only that block's lanes
 // (the others zero), so every partial is exact (products of E2M1 values are
 // multiples of 1/4 below 36, 32 of them summed in fp32).  A wave covers 256
 // keys as 16 tiles of 16 keys; lane (key n, block g) loads its 16 bytes of
@@ -511,6 +511,18 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     qa[mt] = v8i32_t{static_cast<int>(c[0]), static_cast<int>(c[1]), static_cast<int>(c[2]),
                      static_cast<int>(c[3]), 0, 0, 0, 0};
   }
+  // the A operand of block blk keeps only the lanes of that block (the others
+  // zero), built once per wave: every key tile then feeds its codes unmasked
+  // (masking B per tile cost 16 VALU instructions per tile, 10 % of the time)
+  v8i32_t qm[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+      const bool mine = g == blk;
+      qm[mt][blk] = v8i32_t{mine ? qa[mt][0] : 0, mine ? qa[mt][1] : 0, mine ? qa[mt][2] : 0,
+                            mine ? qa[mt][3] : 0, 0, 0, 0, 0};
+    }
   // accumulator rows: head = 16*mt + 4*g + r
   float sq[4][4][4];   // [mt][r][blk]
   float wv[4][4];
@@ -538,15 +550,13 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
     f32x4_t p[4][4];     // [mt][blk]
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) {
-      const bool mine = g == blk;
-      const v8i32_t bm = {mine ? static_cast<int>(c[0]) : 0, mine ? static_cast<int>(c[1]) : 0,
-                          mine ? static_cast<int>(c[2]) : 0, mine ? static_cast<int>(c[3]) : 0,
-                          0, 0, 0, 0};
+      const v8i32_t bm = {static_cast<int>(c[0]), static_cast<int>(c[1]), static_cast<int>(c[2]),
+                          static_cast<int>(c[3]), 0, 0, 0, 0};
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4_t z = {};
-        p[mt][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[mt], bm, z, 4, 4, 0, 127,
-                                                                        0, 127);
+        p[mt][blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qm[mt][blk], bm, z, 4, 4, 0,
+                                                                        127, 0, 127);
       }
     }
     float sum = 0.f;

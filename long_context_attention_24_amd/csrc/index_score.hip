@@ -118,14 +118,17 @@ static_assert(kKeysPerWave == kBoundChunk, "one bound chunk per wave");
 // per-wave regions at about 5.6 (the chunk reports only need disjoint sets
 // of keys).  In the decode kernel a wave takes two chunks, w and w + nw (nw
 // waves per row), one after the other: half the waves, each amortising its
-// query staging over twice the keys (4 % faster than one chunk per wave,
-// four chunks per wave 50 % slower).
-// Straight-line code over the wave's 8 tiles with a 2-deep ring of
+// query staging over twice the keys (4 % faster than one chunk per wave;
+// four chunks per wave leave half the compute units idle at 128K).  At 128K
+// that is one 4-wave workgroup per compute unit, one wave per SIMD, which
+// leaves the registers to hold the query heads (the A operand) for the whole
+// wave instead of re-reading them from LDS every tile.
+// Straight-line code over the wave's 16 tiles with a 2-deep ring of
 // registers: the loads of tile t+1 are issued before tile t is staged and
-// multiplied and no register is copied, so one tile (8 KB per wave, 64 KB per
-// compute unit) stays in flight behind the math (two in flight measured
-// slower: more requests queued at HBM at once); the epilogue of tile t-1 runs
-// while the MFMAs of tile t do.
+// multiplied and no register is copied, so one tile (8 KB per wave) stays in
+// flight behind the math (two in flight measured slower: more requests
+// queued at HBM at once); the epilogue of tile t-1 runs while the MFMAs of
+// tile t do.
 // Loads are coalesced and non-temporal (instruction i of a tile reads key
 // rows 4i .. 4i+3 whole, 16 lanes per row); each tile then passes through a
 // wave-private LDS buffer to reach the MFMA B-operand layout (lane (j, g)
@@ -137,7 +140,7 @@ constexpr int kChunksPerWave = 2;                 // 256-key chunks per wave (de
 constexpr int kDecodeTiles = kTilesPerWave * kChunksPerWave;
 
 template <typename SO>
-__global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
+__global__ __launch_bounds__(256, 1) void score_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, SO* __restrict__ scores,
@@ -151,8 +154,9 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
   const int wid = blockIdx.x * kWavesPerWg + wave;    // this wave within the row
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  // q_I rows (heads) of this query go to LDS and are read back per tile as
-  // the A operand (the registers hold the accumulators of two tiles instead)
+  // q_I rows (heads) of this query are staged in LDS by the whole workgroup
+  // (coalesced 16-byte loads) and read back by every wave in the A-operand
+  // layout
   const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
   u32x4_t qv[4];
 #pragma unroll
@@ -214,6 +218,16 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     w1[r] = wrow[32 + h];
   }
 
+  // the A operand (32 heads x 128 dims per 32x32 tile, two tiles) read from
+  // LDS once into registers: one wave per SIMD leaves room for it
+  bf16x8_t qa0[8], qa1[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const u32x4_t x0 = *(const lds_u32x4*)(ql + 16 * s);
+    const u32x4_t x1 = *(const lds_u32x4*)(ql + 32 * kKeyPitch + 16 * s);
+    __builtin_memcpy(&qa0[s], &x0, 16);
+    __builtin_memcpy(&qa1[s], &x1, 16);
+  }
   float sc[kChunksPerWave][kTilesPerWave];
   const int thr_c = bound_c_row(V, bound_k);
   // epilogue of tile t from its accumulators: sum_h w[h] ReLU(s_h), then the
@@ -261,16 +275,10 @@ __global__ __launch_bounds__(256, 2) void score_bf16_h64d128_kernel(
     f32x16_t (&c)[2] = acc[t & 1];
     c[0] = f32x16_t{};
     c[1] = f32x16_t{};
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);     // re-read the A operands from LDS
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8_t a0, a1;
-      const u32x4_t x0 = *(const lds_u32x4*)(ql + 16 * s);
-      const u32x4_t x1 = *(const lds_u32x4*)(ql + 32 * kKeyPitch + 16 * s);
-      __builtin_memcpy(&a0, &x0, 16);
-      __builtin_memcpy(&a1, &x1, 16);
-      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, cur[s], c[0], 0, 0, 0);
-      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, cur[s], c[1], 0, 0, 0);
+      c[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa0[s], cur[s], c[0], 0, 0, 0);
+      c[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa1[s], cur[s], c[1], 0, 0, 0);
     }
     if (t > 0) epilogue(t - 1, acc[(t - 1) & 1][0], acc[(t - 1) & 1][1]);
     __builtin_amdgcn_sched_barrier(0);

@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
     }
   }
   int p = 0;
-  zero_hist<NW>(g_sm);
+  sel::zero_hist<NW>(g_sm);
   __syncthreads();
   float v[R];
 #pragma unroll

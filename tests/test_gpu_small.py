@@ -173,6 +173,36 @@ def test_tuned_kernels_ragged():
             check_lse(LH[b, t], lh_ref, 2.5e-3)
 
 
+@pytest.mark.parametrize("N_max", [1037, 2600, 4999])
+def test_decode_scores_odd_chunk_counts(N_max):
+    """The decode score kernel gives each wave two strided 256-key chunks; with
+    an odd chunk count the last wave has one.  Scores against the oracle, -inf
+    past the visible count (which ends inside either chunk of a wave), and the
+    selection (through the chunk reports) against the oracle's top-k."""
+    B, Tq, m, k = 3, 2, 4, 200
+    _say(f"decode scores, odd chunk counts: N_max={N_max}")
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 121)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 122)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 123)
+    pos = [[4 * N_max + 3, 4 * (N_max // 2) + 1], [4 * 300, 4 * (N_max - 40)], [4 * 257, 7]]
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor([N_max, N_max - 5, N_max], dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qi, wi, ki, q_pos, n_ent, m)
+    idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k)
+    torch.cuda.synchronize()
+    S, I, QI, KI, W = np64(scores), np64(idx), np64(qi), np64(ki), np64(wi)
+    ne = n_ent.cpu().numpy()
+    for b in range(B):
+        for t in range(Tq):
+            V = oracle.visible_count(pos[b][t], m, int(ne[b]))
+            s_ref = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+            assert np.all(np.isneginf(S[b, t, V:])), (b, t, V)
+            if V:
+                bound = score_bound(QI[b, t], W[b, t], KI[b, :V], 128, 64)
+                assert np.all(np.abs(S[b, t, :V] - s_ref[:V]) <= bound), (b, t, V)
+            check_topk(I[b, t], s_ref, V, k)
+
+
 def test_hca_multi_split_ragged():
     """HCA on the tuned kernel with visible counts that end exactly on, just
     past and just before split boundaries, several splits per query, a

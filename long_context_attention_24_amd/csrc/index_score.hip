@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256) void score_generic_kernel(
 // kBoundChunk keys, held as NV scores by each of 16 or 32 lanes), a value
 // that c of them reach, c = bound_c_row(V, k) for the row: the c-th largest
 // of the per-lane maxima (c lanes hold an entry at or above it; a little
-// below the exact c-th largest, for a fraction of its cost), and the
-// largest score.  Every chunk that reports a finite value holds c entries at
+// below the exact c-th largest, for a fraction of its cost; the valid lanes
+// are among lanes 0..31), and the largest score.  Every chunk that reports a finite value holds c entries at
 // or above it, and the floor(V / kBoundChunk) full chunks all do (every lane
 // holds valid entries, c <= 16), so the ceil(k / c)-th largest report is at
 // most the row's k-th largest score.  The top-k kernels use that bound to
@@ -81,26 +81,47 @@ __global__ __launch_bounds__(256) void score_generic_kernel(
 // bound (c = 0) write nothing.
 constexpr float kPosInf = __builtin_inff();
 
+// The value of lane l ^ j (j = 1, 2, 4, 8, 16) for the sorting network
+// below: DPP inside a 16-lane row for j < 16 (quad permutes; for j = 4 the
+// half-row mirror 8h + 7 - i followed by the quad reversal 4q + 3 - i, which
+// together give 8h + 4(1 - a) + i = l ^ 4 for l = 8h + 4a + i; the row
+// rotation by 8), a lane swizzle for j = 16.  j is a constant after unrolling.
+__device__ __forceinline__ float lane_xor(float v, int j) {
+  const int x = __float_as_int(v);
+  if (j == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+  if (j == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+  if (j == 4) {
+    const int m = __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);
+    return __int_as_float(__builtin_amdgcn_mov_dpp(m, 0x1B, 0xF, 0xF, false));
+  }
+  if (j == 8) return __int_as_float(__builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false));
+  return __shfl_xor(v, 16, 64);
+}
+
 template <int NV>
 __device__ float2 wave_chunk_report(const float (&vals)[NV], bool active, int c) {
   const int lane = threadIdx.x & 63;
-  float lm = kNegInf;
+  float v = kNegInf;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) lm = fmaxf(lm, vals[i]);
-  if (!active) lm = kNegInf;
-  float cur = kPosInf, top = kNegInf;
-  for (int r = 0; r < c; ++r) {
-    const float wm = wave_max(lm);
-    if (r == 0) top = wm;
-    if (wm == kNegInf) {
-      cur = kPosInf;
-      break;
+  for (int i = 0; i < NV; ++i) v = fmaxf(v, vals[i]);
+  if (!active) v = kNegInf;
+  // Bitonic sort of the 32 lane maxima of lanes 0..31 into descending order
+  // (15 compare-exchange stages, all in registers; lanes 32..63 sort their
+  // own values, unused).  Before it, c rounds of a full-wave maximum and
+  // removal took 2 us of a 23 us launch.
+#pragma unroll
+  for (int k = 2; k <= 32; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float o = lane_xor(v, j);
+      const bool want_max = ((lane & j) == 0) == ((lane & k) == 0);
+      v = want_max ? fmaxf(v, o) : fminf(v, o);
     }
-    const unsigned long long msk = __ballot(lm == wm);
-    if (lane == __ffsll(msk) - 1) lm = kNegInf;
-    cur = wm;
   }
-  return make_float2(cur, top);
+  const float top = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const int cu = __builtin_amdgcn_readfirstlane(c);
+  const float cth = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), cu - 1));
+  return make_float2(cth == kNegInf ? kPosInf : cth, top);
 }
 
 // ---------------------------------------------------------------- bf16, 64 heads x 128

@@ -232,6 +232,13 @@ csa_status_t csa_topk_workspace(int B, int Tq, int N_max, int k, size_t* bytes);
 /*
  * csa_index_topk - csa_index_score followed by csa_topk, with the score
  * matrix kept in the workspace.  Arguments as in those two calls.
+ * ws        csa_index_topk_workspace bytes, 16-byte aligned, ZERO-FILLED before
+ *           its first use: it starts with counters through which the
+ *           workgroups that share a long row hand its survivors to the last
+ *           of them (tuned indexers, at most 64 rows).  Every call leaves
+ *           them zero, so a workspace is cleared once and then reused by
+ *           calls of any shape; calls that may run concurrently need
+ *           separate workspaces.
  */
 csa_status_t csa_index_topk(const void* q_idx, const void* q_scale, const float* w_idx,
                             const void* k_idx, const void* k_scale,
@@ -256,7 +263,8 @@ csa_status_t csa_index_topk_workspace(int B, int Tq, int N_max, int k, size_t* b
  * Arguments as in csa_index_topk for the BF16 64 x 128 indexer (q_idx
  * [B, Tq, 64, 128], k_idx [B, N_max, 128] with strides (k_sb, k_sn)); no
  * scale arguments.  topk_score returns the rounded scores (fp32) or is NULL.
- * Workspace: csa_index_topk_bf16_workspace bytes, 16-byte aligned.
+ * Workspace: csa_index_topk_bf16_workspace bytes, 16-byte aligned, ZERO-FILLED
+ * before its first use (as for csa_index_topk).
  * Supported: N_max <= 262144 and k as for csa_topk; else CSA_ERR_UNSUPPORTED.
  */
 csa_status_t csa_index_topk_bf16(const void* q_idx, const float* w_idx, const void* k_idx,
@@ -346,8 +354,8 @@ csa_status_t csa_attend_merge(const void* o_a, const float* lse_a, const void* o
  * attention arguments as in csa_attend (q, k_c, v_c, kv_sb, kv_sn, dtype, H,
  * D, scale, out, lse); q_pos, n_entries, B, Tq, N_max, m, k as in both.
  * ws        csa_index_topk_attend_workspace bytes, 16-byte aligned, ZERO-FILLED
- *           before its first use (it starts with the attention's
- *           synchronisation words; every call leaves them zero).
+ *           before its first use (it starts with the selection's and the
+ *           attention's synchronisation words; every call leaves them zero).
  * The step runs the score kernel, the selection kernel(s) and the split
  * attention kernel (which merges its splits itself) back to back on
  * `stream`, with the index lists in the workspace when topk_idx is NULL.
@@ -380,8 +388,9 @@ csa_status_t csa_index_topk_attend_workspace(csa_dtype_t idx_dtype, csa_dtype_t 
  * uses that GPU's one array, so calls that may overlap on one GPU (other
  * streams, other threads) race and must not be issued.  The stream must
  * belong to the calling thread's current device.  Limits: B * Tq <= 4096 and
- * the step's buffers within the scratch size (csa_index_topk_attend_workspace
- * minus its 8 MiB counter block gives them), else CSA_ERR_UNSUPPORTED.
+ * the step's buffers within the scratch size: csa_index_topk_attend_workspace
+ * less 7.5 MiB (its attention counters serve 65536 rows in 8 MiB, the
+ * scratch's 4096 rows in 0.5 MiB) at most 32 MiB, else CSA_ERR_UNSUPPORTED.
  */
 csa_status_t csa_index_topk_attend_noalloc(const void* q_idx, const void* q_scale,
                                            const float* w_idx, const void* k_idx,

@@ -98,11 +98,13 @@ int bound_k(csa_dtype_t dt, int H_I, int D_I, int N_max, int k) {
   return csa::score_tuned(dt, H_I, D_I) && csa::topk_bounded_ok(N_max) ? k : 0;
 }
 
-// scores | chunk bounds | selection workspace
+// selection counters (fixed size, zero between calls) | scores | chunk bounds
+// | selection workspace
+size_t sel_sync_bytes() { return round_up(csa::topk_sync_bytes()); }
 size_t index_topk_ws_bytes(int B, int Tq, int N_max, size_t topk_ws, size_t score_bytes) {
   const size_t rows = static_cast<size_t>(B) * Tq;
   const size_t bws = csa::topk_bounded_workspace_bytes(static_cast<int>(rows), N_max);
-  return round_up(rows * score_row_stride(N_max) * score_bytes) +
+  return sel_sync_bytes() + round_up(rows * score_row_stride(N_max) * score_bytes) +
          round_up(rows * bound_chunks(N_max) * sizeof(float2)) +
          round_up(topk_ws > bws ? topk_ws : bws);
 }
@@ -299,7 +301,7 @@ csa_status_t csa_topk(const float* scores, int64_t s_rs, const int32_t* q_pos,
   CSA_REQUIRE(ws_bytes >= need && (need == 0 || ws), CSA_ERR_WORKSPACE_TOO_SMALL,
               "topk: workspace %zu < %zu bytes", ws_bytes, need);
   return hip_status(csa::launch_topk(scores, false, s_rs, q_pos, n_entries, B, Tq, N_max, m, k,
-                                     nullptr, 0, topk_idx, topk_score, ws, stream),
+                                     nullptr, 0, topk_idx, topk_score, ws, nullptr, stream),
                     "topk launch");
 }
 
@@ -336,8 +338,9 @@ struct IndexWs {
   void* sel_ws;
 };
 
-// Lays out the workspace and launches the score kernel (with chunk reports
-// when the bounded selection will use them).
+// Lays out the workspace after its selection counters (scores | chunk
+// bounds | selection workspace from ws) and launches the score kernel (with
+// chunk reports when the bounded selection will use them).
 csa_status_t launch_index_scores(const void* q_idx, const void* q_scale, const float* w_idx,
                                  const void* k_idx, const void* k_scale, int64_t k_sb,
                                  int64_t k_sn, int64_t ks_sb, int64_t ks_sn, csa_dtype_t idx_dtype,
@@ -385,12 +388,12 @@ csa_status_t index_topk_impl(const void* q_idx, const void* q_scale, const float
               "index topk: workspace %zu < %zu bytes (or misaligned)", ws_bytes, need);
   IndexWs iw;
   st = launch_index_scores(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb, ks_sn,
-                           idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, k, ws, score16,
-                           stream, iw);
+                           idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I, m, k,
+                           static_cast<char*>(ws) + sel_sync_bytes(), score16, stream, iw);
   if (st != CSA_OK) return st;
   return hip_status(csa::launch_topk(iw.scores, score16, iw.srs, q_pos, n_entries, B, Tq, N_max, m,
                                      k, iw.bounds, iw.n_chunks, topk_idx, topk_score, iw.sel_ws,
-                                     stream),
+                                     static_cast<uint32_t*>(ws), stream),
                     "topk launch");
 }
 
@@ -533,9 +536,10 @@ csa_status_t swa_attend(const void* q, const void* k, const void* v, int64_t kv_
 // ---------------------------------------------------------------- score -> top-k -> attention
 namespace {
 
-// Intermediate buffers of one decode step: attention merge counters (zero
-// before the call, zero after it) for `sync_rows` rows, attention partials,
-// top-k lists (used when the caller passes none), index + top-k workspace.
+// Intermediate buffers of one decode step: selection counters and attention
+// merge counters for `sync_rows` rows (both fixed in size and place, zero
+// before the call, zero after it), attention partials, top-k lists (used when
+// the caller passes none), index + top-k workspace.
 struct StepSizes {
   size_t sync, part, idx, index;
   size_t total() const { return sync + part + idx + index; }
@@ -545,8 +549,7 @@ csa_status_t step_sizes(csa_dtype_t dtype, int B, int Tq, int N_max, int H, int 
   size_t t = 0;
   csa_status_t st = csa_index_topk_workspace(B, Tq, N_max, k, &t);
   if (st != CSA_OK) return st;
-  const bool tuned = csa::attend_part_bytes(dtype, false, B, Tq, H, D, k) > 0;
-  z.sync = tuned ? round_up(csa::attend_sync_block_bytes(sync_rows)) : 0;
+  z.sync = sel_sync_bytes() + round_up(csa::attend_sync_block_bytes(sync_rows));
   z.part = round_up(csa::attend_part_bytes(dtype, false, B, Tq, H, D, k));
   z.idx = round_up(static_cast<size_t>(B) * Tq * k * sizeof(int32_t));
   z.index = t;
@@ -581,18 +584,21 @@ csa_status_t step_impl(const void* q_idx, const void* q_scale, const float* w_id
                        int Tq, int N_max, int H_I, int D_I, int H, int D, int m, int k, float scale,
                        void* out, float* lse, int32_t* topk_idx, const StepSizes& z, char* base,
                        hipStream_t stream) {
-  int32_t* sync = reinterpret_cast<int32_t*>(base);
+  uint32_t* sel_sync = reinterpret_cast<uint32_t*>(base);
+  int32_t* sync = reinterpret_cast<int32_t*>(base + sel_sync_bytes());
   float* part = reinterpret_cast<float*>(base + z.sync);
   int32_t* idx_buf = reinterpret_cast<int32_t*>(base + z.sync + z.part);
   void* index_ws = base + z.sync + z.part + z.idx;
   IndexWs iw;
   csa_status_t st = launch_index_scores(q_idx, q_scale, w_idx, k_idx, k_scale, k_sb, k_sn, ks_sb,
                                         ks_sn, idx_dtype, q_pos, n_entries, B, Tq, N_max, H_I, D_I,
-                                        m, k, index_ws, false, stream, iw);
+                                        m, k, static_cast<char*>(index_ws) + sel_sync_bytes(),
+                                        false, stream, iw);
   if (st != CSA_OK) return st;
   int32_t* idx = topk_idx != nullptr ? topk_idx : idx_buf;
   st = hip_status(csa::launch_topk(iw.scores, false, iw.srs, q_pos, n_entries, B, Tq, N_max, m, k,
-                                   iw.bounds, iw.n_chunks, idx, nullptr, iw.sel_ws, stream),
+                                   iw.bounds, iw.n_chunks, idx, nullptr, iw.sel_ws, sel_sync,
+                                   stream),
                   "topk launch");
   if (st != CSA_OK) return st;
   csa::AttendArgs a{q, k_c, v_c, kv_sb, kv_sn, idx, nullptr, n_entries, B, Tq, H, D,
@@ -605,9 +611,9 @@ csa_status_t step_impl(const void* q_idx, const void* q_scale, const float* w_id
 // process ends.  Host code never uses its name as an address: the device
 // address comes from hipGetSymbolAddress, taken once per device (with that
 // device current) on the first call there and kept in g_scratch_addr.  The
-// array is zero when the code object is loaded; the attention merge counters
-// at its front are the only part that must be zero before a call, and every
-// call leaves them zero.
+// array is zero when the code object is loaded; the selection and attention
+// merge counters at its front are the only part that must be zero before a
+// call, and every call leaves them zero.
 constexpr size_t kScratchBytes = size_t(32) << 20;
 constexpr int kScratchRows = 4096;                // B * Tq the counter block serves
 constexpr int kMaxDevices = 64;

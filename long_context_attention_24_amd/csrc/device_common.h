@@ -45,14 +45,19 @@ __device__ __forceinline__ int visible_count(int q_pos, int m, int n_entries, in
 // kBoundChunk keys reports its c-th largest score, c being the smallest value
 // with floor(V / kBoundChunk) * c >= k for a row with V visible entries.  Any
 // value reached by ceil(k / c) of the reports is then at most the row's k-th
-// largest score (the minimum of the full chunks' reports always is).
-// Returns 0 (no bound) when that c would exceed kMaxBoundC.
+// largest score (the minimum of the full chunks' reports always is).  Where
+// that c is 1 but k is more than half the full chunks, c = 2 instead (also
+// valid): the ceil(k / 2)-th largest of the chunks' second largest scores sits
+// far closer to the k-th largest than the minimum of (almost) every chunk's
+// largest, so far fewer entries survive the bound.
+// Returns 0 (no bound) when c would exceed kMaxBoundC.
 constexpr int kBoundChunk = 256;
 constexpr int kMaxBoundC = 16;
 __device__ __forceinline__ int bound_c_row(int V, int k) {
   const int full = V / kBoundChunk;
   if (full == 0 || k <= 0) return 0;
-  const int c = (k + full - 1) / full;
+  int c = (k + full - 1) / full;
+  if (c == 1 && 2 * k > full) c = 2;
   return c <= kMaxBoundC ? c : 0;
 }
 

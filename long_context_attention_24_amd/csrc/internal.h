@@ -57,18 +57,20 @@ int score_chunk_keys();                            // keys per bound chunk
 // Selection from rows of N_max scores.  chunk_rep (nullable): per-row chunk
 // reports written by the tuned score kernels (one per 256-key chunk, n_chunks
 // per row, for the same k); they are used when topk_bounded_ok(N_max), with
-// a workspace of topk_bounded_workspace_bytes (zero for rows short enough to
-// be streamed by one workgroup).  Otherwise the workspace is
-// topk_workspace_bytes.
+// a workspace of topk_bounded_workspace_bytes (zero for rows that one
+// workgroup per row streams) and, for few long rows, topk_sync_bytes() of
+// counters at `sync` (zero before the call; every call leaves them zero).
+// Otherwise the workspace is topk_workspace_bytes and sync is unused.
 size_t topk_workspace_bytes(int rows, int N_max, int k);
 bool topk_bounded_ok(int N_max);
 size_t topk_bounded_workspace_bytes(int rows, int N_max);
+size_t topk_sync_bytes();
 bool topk_supported(int N_max, int k);
 // score16: bf16 score rows (chunk_rep required and topk_bounded_ok(N_max)).
 hipError_t launch_topk(const void* scores, bool score16, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
                        const float2* chunk_rep, int n_chunks, int32_t* idx,
-                       float* out_scores, void* ws, hipStream_t s);
+                       float* out_scores, void* ws, uint32_t* sync, hipStream_t s);
 
 // ---- attend.hip
 struct AttendArgs {

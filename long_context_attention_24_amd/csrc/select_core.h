@@ -25,7 +25,6 @@ constexpr int kMaxWaves = 16;
 constexpr float kPosInf = __builtin_inff();
 constexpr int kBrute = 256;                       // bin size finished by pairwise ranks
 constexpr int kMaxBoundedN = 262144;              // longest row with chunk reports in registers
-constexpr int kRegion = 1024;                     // entries per survivor region (filtered rows)
 
 typedef __attribute__((address_space(3))) float lds_float;
 typedef __attribute__((address_space(3))) int lds_int;
@@ -38,8 +37,10 @@ struct SelScratch {
   float f0[2][kMaxWaves];
   float f1[2][kMaxWaves];
   uint32_t u[2][kMaxWaves];
-  uint32_t tab[1024];                 // region offsets, then threshold candidates
+  uint32_t tab[1024];                 // segment offsets, then threshold candidates
   int bstar, bstar_above, bstar_cnt;
+  float lo, hi;                       // a row's bound and top, shared by its waves
+  int last;                           // this workgroup arrived last at the row's counter
   uint32_t cand_n;                    // threshold candidates gathered so far
   float tval;
   int teq;
@@ -282,6 +283,24 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
+// Histogram parameters of the first pass over [lo, hi] in select_sorted_list
+// (a caller that holds the survivors in registers may build that pass's
+// histogram itself): keys of lo and hi and the shift that takes their span
+// down to kBins bins.
+struct HistRange {
+  uint32_t klo, khi;
+  int shift;
+};
+__device__ __forceinline__ HistRange hist_range(float lo, float hi) {
+  const uint32_t klo = f32_order_key(lo + 0.0f), khi = f32_order_key(hi + 0.0f);
+  const uint32_t span = khi - klo;
+  return {klo, khi, span < static_cast<uint32_t>(kBins) ? 0 : 21 - __builtin_clz(span)};
+}
+__device__ __forceinline__ void hist_add(SelScratch& sm, const HistRange& hr, float x) {
+  const uint32_t key = f32_order_key(x);
+  if (key >= hr.klo && key <= hr.khi) atomicAdd(&sm.hist[(key - hr.klo) >> hr.shift], 1);
+}
+
 // Top-k of the survivor list lp[0..n) ((score bits, entry) pairs in
 // ascending entry order, values > -inf and -0.0 stored as +0.0, all within
 // [lo, hi] when have_range, else the range is computed here).  Emits
@@ -298,12 +317,14 @@ __device__ __forceinline__ float f32_from_order_key(uint32_t key) {
 //   (count > T, count == T) over contiguous per-thread runs (two 16-bit
 //   halves of one word: n < 65536) gives every output slot; entries equal to
 //   T are taken lowest index first.
-// Entry: the histogram is zero, sm.cand_n is zero and a barrier separates
-// the list writes from this call.
+// Entry: the histogram is zero (or, with hist_ready, holds the first pass
+// over [lo, hi] as hist_add builds it), sm.cand_n is zero and a barrier
+// separates the list (and histogram) writes from this call.
 template <int NW, typename Out>
 __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32x2* lp, int n,
                                                    float lo, float hi, bool have_range, int k,
-                                                   int& p, const Out& out) {
+                                                   int& p, const Out& out,
+                                                   bool hist_ready = false) {
   constexpr int NT = NW * 64;
   constexpr int BPT = kBins / NT;                 // histogram bins per thread
   const int tid = threadIdx.x;
@@ -332,9 +353,12 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
         break;
       }
       const int shift = span < static_cast<uint32_t>(kBins) ? 0 : 21 - __builtin_clz(span);
-      for (int j = tid; j < n; j += NT) {
-        const uint32_t key = f32_order_key(lval(lp, j));
-        if (key >= klo && key <= khi) atomicAdd(&sm.hist[(key - klo) >> shift], 1);
+      if (!(hist_ready && have_range && pass == 0)) {
+#pragma unroll 4
+        for (int j = tid; j < n; j += NT) {
+          const uint32_t key = f32_order_key(lval(lp, j));
+          if (key >= klo && key <= khi) atomicAdd(&sm.hist[(key - klo) >> shift], 1);
+        }
       }
       __syncthreads();
       uint32_t h[BPT];
@@ -373,6 +397,7 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
       if (cnt <= kBrute) {
         // the need-th largest of the bin: the candidate with fewer than need
         // larger ones and at least need larger-or-equal ones
+#pragma unroll 4
         for (int j = tid; j < n; j += NT) {
           const float x = lval(lp, j);
           const uint32_t key = f32_order_key(x);
@@ -408,6 +433,7 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
   const int R = (n + NT - 1) / NT;
   const int j0 = tid * R, j1 = min(n, j0 + R);
   uint32_t gt = 0, eq = 0;
+#pragma unroll 4
   for (int j = j0; j < j1; ++j) {
     const float x = lval(lp, j);
     gt += x > T ? 1u : 0u;
@@ -440,7 +466,8 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
 // (+inf: the chunk had fewer than c scored entries, or none).  With
 // r = ceil(k / c), any value that at least r reports reach is therefore
 // reached by at least k entries: a valid bound.  bound: the r-th largest
-// report, found from below by bisection over order-preserving keys (the
+// report, approached from below by bisection over order-preserving keys,
+// kBoundSteps steps (the
 // minimum when there are exactly r reports; -inf when fewer).  Taking the
 // r-th largest rather than the minimum keeps a few low chunks (for example
 // freshly pooled entries with smaller norms) from loosening the whole row's
@@ -480,11 +507,11 @@ __device__ __forceinline__ void load_reports(const float2* __restrict__ rep, int
   load_report_slots<kRepB, kRepPerLane>(rep, n_chunks, t, ns > kRepB);
 }
 
-// Order keys, count and extrema of the report slots [U0, U1) (key 0: none).
+// Order keys and extrema of the report slots [U0, U1) (key 0: none).
 template <int U0, int U1>
 __device__ __forceinline__ void report_keys(const float2 (&t)[kRepPerLane], int n_chunks,
                                             uint32_t (&key)[kRepPerLane], uint32_t& kmin,
-                                            uint32_t& kmax, uint32_t& cnt, float& mx) {
+                                            uint32_t& kmax, float& mx) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int u = U0; u < U1; ++u) {
@@ -493,12 +520,45 @@ __device__ __forceinline__ void report_keys(const float2 (&t)[kRepPerLane], int 
     if (key[u] != 0u) {
       kmin = min(kmin, key[u]);
       kmax = max(kmax, key[u]);
-      ++cnt;
     }
     if (in) mx = fmaxf(mx, t[u].y);
   }
 }
 
+// Wave-wide reductions for the bound: DPP quad swaps, half-row and row
+// mirrors leave every lane with its 16-lane row's result, and four readlanes
+// combine the rows on the scalar unit (a short dependent chain, which the
+// bisection below repeats every step).
+template <int C>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(v), C, 0xF, 0xF, false));
+}
+template <typename F>
+__device__ __forceinline__ uint32_t dpp_reduce_u32(uint32_t v, F f) {
+  v = f(v, dpp_u32<0xB1>(v));                     // quad lanes [1, 0, 3, 2]
+  v = f(v, dpp_u32<0x4E>(v));                     // quad lanes [2, 3, 0, 1]
+  v = f(v, dpp_u32<0x141>(v));                    // row half mirror
+  v = f(v, dpp_u32<0x140>(v));                    // row mirror
+  return f(f(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+           f(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t dpp_sum_u32(uint32_t v) {
+  return dpp_reduce_u32(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
+__device__ __forceinline__ uint32_t dpp_min_u32(uint32_t v) {
+  return dpp_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  return dpp_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ float dpp_max_f32(float v) {
+  return __uint_as_float(dpp_reduce_u32(__float_as_uint(v), [](uint32_t a, uint32_t b) {
+    return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+  }));
+}
+
+// Keys of the wave's slots [0, U1) that are >= mid (0: none): this lane's
+// count.
 template <int U1>
 __device__ __forceinline__ uint32_t keys_at_least(const uint32_t (&key)[kRepPerLane], uint32_t mid) {
   uint32_t n = 0;
@@ -506,31 +566,32 @@ __device__ __forceinline__ uint32_t keys_at_least(const uint32_t (&key)[kRepPerL
   for (int u = 0; u < U1; ++u) n += key[u] >= mid ? 1u : 0u;
   return n;
 }
-
 __device__ __forceinline__ float2 row_bound(const float2 (&t)[kRepPerLane], int n_chunks, int c,
                                             int k) {
   float mx = -FLT_MAX;
-  uint32_t kmin = 0xffffffffu, kmax = 0u, cnt = 0;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
   uint32_t key[kRepPerLane];
   const int ns = report_slots(n_chunks);         // uniform: slots in use
-  report_keys<0, kRepA>(t, n_chunks, key, kmin, kmax, cnt, mx);
-  if (ns > kRepA) report_keys<kRepA, kRepB>(t, n_chunks, key, kmin, kmax, cnt, mx);
-  if (ns > kRepB) report_keys<kRepB, kRepPerLane>(t, n_chunks, key, kmin, kmax, cnt, mx);
+  report_keys<0, kRepA>(t, n_chunks, key, kmin, kmax, mx);
+  if (ns > kRepA) report_keys<kRepA, kRepB>(t, n_chunks, key, kmin, kmax, mx);
+  if (ns > kRepB) report_keys<kRepB, kRepPerLane>(t, n_chunks, key, kmin, kmax, mx);
   if (c <= 0) return make_float2(kNegInf, kNegInf);
-  mx = wave_max(mx);
-  cnt = wave_sum_u32(cnt);
+  mx = dpp_max_f32(mx);
+  const uint32_t cnt = dpp_sum_u32(ns > kRepB   ? keys_at_least<kRepPerLane>(key, 1u)
+                                   : ns > kRepA ? keys_at_least<kRepB>(key, 1u)
+                                                : keys_at_least<kRepA>(key, 1u));
   const uint32_t r = static_cast<uint32_t>((k + c - 1) / c);
   if (cnt < r) return make_float2(kNegInf, mx);
   // invariant: at least r keys >= lo, fewer than r keys >= hi
-  uint32_t lo = wave_min_u32(kmin);
+  uint32_t lo = dpp_min_u32(kmin);
   if (cnt > r) {
-    uint64_t hi = static_cast<uint64_t>(wave_max_u32(kmax)) + 1;
+    uint64_t hi = static_cast<uint64_t>(dpp_max_u32(kmax)) + 1;
     for (int it = 0; it < kBoundSteps && hi - lo > 1; ++it) {
       const uint32_t mid = static_cast<uint32_t>(lo + ((hi - lo) >> 1));
-      const uint32_t n = ns > kRepB   ? keys_at_least<kRepPerLane>(key, mid)
-                         : ns > kRepA ? keys_at_least<kRepB>(key, mid)
-                                      : keys_at_least<kRepA>(key, mid);
-      if (wave_sum_u32(n) >= r) lo = mid;
+      const uint32_t n = dpp_sum_u32(ns > kRepB   ? keys_at_least<kRepPerLane>(key, mid)
+                                     : ns > kRepA ? keys_at_least<kRepB>(key, mid)
+                                                  : keys_at_least<kRepA>(key, mid));
+      if (n >= r) lo = mid;
       else hi = mid;
     }
   }
@@ -637,61 +698,6 @@ __device__ __forceinline__ int stream_survivors(SelScratch& sm, const S* __restr
     } else if (more) {
 #pragma unroll
       for (int s = 0; s < SL; ++s) x[s] = y[s];
-    }
-  }
-  return n;
-}
-
-// Copies the survivor regions of a filtered row (per region: a count and up
-// to kRegion (score, entry) pairs in index order, written by a filter pass)
-// into the LDS list in region order, i.e. ascending index order.  The counts
-// are scanned in region order (nreg <= NW * 64) and wave w copies regions w,
-// w + NW, ... (the counts and first 128 survivors of eight regions are
-// loaded together).  Returns the number of survivors; above cap nothing is
-// copied and the caller falls back.  Uses sm.tab for the offsets.
-template <int NW>
-__device__ __forceinline__ int gather_regions(SelScratch& sm, const int32_t* __restrict__ cnt_row,
-                                              const float* __restrict__ val_row,
-                                              const int32_t* __restrict__ idx_row, int nreg,
-                                              lds_u32x2* lp, int cap, int& p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  uint32_t total;
-  const uint32_t off =
-      block_excl_scan<NW>(sm, tid < nreg ? static_cast<uint32_t>(cnt_row[tid]) : 0u, total, p);
-  if (tid < nreg) sm.tab[tid] = off;
-  const int n = static_cast<int>(total);
-  __syncthreads();                                // offsets visible
-  if (n > cap) return n;
-  constexpr int kBatch = 8;
-  for (int r0 = wave; r0 < nreg; r0 += NW * kBatch) {
-    int cnt[kBatch];
-    float v0[kBatch], v1[kBatch];
-    int i0[kBatch], i1[kBatch];
-#pragma unroll
-    for (int rr = 0; rr < kBatch; ++rr) {
-      const int r = r0 + NW * rr;
-      if (r < nreg) {
-        const int64_t base = static_cast<int64_t>(r) * kRegion;
-        cnt[rr] = cnt_row[r];
-        v0[rr] = val_row[base + lane];
-        v1[rr] = val_row[base + 64 + lane];
-        i0[rr] = idx_row[base + lane];
-        i1[rr] = idx_row[base + 64 + lane];
-      }
-    }
-#pragma unroll
-    for (int rr = 0; rr < kBatch; ++rr) {
-      const int r = r0 + NW * rr;
-      if (r < nreg && cnt[rr] > 0) {
-        const int c = cnt[rr];
-        const int o = static_cast<int>(sm.tab[r]);
-        if (lane < c) lp[o + lane] = u32x2_t{__float_as_uint(v0[rr]), static_cast<uint32_t>(i0[rr])};
-        if (64 + lane < c)
-          lp[o + 64 + lane] = u32x2_t{__float_as_uint(v1[rr]), static_cast<uint32_t>(i1[rr])};
-        const int64_t rg = static_cast<int64_t>(r) * kRegion;
-        for (int j = 128 + lane; j < c; j += 64)   // rare: more than 128 survivors
-          lp[o + j] = u32x2_t{__float_as_uint(val_row[rg + j]), static_cast<uint32_t>(idx_row[rg + j])};
-      }
     }
   }
   return n;

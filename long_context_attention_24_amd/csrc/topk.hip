@@ -42,7 +42,6 @@ namespace {
 
 using sel::kBins;
 using sel::kMaxBoundedN;
-using sel::kRegion;
 using sel::lds_float;
 using sel::lds_u32x2;
 using sel::u32x2_t;
@@ -176,7 +175,8 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 }
 
 // ============================================================ bounded path
-// topk_bounded_kernel: one 1024-thread workgroup per row.
+// topk_bounded_kernel: one 1024-thread workgroup per row (topk_fused_kernel
+// below for few long rows).
 //   1. The row bound and the top of the survivors' range come from the chunk
 //      reports, every wave computing them on its own (sel::row_bound), the
 //      reports loaded next to the first score loads.
@@ -187,9 +187,7 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 //      one is compacted; per round the waves count their survivors with
 //      ballots, one block scan gives every wave its offset, and each
 //      survivor's slot is that offset plus its rank among the wave's
-//      survivors (ballot + mbcnt).  Filtered rows (topk_filter_kernel first,
-//      sel::gather_regions): the per-region survivor counts are scanned and
-//      the regions copied at their offsets.
+//      survivors (ballot + mbcnt).
 //   3. sel::select_sorted_list: a 2048-bin equal-width histogram over
 //      [bound, top] locates the bin of the k-th largest; a bin of at most 256
 //      entries is finished by pairwise ranks, a larger one narrows the range
@@ -206,97 +204,190 @@ constexpr int kListCap = 16 * kSelThreads;        // survivors held in LDS
 static_assert(kListCap < 65536, "select_sorted_list packs two list counts into one word");
 constexpr int kStreamSlots = 16;                  // scores per lane per round (64 apart)
 constexpr int kShortRow = 32768;                  // rows streamed in one round of 32 per thread
-static_assert(kMaxBoundedN / kRegion <= kSelThreads, "one region per thread in the offset scan");
 
-// Few long rows (more than kStreamMaxN entries, at most kRegionMaxRows rows:
-// too little parallelism for one workgroup per row) are filtered first by
-// topk_filter_kernel: one 256-thread workgroup per 4096 entries, each wave
-// owning 1024 of them (a region) and working alone (no barrier, no atomic):
-// it derives the row bound from the chunk reports, compacts its entries at or
-// above the bound, in index order, to the front of its region of the
-// survivor buffers and stores their number.  The bounded kernel then gathers
-// the regions instead of streaming the row.
-constexpr int kStreamMaxN = 65536;
-constexpr int kRegionMaxRows = 64;
-constexpr int kFiltSeg = 4096;
+// Few long rows (at most kFusedMaxRows rows of more than kFusedMinN entries:
+// one workgroup per row would leave most of the chip idle while it reads the
+// row) are filtered and selected by one kernel, topk_fused_kernel: one
+// 1024-thread workgroup per 4096 entries of a row, each wave owning 256 of
+// them (four per lane, one 16- or 8-byte load).  Wave 0 derives the row
+// bound and the top of the survivors' range from the chunk reports while the
+// other waves' loads are in flight; every workgroup then compacts its entries
+// at or above the bound, in index order, to its segment of the survivor
+// buffer (one block scan of the wave counts), stores their number, and
+// arrives at the row's counter.  The workgroup that arrives last (no wait:
+// the others simply end) gathers the row's segments into an LDS list in
+// index order, one load per list position (the position's segment found by
+// binary search over the segment offsets), and selects from it with
+// sel::select_sorted_list.  Survivor stores, counts and the gather's loads
+// are device-coherent (they bypass the per-XCD L2), each workgroup's stores
+// complete before it arrives, and the last workgroup resets the counter, so
+// the counters (one 64-byte line per row, at the front of the workspace)
+// are zero before and after every call.
+constexpr int kFusedSeg = kSelThreads / 64 * 256; // entries per workgroup
+constexpr int kFusedMaxRows = 64;
+constexpr int kFusedMinN = 65536;
+constexpr int kSyncStride = 16;                   // uint32 words per row's counter
+static_assert(kMaxBoundedN / kFusedSeg <= 64, "segment offsets scanned by one wave");
 
-template <typename S>
-__global__ __launch_bounds__(kSegThreads) void topk_filter_kernel(
-    const S* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
-    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
-    const float2* __restrict__ chunk_rep, int n_chunks, int nreg, float* __restrict__ reg_val,
-    int32_t* __restrict__ reg_idx, int32_t* __restrict__ reg_cnt) {
-  const int seg = blockIdx.x, row = blockIdx.y, b = row / Tq;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int e0 = seg * kFiltSeg + wave * kRegion;
-  const int r = seg * (kFiltSeg / kRegion) + wave;
-  if (r >= nreg) return;
-  // loads bounded by N_max, issued before the visible count is known
-  const int Ln = max(0, min(N_max - e0, kRegion));
-  const S* src = scores + row * s_rs + e0;
-  float v[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = 256 * i + 4 * lane;
-    if (q + 3 < Ln) {
-      const float4 x = sel::load4_scores(src + q);
-      v[i][0] = x.x; v[i][1] = x.y; v[i][2] = x.z; v[i][3] = x.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[i][e] = (q + e < Ln) ? get_score(src + q + e) : kNegInf;
-    }
-  }
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-  const int L = max(0, min(V - e0, kRegion));
-  if (L < kRegion) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (256 * i + 4 * lane + e >= L) v[i][e] = kNegInf;
-  }
-  const float bound = sel::wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks,
-                                     bound_c_row(V, k), k).x;
-  const float bnd = bound > kNegInf ? bound : -FLT_MAX;   // x >= bnd: a finite survivor
-  const int64_t base = (static_cast<int64_t>(row) * nreg + r) * kRegion;
-  uint32_t o = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t cl = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) cl += v[i][e] >= bnd ? 1u : 0u;
-    const uint32_t incl = wave_incl_scan_u32(cl);
-    uint32_t q = o + incl - cl;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (v[i][e] >= bnd) {
-        reg_val[base + q] = v[i][e];
-        reg_idx[base + q] = e0 + 256 * i + 4 * lane + e;
-        ++q;
-      }
-    }
-    o += __builtin_amdgcn_readlane(incl, 63);
-  }
-  if (lane == 0) reg_cnt[static_cast<int64_t>(row) * nreg + r] = static_cast<int32_t>(o);
+__device__ __forceinline__ void st_coherent(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_coherent(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-int filter_regions(int N_max) { return (N_max + kFiltSeg - 1) / kFiltSeg * (kFiltSeg / kRegion); }
+int fused_segments(int N_max) { return (N_max + kFusedSeg - 1) / kFusedSeg; }
 
-// One 1024-thread workgroup per row builds the row's survivor list in LDS in
-// ascending index order and selects from it.  Streaming (REGIONS false): the
-// first round's score loads are issued before the row's visible count and
-// bound are known (bounded by N_max, masked after).  REGIONS: the per-region
-// counts of topk_filter_kernel are gathered.  The bound (when the row has
-// one) and the largest chunk report delimit the survivors' range.  More than
-// kListCap survivors (inputs far from the expected distribution): the row is
-// selected from global memory by block_select instead.
-template <bool REGIONS, int SL, typename S>
+template <typename S>
+__global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
+    const S* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
+    const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
+    const float2* __restrict__ chunk_rep, int n_chunks, int nseg, uint64_t* __restrict__ seg_buf,
+    uint32_t* __restrict__ seg_cnt, uint32_t* __restrict__ sync, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_val) {
+  constexpr int NW = kSelWaves;
+  constexpr int NT = kSelThreads;
+  __shared__ u32x2_t lp_s[kListCap];
+  lds_u32x2* lp = (lds_u32x2*)lp_s;
+  const int seg = blockIdx.x, row = blockIdx.y, b = row / Tq;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const S* srow = scores + row * s_rs;
+  // four scores per lane: entries e0 .. e0 + 3, loads bounded by N_max
+  const int e0 = seg * kFusedSeg + wave * 256 + 4 * lane;
+  float v[4];
+  if (e0 + 3 < N_max) {
+    const float4 x = sel::load4_scores(srow + e0);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = e0 + e < N_max ? get_score(srow + e0 + e) : kNegInf;
+  }
+  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
+  if (wave == 0) {
+    const float2 rb = sel::wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks,
+                                          n_chunks, bound_c_row(V, k), k);
+    if (lane == 0) {
+      g_sm.lo = rb.x;
+      g_sm.hi = rb.y;
+    }
+  }
+  g_sm.hist[2 * tid] = 0;
+  g_sm.hist[2 * tid + 1] = 0;
+  if (tid == 0) g_sm.cand_n = 0;
+  __syncthreads();
+  const float lo = g_sm.lo, hi = g_sm.hi;
+  const float bnd = lo > kNegInf ? lo : -FLT_MAX;            // x >= bnd: a finite survivor
+  bool keep[4];
+  uint32_t cl = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    keep[e] = e0 + e < V && v[e] >= bnd;
+    cl += keep[e] ? 1u : 0u;
+  }
+  int p = 0;
+  uint32_t seg_n;
+  uint32_t q = sel::block_excl_scan<NW>(g_sm, cl, seg_n, p);
+  uint64_t* dst = seg_buf + (static_cast<int64_t>(row) * nseg + seg) * kFusedSeg;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (keep[e]) {
+      st_coherent(dst + q, static_cast<uint64_t>(__float_as_uint(v[e] + 0.0f)) |
+                               (static_cast<uint64_t>(e0 + e) << 32));
+      ++q;
+    }
+  }
+  if (tid == 0) st_coherent(seg_cnt + static_cast<int64_t>(row) * nseg + seg, seg_n);
+  __builtin_amdgcn_s_waitcnt(0);                  // this thread's stores are complete
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* ctr = sync + kSyncStride * row;
+    const bool last =
+        __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        static_cast<uint32_t>(nseg - 1);
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g_sm.last = last ? 1 : 0;
+  }
+  __syncthreads();
+  if (g_sm.last == 0) return;                     // block-uniform
+  // the last workgroup of the row: segment offsets (nseg <= 64: wave 0 scans),
+  // padded to 64 entries with an offset no list position reaches
+  if (wave == 0) {
+    const uint32_t c = lane < nseg ? ld_coherent(seg_cnt + static_cast<int64_t>(row) * nseg + lane) : 0u;
+    const uint32_t incl = wave_incl_scan_u32(c);
+    g_sm.tab[lane] = lane < nseg ? incl - c : 0x7fffffffu;
+    if (lane == 63) g_sm.cand_n = incl;           // the list length, read below
+  }
+  __syncthreads();
+  const int n = static_cast<int>(g_sm.cand_n);
+  __syncthreads();
+  if (tid == 0) g_sm.cand_n = 0;
+  sel::GlobalOut out{out_idx + static_cast<int64_t>(row) * k,
+                     out_val ? out_val + static_cast<int64_t>(row) * k : nullptr};
+  if (n > kListCap) {                             // far from the expected distribution
+    const int n_sel = sel::block_select<NW>(
+        g_sm, sel::GlobalRun<S>{srow, V, (V + NT - 1) / NT}, k, p, out);
+    sel::pad_output<NW>(out, n_sel, k);
+    return;
+  }
+  // gather: list position j from segment s = the last with offset <= j; all
+  // of a thread's loads in flight together; the first histogram pass of the
+  // selection is built from the gathered values
+  const uint64_t* rowbuf = seg_buf + static_cast<int64_t>(row) * nseg * kFusedSeg;
+  constexpr int kG = kListCap / NT;
+  constexpr int kQ = 4;                           // positions searched together
+  uint64_t e[kG];
+#pragma unroll
+  for (int g0 = 0; g0 < kG; g0 += kQ) {
+    if (g0 * NT >= n) break;                      // uniform
+    int sg[kQ];
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) sg[q] = 0;
+#pragma unroll
+    for (int st = 32; st > 0; st >>= 1) {         // six halvings over the 64 offsets, every
+#pragma unroll                                    // position's read issued unconditionally
+      for (int q = 0; q < kQ; ++q)
+        sg[q] += static_cast<int>(g_sm.tab[sg[q] + st]) <= tid + (g0 + q) * NT ? st : 0;
+    }
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const int j = tid + (g0 + q) * NT;
+      if (j < n)
+        e[g0 + q] = ld_coherent(rowbuf + static_cast<int64_t>(sg[q]) * kFusedSeg +
+                                (j - static_cast<int>(g_sm.tab[sg[q]])));
+    }
+  }
+  const bool have_range = lo > kNegInf;           // survivors lie in [bound, largest report]
+  const sel::HistRange hr = sel::hist_range(lo, hi);
+#pragma unroll
+  for (int g = 0; g < kG; ++g) {
+    const int j = tid + g * NT;
+    if (j < n) {
+      lp[j] = u32x2_t{static_cast<uint32_t>(e[g]), static_cast<uint32_t>(e[g] >> 32)};
+      if (have_range) sel::hist_add(g_sm, hr, __uint_as_float(static_cast<uint32_t>(e[g])));
+    }
+  }
+  __syncthreads();                                // the list and first histogram are complete
+  sel::select_sorted_list<NW>(g_sm, lp, n, lo, hi, have_range, k, p, out, true);
+}
+
+// One 1024-thread workgroup per row streams the row into a survivor list in
+// LDS, in ascending index order, and selects from it.  The first round's
+// score loads are issued before the row's visible count and bound are known
+// (bounded by N_max, masked after).  The bound (when the row has one) and the
+// largest chunk report delimit the survivors' range.  More than kListCap
+// survivors (inputs far from the expected distribution): the row is selected
+// from global memory by block_select instead.
+template <int SL, typename S>
 __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
     const S* __restrict__ scores, int64_t s_rs, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, int k,
-    const float2* __restrict__ chunk_rep, int n_chunks, int nreg,
-    const float* __restrict__ reg_val, const int32_t* __restrict__ reg_idx,
-    const int32_t* __restrict__ reg_cnt, int32_t* __restrict__ out_idx,
+    const float2* __restrict__ chunk_rep, int n_chunks, int32_t* __restrict__ out_idx,
     float* __restrict__ out_val) {
   constexpr int NW = kSelWaves;
   constexpr bool kOneRound = SL * kSelThreads >= kShortRow;
@@ -307,28 +398,17 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
   const S* srow = scores + row * s_rs;
   float x[SL];
   float2 rt[sel::kRepPerLane];
-  if (!REGIONS) {
-    sel::load_round(srow, wave * 64 * SL, N_max, x);
-    sel::load_reports(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks, rt);
-  }
+  sel::load_round(srow, wave * 64 * SL, N_max, x);
+  sel::load_reports(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks, rt);
   const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
-  float2 rb = make_float2(kNegInf, kNegInf);
-  if (!REGIONS) rb = sel::row_bound(rt, n_chunks, bound_c_row(V, k), k);
+  const float2 rb = sel::row_bound(rt, n_chunks, bound_c_row(V, k), k);
   g_sm.hist[2 * tid] = 0;
   g_sm.hist[2 * tid + 1] = 0;
   if (tid == 0) g_sm.cand_n = 0;
   int p = 0;
-  int n;                                          // block-uniform
-  if (REGIONS) {
-    const int64_t rbase = static_cast<int64_t>(row) * nreg;
-    n = sel::gather_regions<NW>(g_sm, reg_cnt + rbase, reg_val + rbase * kRegion,
-                                reg_idx + rbase * kRegion, nreg, lp, kListCap, p);
-    rb = sel::wave_row_bound(chunk_rep + static_cast<int64_t>(row) * n_chunks, n_chunks,
-                             bound_c_row(V, k), k);
-  } else {
-    const float bnd = rb.x > kNegInf ? rb.x : -FLT_MAX;     // x >= bnd: a finite survivor
-    n = sel::stream_survivors<NW, SL, kOneRound>(g_sm, srow, V, N_max, bnd, lp, kListCap, x, p);
-  }
+  const float bnd = rb.x > kNegInf ? rb.x : -FLT_MAX;       // x >= bnd: a finite survivor
+  const int n =                                             // block-uniform
+      sel::stream_survivors<NW, SL, kOneRound>(g_sm, srow, V, N_max, bnd, lp, kListCap, x, p);
   __syncthreads();                                // the list is complete
   sel::GlobalOut out{out_idx + static_cast<int64_t>(row) * k,
                      out_val ? out_val + static_cast<int64_t>(row) * k : nullptr};
@@ -360,76 +440,55 @@ size_t topk_workspace_bytes(int rows, int N_max, int k) {
 
 bool topk_bounded_ok(int N_max) { return N_max <= kMaxBoundedN; }
 
-bool use_regions(int rows, int N_max) { return N_max > kStreamMaxN && rows <= kRegionMaxRows; }
+bool use_fused(int rows, int N_max) { return N_max > kFusedMinN && rows <= kFusedMaxRows; }
 
 size_t topk_bounded_workspace_bytes(int rows, int N_max) {
-  if (!topk_bounded_ok(N_max) || !use_regions(rows, N_max)) return 0;
-  const size_t regs = static_cast<size_t>(rows) * filter_regions(N_max);
-  return regs * kRegion * (sizeof(float) + sizeof(int32_t)) + regs * sizeof(int32_t);
+  if (!topk_bounded_ok(N_max) || !use_fused(rows, N_max)) return 0;
+  const size_t segs = static_cast<size_t>(rows) * fused_segments(N_max);
+  return segs * kFusedSeg * sizeof(uint64_t) + segs * sizeof(uint32_t);
 }
 
-// survivor region buffers at the front of ws: values, entries, counts
-void region_buffers(void* ws, int rows, int N_max, float** rv, int32_t** ri, int32_t** rc) {
-  const size_t slots = static_cast<size_t>(rows) * filter_regions(N_max) * kRegion;
-  *rv = static_cast<float*>(ws);
-  *ri = reinterpret_cast<int32_t*>(*rv + slots);
-  *rc = *ri + slots;
-}
-
-template <typename S>
-hipError_t launch_filter(const S* scores, int64_t s_rs, const int32_t* q_pos,
-                         const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
-                         const float2* chunk_rep, int n_chunks, float* rv, int32_t* ri,
-                         int32_t* rc, hipStream_t s) {
-  const int rows = B * Tq;
-  hipLaunchKernelGGL(topk_filter_kernel<S>, dim3((N_max + kFiltSeg - 1) / kFiltSeg, rows),
-                     dim3(kSegThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
-                     chunk_rep, n_chunks, filter_regions(N_max), rv, ri, rc);
-  return hipGetLastError();
-}
+size_t topk_sync_bytes() { return static_cast<size_t>(kFusedMaxRows) * kSyncStride * sizeof(uint32_t); }
 
 template <typename S>
 hipError_t launch_topk_bounded(const S* scores, int64_t s_rs, const int32_t* q_pos,
                                const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
                                const float2* chunk_rep, int n_chunks, int32_t* idx,
-                               float* out_scores, void* ws, hipStream_t s) {
+                               float* out_scores, void* ws, uint32_t* sync, hipStream_t s) {
   const int rows = B * Tq;
-  if (!use_regions(rows, N_max)) {
+  if (!use_fused(rows, N_max)) {
     if (N_max <= kShortRow)
-      hipLaunchKernelGGL((topk_bounded_kernel<false, kShortRow / kSelThreads, S>), dim3(rows),
+      hipLaunchKernelGGL((topk_bounded_kernel<kShortRow / kSelThreads, S>), dim3(rows),
                          dim3(kSelThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
-                         chunk_rep, n_chunks, 0, nullptr, nullptr, nullptr, idx, out_scores);
+                         chunk_rep, n_chunks, idx, out_scores);
     else
-      hipLaunchKernelGGL((topk_bounded_kernel<false, kStreamSlots, S>), dim3(rows),
-                         dim3(kSelThreads), 0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k,
-                         chunk_rep, n_chunks, 0, nullptr, nullptr, nullptr, idx, out_scores);
+      hipLaunchKernelGGL((topk_bounded_kernel<kStreamSlots, S>), dim3(rows), dim3(kSelThreads),
+                         0, s, scores, s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep,
+                         n_chunks, idx, out_scores);
     return hipGetLastError();
   }
-  const int nreg = filter_regions(N_max);
-  float* rv;
-  int32_t *ri, *rc;
-  region_buffers(ws, rows, N_max, &rv, &ri, &rc);
-  const hipError_t e = launch_filter(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, chunk_rep,
-                                     n_chunks, rv, ri, rc, s);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((topk_bounded_kernel<true, kStreamSlots, S>), dim3(rows), dim3(kSelThreads), 0, s, scores,
-                     s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, nreg, rv, ri,
-                     rc, idx, out_scores);
+  // survivor segments at the front of ws, then their counts
+  const int nseg = fused_segments(N_max);
+  uint64_t* seg_buf = static_cast<uint64_t*>(ws);
+  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(seg_buf + static_cast<size_t>(rows) * nseg * kFusedSeg);
+  hipLaunchKernelGGL(topk_fused_kernel<S>, dim3(nseg, rows), dim3(kSelThreads), 0, s, scores,
+                     s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, nseg, seg_buf,
+                     seg_cnt, sync, idx, out_scores);
   return hipGetLastError();
 }
 
 hipError_t launch_topk(const void* scores_v, bool score16, int64_t s_rs, const int32_t* q_pos,
                        const int32_t* n_entries, int B, int Tq, int N_max, int m, int k,
                        const float2* chunk_rep, int n_chunks, int32_t* idx, float* out_scores,
-                       void* ws, hipStream_t s) {
+                       void* ws, uint32_t* sync, hipStream_t s) {
   const int rows = B * Tq;
   if (score16)   // bf16 rows: the bounded path only (the caller checks chunk_rep and N_max)
     return launch_topk_bounded(static_cast<const uint16_t*>(scores_v), s_rs, q_pos, n_entries, B,
-                               Tq, N_max, m, k, chunk_rep, n_chunks, idx, out_scores, ws, s);
+                               Tq, N_max, m, k, chunk_rep, n_chunks, idx, out_scores, ws, sync, s);
   const float* scores = static_cast<const float*>(scores_v);
   if (chunk_rep != nullptr && topk_bounded_ok(N_max))
     return launch_topk_bounded(scores, s_rs, q_pos, n_entries, B, Tq, N_max, m, k, chunk_rep,
-                               n_chunks, idx, out_scores, ws, s);
+                               n_chunks, idx, out_scores, ws, sync, s);
   const int nseg = num_segments(N_max);
   float* cv = static_cast<float*>(ws);
   int32_t* ci = reinterpret_cast<int32_t*>(cv + static_cast<size_t>(rows) * nseg * k);

@@ -276,7 +276,7 @@ def _low_chunks(ki, chunks, scale):
 
 @pytest.mark.parametrize("Tq,N_max,k,chunks", [
     (72, 40000, 256, (3, 50, 151, 155)),        # streamed rows: c = 2, r = 128 of ~157 reports
-    (1, 100000, 1024, (0, 7, 200, 389)),        # filtered regions: c = 3, r = 342 of 391 reports
+    (1, 100000, 1024, (0, 7, 200, 389)),        # few long rows: c = 3, r = 342 of 391 reports
 ])
 def test_topk_bound_rth_report(Tq, N_max, k, chunks):
     """Selection with more chunk reports than the bound needs (the bound is
@@ -302,9 +302,39 @@ def test_topk_bound_rth_report(Tq, N_max, k, chunks):
         check_topk(I[b, t], s_ref, V, k)
 
 
+def test_fused_selection_ragged_rows_and_reuse():
+    """Few long rows (the selection's workgroups share each row and the last
+    to finish selects): visible counts that end mid-segment, leave whole
+    segments invisible, fall below k and reach zero, over two calls on one
+    zero-filled workspace with different head weights.  Each selection
+    against the oracle's exact top-k; the row counters at the front of the
+    workspace are zero again after each call."""
+    N_max, k, m = 140000, 1024, 4
+    bf = torch.bfloat16
+    qi = _randn((5, 1, 64, 128), 1 / math.sqrt(128), bf, 111)
+    ki = _randn((5, N_max, 128), 1 / math.sqrt(128), bf, 112)
+    pos = [4 * N_max + 3, 4 * 70000 + 1, 4 * 90000, 4 * N_max, 2]
+    ne = [N_max, 100001, 6000, 3, 100]
+    q_pos = torch.tensor([[p_] for p_ in pos], dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    ws = csa.new_workspace(csa.index_topk_workspace_bytes(5, 1, N_max, k), DEV)
+    QI, KI = np64(qi), np64(ki)
+    for call in range(2):
+        _say(f"fused selection, ragged rows: call {call}")
+        wi = _randn((5, 1, 64), 1 / 8, torch.float32, 113 + call)
+        idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k, workspace=ws)
+        torch.cuda.synchronize()
+        assert not ws[:4096].any(), "selection counters left non-zero"
+        I, W = np64(idx), np64(wi)
+        for b in range(5):
+            V = oracle.visible_count(pos[b], m, ne[b])
+            s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
+            check_topk(I[b, 0], s_ref, V, k)
+
+
 @pytest.mark.parametrize("B,Tq,N_max,k", [
     (2, 13, 2 * 2048 + 300, 300),   # prefill kernel; rows with and without a bound
-    (3, 1, 70000, 1024),            # decode kernel; long rows: filter + regions
+    (3, 1, 70000, 1024),            # decode kernel; few long rows (shared by workgroups)
     (1, 1, 20000, 2048),            # no bound (c > 16): the row overflows the LDS list
 ])
 def test_index_topk_bf16_scores_exact(B, Tq, N_max, k):
@@ -627,8 +657,8 @@ def test_bounded_selection_all_equal_long_rows(B, Tq, N):
     survivor list: the selection falls back to the whole row, where the
     counts of entries equal to the threshold exceed 16 bits.  The top-k of a
     constant row is its first k entries (ties to the lower index).  (2, 1,
-    262144): few long rows, filtered regions; (1, 72, 66560): more rows than
-    the region path takes, streamed rows."""
+    262144): few long rows, each shared by several workgroups; (1, 72,
+    66560): more rows than that path takes, one workgroup per row."""
     m, k = 4, 1024
     bf = torch.bfloat16
     _say(f"all-equal rows: B={B} Tq={Tq} N={N}")

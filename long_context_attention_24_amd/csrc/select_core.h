@@ -558,13 +558,28 @@ __device__ __forceinline__ float dpp_max_f32(float v) {
 }
 
 // Keys of the wave's slots [0, U1) that are >= mid (0: none): this lane's
-// count.
+// count, summed in four independent chains.
 template <int U1>
 __device__ __forceinline__ uint32_t keys_at_least(const uint32_t (&key)[kRepPerLane], uint32_t mid) {
-  uint32_t n = 0;
+  uint32_t n[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int u = 0; u < U1; ++u) n += key[u] >= mid ? 1u : 0u;
-  return n;
+  for (int u = 0; u < U1; ++u) n[u & 3] += key[u] >= mid ? 1u : 0u;
+  return (n[0] + n[1]) + (n[2] + n[3]);
+}
+
+// Bisection over [lo, hi) for the r-th largest of the keys in slots [0, U1)
+// (invariant: at least r keys >= lo, fewer than r keys >= hi; keys of finite
+// scores are below 0xff800000, so hi fits 32 bits).
+template <int U1>
+__device__ __forceinline__ uint32_t bisect_keys(const uint32_t (&key)[kRepPerLane], uint32_t lo,
+                                                uint32_t hi, uint32_t r) {
+#pragma unroll 1
+  for (int it = 0; it < kBoundSteps && hi - lo > 1; ++it) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (dpp_sum_u32(keys_at_least<U1>(key, mid)) >= r) lo = mid;
+    else hi = mid;
+  }
+  return lo;
 }
 __device__ __forceinline__ float2 row_bound(const float2 (&t)[kRepPerLane], int n_chunks, int c,
                                             int k) {
@@ -582,18 +597,12 @@ __device__ __forceinline__ float2 row_bound(const float2 (&t)[kRepPerLane], int 
                                                 : keys_at_least<kRepA>(key, 1u));
   const uint32_t r = static_cast<uint32_t>((k + c - 1) / c);
   if (cnt < r) return make_float2(kNegInf, mx);
-  // invariant: at least r keys >= lo, fewer than r keys >= hi
   uint32_t lo = dpp_min_u32(kmin);
-  if (cnt > r) {
-    uint64_t hi = static_cast<uint64_t>(dpp_max_u32(kmax)) + 1;
-    for (int it = 0; it < kBoundSteps && hi - lo > 1; ++it) {
-      const uint32_t mid = static_cast<uint32_t>(lo + ((hi - lo) >> 1));
-      const uint32_t n = dpp_sum_u32(ns > kRepB   ? keys_at_least<kRepPerLane>(key, mid)
-                                     : ns > kRepA ? keys_at_least<kRepB>(key, mid)
-                                                  : keys_at_least<kRepA>(key, mid));
-      if (n >= r) lo = mid;
-      else hi = mid;
-    }
+  if (cnt > r) {                                  // uniform; the slot count picked once
+    const uint32_t hi = dpp_max_u32(kmax) + 1;
+    lo = ns > kRepB   ? bisect_keys<kRepPerLane>(key, lo, hi, r)
+         : ns > kRepA ? bisect_keys<kRepB>(key, lo, hi, r)
+                      : bisect_keys<kRepA>(key, lo, hi, r);
   }
   return make_float2(f32_from_order_key(lo), mx);
 }

@@ -41,6 +41,7 @@ struct SelScratch {
   int bstar, bstar_above, bstar_cnt;
   float lo, hi;                       // a row's bound and top, shared by its waves
   int last;                           // this workgroup arrived last at the row's counter
+  uint32_t wcnt[kMaxWaves];           // survivors of each wave's own list
   uint32_t cand_n;                    // threshold candidates gathered so far
   float tval;
   int teq;
@@ -301,10 +302,50 @@ __device__ __forceinline__ void hist_add(SelScratch& sm, const HistRange& hr, fl
   if (key >= hr.klo && key <= hr.khi) atomicAdd(&sm.hist[(key - hr.klo) >> hr.shift], 1);
 }
 
-// Top-k of the survivor list lp[0..n) ((score bits, entry) pairs in
-// ascending entry order, values > -inf and -0.0 stored as +0.0, all within
-// [lo, hi] when have_range, else the range is computed here).  Emits
-// min(k, n) entries in ascending order and pads to k.
+// Survivor lists the selection reads, as (score bits, entry) pairs in LDS.
+// each(f) calls f on the values of this thread's share, in any order;
+// run(q0, q1) gives this thread's contiguous run of list positions, the runs
+// in thread order being the list in ascending entry order; at(q) reads one.
+template <int NT>
+struct FlatList {                  // one list lp[0, n)
+  const lds_u32x2* lp;
+  int n;
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) const {
+#pragma unroll 4
+    for (int j = static_cast<int>(threadIdx.x); j < n; j += NT) f(lval(lp, j));
+  }
+  __device__ __forceinline__ void run(int& q0, int& q1) const {
+    const int R = (n + NT - 1) / NT;
+    q0 = static_cast<int>(threadIdx.x) * R;
+    q1 = min(n, q0 + R);
+  }
+  __device__ __forceinline__ u32x2_t at(int q) const { return lp[q]; }
+};
+template <int CAP>
+struct WaveLists {                 // wave w's list at lp[w CAP, w CAP + cnt_w), in wave order
+  const lds_u32x2* lp;
+  int cnt;                         // this wave's count (wave-uniform)
+  int n;                           // all waves' (block-uniform)
+  __device__ __forceinline__ int base() const { return static_cast<int>(threadIdx.x >> 6) * CAP; }
+  template <typename F>
+  __device__ __forceinline__ void each(F&& f) const {
+    const int b = base();
+#pragma unroll 4
+    for (int q = static_cast<int>(threadIdx.x & 63); q < cnt; q += 64) f(lval(lp, b + q));
+  }
+  __device__ __forceinline__ void run(int& q0, int& q1) const {
+    const int R = (cnt + 63) / 64;
+    q0 = base() + static_cast<int>(threadIdx.x & 63) * R;
+    q1 = min(base() + cnt, q0 + R);
+  }
+  __device__ __forceinline__ u32x2_t at(int q) const { return lp[q]; }
+};
+
+// Top-k of the survivor list ls (n (score bits, entry) pairs in ascending
+// entry order, values > -inf and -0.0 stored as +0.0, all within [lo, hi]
+// when have_range, else the range is computed here).  Emits min(k, n)
+// entries in ascending order and pads to k.
 //   Threshold: radix selection on order-preserving keys, offset by the key
 //   of lo: each pass histograms (key - klo) >> shift into 2048 LDS bins, the
 //   shift taking the span of the keys still in play down to 11 bits, so at
@@ -320,25 +361,24 @@ __device__ __forceinline__ void hist_add(SelScratch& sm, const HistRange& hr, fl
 // Entry: the histogram is zero (or, with hist_ready, holds the first pass
 // over [lo, hi] as hist_add builds it), sm.cand_n is zero and a barrier
 // separates the list (and histogram) writes from this call.
-template <int NW, typename Out>
-__device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32x2* lp, int n,
-                                                   float lo, float hi, bool have_range, int k,
-                                                   int& p, const Out& out,
-                                                   bool hist_ready = false) {
+template <int NW, typename List, typename Out>
+__device__ __forceinline__ void select_sorted_list(SelScratch& sm, const List& ls, float lo,
+                                                   float hi, bool have_range, int k, int& p,
+                                                   const Out& out, bool hist_ready = false) {
   constexpr int NT = NW * 64;
   constexpr int BPT = kBins / NT;                 // histogram bins per thread
   const int tid = threadIdx.x;
+  const int n = ls.n;
   float T = kNegInf;
   int take_eq = 1 << 30;                          // n <= k: everything is taken
   if (n > k) {
     if (!have_range) {
       float mn = FLT_MAX, mx = -FLT_MAX;
       uint32_t unused = 0;
-      for (int j = tid; j < n; j += NT) {
-        const float x = lval(lp, j);
+      ls.each([&](float x) {
         mn = fminf(mn, x);
         mx = fmaxf(mx, x);
-      }
+      });
       block_minmax_count<NW>(sm, mn, mx, unused, p);
       lo = mn;
       hi = mx;
@@ -354,11 +394,10 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
       }
       const int shift = span < static_cast<uint32_t>(kBins) ? 0 : 21 - __builtin_clz(span);
       if (!(hist_ready && have_range && pass == 0)) {
-#pragma unroll 4
-        for (int j = tid; j < n; j += NT) {
-          const uint32_t key = f32_order_key(lval(lp, j));
+        ls.each([&](float x) {
+          const uint32_t key = f32_order_key(x);
           if (key >= klo && key <= khi) atomicAdd(&sm.hist[(key - klo) >> shift], 1);
-        }
+        });
       }
       __syncthreads();
       uint32_t h[BPT];
@@ -397,15 +436,13 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
       if (cnt <= kBrute) {
         // the need-th largest of the bin: the candidate with fewer than need
         // larger ones and at least need larger-or-equal ones
-#pragma unroll 4
-        for (int j = tid; j < n; j += NT) {
-          const float x = lval(lp, j);
+        ls.each([&](float x) {
           const uint32_t key = f32_order_key(x);
           if (key >= blo && key <= bhi) {
             const uint32_t slot = atomicAdd(&sm.cand_n, 1u);
             sm.tab[slot] = __float_as_uint(x);
           }
-        }
+        });
         __syncthreads();
         for (int c = tid; c < cnt; c += NT) {
           const float v = __uint_as_float(sm.tab[c]);
@@ -429,13 +466,13 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
       khi = bhi;
     }
   }
-  // ordered compaction over contiguous runs of R list positions per thread
-  const int R = (n + NT - 1) / NT;
-  const int j0 = tid * R, j1 = min(n, j0 + R);
+  // ordered compaction over contiguous runs of list positions per thread
+  int j0, j1;
+  ls.run(j0, j1);
   uint32_t gt = 0, eq = 0;
 #pragma unroll 4
   for (int j = j0; j < j1; ++j) {
-    const float x = lval(lp, j);
+    const float x = __uint_as_float(ls.at(j).x);
     gt += x > T ? 1u : 0u;
     eq += x == T ? 1u : 0u;
   }
@@ -444,7 +481,7 @@ __device__ __forceinline__ void select_sorted_list(SelScratch& sm, const lds_u32
   int eq_before = static_cast<int>(pre >> 16);
   int slot = static_cast<int>(pre & 0xffffu) + min(eq_before, take_eq);
   for (int j = j0; j < j1; ++j) {
-    const u32x2_t e = lp[j];
+    const u32x2_t e = ls.at(j);
     const float x = __uint_as_float(e.x);
     bool take = x > T;
     if (!take && x == T) {
@@ -653,14 +690,13 @@ __device__ __forceinline__ void load_round(const S* __restrict__ srow, int base,
 // ascending index order, keeping those >= bnd: rounds of NW * 64 * SL
 // entries, wave w owning the round's w-th contiguous segment with lane l
 // taking every 64th entry from l.  x holds the first round (loaded by the
-// caller with load_round at w * 64 * SL); with ONE_ROUND the caller
-// guarantees V <= that round, otherwise the next round's loads are issued
+// caller with load_round at w * 64 * SL); the next round's loads are issued
 // before the current round is compacted.  Per round: per-wave survivor
 // counts (ballots) -> block scan -> every wave writes its survivors at its
 // offset plus their rank among the wave's survivors (ballot + mbcnt).
 // Returns the number of survivors (block-uniform); a value above cap means
 // the list overflowed and is incomplete.  -0.0 is stored as +0.0.
-template <int NW, int SL, bool ONE_ROUND, typename S>
+template <int NW, int SL, typename S>
 __device__ __forceinline__ int stream_survivors(SelScratch& sm, const S* __restrict__ srow, int V,
                                                 int N_max, float bnd, lds_u32x2* lp, int cap,
                                                 float (&x)[SL], int& p) {
@@ -670,10 +706,8 @@ __device__ __forceinline__ int stream_survivors(SelScratch& sm, const S* __restr
   int n = 0;                                      // block-uniform
   for (int r0 = 0; r0 < V; r0 += kRoundLen) {
     float y[SL];
-    const bool more = !ONE_ROUND && r0 + kRoundLen < V;
-    if constexpr (!ONE_ROUND) {
-      if (more) load_round(srow, r0 + kRoundLen + wave * kWaveSeg, N_max, y);
-    }
+    const bool more = r0 + kRoundLen < V;
+    if (more) load_round(srow, r0 + kRoundLen + wave * kWaveSeg, N_max, y);
     const int sb = r0 + wave * kWaveSeg;
     if (sb + kWaveSeg > V) {                     // entries at or past V are not visible
 #pragma unroll
@@ -702,14 +736,53 @@ __device__ __forceinline__ int stream_survivors(SelScratch& sm, const S* __restr
             u32x2_t{__float_as_uint(x[s] + 0.0f), static_cast<uint32_t>(sb + 64 * s + lane)};
       o += static_cast<uint32_t>(__builtin_popcountll(msk));
     }
-    if constexpr (ONE_ROUND) {
-      break;
-    } else if (more) {
+    if (more) {
 #pragma unroll
       for (int s = 0; s < SL; ++s) x[s] = y[s];
     }
   }
   return n;
+}
+
+// One round of a wave's segment (entries sb + 64 s + lane, as load_round
+// lays them out) into the wave's own list lp[w CAP, ...), in ascending entry
+// order, keeping those >= bnd: the wave's ballots give each survivor its rank
+// among the wave's survivors, with no barrier and no exchange with the other
+// waves, so each wave compacts as soon as its own scores have arrived.
+// Every lane stores for every slot, a lane without a survivor (or with one
+// past CAP, counted but not kept: the caller checks the counts) into its own
+// spare entry lp[spare + tid], so the stores need no branch.  Returns the
+// wave's count (wave-uniform).  -0.0 is stored as +0.0.
+template <int CAP, int SL>
+__device__ __forceinline__ int stream_wave_list(int sb, int V, float bnd, lds_u32x2* lp,
+                                                int spare, float (&x)[SL]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (sb + 64 * SL > V) {                        // entries at or past V are not visible
+#pragma unroll
+    for (int s = 0; s < SL; ++s)
+      if (sb + 64 * s + lane >= V) x[s] = kNegInf;
+  }
+  lds_u32x2* wl = lp + wave * CAP;
+  // all ballots first, then their running counts on the scalar unit, so that
+  // no slot's position waits for the previous slot's ballot
+  uint64_t msk[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) msk[s] = __builtin_amdgcn_ballot_w64(x[s] >= bnd);
+  uint32_t off[SL];
+  uint32_t o = 0;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    off[s] = o;
+    o += static_cast<uint32_t>(__builtin_popcountll(msk[s]));
+  }
+  lds_u32x2* own = lp + spare + threadIdx.x;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const uint32_t pos = lanes_below(msk[s], off[s]);
+    lds_u32x2* dst = x[s] >= bnd && pos < static_cast<uint32_t>(CAP) ? wl + pos : own;
+    *dst = u32x2_t{__float_as_uint(x[s] + 0.0f), static_cast<uint32_t>(sb + 64 * s + lane)};
+  }
+  return static_cast<int>(o);
 }
 
 }  // namespace sel

@@ -180,12 +180,17 @@ __global__ __launch_bounds__(kSegThreads) void topk_seg_kernel(
 //   1. The row bound and the top of the survivors' range come from the chunk
 //      reports, every wave computing them on its own (sel::row_bound), the
 //      reports loaded next to the first score loads.
-//   2. Survivor list in LDS, in ascending index order, as (score bits, entry
-//      index) pairs.  Streamed rows (sel::stream_survivors): rounds of 16384
-//      scores, each lane loading 16 scalar scores (entries 64 s + lane of its
-//      wave's segment), the next round's loads in flight while the current
-//      one is compacted; per round the waves count their survivors with
-//      ballots, one block scan gives every wave its offset, and each
+//   2. Survivor lists in LDS, in ascending index order, as (score bits, entry
+//      index) pairs, each lane loading scalar scores (entries 64 s + lane of
+//      its wave's segment).  Rows of at most 32768 entries are read in one
+//      round of 32 scores per lane, and every wave compacts its segment into
+//      its own list as soon as its scores arrive (sel::stream_wave_list:
+//      ballots, mbcnt, branch-free stores), the wave lists in wave order
+//      being the row's survivors in index order (sel::WaveLists).  Longer
+//      rows stream in rounds of 16384 scores into one list
+//      (sel::stream_survivors), the next round's loads in flight while the
+//      current one is compacted; per round the waves count their survivors
+//      with ballots, one block scan gives every wave its offset, and each
 //      survivor's slot is that offset plus its rank among the wave's
 //      survivors (ballot + mbcnt).
 //   3. sel::select_sorted_list: a 2048-bin equal-width histogram over
@@ -201,6 +206,7 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 static_assert(kBins % kSelThreads == 0, "whole bins per thread");
 constexpr int kListCap = 16 * kSelThreads;        // survivors held in LDS
+constexpr int kWaveCap = kListCap / kSelWaves;    // per wave, for rows streamed in one round
 static_assert(kListCap < 65536, "select_sorted_list packs two list counts into one word");
 constexpr int kStreamSlots = 16;                  // scores per lane per round (64 apart)
 constexpr int kShortRow = 32768;                  // rows streamed in one round of 32 per thread
@@ -373,7 +379,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
     }
   }
   __syncthreads();                                // the list and first histogram are complete
-  sel::select_sorted_list<NW>(g_sm, lp, n, lo, hi, have_range, k, p, out, true);
+  sel::select_sorted_list<NW>(g_sm, sel::FlatList<NT>{lp, n}, lo, hi, have_range, k, p, out,
+                              true);
 }
 
 // One 1024-thread workgroup per row streams the row into a survivor list in
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
     float* __restrict__ out_val) {
   constexpr int NW = kSelWaves;
   constexpr bool kOneRound = SL * kSelThreads >= kShortRow;
-  __shared__ u32x2_t lp_s[kListCap];
+  __shared__ u32x2_t lp_s[kListCap + (kOneRound ? kSelThreads : 0)];   // + a spare entry per thread
   lds_u32x2* lp = (lds_u32x2*)lp_s;
   const int row = blockIdx.x, b = row / Tq;
   const int tid = threadIdx.x, wave = tid >> 6;
@@ -407,15 +414,31 @@ __global__ __launch_bounds__(kSelThreads) void topk_bounded_kernel(
   if (tid == 0) g_sm.cand_n = 0;
   int p = 0;
   const float bnd = rb.x > kNegInf ? rb.x : -FLT_MAX;       // x >= bnd: a finite survivor
-  const int n =                                             // block-uniform
-      sel::stream_survivors<NW, SL, kOneRound>(g_sm, srow, V, N_max, bnd, lp, kListCap, x, p);
-  __syncthreads();                                // the list is complete
+  const bool have_range = rb.x > kNegInf;         // survivors lie in [bound, largest report]
   sel::GlobalOut out{out_idx + static_cast<int64_t>(row) * k,
                      out_val ? out_val + static_cast<int64_t>(row) * k : nullptr};
-  if (n <= kListCap) {
-    const bool have_range = rb.x > kNegInf;       // survivors lie in [bound, largest report]
-    sel::select_sorted_list<NW>(g_sm, lp, n, rb.x, rb.y, have_range, k, p, out);
+  bool fits;
+  if constexpr (kOneRound) {
+    // every wave compacts into its own list as its scores arrive
+    const int cnt = sel::stream_wave_list<kWaveCap, SL>(wave * 64 * SL, V, bnd, lp, kListCap, x);
+    if ((tid & 63) == 0) g_sm.wcnt[wave] = static_cast<uint32_t>(cnt);
+    __syncthreads();                              // the lists are complete
+    const uint32_t c = (tid & 63) < NW ? g_sm.wcnt[tid & 63] : 0u;
+    const int n = static_cast<int>(sel::dpp_sum_u32(c));
+    fits = sel::dpp_max_u32(c) <= static_cast<uint32_t>(kWaveCap);
+    if (fits)
+      sel::select_sorted_list<NW>(g_sm, sel::WaveLists<kWaveCap>{lp, cnt, n}, rb.x, rb.y,
+                                  have_range, k, p, out);
   } else {
+    const int n =                                 // block-uniform
+        sel::stream_survivors<NW, SL>(g_sm, srow, V, N_max, bnd, lp, kListCap, x, p);
+    __syncthreads();                              // the list is complete
+    fits = n <= kListCap;
+    if (fits)
+      sel::select_sorted_list<NW>(g_sm, sel::FlatList<kSelThreads>{lp, n}, rb.x, rb.y,
+                                  have_range, k, p, out);
+  }
+  if (!fits) {
     const int n_sel = sel::block_select<NW>(
         g_sm, sel::GlobalRun<S>{srow, V, (V + kSelThreads - 1) / kSelThreads}, k, p, out);
     sel::pad_output<NW>(out, n_sel, k);

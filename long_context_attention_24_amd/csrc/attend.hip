@@ -442,15 +442,34 @@ __device__ __forceinline__ void split_attention(
   RoundRegs ra, rb;
   int ea = entry_raw(0), eb = entry_raw(1);
   // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
-  // (issued after the first entry indices, which the first loads wait for)
+  // (q issued after the first entry indices, which the first loads wait for)
   const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
-  bf16x8_t bq[8];
+  constexpr int kNT = 128 * KG;
+  constexpr int kQC = 64 * 128 / 8 / kNT;          // 16-byte chunks of q per thread
+  constexpr int kQPitch = 136;                     // bf16 per head row in LDS (padded)
+  static_assert(64 * kQPitch * 2 <= sizeof(sm.v[1]), "q staging area");
+  uint4 qc[kQC];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) bq[s] = ld_bf16x8(qrow + h * 128 + 16 * s + 8 * g);
+  for (int i = 0; i < kQC; ++i) qc[i] = ld16(qrow + 8 * (tid + kNT * i));
   load_round(Kb, Vb, kv_sn, entry_ok(0, ea), t128, ra);
   ea = entry_raw(2);
   load_round(Kb, Vb, kv_sn, entry_ok(1, eb), t128, rb);
   eb = entry_raw(3);
+  // q read once per workgroup and shared through the second tile buffer
+  // (not written until round 1 is staged, after the first barrier below)
+  lds_u16* qs = (lds_u16*)&sm.v[1][0][0];
+#pragma unroll
+  for (int i = 0; i < kQC; ++i) {
+    const int c = tid + kNT * i;                   // chunk c: head c / 16, dims 8 (c % 16)
+    *(lds_u32x4*)(qs + (c >> 4) * kQPitch + 8 * (c & 15)) = u32x4{qc[i].x, qc[i].y, qc[i].z, qc[i].w};
+  }
+  __syncthreads();
+  bf16x8_t bq[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const u32x4 w = *(const lds_u32x4*)(qs + h * kQPitch + 16 * s + 8 * g);
+    __builtin_memcpy(&bq[s], &w, 16);
+  }
   // q resident before the loop (rounds 0 and 1 stay in flight), so that no
   // wait inside the loop is computed as if it were still loading; the loop
   // runs at least once so that the loads above stay ahead of this point

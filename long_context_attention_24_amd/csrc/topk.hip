@@ -219,8 +219,9 @@ constexpr int kShortRow = 32768;                  // rows streamed in one round 
 // bound and the top of the survivors' range from the chunk reports while the
 // other waves' loads are in flight; every workgroup then compacts its entries
 // at or above the bound, in index order, to its segment of the survivor
-// buffer (one block scan of the wave counts), stores their number, and
-// arrives at the row's counter.  The workgroup that arrives last (no wait:
+// buffer (one block scan of the wave counts; a segment keeps at most
+// kFusedSegCap, and a row with a fuller segment takes the fallback), stores
+// their number, and arrives at the row's counter.  The workgroup that arrives last (no wait:
 // the others simply end) gathers the row's segments into an LDS list in
 // index order, one load per list position (the position's segment found by
 // binary search over the segment offsets), and selects from it with
@@ -230,6 +231,7 @@ constexpr int kShortRow = 32768;                  // rows streamed in one round 
 // the counters (one 64-byte line per row, at the front of the workspace)
 // are zero before and after every call.
 constexpr int kFusedSeg = kSelThreads / 64 * 256; // entries per workgroup
+constexpr int kFusedSegCap = 1024;                // survivors a segment keeps (more: fallback)
 constexpr int kFusedMaxRows = 64;
 constexpr int kFusedMinN = 65536;
 constexpr int kSyncStride = 16;                   // uint32 words per row's counter
@@ -299,12 +301,13 @@ __global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
   int p = 0;
   uint32_t seg_n;
   uint32_t q = sel::block_excl_scan<NW>(g_sm, cl, seg_n, p);
-  uint64_t* dst = seg_buf + (static_cast<int64_t>(row) * nseg + seg) * kFusedSeg;
+  uint64_t* dst = seg_buf + (static_cast<int64_t>(row) * nseg + seg) * kFusedSegCap;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     if (keep[e]) {
-      st_coherent(dst + q, static_cast<uint64_t>(__float_as_uint(v[e] + 0.0f)) |
-                               (static_cast<uint64_t>(e0 + e) << 32));
+      if (q < static_cast<uint32_t>(kFusedSegCap))   // the count keeps growing: see below
+        st_coherent(dst + q, static_cast<uint64_t>(__float_as_uint(v[e] + 0.0f)) |
+                                 (static_cast<uint64_t>(e0 + e) << 32));
       ++q;
     }
   }
@@ -322,20 +325,22 @@ __global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
   __syncthreads();
   if (g_sm.last == 0) return;                     // block-uniform
   // the last workgroup of the row: segment offsets (nseg <= 64: wave 0 scans),
-  // padded to 64 entries with an offset no list position reaches
+  // padded to 64 entries with an offset no list position reaches; a segment
+  // with more survivors than it kept sends the row to the fallback
   if (wave == 0) {
     const uint32_t c = lane < nseg ? ld_coherent(seg_cnt + static_cast<int64_t>(row) * nseg + lane) : 0u;
     const uint32_t incl = wave_incl_scan_u32(c);
     g_sm.tab[lane] = lane < nseg ? incl - c : 0x7fffffffu;
-    if (lane == 63) g_sm.cand_n = incl;           // the list length, read below
+    const bool over = __builtin_amdgcn_ballot_w64(c > static_cast<uint32_t>(kFusedSegCap)) != 0;
+    if (lane == 63) g_sm.cand_n = over ? 0xffffffffu : incl;   // the list length, read below
   }
   __syncthreads();
-  const int n = static_cast<int>(g_sm.cand_n);
+  const uint32_t nl = g_sm.cand_n;
   __syncthreads();
   if (tid == 0) g_sm.cand_n = 0;
   sel::GlobalOut out{out_idx + static_cast<int64_t>(row) * k,
                      out_val ? out_val + static_cast<int64_t>(row) * k : nullptr};
-  if (n > kListCap) {                             // far from the expected distribution
+  if (nl > static_cast<uint32_t>(kListCap)) {     // far from the expected distribution
     const int n_sel = sel::block_select<NW>(
         g_sm, sel::GlobalRun<S>{srow, V, (V + NT - 1) / NT}, k, p, out);
     sel::pad_output<NW>(out, n_sel, k);
@@ -344,7 +349,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
   // gather: list position j from segment s = the last with offset <= j; all
   // of a thread's loads in flight together; the first histogram pass of the
   // selection is built from the gathered values
-  const uint64_t* rowbuf = seg_buf + static_cast<int64_t>(row) * nseg * kFusedSeg;
+  const int n = static_cast<int>(nl);
+  const uint64_t* rowbuf = seg_buf + static_cast<int64_t>(row) * nseg * kFusedSegCap;
   constexpr int kG = kListCap / NT;
   constexpr int kQ = 4;                           // positions searched together
   uint64_t e[kG];
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
     for (int q = 0; q < kQ; ++q) {
       const int j = tid + (g0 + q) * NT;
       if (j < n)
-        e[g0 + q] = ld_coherent(rowbuf + static_cast<int64_t>(sg[q]) * kFusedSeg +
+        e[g0 + q] = ld_coherent(rowbuf + static_cast<int64_t>(sg[q]) * kFusedSegCap +
                                 (j - static_cast<int>(g_sm.tab[sg[q]])));
     }
   }
@@ -468,7 +474,7 @@ bool use_fused(int rows, int N_max) { return N_max > kFusedMinN && rows <= kFuse
 size_t topk_bounded_workspace_bytes(int rows, int N_max) {
   if (!topk_bounded_ok(N_max) || !use_fused(rows, N_max)) return 0;
   const size_t segs = static_cast<size_t>(rows) * fused_segments(N_max);
-  return segs * kFusedSeg * sizeof(uint64_t) + segs * sizeof(uint32_t);
+  return segs * kFusedSegCap * sizeof(uint64_t) + segs * sizeof(uint32_t);
 }
 
 size_t topk_sync_bytes() { return static_cast<size_t>(kFusedMaxRows) * kSyncStride * sizeof(uint32_t); }
@@ -493,7 +499,8 @@ hipError_t launch_topk_bounded(const S* scores, int64_t s_rs, const int32_t* q_p
   // survivor segments at the front of ws, then their counts
   const int nseg = fused_segments(N_max);
   uint64_t* seg_buf = static_cast<uint64_t*>(ws);
-  uint32_t* seg_cnt = reinterpret_cast<uint32_t*>(seg_buf + static_cast<size_t>(rows) * nseg * kFusedSeg);
+  uint32_t* seg_cnt =
+      reinterpret_cast<uint32_t*>(seg_buf + static_cast<size_t>(rows) * nseg * kFusedSegCap);
   hipLaunchKernelGGL(topk_fused_kernel<S>, dim3(nseg, rows), dim3(kSelThreads), 0, s, scores,
                      s_rs, q_pos, n_entries, Tq, N_max, m, k, chunk_rep, n_chunks, nseg, seg_buf,
                      seg_cnt, sync, idx, out_scores);

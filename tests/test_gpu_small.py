@@ -332,6 +332,32 @@ def test_fused_selection_ragged_rows_and_reuse():
             check_topk(I[b, 0], s_ref, V, k)
 
 
+def test_fused_selection_crowded_segment():
+    """Few long rows where one 4096-entry stretch holds far more survivors
+    than a segment keeps (3,500 of its keys scaled by 8: the positive-scoring
+    ones, some 1,400, clear the row bound): that row takes the exact
+    fallback, the other row the shared path.  Both against the oracle's exact
+    top-k."""
+    N_max, k, m = 140000, 1024, 4
+    bf = torch.bfloat16
+    _say("fused selection: a crowded segment")
+    qi = _randn((2, 1, 64, 128), 1 / math.sqrt(128), bf, 121)
+    ki = _randn((2, N_max, 128), 1 / math.sqrt(128), torch.float32, 122)
+    ki[0, 8192:8192 + 3500] *= 8.0
+    ki = ki.to(bf)
+    wi = _randn((2, 1, 64), 1 / 8, torch.float32, 123)
+    q_pos = torch.full((2, 1), 4 * N_max + 3, dtype=torch.int32, device=DEV)
+    n_ent = torch.full((2,), N_max, dtype=torch.int32, device=DEV)
+    idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k)
+    torch.cuda.synchronize()
+    I, QI, KI, W = np64(idx), np64(qi), np64(ki), np64(wi)
+    for b in range(2):
+        s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], N_max)
+        check_topk(I[b, 0], s_ref, N_max, k)
+    hot = (I[0, 0] >= 8192) & (I[0, 0] < 8192 + 3500)
+    assert hot.sum() > 500, "the crowded stretch should dominate row 0's selection"
+
+
 @pytest.mark.parametrize("B,Tq,N_max,k", [
     (2, 13, 2 * 2048 + 300, 300),   # prefill kernel; rows with and without a bound
     (3, 1, 70000, 1024),            # decode kernel; few long rows (shared by workgroups)

@@ -221,11 +221,11 @@ constexpr int kShortRow = 32768;                  // rows streamed in one round 
 // at or above the bound, in index order, to its segment of the survivor
 // buffer (one block scan of the wave counts; a segment keeps at most
 // kFusedSegCap, and a row with a fuller segment takes the fallback), stores
-// their number, and arrives at the row's counter.  The workgroup that arrives last (no wait:
-// the others simply end) gathers the row's segments into an LDS list in
-// index order, one load per list position (the position's segment found by
-// binary search over the segment offsets), and selects from it with
-// sel::select_sorted_list.  Survivor stores, counts and the gather's loads
+// their number, and arrives at the row's counter.  The workgroup that
+// arrives last (no wait: the others simply end) gathers the row's segments
+// into an LDS list in index order, one load per list position (the
+// position's segment found by binary search over the segment offsets), and
+// selects from it with sel::select_sorted_list.  Survivor stores, counts and the gather's loads
 // are device-coherent (they bypass the per-XCD L2), each workgroup's stores
 // complete before it arrives, and the last workgroup resets the counter, so
 // the counters (one 64-byte line per row, at the front of the workspace)
@@ -328,7 +328,8 @@ __global__ __launch_bounds__(kSelThreads) void topk_fused_kernel(
   // padded to 64 entries with an offset no list position reaches; a segment
   // with more survivors than it kept sends the row to the fallback
   if (wave == 0) {
-    const uint32_t c = lane < nseg ? ld_coherent(seg_cnt + static_cast<int64_t>(row) * nseg + lane) : 0u;
+    const uint32_t c =
+        lane < nseg ? ld_coherent(seg_cnt + static_cast<int64_t>(row) * nseg + lane) : 0u;
     const uint32_t incl = wave_incl_scan_u32(c);
     g_sm.tab[lane] = lane < nseg ? incl - c : 0x7fffffffu;
     const bool over = __builtin_amdgcn_ballot_w64(c > static_cast<uint32_t>(kFusedSegCap)) != 0;
@@ -477,7 +478,9 @@ size_t topk_bounded_workspace_bytes(int rows, int N_max) {
   return segs * kFusedSegCap * sizeof(uint64_t) + segs * sizeof(uint32_t);
 }
 
-size_t topk_sync_bytes() { return static_cast<size_t>(kFusedMaxRows) * kSyncStride * sizeof(uint32_t); }
+size_t topk_sync_bytes() {
+  return static_cast<size_t>(kFusedMaxRows) * kSyncStride * sizeof(uint32_t);
+}
 
 template <typename S>
 hipError_t launch_topk_bounded(const S* scores, int64_t s_rs, const int32_t* q_pos,

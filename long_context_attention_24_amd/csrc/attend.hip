@@ -121,7 +121,10 @@ constexpr int kCsaSplit = 128;     // entries of the top-k list per workgroup
 constexpr int kCsaGroups = 2;      // key groups per CSA workgroup (4 waves)
 constexpr int kHcaSplit = 1024;    // visible entries per workgroup
 constexpr int kHcaGroups = 4;      // key groups per HCA workgroup (8 waves)
-constexpr int kPartRows = 130;     // per (query, split): O^T[128][64], then m[64], l[64]
+// Partial of one (query, split): 66 rows of 64 32-bit words, O^T as bf16
+// pairs of dims (row d / 2 holds dims d, d + 1 of the 64 heads), then the
+// running maximum m and sum l in fp32.
+constexpr int kPartRows = 66;
 constexpr int kVPitch = 160;       // bf16 per V row in LDS (256 B + 64 B pad)
 constexpr int kKPitch = 136;       // bf16 per K row in LDS (256 B + 16 B pad)
 constexpr float kRescaleLog2 = 8.f; // probabilities stay below 2^8 between rescales
@@ -314,9 +317,10 @@ __device__ __forceinline__ void row_barrier(int32_t* sync, int rows, int row, in
 // Split s of nsplit merges output dims [d0, d1), d0 = s * Ld, Ld = ceil(128 /
 // nsplit) rounded up to a multiple of 4.  Thread (h, grp) owns dims
 // db .. db + 3 of head h for db = d0 + 4 grp, d0 + 4 (grp + NT / 64), ...:
-// every load is a coalesced 64-float row of a partial.  Splits are taken in
-// groups of eight, every load of a group issued before its arithmetic, and
-// the running maximum rescales what is already summed.
+// every load is a coalesced 64-word row of a partial (two bf16 dims per
+// word, or m or l).  Splits are taken in groups of eight, every load of a
+// group issued before its arithmetic, and the running maximum rescales what
+// is already summed.
 template <int NT>
 __device__ __forceinline__ void merge_splits(const float* __restrict__ prow, int nsplit, int split,
                                              uint16_t* __restrict__ orow, float* __restrict__ lrow) {
@@ -337,10 +341,14 @@ __device__ __forceinline__ void merge_splits(const float* __restrict__ prow, int
         const bool ok = s0 + u < nsplit;
         const float* ps = prow + static_cast<int64_t>(ok ? s0 + u : s0) * sstride + h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[u][i] = ld_coherent(ps + (db + i) * 64);
-        const float mu = ld_coherent(ps + 128 * 64);
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t w = __float_as_uint(ld_coherent(ps + (db / 2 + i) * 64));
+          v[u][2 * i] = __uint_as_float(w << 16);
+          v[u][2 * i + 1] = __uint_as_float(w & 0xffff0000u);
+        }
+        const float mu = ld_coherent(ps + 64 * 64);
         ms[u] = ok ? mu : kNegInf;
-        ls[u] = ld_coherent(ps + 129 * 64);
+        ls[u] = ld_coherent(ps + 65 * 64);
       }
       float mg = M;
 #pragma unroll
@@ -562,20 +570,23 @@ __device__ __forceinline__ void split_attention(
       return;
     }
     // partial of this split, stored coherently at device scope (read by the
-    // other workgroups of the row): O^T d-major, then m and l
+    // other workgroups of the row): O^T d-major as bf16 pairs (rounded to
+    // nearest even: the merge's output is bf16 too, and halving the bytes
+    // every split stores and every split reads back shortens the row's
+    // tail), then m and l in fp32
     float* pr = part + (static_cast<int64_t>(row) * nsplit + split) * kPartRows * 64;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
       if (dt % KG != kg) continue;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);
-        st_coherent(pr + d * 64 + h, vals[dt][i]);
+      for (int i = 0; i < 16; i += 2) {
+        const int d = 32 * dt + 8 * (i >> 2) + 4 * g + (i & 3);   // even
+        st_coherent(pr + (d / 2) * 64 + h, __uint_as_float(pack_bf16x2(vals[dt][i], vals[dt][i + 1])));
       }
     }
     if (kg == 0 && g == 0) {
-      st_coherent(pr + 128 * 64 + h, M);
-      st_coherent(pr + 129 * 64 + h, L);
+      st_coherent(pr + 64 * 64 + h, M);
+      st_coherent(pr + 65 * 64 + h, L);
     }
   }
   row_barrier(sync, rows, row, nsplit);

@@ -278,7 +278,8 @@ __device__ __forceinline__ void compute_round(uint32_t vmask, bool active, const
 // the front of the workspace (separate lines keep the rows' atomics apart),
 // holding the row's arrivals, departures and a count of waits that gave up;
 // zero before the first call, and every call leaves them zero (the last
-// workgroup of a row to leave the barrier resets the row's two counters).
+// workgroup of a row to depart, after its merge, resets the row's two
+// counters).
 // The wait is bounded so that a kernel always ends.  The splits of a row are
 // consecutive workgroups and dispatch follows workgroup order, so a waiting
 // workgroup only ever waits for workgroups that are already running.
@@ -292,12 +293,11 @@ __device__ __forceinline__ float ld_coherent(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void row_barrier(int32_t* sync, int rows, int row, int n) {
+__device__ __forceinline__ void row_barrier(int32_t* sync, int row, int n) {
   __builtin_amdgcn_s_waitcnt(0);                  // this thread's partial stores are complete
   __syncthreads();
   if (threadIdx.x == 0) {
     int32_t* arrive = sync + kSyncStride * row;     // one 128-byte line per row
-    int32_t* depart = arrive + 1;
     __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     for (int it = 0; __hip_atomic_load(arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < n; ++it) {
       if (it == kSpinLimit) {
@@ -306,12 +306,24 @@ __device__ __forceinline__ void row_barrier(int32_t* sync, int rows, int row, in
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    if (__hip_atomic_fetch_add(depart, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n - 1) {
-      __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(depart, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
   }
   __syncthreads();
+}
+// Departure, issued by thread 0 right after the barrier (no barrier follows
+// it, so its round trip overlaps the merge) and checked after the merge: the
+// row's last workgroup to depart resets the two counters.
+__device__ __forceinline__ int row_depart_issue(int32_t* sync, int row) {
+  return threadIdx.x == 0
+             ? __hip_atomic_fetch_add(sync + kSyncStride * row + 1, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT)
+             : 0;
+}
+__device__ __forceinline__ void row_depart_finish(int32_t* sync, int row, int n, int departed) {
+  if (threadIdx.x == 0 && departed == n - 1) {
+    int32_t* arrive = sync + kSyncStride * row;
+    __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(arrive + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // Split s of nsplit merges output dims [d0, d1), d0 = s * Ld, Ld = ceil(128 /
@@ -589,10 +601,12 @@ __device__ __forceinline__ void split_attention(
       st_coherent(pr + 65 * 64 + h, L);
     }
   }
-  row_barrier(sync, rows, row, nsplit);
+  row_barrier(sync, row, nsplit);
+  const int departed = row_depart_issue(sync, row);
   merge_splits<128 * KG>(part + static_cast<int64_t>(row) * nsplit * kPartRows * 64, nsplit, split,
                          out + static_cast<int64_t>(row) * 64 * 128,
                          lse != nullptr ? lse + static_cast<int64_t>(row) * 64 : nullptr);
+  row_depart_finish(sync, row, nsplit, departed);
 }
 
 // One workgroup per (split, query row): CSA over the caller's top-k lists, or

@@ -120,6 +120,7 @@ __global__ __launch_bounds__(kGenThreads) void attend_generic_kernel(
 constexpr int kCsaSplit = 128;     // entries of the top-k list per workgroup
 constexpr int kCsaGroups = 2;      // key groups per CSA workgroup (4 waves)
 constexpr int kHcaSplit = 1024;    // visible entries per workgroup
+constexpr int kSwaSplit = 512;     // window entries per workgroup (HCA with a window)
 constexpr int kHcaGroups = 4;      // key groups per HCA workgroup (8 waves)
 // Partial of one (query, split): 66 rows of 64 32-bit words, O^T as bf16
 // pairs of dims (row d / 2 holds dims d, d + 1 of the 64 heads), then the
@@ -688,7 +689,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const T* __restrict__ oa, co
 
 bool tuned(csa_dtype_t dt, int H, int D) { return dt == CSA_BF16 && H == 64 && D == 128; }
 
-int split_len(bool hca) { return hca ? kHcaSplit : kCsaSplit; }
+// Entries per workgroup.  A window caps the entries of a row, so windowed
+// calls take shorter splits to fill the chip at decode batch sizes; the
+// length depends on the call's mode only, never on its batch, so a row's
+// result does not change with the batch it is computed in.
+int split_len(bool hca, int win) { return hca ? (win > 0 ? kSwaSplit : kHcaSplit) : kCsaSplit; }
 
 template <typename T, int D, bool HCA>
 void launch_generic(const AttendArgs& a, float scale_log2, hipStream_t s) {
@@ -722,18 +727,19 @@ size_t attend_sync_block_bytes(int rows) {
   return (static_cast<size_t>(kSyncStride) * rows * sizeof(int32_t) + 255) / 256 * 256;
 }
 
-size_t attend_part_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax) {
+size_t attend_part_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax,
+                         int win) {
   if (!tuned(dt, H, D)) return 0;
-  const int sl = split_len(hca);
+  const int sl = split_len(hca, win);
   const int nsplit = (k_or_nmax + sl - 1) / sl;
   return static_cast<size_t>(B) * Tq * (nsplit < 1 ? 1 : nsplit) * kPartRows * 64 * sizeof(float);
 }
 
 size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D,
-                              int k_or_nmax) {
+                              int k_or_nmax, int win) {
   if (!tuned(dt, H, D)) return 0;
   return attend_sync_block_bytes(kAttendMaxRows) +
-         attend_part_bytes(dt, hca, B, Tq, H, D, k_or_nmax);
+         attend_part_bytes(dt, hca, B, Tq, H, D, k_or_nmax, win);
 }
 
 bool attend_rows_ok(int B, int Tq) {
@@ -752,7 +758,7 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
     }
     return hipGetLastError();
   }
-  const int sl = split_len(hca);
+  const int sl = split_len(hca, a.win);
   const int n = hca ? (a.win > 0 ? min(a.win, a.N_max) : a.N_max) : a.topk;
   int nsplit = (n + sl - 1) / sl;
   if (nsplit < 1) nsplit = 1;

@@ -508,8 +508,8 @@ csa_status_t swa_attend_workspace(csa_dtype_t dtype, int B, int Tq, int H, int D
   CSA_REQUIRE(bytes, CSA_ERR_INVALID_ARGUMENT, "swa workspace: NULL result");
   CSA_REQUIRE(B >= 1 && Tq >= 1 && H >= 1 && D >= 1 && N_max >= 1 && window >= 1,
               CSA_ERR_INVALID_ARGUMENT, "swa workspace: sizes must be >= 1");
-  *bytes = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D,
-                                      window < N_max ? window : N_max);
+  const int wn = window < N_max ? window : N_max;
+  *bytes = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D, wn, wn);
   return CSA_OK;
 }
 
@@ -523,7 +523,7 @@ csa_status_t swa_attend(const void* q, const void* k, const void* v, int64_t kv_
   if (st != CSA_OK) return st;
   CSA_REQUIRE(q_pos && window >= 1, CSA_ERR_INVALID_ARGUMENT, "swa: bad q_pos / window");
   const int wn = window < N_max ? window : N_max;
-  const size_t need = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D, wn);
+  const size_t need = csa::attend_workspace_bytes(dtype, true, B, Tq, H, D, wn, wn);
   CSA_REQUIRE(ws_bytes >= need && (need == 0 || (ws && aligned16(ws))),
               CSA_ERR_WORKSPACE_TOO_SMALL, "swa: workspace %zu < %zu bytes", ws_bytes, need);
   csa::AttendArgs a{q, k, v, kv_sb, kv_sn, nullptr, q_pos, n_tokens, B, Tq, H, D,

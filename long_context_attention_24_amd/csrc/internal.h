@@ -91,15 +91,18 @@ struct AttendArgs {
   float* part = nullptr;    // and partials (attend_part_bytes)
 };
 constexpr int kAttendMaxRows = 65536;   // B * Tq of the tuned kernels (the grid's y extent)
-// k_or_nmax: k (CSA), N_max (HCA) or min(window, N_max) (HCA with a window).
+// k_or_nmax: k (CSA), N_max (HCA) or min(window, N_max) (HCA with a window);
+// win: that min(window, N_max) for a windowed call, else 0.
 // The tuned path's workspace starts with merge counters that must be zero
 // before a call; every call leaves them zero.
-size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax);
+size_t attend_workspace_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax,
+                              int win = 0);
 bool attend_rows_ok(int B, int Tq);   // B * Tq within the tuned kernels' row limit
 // Explicit layout (AttendArgs::sync / part): counters for `rows` query rows
 // and the split partials of the tuned path (both 0 for the generic path).
 size_t attend_sync_block_bytes(int rows);
-size_t attend_part_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax);
+size_t attend_part_bytes(csa_dtype_t dt, bool hca, int B, int Tq, int H, int D, int k_or_nmax,
+                         int win = 0);
 
 bool attend_supported(csa_dtype_t dt, int H, int D);
 hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStream_t s);

@@ -152,27 +152,47 @@ struct RoundRegs {
   uint32_t vmask;                    // bit j: tile row j holds a valid entry
 };
 
-// ej: this lane's entry for tile row jl (lanes 0..31 and 32..63 agree), -1 if
-// none; a chunk's row takes its entry from lane (row) by a shuffle.  Every
-// load is issued: a row without an entry reads row 0 (in bounds, as N_max is
-// at least 1); its V chunk is zeroed when it is staged (probability 0 times a
-// non-finite value would not be 0) and its K chunk only feeds a score that
-// the mask drops.  Branch-free loads whose values are first used at staging
-// keep the compiler's count of loads in flight exact, so that waiting for
-// one round never waits for the round after it.
-__device__ __forceinline__ void load_round(const uint16_t* __restrict__ Kb,
-                                           const uint16_t* __restrict__ Vb, int64_t kv_sn, int ej,
-                                           int t128, RoundRegs& rr) {
-  rr.vmask = static_cast<uint32_t>(__ballot(ej >= 0));
+// ea: the cache row this lane's tile row jl reads (lanes 0..31 and 32..63
+// agree; 0 <= ea < N_max); a chunk's row takes it from lane (row) by a
+// shuffle.  Only the loads: the validity mask is set by the caller.
+__device__ __forceinline__ void issue_round(const uint16_t* __restrict__ Kb,
+                                            const uint16_t* __restrict__ Vb, int64_t kv_sn, int ea,
+                                            int t128, RoundRegs& rr) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int pair = t128 + 128 * it;
     const int vr = pair >> 4, ch = pair & 15;
-    const int ev = __shfl(ej, vr, 64);
-    const int64_t off = static_cast<int64_t>(ev < 0 ? 0 : ev) * kv_sn + 8 * ch;
+    const int64_t off = static_cast<int64_t>(__shfl(ea, vr, 64)) * kv_sn + 8 * ch;
     rr.kv[it] = ld16(Kb + off);
     rr.vv[it] = ld16(Vb + off);
   }
+}
+// The same for rows base + r of tile row r, clamped into the cache: no
+// cross-lane step (its LDS wait would also wait for scalar loads in flight).
+__device__ __forceinline__ void issue_round_rows(const uint16_t* __restrict__ Kb,
+                                                 const uint16_t* __restrict__ Vb, int64_t kv_sn,
+                                                 int base, int N_max, int t128, RoundRegs& rr) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int pair = t128 + 128 * it;
+    const int vr = pair >> 4, ch = pair & 15;
+    const int64_t off = static_cast<int64_t>(min(base + vr, N_max - 1)) * kv_sn + 8 * ch;
+    rr.kv[it] = ld16(Kb + off);
+    rr.vv[it] = ld16(Vb + off);
+  }
+}
+// ej: this lane's entry for tile row jl, -1 if none.  Every load is issued:
+// a row without an entry reads row 0 (in bounds, as N_max is at least 1);
+// its V chunk is zeroed when it is staged (probability 0 times a non-finite
+// value would not be 0) and its K chunk only feeds a score that the mask
+// drops.  Branch-free loads whose values are first used at staging keep the
+// compiler's count of loads in flight exact, so that waiting for one round
+// never waits for the round after it.
+__device__ __forceinline__ void load_round(const uint16_t* __restrict__ Kb,
+                                           const uint16_t* __restrict__ Vb, int64_t kv_sn, int ej,
+                                           int t128, RoundRegs& rr) {
+  rr.vmask = static_cast<uint32_t>(__ballot(ej >= 0));
+  issue_round(Kb, Vb, kv_sn, ej < 0 ? 0 : ej, t128, rr);
 }
 
 // One key group of the workgroup processes one 32-entry tile per round:
@@ -405,33 +425,65 @@ struct GlobalIdxSrc {              // CSA: the caller's top-k list in global mem
   int kk;
   __device__ __forceinline__ int raw(int p) const { return irow[min(p, kk - 1)]; }
 };
-template <bool HCA, int KG, typename Src>
+template <bool HCA, int KG, bool WIN, typename Src>
 __device__ __forceinline__ void split_attention(
     AttnSmem<KG>& sm, const Src& src, int split, int row, const uint16_t* __restrict__ q,
     const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn,
-    int kk, const int32_t* __restrict__ q_pos, const int32_t* __restrict__ n_entries, int Tq,
-    int N_max, int m, int win, float scale_log2, int split_len, int nsplit,
-    float* __restrict__ part, int32_t* __restrict__ sync, int rows, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    int kk, int qp, int ne, int Tq, int N_max, int m, int win, float scale_log2, int split_len,
+    int nsplit, float* __restrict__ part, int32_t* __restrict__ sync, int rows,
+    uint16_t* __restrict__ out, float* __restrict__ lse) {
   const int b = row / Tq;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = wave & 1, kg = wave >> 1;
   const int jl = lane & 31, g = lane >> 5;
   const int t128 = hh * 64 + lane;
   const int h = 32 * hh + jl;        // this lane's head (S^T / O^T column)
-  const int n_ent = min(n_entries[b], N_max);
-  const int nv = HCA ? visible_count(q_pos[row], m, n_entries[b], N_max) : kk;
+  const int s0 = split * split_len;
+  const uint16_t* Kb = K + b * kv_sb;
+  const uint16_t* Vb = Vc + b * kv_sb;
+
+  // Loads that need no scalar value from memory go out first: q, then the
+  // first two rounds' index-list entries (CSA) or, without a window, their
+  // cache rows (HCA: a position is its entry, so the rows are known; rows
+  // clamped into the cache, validity applied once q_pos and n_entries are
+  // in).  The scheduling barrier keeps the loads of those two values, and
+  // every wait for them, behind these loads.
+  // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
+  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
+  constexpr int kNT = 128 * KG;
+  constexpr int kQC = 64 * 128 / 8 / kNT;          // 16-byte chunks of q per thread
+  constexpr int kQPitch = 136;                     // bf16 per head row in LDS (padded)
+  static_assert(64 * kQPitch * 2 <= sizeof(sm.v[1]), "q staging area");
+  uint4 qc[kQC];
+#pragma unroll
+  for (int i = 0; i < kQC; ++i) qc[i] = ld16(qrow + 8 * (tid + kNT * i));
+  // Two register sets, rounds taken in pairs (an odd count ends with an
+  // empty round).  Loads, including those of rounds past the end (no
+  // entries), are issued on every path, with no branch around them: the
+  // compiler then counts the loads in flight exactly and waiting for one
+  // round never waits for a later one.
+  RoundRegs ra, rb;
+  const int p0 = s0 + 32 * kg + jl, p1 = p0 + 32 * KG;   // tile row jl of rounds 0 and 1
+  int ea = 0, eb = 0;
+  if constexpr (HCA && !WIN) {
+    issue_round_rows(Kb, Vb, kv_sn, s0 + 32 * kg, N_max, t128, ra);
+    issue_round_rows(Kb, Vb, kv_sn, s0 + 32 * (KG + kg), N_max, t128, rb);
+  } else if constexpr (!HCA) {
+    ea = src.raw(p0);
+    eb = src.raw(p1);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  const int n_ent = min(ne, N_max);
+  const int nv = HCA ? visible_count(qp, m, ne, N_max) : kk;
   // HCA with a window: positions count from lo, the first of the last win
   // visible entries (splits laid over the window, not the whole cache)
-  const int lo = HCA && win > 0 ? max(0, nv - win) : 0;
+  const int lo = HCA && WIN ? max(0, nv - win) : 0;
   const int n = nv - lo;
-  const int s0 = split * split_len;
   const int s_end = min(n, s0 + split_len);
   const int ntiles = s_end > s0 ? (s_end - s0 + 31) / 32 : 0;
   const int nrounds = (ntiles + KG - 1) / KG;
 
-  const uint16_t* Kb = K + b * kv_sb;
-  const uint16_t* Vb = Vc + b * kv_sb;
   f32x16_t o[4] = {};
   float m_run = kNegInf, l_run = 0.f;
   lds_u16* const vt0 = (lds_u16*)&sm.v[0][kg][0];
@@ -455,26 +507,18 @@ __device__ __forceinline__ void split_attention(
     return ok ? e : -1;
   };
 
-  // Two register sets, rounds taken in pairs (an odd count ends with an
-  // empty round).  Loads, including those of rounds past the end (no
-  // entries), are issued on every path, with no branch around them: the
-  // compiler then counts the loads in flight exactly and waiting for one
-  // round never waits for a later one.
-  RoundRegs ra, rb;
-  int ea = entry_raw(0), eb = entry_raw(1);
-  // B operand: q^T for this wave's 32 heads, 8 k-steps; dims 16s + 8g + e
-  // (q issued after the first entry indices, which the first loads wait for)
-  const uint16_t* qrow = q + static_cast<int64_t>(row) * 64 * 128;
-  constexpr int kNT = 128 * KG;
-  constexpr int kQC = 64 * 128 / 8 / kNT;          // 16-byte chunks of q per thread
-  constexpr int kQPitch = 136;                     // bf16 per head row in LDS (padded)
-  static_assert(64 * kQPitch * 2 <= sizeof(sm.v[1]), "q staging area");
-  uint4 qc[kQC];
-#pragma unroll
-  for (int i = 0; i < kQC; ++i) qc[i] = ld16(qrow + 8 * (tid + kNT * i));
-  load_round(Kb, Vb, kv_sn, entry_ok(0, ea), t128, ra);
+  if constexpr (HCA && !WIN) {
+    ra.vmask = static_cast<uint32_t>(__ballot(entry_ok(0, p0) >= 0));
+    rb.vmask = static_cast<uint32_t>(__ballot(entry_ok(1, p1) >= 0));
+  } else {
+    if constexpr (HCA) {
+      ea = lo + p0;
+      eb = lo + p1;
+    }
+    load_round(Kb, Vb, kv_sn, entry_ok(0, ea), t128, ra);
+    load_round(Kb, Vb, kv_sn, entry_ok(1, eb), t128, rb);
+  }
   ea = entry_raw(2);
-  load_round(Kb, Vb, kv_sn, entry_ok(1, eb), t128, rb);
   eb = entry_raw(3);
   // q read once per workgroup and shared through the second tile buffer
   // (not written until round 1 is staged, after the first barrier below)
@@ -612,7 +656,7 @@ __device__ __forceinline__ void split_attention(
 
 // One workgroup per (split, query row): CSA over the caller's top-k lists, or
 // HCA / a sliding window over the visible entries.
-template <bool HCA, int KG>
+template <bool HCA, int KG, bool WIN>
 __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ Vc, int64_t kv_sb, int64_t kv_sn, const int32_t* __restrict__ idx,
@@ -622,10 +666,18 @@ __global__ __launch_bounds__(128 * KG, 4 / KG) void attend_split_kernel(
     float* __restrict__ lse) {
   __shared__ AttnSmem<KG> sm;
   const int row = blockIdx.y;
+  // Every argument goes into registers before its first use, so that the
+  // argument loads go out together (one round trip instead of one per first
+  // use); then the two values read from memory.
+  asm volatile("" ::"s"(q), "s"(K), "s"(Vc), "s"(kv_sb), "s"(kv_sn), "s"(idx), "s"(kk), "s"(q_pos),
+               "s"(n_entries), "s"(Tq), "s"(N_max), "s"(m), "s"(win), "s"(scale_log2),
+               "s"(split_len), "s"(nsplit), "s"(part), "s"(sync), "s"(rows), "s"(out), "s"(lse));
+  const int qp = HCA ? q_pos[row] : 0;
+  const int ne = n_entries[row / Tq];
   const GlobalIdxSrc src{HCA ? idx : idx + static_cast<int64_t>(row) * kk, kk};
-  split_attention<HCA, KG>(sm, src, blockIdx.x, row, q, K, Vc, kv_sb, kv_sn, kk, q_pos, n_entries,
-                           Tq, N_max, m, win, scale_log2, split_len, nsplit, part, sync, rows, out,
-                           lse);
+  split_attention<HCA, KG, WIN>(sm, src, blockIdx.x, row, q, K, Vc, kv_sb, kv_sn, kk, qp, ne, Tq,
+                                N_max, m, win, scale_log2, split_len, nsplit, part, sync, rows,
+                                out, lse);
 }
 
 
@@ -769,14 +821,20 @@ hipError_t launch_attend(const AttendArgs& a, csa_dtype_t dt, bool hca, hipStrea
                                                              attend_sync_block_bytes(kAttendMaxRows));
   uint16_t* out = static_cast<uint16_t*>(a.out);
   const dim3 grid(nsplit, rows);
-  if (hca)
-    hipLaunchKernelGGL((attend_split_kernel<true, kHcaGroups>), grid, dim3(128 * kHcaGroups), 0, s,
-                       static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
+  if (hca && a.win > 0)
+    hipLaunchKernelGGL((attend_split_kernel<true, kHcaGroups, true>), grid, dim3(128 * kHcaGroups),
+                       0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
+                       static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
+                       a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part, sync, rows,
+                       out, a.lse);
+  else if (hca)
+    hipLaunchKernelGGL((attend_split_kernel<true, kHcaGroups, false>), grid, dim3(128 * kHcaGroups),
+                       0, s, static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
                        a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part, sync, rows,
                        out, a.lse);
   else
-    hipLaunchKernelGGL((attend_split_kernel<false, kCsaGroups>), grid, dim3(128 * kCsaGroups), 0, s,
+    hipLaunchKernelGGL((attend_split_kernel<false, kCsaGroups, false>), grid, dim3(128 * kCsaGroups), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.kc),
                        static_cast<const uint16_t*>(a.vc), a.kv_sb, a.kv_sn, a.idx, a.topk, a.q_pos,
                        a.n_entries, a.Tq, a.N_max, a.m, a.win, scale_log2, sl, nsplit, part, sync, rows,

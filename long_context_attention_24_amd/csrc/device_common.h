@@ -32,13 +32,16 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// Entries visible to a query at position q_pos for pooling factor m:
+// Entries visible to a query at position q_pos for pooling factor m >= 1:
 // entry j is visible iff m*(j+1) <= q_pos+1, capped by the valid rows.
+// q_pos + 1 is at most 2^31, so an unsigned 32-bit quotient is exact (a
+// 64-bit division would put a long dependent sequence in front of every
+// kernel's first loads); no branch either, so that a kernel's scalar loads
+// stay in one block and go out together.  q_pos < 0: max(q_pos, -1) + 1 = 0.
 __device__ __forceinline__ int visible_count(int q_pos, int m, int n_entries, int n_max) {
-  long long v = (static_cast<long long>(q_pos) + 1) / m;
-  if (v > n_entries) v = n_entries;
-  if (v > n_max) v = n_max;
-  return v < 0 ? 0 : static_cast<int>(v);
+  const unsigned v = (static_cast<unsigned>(max(q_pos, -1)) + 1u) / static_cast<unsigned>(m);
+  const int cap = max(min(n_entries, n_max), 0);
+  return v < static_cast<unsigned>(cap) ? static_cast<int>(v) : cap;
 }
 
 // Selection bound shared by the score and top-k kernels: every chunk of

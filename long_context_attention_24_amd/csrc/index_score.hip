@@ -169,9 +169,16 @@ __global__ __launch_bounds__(256, 1) void score_bf16_h64d128_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t key_lds[kWavesPerWg][32 * kKeyPitch];
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[64 * kKeyPitch];
   const int row = blockIdx.y, b = row / Tq;
+  // Every argument in registers before its first use (the argument loads go
+  // out together, one round trip); then the two values read from memory,
+  // whose loads go out ahead of the query and key loads below and which
+  // only the masking waits for.
+  asm volatile("" ::"s"(q), "s"(w), "s"(k), "s"(k_sb), "s"(k_sn), "s"(q_pos), "s"(n_entries),
+               "s"(Tq), "s"(N_max), "s"(m), "s"(scores), "s"(s_rs), "s"(chunk_rep), "s"(n_chunks),
+               "s"(bound_k));
+  const int qp = q_pos[row], ne = n_entries[b];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int jl = lane & 31, g = lane >> 5;
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int wid = blockIdx.x * kWavesPerWg + wave;    // this wave within the row
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
@@ -185,28 +192,33 @@ __global__ __launch_bounds__(256, 1) void score_bf16_h64d128_kernel(
     qv[i] = *reinterpret_cast<const u32x4_t*>(qrow + 8 * (static_cast<int>(threadIdx.x) + 256 * i));
   const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
   const int nw = (nch + kChunksPerWave - 1) / kChunksPerWave;   // waves per row
-  const int vis = min(V, N_max);
   // tile t of the wave: tile t % 8 of its chunk wid + (t / 8) nw
   auto chunk_of = [&](int t) { return wid + (t / kTilesPerWave) * nw; };
   auto tile_key0 = [&](int t) { return 32 * ((t % kTilesPerWave) * nch + chunk_of(t)); };
   // The first key tile is requested before the query is staged and the
   // barrier passed, so that its latency overlaps the query's (the
   // empty asm with a memory clobber keeps the compiler from sinking them
-  // below).  Every wave issues it, also one that exits below: rows are
-  // clamped to [0, vis - 1] (row 0 when nothing is visible; N_max >= 1).
+  // below).  Every wave issues it, also one that exits below, with rows
+  // clamped into the cache (N_max >= 1): it needs neither q_pos nor
+  // n_entries, and the keys past the visible ones are masked in the
+  // epilogue.  Later tiles are clamped to [0, vis - 1] (row 0 when nothing
+  // is visible), so that a partly visible row reads no more than it shows.
   const uint16_t* kb = k + b * k_sb + 8 * (lane & 15);
   const int lrow = lane >> 4;                     // row within each 4-row load
-  const int jmax = max(vis - 1, 0);
   u32x4_t kt[2][8];
-  auto load_tile = [&](int t, u32x4_t (&dst)[8]) {
+  auto load_tile_clamped = [&](int t, u32x4_t (&dst)[8], int jcap) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int j = min(tile_key0(t) + 4 * i + lrow, jmax);
+      const int j = min(tile_key0(t) + 4 * i + lrow, jcap);
       dst[i] = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
     }
   };
-  load_tile(0, kt[0]);
+  load_tile_clamped(0, kt[0], N_max - 1);
   asm volatile("" ::"s"(k) : "memory");
+  const int V = visible_count(qp, m, ne, N_max);
+  const int vis = min(V, N_max);
+  const int jmax = max(vis - 1, 0);
+  auto load_tile = [&](int t, u32x4_t (&dst)[8]) { load_tile_clamped(t, dst, jmax); };
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int c = static_cast<int>(threadIdx.x) + 256 * i;       // 16-byte chunk: head c / 16
@@ -498,14 +510,36 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int chunk = blockIdx.x * kWavesPerWg + wave;
   // tiles of 16 keys in the interleaved order of the bf16 kernel: wave c of
   // the row takes tiles c, c + nch, c + 2 nch, ...
+  // Every argument in registers before its first use (one round trip for
+  // the argument loads); then q_pos and n_entries, whose loads go out ahead
+  // of the key loads and which only the masking waits for.
+  asm volatile("" ::"s"(q), "s"(q_scale), "s"(w), "s"(k), "s"(k_scale), "s"(k_sb), "s"(k_sn),
+               "s"(ks_sb), "s"(ks_sn), "s"(q_pos), "s"(n_entries), "s"(Tq), "s"(N_max), "s"(m),
+               "s"(scores), "s"(s_rs), "s"(chunk_rep), "s"(n_chunks), "s"(bound_k));
   const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
   if (chunk >= nch) return;
-  const int vis = min(V, N_max);
+  const int qp = q_pos[row], ne = n_entries[b];
   auto tile_key0 = [&](int t) { return 16 * (t * nch + chunk); };
+  const uint8_t* kb = k + b * k_sb + 16 * g;
+  const float* ksb = k_scale + b * ks_sb;
+  u32x4_t kc[3], ks[3];
+  auto load_tile_clamped = [&](int t, u32x4_t& c, u32x4_t& sc4, int jcap) {
+    const int j = min(tile_key0(t) + nl, jcap);
+    c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
+    sc4 = ld16_stream(ksb + static_cast<int64_t>(j) * ks_sn);
+  };
+  // the first two tiles with rows clamped into the cache (N_max >= 1): they
+  // need neither q_pos nor n_entries; keys past the visible ones are masked
+  // on output
+  load_tile_clamped(0, kc[0], ks[0], N_max - 1);
+  load_tile_clamped(1, kc[1], ks[1], N_max - 1);
+  asm volatile("" ::"s"(k) : "memory");           // the loads above stay ahead of the exit below
+
+  const int V = visible_count(qp, m, ne, N_max);
+  const int vis = min(V, N_max);
   float* srow = scores + row * s_rs;
   if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
     for (int t = 0; t < kFp4Tiles; ++t) {
@@ -516,19 +550,9 @@ __global__ __launch_bounds__(256) void score_fp4_h64d128_kernel(
       chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
     return;
   }
-
-  // keys past the visible range are clamped to the last visible one (in
-  // bounds, masked on output)
-  const uint8_t* kb = k + b * k_sb + 16 * g;
-  const float* ksb = k_scale + b * ks_sb;
-  u32x4_t kc[3], ks[3];
-  auto load_tile = [&](int t, u32x4_t& c, u32x4_t& sc4) {
-    const int j = min(tile_key0(t) + nl, vis - 1);
-    c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
-    sc4 = ld16_stream(ksb + static_cast<int64_t>(j) * ks_sn);
-  };
-  load_tile(0, kc[0], ks[0]);
-  load_tile(1, kc[1], ks[1]);
+  // later tiles: keys past the visible range clamped to the last visible one
+  // (in bounds, masked on output)
+  auto load_tile = [&](int t, u32x4_t& c, u32x4_t& sc4) { load_tile_clamped(t, c, sc4, vis - 1); };
 
   // A operand per head tile mt: head 16 mt + n, block g (16 bytes of codes)
   const uint8_t* qrow = q + static_cast<int64_t>(row) * 64 * 64;
@@ -634,38 +658,33 @@ __global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
   const int row = blockIdx.y, b = row / Tq;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const int V = visible_count(q_pos[row], m, n_entries[b], N_max);
   const int chunk = blockIdx.x * kWavesPerWg + wave;
   // tiles of 16 keys in the interleaved order of the bf16 kernel: wave c of
   // the row takes tiles c, c + nch, c + 2 nch, ...
+  // Every argument in registers before its first use (one round trip for
+  // the argument loads); then q_pos and n_entries, whose loads go out ahead
+  // of the query and key loads and which only the masking waits for.
+  asm volatile("" ::"s"(q), "s"(q_scale), "s"(w), "s"(k), "s"(k_scale), "s"(k_sb), "s"(k_sn),
+               "s"(ks_sb), "s"(ks_sn), "s"(q_pos), "s"(n_entries), "s"(Tq), "s"(N_max), "s"(m),
+               "s"(scores), "s"(s_rs), "s"(chunk_rep), "s"(n_chunks), "s"(bound_k));
   const int nch = (N_max + kKeysPerWave - 1) / kKeysPerWave;
   if (chunk >= nch) return;
-  const int vis = min(V, N_max);
+  const int qp = q_pos[row], ne = n_entries[b];
   auto tile_key0 = [&](int t) { return 16 * (t * nch + chunk); };
-  float* srow = scores + row * s_rs;
-  if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
-    for (int t = 0; t < kFp4Tiles; ++t) {
-      const int j = tile_key0(t) + nl;
-      if (g == 0 && j < N_max) srow[j] = kNegInf;
-    }
-    if (chunk_rep != nullptr && lane == 0)
-      chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
-    return;
-  }
-
-  // keys past the visible range are clamped to the last visible one (in
-  // bounds, masked on output)
   const uint8_t* kb = k + b * k_sb + 16 * g;
   const uint8_t* ksb = k_scale + b * ks_sb;
   u32x4_t kc[kMxAhead + 1];
   uint32_t ks[kMxAhead + 1];
-  auto load_tile = [&](int t, u32x4_t& c, uint32_t& sw) {
-    const int j = min(tile_key0(t) + nl, vis - 1);
+  auto load_tile_clamped = [&](int t, u32x4_t& c, uint32_t& sw, int jcap) {
+    const int j = min(tile_key0(t) + nl, jcap);
     c = ld16_stream(kb + static_cast<int64_t>(j) * k_sn);
     sw = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(ksb + static_cast<int64_t>(j) * ks_sn));
   };
+  // the first tiles with rows clamped into the cache (N_max >= 1): they need
+  // neither q_pos nor n_entries; keys past the visible ones are masked on
+  // output
 #pragma unroll
-  for (int t = 0; t < kMxAhead; ++t) load_tile(t, kc[t], ks[t]);
+  for (int t = 0; t < kMxAhead; ++t) load_tile_clamped(t, kc[t], ks[t], N_max - 1);
 
   // A operand per head tile mt: head 16 mt + n, block g (16 bytes of codes)
   // and that block's scale byte
@@ -687,6 +706,23 @@ __global__ __launch_bounds__(256) void score_mx4_h64d128_kernel(
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) wv[mt][r] = wrow[16 * mt + 4 * g + r];
+  asm volatile("" ::"s"(k) : "memory");           // the loads above stay ahead of the exit below
+
+  const int V = visible_count(qp, m, ne, N_max);
+  const int vis = min(V, N_max);
+  float* srow = scores + row * s_rs;
+  if (tile_key0(0) >= vis) {                      // no visible key in this wave's tiles
+    for (int t = 0; t < kFp4Tiles; ++t) {
+      const int j = tile_key0(t) + nl;
+      if (g == 0 && j < N_max) srow[j] = kNegInf;
+    }
+    if (chunk_rep != nullptr && lane == 0)
+      chunk_rep[static_cast<int64_t>(row) * n_chunks + chunk] = make_float2(kPosInf, kNegInf);
+    return;
+  }
+  // later tiles: keys past the visible range clamped to the last visible one
+  // (in bounds, masked on output)
+  auto load_tile = [&](int t, u32x4_t& c, uint32_t& sw) { load_tile_clamped(t, c, sw, vis - 1); };
 
   float scv[kFp4Tiles];
 #pragma unroll

@@ -232,6 +232,74 @@ def test_hca_multi_split_ragged():
     assert np.array_equal(OH[1, 2], np.tile(Vv[1, 0], (64, 1)))
 
 
+def test_visible_count_extremes():
+    """Query positions at the edges of the visible-count rule, through every
+    decode kernel that reads them: q_pos = -1 and far below 0 (nothing
+    visible), the largest int32 (visible count capped by n_entries, below
+    N_max), and a count inside the second HCA split.  The decode kernels
+    issue their first loads before q_pos and n_entries arrive, so these rows
+    check that the masks applied afterwards are right.  bf16, MX and FP4
+    scores with the selection, CSA attention over the selection, HCA and the
+    sliding window, each against the oracle."""
+    from csa_synth import mx4_quantize
+    from csa_synth.generate import fp4_quantize
+    B, N_max, m, k, win = 4, 2500, 4, 300, 700
+    _say("visible-count extremes: bf16 / MX / FP4 scores, selection, CSA, HCA, window")
+    pos = [-1, -1000, 2 ** 31 - 1, 4 * 1300 + 3]
+    ne = [N_max, N_max, N_max - 37, N_max]
+    q_pos = torch.tensor([[p] for p in pos], dtype=torch.int32, device=DEV)
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    vis = [oracle.visible_count(p, m, n) for p, n in zip(pos, ne)]
+    assert vis == [0, 0, N_max - 37, 1301]
+    qi = _randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 131)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 132)
+    wi = _randn((B, 1, 64), 1 / 8, torch.float32, 133)
+    q = _randn((B, 1, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 134)
+    kc = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 135)
+    vc = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 136)
+    scores = csa.index_score(qi, wi, ki, q_pos, n_ent, m)
+    idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k)
+    o, lse = csa.attend(q, kc, vc, idx, n_ent, with_lse=True)
+    oh, lseh = csa.hca_attend(q, kc, vc, q_pos, n_ent, m, with_lse=True)
+    ow, lsew = csa.swa_attend(q, kc, vc, q_pos, n_ent, win, with_lse=True)
+    qf, kf = qi.float(), ki.float()
+    quant = {}
+    for name, fn, deq in (("mx4", mx4_quantize, oracle.mx4_dequantize),
+                          ("fp4", fp4_quantize, oracle.fp4_dequantize)):
+        qc, qs = (t.to(DEV) for t in fn(qf))
+        kcq, ksq = (t.to(DEV) for t in fn(kf))
+        sq = csa.index_score(qc, wi, kcq, q_pos, n_ent, m, q_scale=qs, k_scale=ksq)
+        iq = csa.index_topk(qc, wi, kcq, q_pos, n_ent, m, k, q_scale=qs, k_scale=ksq)
+        quant[name] = (sq, iq, deq(qc.cpu().numpy(), qs.cpu().numpy()),
+                       deq(kcq.cpu().numpy(), ksq.cpu().numpy()))
+    torch.cuda.synchronize()
+    W, Q, K, Vv = np64(wi), np64(q), np64(kc), np64(vc)
+    runs = [("bf16", np64(scores), np64(idx), np64(qi), np64(ki))]
+    runs += [(n, np64(sq), np64(iq), qd, kd) for n, (sq, iq, qd, kd) in quant.items()]
+    O, L, OH, LH, OW, LW = (np64(t) for t in (o, lse, oh, lseh, ow, lsew))
+    for b in range(B):
+        V = vis[b]
+        for name, S, I, QI, KI in runs:
+            s_ref = oracle.index_scores(QI[b, 0], W[b, 0], KI[b], V)
+            assert np.all(np.isneginf(S[b, 0, V:])), (name, b, V)
+            if V:
+                bound = score_bound(QI[b, 0], W[b, 0], KI[b, :V], 128, 64)
+                assert np.all(np.abs(S[b, 0, :V] - s_ref[:V]) <= bound), (name, b, V)
+            check_topk(I[b, 0], s_ref, V, k)
+        o_ref, l_ref = oracle.attend(Q[b, 0], K[b], Vv[b], runs[0][2][b, 0])
+        check_attention(O[b, 0], o_ref, "bf16", f"csa b={b}")
+        check_lse(L[b, 0], l_ref, 2.5e-3)
+        oh_ref, lh_ref = oracle.hca_attend(Q[b, 0], K[b], Vv[b], V)
+        check_attention(OH[b, 0], oh_ref, "bf16", f"hca b={b}")
+        check_lse(LH[b, 0], lh_ref, 2.5e-3)
+        ow_ref, lw_ref = oracle.swa_attend(Q[b, 0], K[b], Vv[b], pos[b], ne[b], win)
+        check_attention(OW[b, 0], ow_ref, "bf16", f"swa b={b}")
+        check_lse(LW[b, 0], lw_ref, 2.5e-3)
+    for i in (0, 1):                                       # nothing visible
+        assert np.all(OH[i, 0] == 0) and np.all(np.isneginf(LH[i, 0]))
+        assert np.all(np.asarray(runs[0][2][i, 0]) == -1)
+
+
 def test_tuned_prefill_scores_ragged():
     """bf16 64 x 128 with many queries per sequence (the prefill score
     kernel: 8 queries per workgroup, 2048 keys per workgroup): a query count

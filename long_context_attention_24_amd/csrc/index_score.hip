@@ -324,18 +324,48 @@ __global__ __launch_bounds__(256, 1) void score_bf16_h64d128_kernel(
 // head) pairs as rows, keys as columns and the 128 dims as the reduction,
 // followed by the per-query epilogue sum_h w[h] ReLU(.).  One workgroup of
 // 8 waves takes 8 queries of one sequence (one per wave: two 32-row A tiles
-// of q_I held in registers) against 2048 keys.  Key tiles of 32 rows are read
-// once per workgroup with coalesced loads (one 16-byte load per thread per
-// tile), kept four tiles ahead in registers, staged through a triple-buffered
-// LDS tile shared by the waves (one barrier per tile) and multiplied by all 8
-// queries: 16 MFMA 32x32x16 per wave per 8 KB tile.  The kernel holds 220
-// VGPRs, so a compute unit runs one workgroup (two waves per SIMD, at the
-// same barrier every tile); MFMA and epilogue overlap inside each wave.  The
+// of q_I held in registers) against 4096 keys (2048 measured 4 % slower: the
+// query and first-tile loads of each workgroup are not overlapped by anything
+// else on its compute unit).  Key tiles of 32 rows are read once per
+// workgroup with coalesced loads (one 16-byte load per thread per tile), kept
+// four tiles ahead in registers, staged through a triple-buffered LDS tile
+// shared by the waves (one barrier per tile) and multiplied by all 8 queries:
+// 16 MFMA 32x32x16 per wave per 8 KB tile.  The kernel holds about 240 VGPRs,
+// so a compute unit runs one workgroup (two waves per SIMD, at the same
+// barrier every tile); MFMA and epilogue overlap inside each wave.  The
 // selection bounds are produced per 256-key chunk exactly as in the decode
 // kernel.
+//
+// Every iteration of the tile loop issues the same memory instructions on
+// every path (one key load, one score store, one report store, the stores
+// made conditional through out-of-range buffer offsets instead of branches):
+// the compiler's wait before staging a tile then counts exactly the
+// operations issued behind that tile's load, and waits for that load alone.
+// With the stores behind branches it had to assume the shortest path and
+// waited for the loads of the two following tiles as well, so the four-tile
+// ring held two tiles in flight (4.29 -> 4.07 ms together with the wider key
+// block, same box).
+
+// Raw buffer stores: the hardware drops a store whose byte offset is at or
+// past the record count of the buffer resource, so kOob turns a store off
+// without a branch.
+constexpr uint32_t kOob = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void buf_score(__amdgpu_buffer_rsrc_t r, uint32_t off, float v, float*) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_score(__amdgpu_buffer_rsrc_t r, uint32_t off, float v, uint16_t*) {
+  __builtin_amdgcn_raw_buffer_store_b16(bf16_rne_bits(v), r, off, 0, 0);
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void buf_rep(__amdgpu_buffer_rsrc_t r, uint32_t off, float2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2_t{__float_as_uint(v.x), __float_as_uint(v.y)}, r, off, 0, 0);
+}
 constexpr int kPfQueries = 8;
 constexpr int kPfThreads = 64 * kPfQueries;
-constexpr int kPfKeys = 2048;
+constexpr int kPfKeys = 4096;
 constexpr int kPfStages = 4;
 
 template <typename SO>
@@ -380,14 +410,6 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   const uint16_t* kb = k + b * k_sb + 8 * (tid & 15);
   const int jcap = max(vmax, 1) - 1;              // clamp rows to visible ones (in bounds)
   const int lrow = tid >> 4;                      // tile row this thread loads
-  // Key tile loads are issued on every path (rows clamped, so tiles past
-  // the end read visible rows again): with no branch around them the
-  // compiler counts the loads in flight exactly and waiting for one tile
-  // never waits for the tiles behind it.
-  u32x4_t ring[kPfStages];
-#pragma unroll
-  for (int u = 0; u < kPfStages; ++u)
-    ring[u] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * u + lrow, jcap)) * k_sn);
 
   // A operand: q_I rows of the wave's query (an invalid query reads row 0
   // and its results are never stored)
@@ -405,6 +427,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
       for (int r = 0; r < 16; ++r) wv[hf][r] = wrow[32 * hf + 8 * (r >> 2) + 4 * g + (r & 3)];
     }
   }
+  // Key tile loads, issued after the query and weight loads (kept in that
+  // order by the scheduling barrier) so that the first wait for a tile also
+  // covers those and the loop needs no wait for them; issued on every path
+  // (rows clamped, so tiles past the end read visible rows again).
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4_t ring[kPfStages];
+#pragma unroll
+  for (int u = 0; u < kPfStages; ++u)
+    ring[u] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * u + lrow, jcap)) * k_sn);
   const int cq = __builtin_amdgcn_readfirstlane(chunk_rep != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0);
   float sc[kTilesPerWave];
   lds_u16* const st_ptr0 = (lds_u16*)&tile_lds[0][0] + lrow * kKeyPitch + 8 * (tid & 15);
@@ -427,28 +458,37 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   auto load_tile = [&](int t) -> u32x4_t {
     return *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * t + lrow, jcap)) * k_sn);
   };
+  // store windows: the query's scores of this key block, its chunk reports
+  // (empty for an invalid query or without reports)
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(
+      scores + static_cast<int64_t>(max(rowq, 0)) * s_rs + j0,
+      rowq >= 0 ? static_cast<uint32_t>(j1 - j0) * static_cast<uint32_t>(sizeof(SO)) : 0u);
+  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(
+      chunk_rep + (chunk_rep != nullptr ? static_cast<int64_t>(max(rowq, 0)) * n_chunks : 0),
+      chunk_rep != nullptr && rowq >= 0 ? static_cast<uint32_t>(n_chunks) * 8u : 0u);
   f32x16_t acc[2][2];
 
   // Software pipeline, one barrier per tile.  Iteration tt: stage tile tt+2
   // into LDS buffer (tt+2)%3, load tile tt+6 into the freed register slot,
   // issue the MFMAs of tile tt+1, then the epilogue of tile tt (whose MFMAs
-  // were issued one iteration earlier) while they run.
+  // were issued one iteration earlier) while they run.  The last pass runs
+  // all eight iterations of its chunk; those past the last tile stage and
+  // multiply stale data and store nothing (live == false).
   *(lds_u32x4*)st_ptr0 = ring[0];
   *(lds_u32x4*)(st_ptr0 + kBufElems) = ring[1];
-  ring[0] = load_tile(4);
-  ring[1] = load_tile(5);
+  ring[0] = load_tile(kPfStages);
+  ring[1] = load_tile(kPfStages + 1);
   __syncthreads();
   if (ntiles > 0) mfma_tile(0, acc[0]);
   for (int t = 0; t < ntiles; t += kTilesPerWave) {   // one 256-key chunk per pass
 #pragma unroll
     for (int u = 0; u < kTilesPerWave; ++u) {
       const int tt = t + u;
-      if (tt < ntiles) {
-        __syncthreads();
-        if (tt + 2 < ntiles) *(lds_u32x4*)(st_ptr0 + ((tt + 2) % 3) * kBufElems) = ring[(u + 2) % kPfStages];
-      }
-      ring[(u + 2) % kPfStages] = load_tile(tt + 6);
-      if (tt < ntiles) {
+      const bool live = tt < ntiles;
+      __syncthreads();
+      *(lds_u32x4*)(st_ptr0 + ((tt + 2) % 3) * kBufElems) = ring[(u + 2) % kPfStages];
+      ring[(u + 2) % kPfStages] = load_tile(tt + 2 + kPfStages);
+      {
         // the MFMAs of tile tt+1 (past the last tile they read a stale
         // buffer and are discarded: unconditional, so they share one
         // scheduling region with the epilogue of tile tt); the compiler
@@ -465,16 +505,19 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
         const float tot = sum + __shfl_xor(sum, 32, 64);
         const int j = j0 + 32 * tt + jl;
         const bool ok = j < vq;
-        if (g == 0 && rowq >= 0 && j < j1) put_score(&scores[rowq * s_rs + j], ok ? tot : kNegInf);
+        const uint32_t so = static_cast<uint32_t>(32 * tt + jl) * static_cast<uint32_t>(sizeof(SO));
+        buf_score(srs, g == 0 && live ? so : kOob, ok ? tot : kNegInf, (SO*)nullptr);
         sc[u] = ok ? tot : kNegInf;
         // after each 256-key chunk (or the last computed tile): its bound
-        if (cq > 0 && (u == kTilesPerWave - 1 || tt == ntiles - 1)) {
+        const bool do_rep = cq > 0 && live && (u == kTilesPerWave - 1 || tt == ntiles - 1);
+        float2 rep = make_float2(0.f, 0.f);
+        if (do_rep) {
 #pragma unroll
           for (int v = u + 1; v < kTilesPerWave; ++v) sc[v] = kNegInf;
-          const float2 rep = wave_chunk_report<kTilesPerWave>(sc, g == 0, cq);
-          if (lane == 0)
-            chunk_rep[static_cast<int64_t>(rowq) * n_chunks + (j0 + 32 * tt) / kBoundChunk] = stored_report<SO>(rep);
+          rep = stored_report<SO>(wave_chunk_report<kTilesPerWave>(sc, g == 0, cq));
         }
+        const uint32_t ro = static_cast<uint32_t>((j0 + 32 * tt) / kBoundChunk) * 8u;
+        buf_rep(rrs, do_rep && lane == 0 ? ro : kOob, rep);
       }
     }
   }

@@ -302,16 +302,17 @@ def test_visible_count_extremes():
 
 def test_tuned_prefill_scores_ragged():
     """bf16 64 x 128 with many queries per sequence (the prefill score
-    kernel: 8 queries per workgroup, 2048 keys per workgroup): a query count
-    that is not a multiple of 8, several key blocks with a ragged tail,
-    visible counts from 0 to all, a partially valid cache.  Scores, the
-    chunk bounds (through the selection) and the selection are checked."""
-    B, Tq, N_max, m, k = 2, 13, 2 * 2048 + 300, 4, 300
+    kernel: 8 queries per workgroup, 4096 keys per workgroup): a query count
+    that is not a multiple of 8, three key blocks with a ragged tail, visible
+    counts from 0 to all (ending on and next to block boundaries), a
+    partially valid cache.  Scores, the chunk bounds (through the selection)
+    and the selection are checked."""
+    B, Tq, N_max, m, k = 2, 13, 2 * 4096 + 300, 4, 300
     _say("tuned prefill bf16 64x128 ragged")
     qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 31)
     ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 32)
     wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 33)
-    pos = [[4 * N_max + 7, 2, 3, 4 * 1024 - 1, 4 * 2048 - 1, 4 * 2048 + 3, 4 * 2100 + 1, 4 * 4000,
+    pos = [[4 * N_max + 7, 2, 3, 4 * 1024 - 1, 4 * 2048 - 1, 4 * 8192 - 1, 4 * 8192 + 3, 4 * 4000,
             4 * 4095 + 3, 4 * 4096 - 1, 4 * 4100, 4 * 300 + 2, 4 * 37],
            [4 * 1000, 4 * 2500, 4 * 4300, 1, 4 * 257, 4 * 256 - 1, 4 * 512, 4 * 3000, 4 * 3500,
             4 * 4000, 4 * 4200, 4 * 4390, 4 * 100]]

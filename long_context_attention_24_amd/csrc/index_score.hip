@@ -324,27 +324,29 @@ __global__ __launch_bounds__(256, 1) void score_bf16_h64d128_kernel(
 // head) pairs as rows, keys as columns and the 128 dims as the reduction,
 // followed by the per-query epilogue sum_h w[h] ReLU(.).  One workgroup of
 // 8 waves takes 8 queries of one sequence (one per wave: two 32-row A tiles
-// of q_I held in registers) against 4096 keys (2048 measured 4 % slower: the
-// query and first-tile loads of each workgroup are not overlapped by anything
-// else on its compute unit).  Key tiles of 32 rows are read once per
-// workgroup with coalesced loads (one 16-byte load per thread per tile), kept
-// four tiles ahead in registers, staged through a triple-buffered LDS tile
-// shared by the waves (one barrier per tile) and multiplied by all 8 queries:
-// 16 MFMA 32x32x16 per wave per 8 KB tile.  The kernel holds about 240 VGPRs,
-// so a compute unit runs one workgroup (two waves per SIMD, at the same
-// barrier every tile); MFMA and epilogue overlap inside each wave.  The
-// selection bounds are produced per 256-key chunk exactly as in the decode
-// kernel.
+// of q_I held in registers) against 4096 keys, in blocks of 256 keys (one
+// selection chunk, 64 KB) that go from memory straight into LDS
+// (global_load_lds_dwordx4, no staging registers), double-buffered, with one
+// barrier per block: the block after next is requested while a block is
+// multiplied, and all 8 queries read it, 16 MFMA 32x32x16 per wave per
+// 32-key tile, the ReLU-w epilogue of tile u-1 running under the MFMAs of
+// tile u.  The kernel holds about 240 VGPRs and 128 KB of LDS, so a compute
+// unit runs one workgroup (two waves per SIMD).  The selection bounds are
+// produced per 256-key chunk exactly as in the decode kernel.
 //
-// Every iteration of the tile loop issues the same memory instructions on
-// every path (one key load, one score store, one report store, the stores
-// made conditional through out-of-range buffer offsets instead of branches):
-// the compiler's wait before staging a tile then counts exactly the
-// operations issued behind that tile's load, and waits for that load alone.
-// With the stores behind branches it had to assume the shortest path and
-// waited for the loads of the two following tiles as well, so the four-tile
-// ring held two tiles in flight (4.29 -> 4.07 ms together with the wider key
-// block, same box).
+// Measured on one box against the former design (32-key tiles staged
+// through registers and an LDS tile, one barrier per tile, 2048 keys per
+// workgroup): 4.29 -> 3.68 ms for the 4096-query chunk at 66,560 entries,
+// scores bitwise identical.  Steps, each kept for what it measured: the
+// stores made branch-free so the compiler's waits count exactly (the four-
+// tile register ring had held two tiles in flight), 4096 keys per workgroup,
+// blocks loaded straight into LDS with one barrier per block, the lane
+// halves' sums added by a register swap instead of an LDS permute (whose
+// wait had also waited for every B-operand read in flight).  Measured and
+// dropped: B operands of the next tile read ahead under a scheduling
+// barrier (8 % slower), a single accumulator set (equal), 12 waves of 168
+// VGPRs (three per SIMD, equal), waves of a SIMD staggered by a sleep
+// (equal), 8192 or 16384 keys per workgroup (equal, 3 % slower).
 
 // Raw buffer stores: the hardware drops a store whose byte offset is at or
 // past the record count of the buffer resource, so kOob turns a store off
@@ -368,15 +370,24 @@ constexpr int kPfThreads = 64 * kPfQueries;
 constexpr int kPfKeys = 4096;
 constexpr int kPfStages = 4;
 
+constexpr int kPbRows = kBoundChunk;             // keys per LDS block: one report chunk
+constexpr int kPbBytes = kPbRows * 256;           // 64 KB of bf16 keys
+constexpr int kPbTiles = kPbRows / 32;
+static_assert(kPbTiles == kTilesPerWave, "a block is one chunk of tiles");
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt low bits 3:0
+// and high bits 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+#define CSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+
 template <typename SO>
 __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, SO* __restrict__ scores,
     int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
-  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
-  __shared__ __attribute__((aligned(16))) uint16_t tile_lds[3][32 * kKeyPitch];
+  __shared__ __attribute__((aligned(1024))) uint8_t blk_lds[2][kPbBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, g = lane >> 5;
   const int groups = (Tq + kPfQueries - 1) / kPfQueries;
@@ -401,15 +412,15 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   const int rowq = __builtin_amdgcn_readfirstlane(t0 + wave < Tq ? b * Tq + t0 + wave : -1);
   const int je = min(j1, vmax);                   // keys past je are masked for all queries
   const int ntiles = __builtin_amdgcn_readfirstlane(je > j0 ? (je - j0 + 31) / 32 : 0);
+  const int nblk = (ntiles + kPbTiles - 1) / kPbTiles;
 
   // -inf for every key this workgroup covers but does not compute
   if (rowq >= 0) {
     SO* srow = scores + rowq * s_rs;
     for (int j = j0 + 32 * ntiles + lane; j < j1; j += 64) put_score(&srow[j], kNegInf);
   }
-  const uint16_t* kb = k + b * k_sb + 8 * (tid & 15);
+  const uint16_t* kb = k + b * k_sb;
   const int jcap = max(vmax, 1) - 1;              // clamp rows to visible ones (in bounds)
-  const int lrow = tid >> 4;                      // tile row this thread loads
 
   // A operand: q_I rows of the wave's query (an invalid query reads row 0
   // and its results are never stored)
@@ -427,37 +438,33 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
       for (int r = 0; r < 16; ++r) wv[hf][r] = wrow[32 * hf + 8 * (r >> 2) + 4 * g + (r & 3)];
     }
   }
-  // Key tile loads, issued after the query and weight loads (kept in that
-  // order by the scheduling barrier) so that the first wait for a tile also
-  // covers those and the loop needs no wait for them; issued on every path
-  // (rows clamped, so tiles past the end read visible rows again).
-  __builtin_amdgcn_sched_barrier(0);
-  u32x4_t ring[kPfStages];
+  // A block of 256 keys goes straight from memory into LDS buffer `buf`,
+  // laid out by k-slice: the 32 bytes of dims 16 s .. 16 s + 15 of block row
+  // r sit at 8192 s + 32 r, their two 16-byte halves swapped in rows with
+  // (r / 8) odd, so that 16 lanes reading one half of rows r0 .. r0 + 15
+  // touch 64 distinct 4-byte banks (measured as fast as an XOR-swizzled
+  // row-major layout, whose reads need a per-slice address).  Each 16-byte load
+  // writes LDS byte 16 l of its kilobyte for lane l, so instruction i of
+  // wave v (kilobyte 8 v + i: slice v, rows 32 i .. 32 i + 31) has lane l
+  // fetch row 32 i + l / 2, the half that belongs at position l % 2.  Rows
+  // past the visible ones are clamped (in bounds; their scores are masked).
+  auto load_block = [&](int blk, int buf) {
 #pragma unroll
-  for (int u = 0; u < kPfStages; ++u)
-    ring[u] = *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * u + lrow, jcap)) * k_sn);
-  const int cq = __builtin_amdgcn_readfirstlane(chunk_rep != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0);
-  float sc[kTilesPerWave];
-  lds_u16* const st_ptr0 = (lds_u16*)&tile_lds[0][0] + lrow * kKeyPitch + 8 * (tid & 15);
-  const lds_u16* const ld_ptr0 = (const lds_u16*)&tile_lds[0][0] + jl * kKeyPitch + 8 * g;
-  constexpr int kBufElems = 32 * kKeyPitch;
-  // MFMAs of one key tile from LDS buffer `buf` into acc
-  auto mfma_tile = [&](int buf, f32x16_t (&acc)[2]) {
-    const lds_u16* src = ld_ptr0 + buf * kBufElems;
-    acc[0] = f32x16_t{};
-    acc[1] = f32x16_t{};
-#pragma unroll
-    for (int s2 = 0; s2 < 8; ++s2) {
-      const u32x4_t x = *(const lds_u32x4*)(src + 16 * s2);
-      bf16x8_t bb;
-      __builtin_memcpy(&bb, &x, 16);
-      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s2], bb, acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s2], bb, acc[1], 0, 0, 0);
+    for (int i = 0; i < 8; ++i) {
+      const int kk = 8 * wave + i;                  // kilobyte of the buffer
+      const int s2 = kk >> 3;                       // its k-slice
+      const int r = 32 * (kk & 7) + (lane >> 1);    // block row
+      const int c = 2 * s2 + ((lane & 1) ^ ((r >> 3) & 1));   // 16-byte chunk of the row
+      const int j = min(j0 + kPbRows * blk + r, jcap);
+      const uint16_t* gp = kb + static_cast<int64_t>(j) * k_sn + 8 * c;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)gp,
+                                       (void __attribute__((address_space(3)))*)&blk_lds[buf][1024 * (8 * wave + i)],
+                                       16, 0, 0);
     }
   };
-  auto load_tile = [&](int t) -> u32x4_t {
-    return *reinterpret_cast<const u32x4_t*>(kb + static_cast<int64_t>(min(j0 + 32 * t + lrow, jcap)) * k_sn);
-  };
+  __builtin_amdgcn_sched_barrier(0);
+  load_block(0, 0);
+  const int cq = __builtin_amdgcn_readfirstlane(chunk_rep != nullptr && rowq >= 0 ? bound_c_row(vq, bound_k) : 0);
   // store windows: the query's scores of this key block, its chunk reports
   // (empty for an invalid query or without reports)
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(
@@ -466,60 +473,69 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
   const __amdgpu_buffer_rsrc_t rrs = make_rsrc(
       chunk_rep + (chunk_rep != nullptr ? static_cast<int64_t>(max(rowq, 0)) * n_chunks : 0),
       chunk_rep != nullptr && rowq >= 0 ? static_cast<uint32_t>(n_chunks) * 8u : 0u);
+  // B operand of tile u, k-slice s: block row 32 u + jl, dims 16 s + 8 g .. +7
+  auto mfma_tile = [&](int buf, int u, f32x16_t (&acc)[2]) {
+    const lds_u8* rowp = (const lds_u8*)&blk_lds[buf][(32 * u + jl) * 32 + 16 * (g ^ ((jl >> 3) & 1))];
+    acc[0] = f32x16_t{};
+    acc[1] = f32x16_t{};
+#pragma unroll
+    for (int s2 = 0; s2 < 8; ++s2) {
+      const u32x4_t x = *(const lds_u32x4*)(rowp + 8192 * s2);
+      bf16x8_t bb;
+      __builtin_memcpy(&bb, &x, 16);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0][s2], bb, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1][s2], bb, acc[1], 0, 0, 0);
+    }
+  };
+  float sc[kTilesPerWave];
+  // epilogue of tile u of block blk from its accumulators: the score store
+  // (dropped past the last computed tile or the key block) and sc[u]
+  auto epilogue = [&](int blk, int u, const f32x16_t (&c)[2]) {
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum = fmaf(wv[0][r], relu_f32(c[0][r]), sum);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum = fmaf(wv[1][r], relu_f32(c[1][r]), sum);
+    // the two lane halves' sums added by a register swap of the halves (no
+    // LDS instruction, so no wait on the B-operand reads in flight)
+    const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+    const float tot = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+    const int tt = kPbTiles * blk + u;
+    const bool live = tt < ntiles;
+    const bool ok = live && j0 + 32 * tt + jl < vq;
+    const uint32_t so = static_cast<uint32_t>(32 * tt + jl) * static_cast<uint32_t>(sizeof(SO));
+    buf_score(srs, g == 0 && live ? so : kOob, ok ? tot : kNegInf, (SO*)nullptr);
+    sc[u] = ok ? tot : kNegInf;
+  };
   f32x16_t acc[2][2];
 
-  // Software pipeline, one barrier per tile.  Iteration tt: stage tile tt+2
-  // into LDS buffer (tt+2)%3, load tile tt+6 into the freed register slot,
-  // issue the MFMAs of tile tt+1, then the epilogue of tile tt (whose MFMAs
-  // were issued one iteration earlier) while they run.  The last pass runs
-  // all eight iterations of its chunk; those past the last tile stage and
-  // multiply stale data and store nothing (live == false).
-  *(lds_u32x4*)st_ptr0 = ring[0];
-  *(lds_u32x4*)(st_ptr0 + kBufElems) = ring[1];
-  ring[0] = load_tile(kPfStages);
-  ring[1] = load_tile(kPfStages + 1);
+  // One barrier per block.  At the top of block blk its loads have landed
+  // (each thread waits for its own, the barrier for everybody's) and every
+  // wave is done with block blk - 1, whose buffer then takes block blk + 1.
+  // Inside a block the MFMAs of tile u run under the epilogue of tile u - 1.
+  // The waits count exactly: after a block's loads come, on every path, the
+  // eight score stores and one report store of the block before it.
+  CSA_WAIT_VMCNT(0);
   __syncthreads();
-  if (ntiles > 0) mfma_tile(0, acc[0]);
-  for (int t = 0; t < ntiles; t += kTilesPerWave) {   // one 256-key chunk per pass
-#pragma unroll
-    for (int u = 0; u < kTilesPerWave; ++u) {
-      const int tt = t + u;
-      const bool live = tt < ntiles;
+  for (int blk = 0; blk < nblk; ++blk) {
+    const int buf = blk & 1;
+    if (blk > 0) {
+      CSA_WAIT_VMCNT(kPbTiles + 1);
       __syncthreads();
-      *(lds_u32x4*)(st_ptr0 + ((tt + 2) % 3) * kBufElems) = ring[(u + 2) % kPfStages];
-      ring[(u + 2) % kPfStages] = load_tile(tt + 2 + kPfStages);
-      {
-        // the MFMAs of tile tt+1 (past the last tile they read a stale
-        // buffer and are discarded: unconditional, so they share one
-        // scheduling region with the epilogue of tile tt); the compiler
-        // interleaves them with the epilogue's VALU work (explicit
-        // scheduling groups of one MFMA and four VALU instructions measured
-        // 5 % slower)
-        mfma_tile((tt + 1) % 3, acc[(u + 1) & 1]);
-        const f32x16_t (&c)[2] = acc[u & 1];
-        float sum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum = fmaf(wv[0][r], relu_f32(c[0][r]), sum);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sum = fmaf(wv[1][r], relu_f32(c[1][r]), sum);
-        const float tot = sum + __shfl_xor(sum, 32, 64);
-        const int j = j0 + 32 * tt + jl;
-        const bool ok = j < vq;
-        const uint32_t so = static_cast<uint32_t>(32 * tt + jl) * static_cast<uint32_t>(sizeof(SO));
-        buf_score(srs, g == 0 && live ? so : kOob, ok ? tot : kNegInf, (SO*)nullptr);
-        sc[u] = ok ? tot : kNegInf;
-        // after each 256-key chunk (or the last computed tile): its bound
-        const bool do_rep = cq > 0 && live && (u == kTilesPerWave - 1 || tt == ntiles - 1);
-        float2 rep = make_float2(0.f, 0.f);
-        if (do_rep) {
-#pragma unroll
-          for (int v = u + 1; v < kTilesPerWave; ++v) sc[v] = kNegInf;
-          rep = stored_report<SO>(wave_chunk_report<kTilesPerWave>(sc, g == 0, cq));
-        }
-        const uint32_t ro = static_cast<uint32_t>((j0 + 32 * tt) / kBoundChunk) * 8u;
-        buf_rep(rrs, do_rep && lane == 0 ? ro : kOob, rep);
-      }
     }
+    if (blk + 1 < nblk) load_block(blk + 1, buf ^ 1);
+    mfma_tile(buf, 0, acc[0]);
+#pragma unroll
+    for (int u = 1; u < kPbTiles; ++u) {
+      mfma_tile(buf, u, acc[u & 1]);
+      epilogue(blk, u - 1, acc[(u - 1) & 1]);
+    }
+    epilogue(blk, kPbTiles - 1, acc[(kPbTiles - 1) & 1]);
+    // the block's chunk bound
+    float2 rep = make_float2(0.f, 0.f);
+    if (cq > 0) rep = stored_report<SO>(wave_chunk_report<kTilesPerWave>(sc, g == 0, cq));
+    const uint32_t ro = static_cast<uint32_t>((j0 + kPbRows * blk) / kBoundChunk) * 8u;
+    buf_rep(rrs, cq > 0 && lane == 0 ? ro : kOob, rep);
   }
   // chunks with no computed key: no bound
   if (cq > 0 && lane == 0) {

@@ -23,7 +23,8 @@ WRITE_SIZE counters).
 
 Measurement notes.
   * Every timed region is queued behind a spin kernel that holds the GPU
-    until the whole region is enqueued, so host launch overhead is not timed.
+    until the whole region is enqueued, so host launch overhead is not timed;
+    the warm-up calls are queued between the spin and the timed region.
   * roofline: the dominant kernel (the score kernel); achieved = its
     algorithmic bytes per launch (indexer keys + indexer queries + head
     weights, the score workspace excluded) / its average launch duration,
@@ -158,11 +159,17 @@ class Timer:
         torch.cuda._sleep(int(self.cycles_per_ms * ms))
 
     def period(self, fn, steps, warmup):
-        """Average ms per call of `steps` back-to-back calls."""
+        """Average ms per call of `steps` back-to-back calls.  The warm-up
+        calls run once on their own (allocation, first-launch costs) and
+        again queued behind the spin, right before the timed region, so
+        that the clocks have left the idle of the spin when timing starts
+        (a 4 ms prefill kernel timed straight after the spin ran 4 % slower)."""
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        self.hold(20.0 + 0.05 * steps)
+        self.hold(20.0 + 0.05 * (steps + warmup))
+        for i in range(warmup):
+            fn(i)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(steps):
@@ -176,9 +183,11 @@ class Timer:
         for i in range(warmup):
             fn(i)
         torch.cuda.synchronize()
-        self.hold(20.0 + 0.05 * steps)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
+        self.hold(20.0 + 0.05 * (steps + warmup))
+        for i in range(warmup):
+            fn(i)
         for i in range(steps):
             ev[i][0].record()
             fn(i)

@@ -524,6 +524,9 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
       __syncthreads();
     }
     if (blk + 1 < nblk) load_block(blk + 1, buf ^ 1);
+    // the next block's loads stay ahead of this block's stores (the wait at
+    // the top of the next block counts the stores issued after them)
+    __builtin_amdgcn_sched_barrier(0);
     mfma_tile(buf, 0, acc[0]);
 #pragma unroll
     for (int u = 1; u < kPbTiles; ++u) {

@@ -384,14 +384,28 @@ __global__ __launch_bounds__(kPfThreads, 2) void score_prefill_bf16_h64d128_kern
     const uint16_t* __restrict__ q, const float* __restrict__ w, const uint16_t* __restrict__ k,
     int64_t k_sb, int64_t k_sn, const int32_t* __restrict__ q_pos,
     const int32_t* __restrict__ n_entries, int Tq, int N_max, int m, SO* __restrict__ scores,
-    int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k) {
+    int64_t s_rs, float2* __restrict__ chunk_rep, int n_chunks, int bound_k, int n_qgroups) {
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   typedef __attribute__((address_space(3))) u32x4_t lds_u32x4;
   __shared__ __attribute__((aligned(1024))) uint8_t blk_lds[2][kPbBytes];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jl = lane & 31, g = lane >> 5;
   const int groups = (Tq + kPfQueries - 1) / kPfQueries;
-  const int kblk = blockIdx.x, qgrp = blockIdx.y;
+  // XCD-aware order (a one-dimensional grid of 8 * ceil(units / 8)
+  // workgroups): the dispatcher hands workgroup i to XCD i % 8, and the
+  // (key block, query group) units, in key-block-major order, are cut into
+  // eight contiguous ranges, range x for the workgroups of XCD x.  Each XCD
+  // then reads about an eighth of the key blocks, which stay in its L2 while
+  // all query groups pass over them: 1.4 GB of L2 fills per launch on the
+  // 4096-query chunk instead of 8.2 GB with the key block varying fastest
+  // across the grid (same time).  Correctness does not depend on the
+  // placement.
+  const int nkb = (N_max + kPfKeys - 1) / kPfKeys;
+  const int units = nkb * n_qgroups;
+  const int per_xcd = (units + 7) / 8;
+  const int unit = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (unit >= units) return;                      // grid padding (no barrier passed yet)
+  const int kblk = unit / n_qgroups, qgrp = unit % n_qgroups;
   const int b = qgrp / groups;
   const int t0 = (qgrp % groups) * kPfQueries;
   const int j0 = kblk * kPfKeys;
@@ -864,19 +878,21 @@ hipError_t launch_score(const ScoreArgs& a, csa_dtype_t dt, hipStream_t s) {
                        a.s_rs, a.chunk_rep, a.n_chunks, a.bound_k);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128 && a.Tq >= kPfQueries) {
     const int groups = (a.Tq + kPfQueries - 1) / kPfQueries;
-    const dim3 grid((a.N_max + kPfKeys - 1) / kPfKeys, a.B * groups);
+    const int nkb = (a.N_max + kPfKeys - 1) / kPfKeys;
+    const int units = nkb * a.B * groups;
+    const dim3 grid(8 * ((units + 7) / 8));
     if (a.score16)
       hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel<uint16_t>, grid, dim3(kPfThreads), 0, s,
                          static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
                          a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m,
                          static_cast<uint16_t*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
-                         a.bound_k);
+                         a.bound_k, a.B * groups);
     else
       hipLaunchKernelGGL(score_prefill_bf16_h64d128_kernel<float>, grid, dim3(kPfThreads), 0, s,
                          static_cast<const uint16_t*>(a.q), a.w, static_cast<const uint16_t*>(a.k),
                          a.k_sb, a.k_sn, a.q_pos, a.n_entries, a.Tq, a.N_max, a.m,
                          static_cast<float*>(a.scores), a.s_rs, a.chunk_rep, a.n_chunks,
-                         a.bound_k);
+                         a.bound_k, a.B * groups);
   } else if (dt == CSA_BF16 && a.H == 64 && a.D == 128) {
     const int nch = (a.N_max + kKeysPerWave - 1) / kKeysPerWave;
     const int nw = (nch + kChunksPerWave - 1) / kChunksPerWave;

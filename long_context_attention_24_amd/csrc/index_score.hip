@@ -327,12 +327,13 @@ __global__ __launch_bounds__(256, 1) void score_bf16_h64d128_kernel(
 // of q_I held in registers) against 4096 keys, in blocks of 256 keys (one
 // selection chunk, 64 KB) that go from memory straight into LDS
 // (global_load_lds_dwordx4, no staging registers), double-buffered, with one
-// barrier per block: the block after next is requested while a block is
-// multiplied, and all 8 queries read it, 16 MFMA 32x32x16 per wave per
-// 32-key tile, the ReLU-w epilogue of tile u-1 running under the MFMAs of
-// tile u.  The kernel holds about 240 VGPRs and 128 KB of LDS, so a compute
-// unit runs one workgroup (two waves per SIMD).  The selection bounds are
-// produced per 256-key chunk exactly as in the decode kernel.
+// barrier per block: the next block is requested at the top of each block,
+// whose 64 KB all 8 queries then read, 16 MFMA 32x32x16 per wave per 32-key
+// tile, the ReLU-w epilogue of tile u-1 running under the MFMAs of tile u.
+// The kernel holds about 240 VGPRs and 128 KB of LDS, so a compute unit runs
+// one workgroup (two waves per SIMD); the grid is ordered so that each XCD
+// works through its own eighth of the key blocks (below).  The selection
+// bounds are produced per 256-key chunk exactly as in the decode kernel.
 //
 // Measured on one box against the former design (32-key tiles staged
 // through registers and an LDS tile, one barrier per tile, 2048 keys per
@@ -368,7 +369,6 @@ __device__ __forceinline__ void buf_rep(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 constexpr int kPfQueries = 8;
 constexpr int kPfThreads = 64 * kPfQueries;
 constexpr int kPfKeys = 4096;
-constexpr int kPfStages = 4;
 
 constexpr int kPbRows = kBoundChunk;             // keys per LDS block: one report chunk
 constexpr int kPbBytes = kPbRows * 256;           // 64 KB of bf16 keys

@@ -115,3 +115,41 @@ def test_noalloc_long_rows_and_limits():
     with pytest.raises(csa.CsaError) as e:
         csa.index_topk_attend_noalloc(q, w, kv, q, kv, kv, pos, ne, 4, 4)
     assert e.value.status == 2 and "4097" in e.value.message
+
+
+def test_noalloc_many_query_rows():
+    """Many query rows per sequence (the prefill score kernel: 8 queries and
+    4096 keys per workgroup, blocks loaded straight into LDS) through the
+    allocation-free step, against the workspace step; two calls in a row,
+    the second smaller."""
+    bf = torch.bfloat16
+    for B, Tq, N, k, seed in ((2, 37, 9000, 512, 800), (1, 12, 3000, 256, 900)):
+        _say(f"noalloc: B={B} Tq={Tq} N={N} k={k} (prefill score kernel)")
+        c = dict(q=_randn((B, Tq, 64, 128), 3 / math.sqrt(128), bf, seed),
+                 kc=_randn((B, N, 128), 1 / math.sqrt(128), bf, seed + 1),
+                 vc=_randn((B, N, 128), 1 / math.sqrt(128), bf, seed + 2),
+                 qi=_randn((B, Tq, 64, 128), 1 / math.sqrt(128), bf, seed + 3),
+                 ki=_randn((B, N, 128), 1 / math.sqrt(128), bf, seed + 4),
+                 wi=_randn((B, Tq, 64), 1 / 8, torch.float32, seed + 5), qs=None, ks=None)
+        # causal positions across the cache, some seeing fewer than k entries
+        pos = [[4 * (N - 61 * t) + (t % 4) for t in range(Tq)] for _ in range(B)]
+        pos[0][-1] = 4 * (k // 2)
+        c["pos"] = torch.tensor(pos, dtype=torch.int32, device=DEV)
+        c["ne"] = torch.tensor([N - 101 * b for b in range(B)], dtype=torch.int32, device=DEV)
+        lse = torch.empty((B, Tq, 64), dtype=torch.float32, device=DEV)
+        idx = torch.empty((B, Tq, k), dtype=torch.int32, device=DEV)
+        o = csa.index_topk_attend_noalloc(c["qi"], c["wi"], c["ki"], c["q"], c["kc"], c["vc"],
+                                          c["pos"], c["ne"], 4, k, lse=lse, idx_out=idx)
+        o2, lse2, idx2 = csa.index_topk_attend(c["qi"], c["wi"], c["ki"], c["q"], c["kc"],
+                                               c["vc"], c["pos"], c["ne"], 4, k, with_lse=True,
+                                               with_idx=True)
+        torch.cuda.synchronize()
+        _same((o, lse, idx), (o2, lse2, idx2), f"Tq={Tq}")
+        I, Q, K, Vv, O = (np64(t) for t in (idx, c["q"], c["kc"], c["vc"], o))
+        QI, KI, W = np64(c["qi"]), np64(c["ki"]), np64(c["wi"])
+        ne = c["ne"].cpu().numpy()
+        for b, t in ((0, 0), (0, Tq - 1), (B - 1, Tq // 2)):
+            Vis = oracle.visible_count(pos[b][t], 4, int(ne[b]))
+            check_topk(I[b, t], oracle.index_scores(QI[b, t], W[b, t], KI[b], Vis), Vis, k)
+            o_ref, _ = oracle.attend(Q[b, t], K[b], Vv[b], I[b, t])
+            check_attention(O[b, t], o_ref, "bf16", f"noalloc b={b} t={t}")

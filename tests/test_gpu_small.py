@@ -1023,3 +1023,36 @@ def test_batch_invariance_and_determinism():
         assert torch.equal(x, y)
     for x, y, z in zip(r1, r3, r4):
         assert torch.equal(x[:1], y[:1]) and torch.equal(x[:1], z)
+
+
+@pytest.mark.parametrize("B,Tq,N_max", [(3, 9, 70), (2, 16, 300), (1, 8, 1)])
+def test_prefill_kernel_tiny_and_empty(B, Tq, N_max):
+    """The prefill score kernel (Tq >= 8) on caches shorter than one 256-key
+    block and one 32-key tile, with an empty sequence, queries that see
+    nothing and a partially valid cache: scores (-inf past the visible
+    entries), and the selection with k above and below the visible count."""
+    _say(f"prefill kernel tiny: B={B} Tq={Tq} N_max={N_max}")
+    m = 4
+    qi = _randn((B, Tq, 64, 128), 1 / math.sqrt(128), torch.bfloat16, 60 + B)
+    ki = _randn((B, N_max, 128), 1 / math.sqrt(128), torch.bfloat16, 61 + B)
+    wi = _randn((B, Tq, 64), 1 / 8, torch.float32, 62 + B)
+    pos = [[(7 * t * t + 3 * b) % (4 * N_max + 9) for t in range(Tq)] for b in range(B)]
+    pos[0][0] = -1
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=DEV)
+    ne = [N_max, 0, max(N_max // 2, 1)][:B]
+    n_ent = torch.tensor(ne, dtype=torch.int32, device=DEV)
+    scores = csa.index_score(qi, wi, ki, q_pos, n_ent, m)
+    for k in (1, 16):
+        idx = csa.index_topk(qi, wi, ki, q_pos, n_ent, m, k)
+        torch.cuda.synchronize()
+        S, I = np64(scores), np64(idx)
+        QI, KI, W = np64(qi), np64(ki), np64(wi)
+        for b in range(B):
+            for t in range(Tq):
+                V = oracle.visible_count(pos[b][t], m, ne[b])
+                s_ref = oracle.index_scores(QI[b, t], W[b, t], KI[b], V)
+                assert np.all(np.isneginf(S[b, t, V:])), (b, t, V)
+                if V:
+                    bound = score_bound(QI[b, t], W[b, t], KI[b, :V], 128, 64)
+                    assert np.all(np.abs(S[b, t, :V] - s_ref[:V]) <= bound), (b, t, V)
+                check_topk(I[b, t], s_ref, V, k)
